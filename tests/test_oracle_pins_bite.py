@@ -1,0 +1,116 @@
+"""The pins must fail when a plausible mistake is planted in the oracle (CPU only).
+
+Each case swaps one oracle function for a subtly wrong version (a transposed
+factor, a dropped zero-point widening, floor instead of round-half-even, a
+sum instead of a mean, an ascending sort, a wrong sign) and checks that at
+least one pin from test_oracle_pins.py then fails.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import exact_obs
+from oracle import gptq_oracle as go
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _hand_cases_pass():
+    with open(os.path.join(GOLDEN, "hand_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        H = np.array(case["H"], dtype=np.float64)
+        W = np.array(case["W"], dtype=np.float64)
+        out = go.gptq_layer(W, H, None, case["bits"], case["group_size"], case["sym"],
+                            desc_act=False, damp_percent=0.0)
+        if out["codes"].tolist() != case["codes"]:
+            return False
+        if not np.allclose(out["loss0"], case["loss0"], rtol=1e-12):
+            return False
+    return True
+
+
+def _exact_route_passes():
+    for seed in range(12):
+        rng = np.random.default_rng(seed)
+        n, m = 4, 2
+        A = rng.integers(-4, 5, size=(n, n + 2)).astype(np.float64)
+        H = A @ A.T + np.eye(n)
+        W = np.round(rng.standard_normal((m, n)) * 0.5, 3)
+        key = np.diag(H).copy()
+        out = go.gptq_layer(W, H, key, 3, 2, False, desc_act=True, damp_percent=0.01)
+        lam = 0.01 * float(np.mean(key))
+        order = sorted(range(n), key=lambda j: (-H[j, j], j))
+        Hd = [[Fraction(float(H[i, j])) + (Fraction(lam) if i == j else 0) for j in order] for i in order]
+        Wp = [[Fraction(float(W[r, j])) for j in order] for r in range(m)]
+        codes, _, _, loss = exact_obs.gptq_exact(Wp, Hd, 3, 2, False)
+        if out["codes_p"].tolist() != codes or not np.isclose(out["loss0"], float(loss), rtol=1e-9):
+            return False
+    return True
+
+
+def _wrong_factor_lower(Hp):
+    U = _orig["inverse_upper_factor"](Hp)
+    return U.T.copy()            # lower factor handed out as if it were U
+
+
+def _wrong_factor_transposed_solve(Hp):
+    L = np.linalg.cholesky(np.asarray(Hp, dtype=np.float64))
+    return L.T.copy()            # chol(H) instead of chol(H^-1)
+
+
+def _no_widening(v, bits, sym):
+    if sym:
+        return _orig["group_params"](v, bits, sym)
+    lo, hi = np.min(v, axis=1), np.max(v, axis=1)
+    s = np.maximum((hi - lo) / (2 ** bits - 1), go.SCALE_FLOOR)
+    return s, np.round(-lo / s)
+
+
+def _floor_codes(w, s, z, bits, sym):
+    if sym:
+        q = 2 ** (bits - 1) - 1
+        return np.clip(np.floor(w / s), -q, q) + z
+    return np.clip(np.floor(w / s + z), 0, 2 ** bits - 1)
+
+
+def _damping_sum(key, p):
+    return float(p) * float(np.sum(key))
+
+
+def _ascending(key, desc_act):
+    if not desc_act:
+        return np.arange(len(key))
+    return np.argsort(np.asarray(key), kind="stable")
+
+
+def _wrong_sign_dequant(q, s, z):
+    return (z - np.asarray(q, dtype=np.float64)) * s
+
+
+_orig = {name: getattr(go, name) for name in
+         ("inverse_upper_factor", "group_params", "quantize_values", "damping", "act_order",
+          "dequantize_values")}
+
+PLANTS = [
+    ("inverse_upper_factor", _wrong_factor_lower),
+    ("inverse_upper_factor", _wrong_factor_transposed_solve),
+    ("group_params", _no_widening),
+    ("quantize_values", _floor_codes),
+    ("damping", _damping_sum),
+    ("act_order", _ascending),
+    ("dequantize_values", _wrong_sign_dequant),
+]
+
+
+def test_unplanted_oracle_passes_the_checks():
+    assert _hand_cases_pass() and _exact_route_passes()
+
+
+@pytest.mark.parametrize("name,fn", PLANTS, ids=[f"{n}:{f.__name__}" for n, f in PLANTS])
+def test_planted_mistake_is_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(go, name, fn)
+    assert not (_hand_cases_pass() and _exact_route_passes())
