@@ -1,0 +1,169 @@
+/*
+ * gptq_mi355x.h -- C ABI of the MI355X (gfx950) GPTQ layer-quantization path.
+ *
+ * The path has the three calls of the GPTQ quantizer sketched on the page
+ * "模型量化实战：从 INT8 PTQ 到 GPTQ 的精度保持与推理加速全解析" (qwbw.cn), §3.2
+ * (accumulate_hessian -> prepare -> quantize), with the quantize_config fields
+ * {bits, group_size, damp_percent, desc_act} of the page "Llama-2 GPTQ
+ * quantization in practice" (mjmagnets.cn), §3.3, and sym of the page
+ * "GPTQ量化损失深度解析" (bmjup.com).
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE memory owned by the caller (allocated
+ *     through PyTorch or hipMalloc).  The library keeps no allocation and no
+ *     global state besides a thread-local error message.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     on it in order; calls return after enqueueing, except where a call says
+ *     it synchronises.
+ *   - Argument errors are detected on the host and returned before anything
+ *     is launched.  A failed HIP launch or copy returns GPTQ_ERR_HIP.
+ *   - Matrices are row-major.  n = in_features (columns of W, size of H),
+ *     m = out_features (rows of W), tokens = calibration rows of X.
+ *   - gptq_last_error() returns a message for the last non-OK status of the
+ *     calling thread (empty string if none).
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad stride      */
+  GPTQ_ERR_UNSUPPORTED = -2, /* bits/group/block/dtype outside what is built */
+  GPTQ_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required   */
+  GPTQ_ERR_NOT_PD = -4,      /* damped Hessian not positive definite         */
+  GPTQ_ERR_NONFINITE = -5,   /* NaN/Inf in the Hessian diagonal or in W      */
+  GPTQ_ERR_HIP = -6          /* a HIP runtime call failed                    */
+} gptq_status;
+
+typedef enum { GPTQ_BF16 = 0, GPTQ_FP32 = 1 } gptq_dtype;
+
+/* Quantizer settings (the quantize_config of the pages, plus sym).
+ *   bits         2, 3, 4 or 8.
+ *   group_size   a power of two dividing block_size (1..128), or -1 for one
+ *                group per output row.  Groups are runs of group_size
+ *                consecutive columns in PROCESSING order (after desc_act).
+ *   sym          0: asymmetric grid with a zero point; 1: symmetric grid.
+ *   desc_act     1: process columns by descending Hessian diagonal.
+ *   block_size   columns per lazy-update block; must be 128.
+ *   damp_percent read by gptq_prepare_hinv only (lambda = damp_percent *
+ *                mean(diag H)); ignored here.                              */
+typedef struct {
+  int32_t bits;
+  int32_t group_size;
+  int32_t sym;
+  int32_t desc_act;
+  int32_t block_size;
+  float damp_percent;
+} gptq_config;
+
+/* ------------------------------------------------------------------------
+ * Stage 1 -- Hessian accumulation.
+ * Defines: H = 2·XᵀX summed over calibration tokens (page "模型量化实战…"
+ * §3.2, accumulate_hessian; the page "Llama-2 GPTQ quantization in practice"
+ * §2.2.1 writes the same matrix as the expectation of x⊗x).
+ *
+ *   H          [n, n] fp32, in/out.  ACCUMULATED: the caller zeroes H (and
+ *              diag_key) once, then calls once per token tile.  On return
+ *              both triangles hold H + alpha·XᵀX (H stays symmetric); the
+ *              kernels read only the lower triangle of the incoming H.
+ *   diag_key   [n] fp64, in/out, accumulated like H: key += alpha·Σ_t x_t²,
+ *              summed in fp64 so that the act-order sort is exact enough.
+ *              May be NULL.
+ *   X          [tokens, ldx] of x_dtype (GPTQ_BF16 or GPTQ_FP32), token-
+ *              major (row t = one token's n activations).  ldx >= n.
+ *              tokens == 0 is a no-op.
+ *   alpha      scale of the product (2.0 gives H = 2·XᵀX).
+ *   workspace  device scratch of at least gptq_hessian_workspace_bytes(n,
+ *              tokens, x_dtype) bytes (split-K partial tiles and counters);
+ *              may be NULL when that size is 0.  Its contents are not kept.
+ * Deterministic: the same inputs give bitwise the same H.
+ * ---------------------------------------------------------------------- */
+size_t gptq_hessian_workspace_bytes(int64_t n, int64_t tokens, int32_t x_dtype);
+gptq_status gptq_hessian_accumulate(float* H, double* diag_key, int64_t n, const void* X,
+                                    int32_t x_dtype, int64_t tokens, int64_t ldx, float alpha,
+                                    void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stages 2-3 -- damping, act-order and the inverse factor.
+ * Defines: H += damp·mean(diag H)·I, then the upper Cholesky factor of the
+ * inverse (page "模型量化实战…" §3.2, prepare: damping, Cholesky, inverse,
+ * upper Cholesky -- the factorisation is taken once); desc_act orders the
+ * columns by the Hessian diagonal (page "GPTQ量化损失深度解析", tuning
+ * section; page "Qwen2.5模型GPTQ量化精度损失实测" on act-order reordering).
+ *
+ *   H_inout    [n, n] fp32.  In: the symmetric H from stage 1 (un-permuted).
+ *              Out: U, upper triangular with positive diagonal and
+ *              UᵀU = (P (H + λI) Pᵀ)⁻¹ in PROCESSING order; the strictly
+ *              lower triangle is set to 0.
+ *   diag_key   [n] fp64 sort key and damping mean (stage 1's diag_key), or
+ *              NULL to use diag(H) in fp32.
+ *   desc_act   1: perm = stable descending sort of the key (ties keep the
+ *              lower original index first); 0: identity.
+ *   perm_out   [n] int32, out: perm_out[p] = original column processed at
+ *              position p.
+ *   workspace  at least gptq_prepare_workspace_bytes(n) bytes.
+ *   damp_out   HOST pointer, may be NULL: receives λ (fp64).
+ * Synchronises `stream` once at the end, to return GPTQ_ERR_NONFINITE (a NaN
+ * or Inf on the Hessian diagonal) or GPTQ_ERR_NOT_PD (a non-positive pivot);
+ * H_inout then holds no usable factor.  n == 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+size_t gptq_prepare_workspace_bytes(int64_t n);
+gptq_status gptq_prepare_hinv(float* H_inout, const double* diag_key, int64_t n,
+                              float damp_percent, int32_t desc_act, int32_t* perm_out,
+                              void* workspace, size_t ws_bytes, double* damp_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 4-5 -- block-wise column quantization with error feedback, then
+ * packing.  Defines: column by column in processing order, each output row's
+ * weight is rounded to the row's group grid and the rounding error is pushed
+ * onto the not-yet-quantized columns through the inverse factor (page
+ * "大模型量化：GPTQ/AWQ/GGUF 原理对比", GPTQ section and its column-flow
+ * description; page "模型量化实战…" §3.2 quantize_block); the grid is the
+ * affine x_q = round(x/scale + zero) of that page's §2.1/§3.1.
+ *
+ *   W        [m, n] of w_dtype, row-major (nn.Linear layout), read only.
+ *   U, perm  outputs of gptq_prepare_hinv for this layer's H.
+ *   cfg      see gptq_config (block_size must be 128).
+ * Outputs, all in ORIGINAL column order where columns appear:
+ *   qweight  [m, gptq_qweight_words(n, bits)] uint32.  bits <= 4: eight
+ *            codes per word, column 8w+i in bits [4i, 4i+4); bits == 8: four
+ *            codes per word, column 4w+i in bits [8i, 8i+8).  Last word of a
+ *            row zero-padded.
+ *   scales   [m, G] fp32, G = gptq_num_groups(n, group_size), group order.
+ *   zeros    [m, G] int32.  Dequantization is always (q - zero)·scale; a
+ *            symmetric grid stores codes offset by 2^(bits-1) and zero =
+ *            2^(bits-1).
+ *   g_idx    [n] int32: group of each original column (p // group_size for
+ *            the column processed at position p; 0 when group_size == -1).
+ *   loss     [2] fp64 device: loss[0] = ½·Σ e² over all columns, which
+ *            equals ½·tr(ΔW (H+λI) ΔWᵀ); loss[1] = ‖W − Ŵ‖²_F.  The
+ *            reconstruction loss ‖ΔW Xᵀ‖²_F = loss[0] − (λ/2)·loss[1].
+ *   workspace at least gptq_quantize_workspace_bytes(m, n, cfg) bytes.
+ * Synchronises `stream` once at the end to return GPTQ_ERR_NONFINITE if W
+ * holds a NaN or Inf.  m == 0 or n == 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+size_t gptq_quantize_workspace_bytes(int64_t m, int64_t n, const gptq_config* cfg);
+gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t m, int64_t n,
+                                const float* U, const int32_t* perm, const gptq_config* cfg,
+                                uint32_t* qweight, float* scales, int32_t* zeros, int32_t* g_idx,
+                                double* loss, void* workspace, size_t ws_bytes, void* stream);
+
+/* Sizes of the outputs above (host-only helpers, no GPU work). */
+int64_t gptq_qweight_words(int64_t n, int32_t bits);
+int64_t gptq_num_groups(int64_t n, int32_t group_size);
+
+/* Message of the calling thread's last non-OK status. */
+const char* gptq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_MI355X_H */

@@ -1,0 +1,20 @@
+"""MI355X (gfx950) GPTQ layer quantization: Hessian accumulation, the damped
+inverse factor with act-order, and block-wise column quantization with error
+feedback, all in hand-written HIP kernels behind a C ABI
+(include/gptq_mi355x.h).  This package is the thin Python binding."""
+from ._lib import GPTQ_BF16, GPTQ_FP32, LIB_PATH, lib  # noqa: F401
+from .gptq import (  # noqa: F401
+    GptqError,
+    QuantConfig,
+    alloc_outputs,
+    gptq_hessian_accumulate,
+    gptq_hessian_workspace_bytes,
+    gptq_last_error,
+    gptq_num_groups,
+    gptq_prepare_hinv,
+    gptq_prepare_workspace_bytes,
+    gptq_quantize_layer,
+    gptq_quantize_workspace_bytes,
+    gptq_qweight_words,
+    quantize_layer,
+)

@@ -1,0 +1,172 @@
+// extern "C" entry points of libgptq_mi355x: argument validation on the host,
+// workspace layout, then the stage launchers (hessian.hip, prepare.hip,
+// quantize.hip).  Every check here runs before any HIP call, so a rejected
+// call touches no GPU state.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "gptq_internal.hpp"
+
+namespace gptq {
+namespace {
+thread_local char g_err[512] = {0};
+}
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+void clear_error() { g_err[0] = 0; }
+
+namespace {
+constexpr int64_t kMaxN = 131072;
+
+gptq_status fail(gptq_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool bad_ptr(const void* p, size_t align) {
+  return p == nullptr || (reinterpret_cast<uintptr_t>(p) % align) != 0;
+}
+
+gptq_status check_config(const gptq_config* cfg) {
+  if (!cfg) return fail(GPTQ_ERR_INVALID_ARG, "cfg is NULL");
+  if (!(cfg->bits == 2 || cfg->bits == 3 || cfg->bits == 4 || cfg->bits == 8))
+    return fail(GPTQ_ERR_UNSUPPORTED, "bits=%d (built: 2, 3, 4, 8)", cfg->bits);
+  if (cfg->block_size != kQBlock)
+    return fail(GPTQ_ERR_UNSUPPORTED, "block_size=%d (built: 128)", cfg->block_size);
+  const int g = cfg->group_size;
+  if (!(g == -1 || g == 8 || g == 16 || g == 32 || g == 64 || g == 128))
+    return fail(GPTQ_ERR_UNSUPPORTED, "group_size=%d (built: -1, 8, 16, 32, 64, 128)", g);
+  if (cfg->sym != 0 && cfg->sym != 1) return fail(GPTQ_ERR_INVALID_ARG, "sym=%d", cfg->sym);
+  if (cfg->desc_act != 0 && cfg->desc_act != 1)
+    return fail(GPTQ_ERR_INVALID_ARG, "desc_act=%d", cfg->desc_act);
+  return GPTQ_OK;
+}
+}  // namespace
+}  // namespace gptq
+
+using namespace gptq;
+
+extern "C" {
+
+const char* gptq_last_error(void) { return g_err; }
+
+int64_t gptq_qweight_words(int64_t n, int32_t bits) {
+  if (n < 0) return -1;
+  if (bits == 2 || bits == 3 || bits == 4) return ceil_div(n, 8);
+  if (bits == 8) return ceil_div(n, 4);
+  return -1;
+}
+
+int64_t gptq_num_groups(int64_t n, int32_t group_size) {
+  if (n < 0) return -1;
+  if (group_size == -1) return n > 0 ? 1 : 0;
+  if (group_size <= 0) return -1;
+  return ceil_div(n, group_size);
+}
+
+size_t gptq_hessian_workspace_bytes(int64_t n, int64_t tokens, int32_t x_dtype) {
+  if (n <= 0 || n > kMaxN || tokens < 0) return 0;
+  if (x_dtype != GPTQ_BF16) return 0;
+  return plan_syrk_bf16(n, tokens).total_bytes;
+}
+
+gptq_status gptq_hessian_accumulate(float* H, double* diag_key, int64_t n, const void* X,
+                                    int32_t x_dtype, int64_t tokens, int64_t ldx, float alpha,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (n <= 0) return fail(GPTQ_ERR_INVALID_ARG, "n=%lld must be positive", (long long)n);
+  if (n > kMaxN) return fail(GPTQ_ERR_UNSUPPORTED, "n=%lld above %lld", (long long)n, (long long)kMaxN);
+  if (tokens < 0) return fail(GPTQ_ERR_INVALID_ARG, "tokens=%lld", (long long)tokens);
+  if (x_dtype != GPTQ_BF16 && x_dtype != GPTQ_FP32)
+    return fail(GPTQ_ERR_UNSUPPORTED, "x_dtype=%d", x_dtype);
+  if (bad_ptr(H, 4)) return fail(GPTQ_ERR_INVALID_ARG, "H is NULL or misaligned");
+  if (diag_key && bad_ptr(diag_key, 8)) return fail(GPTQ_ERR_INVALID_ARG, "diag_key misaligned");
+  if (!std::isfinite(alpha)) return fail(GPTQ_ERR_INVALID_ARG, "alpha not finite");
+  if (tokens == 0) return GPTQ_OK;
+  if (ldx < n) return fail(GPTQ_ERR_INVALID_ARG, "ldx=%lld < n=%lld", (long long)ldx, (long long)n);
+  if (bad_ptr(X, x_dtype == GPTQ_BF16 ? 2 : 4)) return fail(GPTQ_ERR_INVALID_ARG, "X is NULL or misaligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (x_dtype == GPTQ_FP32)
+    return launch_hessian_f32(H, diag_key, n, static_cast<const float*>(X), tokens, ldx, alpha, s);
+  const SyrkPlan plan = plan_syrk_bf16(n, tokens);
+  if (plan.total_bytes > 0 && (workspace == nullptr || ws_bytes < plan.total_bytes || bad_ptr(workspace, 256)))
+    return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu (256-byte aligned)", ws_bytes,
+                plan.total_bytes);
+  return launch_hessian_bf16(H, diag_key, n, static_cast<const uint16_t*>(X), tokens, ldx, alpha,
+                             workspace, plan, s);
+}
+
+size_t gptq_prepare_workspace_bytes(int64_t n) {
+  if (n <= 0 || n > kPrepareMaxN) return 0;
+  return plan_prepare(n).total;
+}
+
+gptq_status gptq_prepare_hinv(float* H_inout, const double* diag_key, int64_t n,
+                              float damp_percent, int32_t desc_act, int32_t* perm_out,
+                              void* workspace, size_t ws_bytes, double* damp_out, void* stream) {
+  clear_error();
+  if (n < 0) return fail(GPTQ_ERR_INVALID_ARG, "n=%lld", (long long)n);
+  if (n == 0) return GPTQ_OK;
+  if (n > kPrepareMaxN)
+    return fail(GPTQ_ERR_UNSUPPORTED, "n=%lld above %lld", (long long)n, (long long)kPrepareMaxN);
+  if (bad_ptr(H_inout, 4)) return fail(GPTQ_ERR_INVALID_ARG, "H_inout is NULL or misaligned");
+  if (diag_key && bad_ptr(diag_key, 8)) return fail(GPTQ_ERR_INVALID_ARG, "diag_key misaligned");
+  if (bad_ptr(perm_out, 4)) return fail(GPTQ_ERR_INVALID_ARG, "perm_out is NULL or misaligned");
+  if (desc_act != 0 && desc_act != 1) return fail(GPTQ_ERR_INVALID_ARG, "desc_act=%d", desc_act);
+  if (!std::isfinite(damp_percent) || damp_percent < 0.f)
+    return fail(GPTQ_ERR_INVALID_ARG, "damp_percent=%g", (double)damp_percent);
+  const PreparePlan plan = plan_prepare(n);
+  if (workspace == nullptr || ws_bytes < plan.total || bad_ptr(workspace, 256))
+    return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu (256-byte aligned)", ws_bytes,
+                plan.total);
+  return run_prepare(H_inout, diag_key, n, damp_percent, desc_act, perm_out, workspace, plan,
+                     damp_out, static_cast<hipStream_t>(stream));
+}
+
+size_t gptq_quantize_workspace_bytes(int64_t m, int64_t n, const gptq_config* cfg) {
+  if (m <= 0 || n <= 0 || n > kPrepareMaxN || check_config(cfg) != GPTQ_OK) {
+    clear_error();
+    return 0;
+  }
+  return plan_quantize(m, n, *cfg).total;
+}
+
+gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t m, int64_t n,
+                                const float* U, const int32_t* perm, const gptq_config* cfg,
+                                uint32_t* qweight, float* scales, int32_t* zeros, int32_t* g_idx,
+                                double* loss, void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (m < 0 || n < 0) return fail(GPTQ_ERR_INVALID_ARG, "m=%lld n=%lld", (long long)m, (long long)n);
+  gptq_status st = check_config(cfg);
+  if (st != GPTQ_OK) return st;
+  if (w_dtype != GPTQ_BF16 && w_dtype != GPTQ_FP32)
+    return fail(GPTQ_ERR_UNSUPPORTED, "w_dtype=%d", w_dtype);
+  if (m == 0 || n == 0) return GPTQ_OK;
+  if (n > kPrepareMaxN)
+    return fail(GPTQ_ERR_UNSUPPORTED, "n=%lld above %lld", (long long)n, (long long)kPrepareMaxN);
+  if (m > (int64_t)1 << 24) return fail(GPTQ_ERR_UNSUPPORTED, "m=%lld too large", (long long)m);
+  if (bad_ptr(W, w_dtype == GPTQ_BF16 ? 2 : 4)) return fail(GPTQ_ERR_INVALID_ARG, "W is NULL or misaligned");
+  if (bad_ptr(U, 4)) return fail(GPTQ_ERR_INVALID_ARG, "U is NULL or misaligned");
+  if (bad_ptr(perm, 4)) return fail(GPTQ_ERR_INVALID_ARG, "perm is NULL or misaligned");
+  if (bad_ptr(qweight, 4) || bad_ptr(scales, 4) || bad_ptr(zeros, 4) || bad_ptr(g_idx, 4))
+    return fail(GPTQ_ERR_INVALID_ARG, "an output pointer is NULL or misaligned");
+  if (bad_ptr(loss, 8)) return fail(GPTQ_ERR_INVALID_ARG, "loss is NULL or misaligned");
+  const QuantPlan plan = plan_quantize(m, n, *cfg);
+  if (workspace == nullptr || ws_bytes < plan.total || bad_ptr(workspace, 256))
+    return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu (256-byte aligned)", ws_bytes,
+                plan.total);
+  return run_quantize(W, w_dtype, m, n, U, perm, *cfg, qweight, scales, zeros, g_idx, loss,
+                      workspace, plan, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

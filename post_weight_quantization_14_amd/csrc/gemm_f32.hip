@@ -1,0 +1,305 @@
+// fp32 MFMA GEMM tiles for gfx950: C = alpha * A * B + beta * C.
+//
+// Used by the blocked Cholesky (panel solve and trailing update), the blocked
+// triangular inverse and the lazy trailing update of the column quantizer.
+// All three are dense fp32 contractions, so they run on v_mfma_f32_32x32x2f32.
+//
+// Tile: 128 x 128 outputs per workgroup of 256 threads (4 waves in 2 x 2);
+// each wave owns 64 x 64 = 2 x 2 MFMA blocks of 32 x 32.  K is staged through
+// LDS 32 at a time, double buffered, with the next stage's global loads in
+// flight while the current one feeds the MFMAs.
+//
+// LDS layouts (floats):
+//   A (row-major source)      [128 rows][34]  -> lane reads (row, k): bank
+//                              34*row + k covers 64 distinct banks per wave.
+//   B row-major source        [32 k][160]     -> bank 32*k + col: distinct.
+//   B column-major source     [128 cols][34]  -> same as A.
+#include "gptq_internal.hpp"
+
+namespace gptq {
+namespace {
+
+constexpr int GT = 128;
+constexpr int GK = 32;
+constexpr int PA = GK + 2;   // row-major tile pitch
+constexpr int PB = GT + 32;  // k-major tile pitch
+constexpr int SA = GT * PA;
+constexpr int SB = (GT * PA > GK * PB) ? GT * PA : GK * PB;
+
+struct GemmSmem {
+  float a[2][SA];
+  float b[2][SB];
+};
+
+// base[row * ld + col + e] for e < 4, zero outside row < row_lim, col + e < col_lim.
+template <bool VEC>
+__device__ __forceinline__ f32x4_t load4(const float* __restrict__ base, int64_t row, int64_t ld,
+                                         int64_t col, int64_t row_lim, int64_t col_lim) {
+  f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+  if (row < row_lim && col < col_lim) {
+    const float* p = base + row * ld + col;
+    if (VEC && col + 4 <= col_lim) {
+      v = *reinterpret_cast<const f32x4_t*>(p);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (col + e < col_lim) v[e] = p[e];
+    }
+  }
+  return v;
+}
+
+// Accumulate one 128 x 128 tile over k in [k_begin, k_end).
+//   A: tile row 0, k = 0 of a row-major [rows x K] operand (lda); rows < a_rows valid.
+//   B: row-major -> points at k = 0, tile column 0 (ldb); column-major -> points at
+//      tile column 0, k = 0 with B[k][j] = B[j * ldb + k].  Columns < b_cols valid.
+template <bool BCOL, bool VEC>
+__device__ __forceinline__ void gemm_tile_acc(const float* __restrict__ A, int64_t lda,
+                                              int64_t a_rows, const float* __restrict__ B,
+                                              int64_t ldb, int64_t b_cols, int64_t k_begin,
+                                              int64_t k_end, GemmSmem& sm, f32x16_t (&acc)[2][2]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int li = lane & 31, lk = lane >> 5;
+
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[bi][bj][v] = 0.f;
+
+  if (k_end <= k_begin) return;
+  const int64_t nst = (k_end - k_begin + GK - 1) / GK;
+
+  f32x4_t ra[4], rb[4];
+  auto gload = [&](int64_t k0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int f = tid + 256 * u;
+      ra[u] = load4<VEC>(A, f >> 3, lda, k0 + 4 * (f & 7), a_rows, k_end);
+      if (BCOL)
+        rb[u] = load4<VEC>(B, f >> 3, ldb, k0 + 4 * (f & 7), b_cols, k_end);
+      else
+        rb[u] = load4<VEC>(B, k0 + (f >> 5), ldb, 4 * (f & 31), k_end, b_cols);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int f = tid + 256 * u;
+      float* pa = &sm.a[buf][(f >> 3) * PA + 4 * (f & 7)];
+      pa[0] = ra[u][0]; pa[1] = ra[u][1]; pa[2] = ra[u][2]; pa[3] = ra[u][3];
+      if (BCOL) {
+        float* pb = &sm.b[buf][(f >> 3) * PA + 4 * (f & 7)];
+        pb[0] = rb[u][0]; pb[1] = rb[u][1]; pb[2] = rb[u][2]; pb[3] = rb[u][3];
+      } else {
+        *reinterpret_cast<f32x4_t*>(&sm.b[buf][(f >> 5) * PB + 4 * (f & 31)]) = rb[u];
+      }
+    }
+  };
+
+  gload(k_begin);
+  sstore(0);
+  __syncthreads();
+  for (int64_t st = 0; st < nst; ++st) {
+    const int cur = (int)(st & 1);
+    if (st + 1 < nst) gload(k_begin + (st + 1) * GK);
+    const float* sa = sm.a[cur];
+    const float* sb = sm.b[cur];
+#pragma unroll
+    for (int kk = 0; kk < GK / 2; ++kk) {
+      const int k = 2 * kk + lk;
+      float af[2], bf[2];
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi) af[bi] = sa[(wr * 64 + bi * 32 + li) * PA + k];
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj)
+        bf[bj] = BCOL ? sb[(wc * 64 + bj * 32 + li) * PA + k] : sb[k * PB + wc * 64 + bj * 32 + li];
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+          acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[bi], bf[bj], acc[bi][bj], 0, 0, 0);
+    }
+    if (st + 1 < nst) sstore(cur ^ 1);
+    __syncthreads();
+  }
+}
+
+// C tile update.  Element (i, j) of the tile sits in lane j % 32 + 32 * ((i / 4) % 2),
+// register (i % 4) + 4 * (i / 8) of the 32 x 32 block (the MFMA output layout).
+template <bool LOWER>
+__device__ __forceinline__ void gemm_tile_store(float* __restrict__ C, int64_t ldc, int64_t c_rows,
+                                                int64_t c_cols, int64_t diag_off, float alpha,
+                                                float beta, const f32x16_t (&acc)[2][2]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int li = lane & 31, lk = lane >> 5;
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int i = wr * 64 + bi * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
+        const int j = wc * 64 + bj * 32 + li;
+        if (i < c_rows && j < c_cols && (!LOWER || i + diag_off >= j)) {
+          float* p = C + (int64_t)i * ldc + j;
+          const float x = alpha * acc[bi][bj][v];
+          *p = (beta == 0.f) ? x : x + beta * *p;
+        }
+      }
+}
+
+template <bool BCOL, bool VEC>
+__global__ __launch_bounds__(256) void gemm_rect_kernel(GemmArgs g) {
+  __shared__ GemmSmem sm;
+  const int64_t i0 = (int64_t)blockIdx.y * GT, j0 = (int64_t)blockIdx.x * GT;
+  const float* A = g.A + i0 * g.lda;
+  const float* B = BCOL ? g.B + j0 * g.ldb : g.B + j0;
+  f32x16_t acc[2][2];
+  const int64_t rows = g.M - i0 < GT ? g.M - i0 : GT;
+  const int64_t cols = g.N - j0 < GT ? g.N - j0 : GT;
+  gemm_tile_acc<BCOL, VEC>(A, g.lda, rows, B, g.ldb, cols, g.k_begin, g.k_end, sm, acc);
+  gemm_tile_store<false>(g.C + i0 * g.ldc + j0, g.ldc, rows, cols, 0, g.alpha, g.beta, acc);
+}
+
+__device__ __forceinline__ void tri_decode(int64_t t, int64_t& ti, int64_t& tj) {
+  int64_t r = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+  while (r * (r + 1) / 2 > t) --r;
+  while ((r + 1) * (r + 2) / 2 <= t) ++r;
+  ti = r;
+  tj = t - r * (r + 1) / 2;
+}
+
+template <bool BCOL, bool VEC>
+__global__ __launch_bounds__(256) void gemm_lower_kernel(GemmArgs g) {
+  __shared__ GemmSmem sm;
+  int64_t ti, tj;
+  tri_decode(blockIdx.x, ti, tj);
+  const int64_t i0 = ti * GT, j0 = tj * GT;
+  const float* A = g.A + i0 * g.lda;
+  const float* B = BCOL ? g.B + j0 * g.ldb : g.B + j0;
+  f32x16_t acc[2][2];
+  const int64_t rows = g.M - i0 < GT ? g.M - i0 : GT;
+  const int64_t cols = g.N - j0 < GT ? g.N - j0 : GT;
+  gemm_tile_acc<BCOL, VEC>(A, g.lda, rows, B, g.ldb, cols, g.k_begin, g.k_end, sm, acc);
+  gemm_tile_store<true>(g.C + i0 * g.ldc + j0, g.ldc, rows, cols, i0 - j0, g.alpha, g.beta, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Triangular inverse, one level of the bottom-up doubling.
+// M = L^{-1} for a lower-triangular L of nblk x nblk blocks of 128.  At the
+// level with `half` blocks per side, node p joins the inverses of blocks
+// [l0, l0+half) and [l0+half, r1) (r1 = min(l0 + 2 half, nblk)):
+//   step 1: T  = L21 * M11           (K restricted to M11's lower triangle)
+//   step 2: M21 = -M22 * T           (K restricted to M22's lower triangle)
+// T is parked, transposed, in the strictly upper block triangle of the
+// Cholesky buffer, which the factorisation never reads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void trtri_step1_kernel(float* Amat, const float* Mmat,
+                                                          int64_t lda, int64_t nblk, int64_t half) {
+  __shared__ GemmSmem sm;
+  const int64_t p = blockIdx.y;
+  const int64_t l0 = p * 2 * half, r0 = l0 + half;
+  const int64_t r1 = (l0 + 2 * half < nblk) ? l0 + 2 * half : nblk;
+  const int64_t ti = blockIdx.x / half, tj = blockIdx.x % half;
+  if (r0 + ti >= r1) return;
+  const float* A = Amat + (r0 + ti) * GT * lda + l0 * GT;           // L21 block row
+  const float* B = Mmat + l0 * GT * lda + l0 * GT + tj * GT;         // M11 column block
+  f32x16_t acc[2][2];
+  gemm_tile_acc<false, true>(A, lda, GT, B, lda, GT, tj * GT, half * GT, sm, acc);
+  // store T^T at rows (l0+tj) block, columns (r0+ti) block
+  float* Tt = Amat + (l0 + tj) * GT * lda + (r0 + ti) * GT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1, li = lane & 31, lk = lane >> 5;
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // registers 4q..4q+3 hold rows i..i+3 of column j: one 16-byte store
+        const int i = wr * 64 + bi * 32 + 8 * q + 4 * lk;
+        const int j = wc * 64 + bj * 32 + li;
+        f32x4_t v = {acc[bi][bj][4 * q], acc[bi][bj][4 * q + 1], acc[bi][bj][4 * q + 2],
+                     acc[bi][bj][4 * q + 3]};
+        *reinterpret_cast<f32x4_t*>(Tt + (int64_t)j * lda + i) = v;
+      }
+}
+
+__global__ __launch_bounds__(256) void trtri_step2_kernel(const float* Amat, float* Mmat,
+                                                          int64_t lda, int64_t nblk, int64_t half) {
+  __shared__ GemmSmem sm;
+  const int64_t p = blockIdx.y;
+  const int64_t l0 = p * 2 * half, r0 = l0 + half;
+  const int64_t r1 = (l0 + 2 * half < nblk) ? l0 + 2 * half : nblk;
+  const int64_t ti = blockIdx.x / half, tj = blockIdx.x % half;
+  if (r0 + ti >= r1) return;
+  const float* A = Mmat + (r0 + ti) * GT * lda + r0 * GT;                 // M22 block row
+  const float* Bt = Amat + (l0 + tj) * GT * lda + r0 * GT;                // T^T (column-major T)
+  f32x16_t acc[2][2];
+  gemm_tile_acc<true, true>(A, lda, GT, Bt, lda, GT, 0, (ti + 1) * GT, sm, acc);
+  gemm_tile_store<false>(Mmat + (r0 + ti) * GT * lda + l0 * GT + tj * GT, lda, GT, GT, 0, -1.f,
+                         0.f, acc);
+}
+
+bool vec_ok(const GemmArgs& g, bool bcol) {
+  auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  return al(g.A) && al(g.B) && (g.lda % 4 == 0) && (g.ldb % 4 == 0) && (g.k_begin % 4 == 0) &&
+         (bcol || true);
+}
+
+}  // namespace
+
+gptq_status launch_gemm_rect(const GemmArgs& g, bool b_colmajor, hipStream_t stream) {
+  if (g.M <= 0 || g.N <= 0) return GPTQ_OK;
+  dim3 grid((unsigned)ceil_div(g.N, GT), (unsigned)ceil_div(g.M, GT));
+  const bool v = vec_ok(g, b_colmajor);
+  if (b_colmajor) {
+    if (v) hipLaunchKernelGGL((gemm_rect_kernel<true, true>), grid, dim3(256), 0, stream, g);
+    else hipLaunchKernelGGL((gemm_rect_kernel<true, false>), grid, dim3(256), 0, stream, g);
+  } else {
+    if (v) hipLaunchKernelGGL((gemm_rect_kernel<false, true>), grid, dim3(256), 0, stream, g);
+    else hipLaunchKernelGGL((gemm_rect_kernel<false, false>), grid, dim3(256), 0, stream, g);
+  }
+  GPTQ_LAUNCH_CHECK();
+  return GPTQ_OK;
+}
+
+gptq_status launch_gemm_lower(const GemmArgs& g, bool b_colmajor, hipStream_t stream) {
+  if (g.M <= 0 || g.N <= 0) return GPTQ_OK;
+  const int64_t t = ceil_div(g.M, GT);
+  dim3 grid((unsigned)(t * (t + 1) / 2));
+  const bool v = vec_ok(g, b_colmajor);
+  if (b_colmajor) {
+    if (v) hipLaunchKernelGGL((gemm_lower_kernel<true, true>), grid, dim3(256), 0, stream, g);
+    else hipLaunchKernelGGL((gemm_lower_kernel<true, false>), grid, dim3(256), 0, stream, g);
+  } else {
+    if (v) hipLaunchKernelGGL((gemm_lower_kernel<false, true>), grid, dim3(256), 0, stream, g);
+    else hipLaunchKernelGGL((gemm_lower_kernel<false, false>), grid, dim3(256), 0, stream, g);
+  }
+  GPTQ_LAUNCH_CHECK();
+  return GPTQ_OK;
+}
+
+gptq_status launch_trtri_level(float* Amat, float* Mmat, int64_t lda, int64_t nblk, int64_t half,
+                               hipStream_t stream) {
+  const int64_t nodes = ceil_div(nblk - half, 2 * half);  // nodes with a right part
+  if (nodes <= 0) return GPTQ_OK;
+  dim3 grid((unsigned)(half * half), (unsigned)nodes);
+  hipLaunchKernelGGL(trtri_step1_kernel, grid, dim3(256), 0, stream, Amat, (const float*)Mmat, lda,
+                     nblk, half);
+  GPTQ_LAUNCH_CHECK();
+  hipLaunchKernelGGL(trtri_step2_kernel, grid, dim3(256), 0, stream, (const float*)Amat, Mmat, lda,
+                     nblk, half);
+  GPTQ_LAUNCH_CHECK();
+  return GPTQ_OK;
+}
+
+}  // namespace gptq

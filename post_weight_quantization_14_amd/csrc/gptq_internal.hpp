@@ -1,0 +1,115 @@
+// Internal declarations shared by the HIP translation units of libgptq_mi355x.
+// Device code targets gfx950 (CDNA4) only: wave64, MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "gptq_mi355x.h"
+
+namespace gptq {
+
+// ---------------------------------------------------------------- vectors
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+// ---------------------------------------------------------------- errors
+void set_error(const char* fmt, ...);
+void clear_error();
+
+#define GPTQ_HIP_CHECK(expr)                                                         \
+  do {                                                                               \
+    hipError_t _e = (expr);                                                          \
+    if (_e != hipSuccess) {                                                          \
+      ::gptq::set_error("%s failed: %s (%s:%d)", #expr, hipGetErrorString(_e),       \
+                        __FILE__, __LINE__);                                         \
+      return GPTQ_ERR_HIP;                                                           \
+    }                                                                                \
+  } while (0)
+
+#define GPTQ_LAUNCH_CHECK()                                                          \
+  do {                                                                               \
+    hipError_t _e = hipGetLastError();                                               \
+    if (_e != hipSuccess) {                                                          \
+      ::gptq::set_error("kernel launch failed: %s (%s:%d)", hipGetErrorString(_e),   \
+                        __FILE__, __LINE__);                                         \
+      return GPTQ_ERR_HIP;                                                           \
+    }                                                                                \
+  } while (0)
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------- Hessian (stage 1)
+constexpr int kSyrkTile = 256;      // output tile edge of the bf16 SYRK
+constexpr int kSyrkStage = 32;      // tokens per LDS stage
+constexpr int kSyrkMaxSliceTokens = 32768;  // fp32 register chains stay this short
+
+struct SyrkPlan {
+  int64_t panels = 0;   // ceil(n / 256)
+  int64_t tiles = 0;    // lower-triangle tiles
+  int64_t splits = 1;   // token slices (split-K)
+  int64_t slice_tokens = 0;
+  size_t partial_bytes = 0, keypart_bytes = 0, counter_bytes = 0;
+  size_t total_bytes = 0;
+};
+SyrkPlan plan_syrk_bf16(int64_t n, int64_t tokens);
+
+gptq_status launch_hessian_bf16(float* H, double* key, int64_t n, const uint16_t* X, int64_t tokens,
+                                int64_t ldx, float alpha, void* ws, const SyrkPlan& plan,
+                                hipStream_t stream);
+gptq_status launch_hessian_f32(float* H, double* key, int64_t n, const float* X, int64_t tokens,
+                               int64_t ldx, float alpha, hipStream_t stream);
+
+// ---------------------------------------------------------------- prepare (stages 2-3)
+constexpr int kNb = 128;            // panel / tile edge of the fp32 factorisations
+constexpr int64_t kPrepareMaxN = 40960;  // one row of H must fit in LDS (160 KB)
+
+struct PreparePlan {
+  int64_t n = 0, n_pad = 0, nblk = 0;
+  size_t a_off = 0, m_off = 0, lam_off = 0, flag_off = 0, total = 0;
+};
+PreparePlan plan_prepare(int64_t n);
+gptq_status run_prepare(float* H, const double* key, int64_t n, float damp, int desc_act,
+                        int32_t* perm, void* ws, const PreparePlan& plan, double* damp_out,
+                        hipStream_t stream);
+
+// ---------------------------------------------------------------- quantize (stages 4-5)
+constexpr int kQBlock = 128;
+
+struct QuantPlan {
+  int64_t m = 0, n = 0, ldw = 0, groups = 0, words = 0;
+  size_t wp_off = 0, part_off = 0, codes_off = 0, err_off = 0, loss_off = 0, inv_off = 0,
+         flag_off = 0, total = 0;
+};
+QuantPlan plan_quantize(int64_t m, int64_t n, const gptq_config& cfg);
+gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const float* U,
+                         const int32_t* perm, const gptq_config& cfg, uint32_t* qweight,
+                         float* scales, int32_t* zeros, int32_t* g_idx, double* loss, void* ws,
+                         const QuantPlan& plan, hipStream_t stream);
+
+// ---------------------------------------------------------------- fp32 MFMA GEMM (shared)
+// C[M,N] = alpha * A[M,K] * B[K,N] + beta * C, A row-major; B row-major or, with
+// b_colmajor, stored as B[k][j] = Bp[j * ldb + k].  Tiles of 128 x 128.
+struct GemmArgs {
+  const float* A; int64_t lda;
+  const float* B; int64_t ldb;
+  float* C; int64_t ldc;
+  int64_t M, N;
+  int64_t k_begin, k_end;
+  float alpha, beta;
+};
+gptq_status launch_gemm_rect(const GemmArgs& g, bool b_colmajor, hipStream_t stream);
+// Lower-triangular output tiles only (tile row >= tile column), M == N: the
+// trailing update of a right-looking Cholesky.
+gptq_status launch_gemm_lower(const GemmArgs& g, bool b_colmajor, hipStream_t stream);
+// One level of the blocked triangular inverse (see prepare.hip).
+gptq_status launch_trtri_level(float* Amat, float* Mmat, int64_t lda, int64_t nblk, int64_t half,
+                               hipStream_t stream);
+
+}  // namespace gptq

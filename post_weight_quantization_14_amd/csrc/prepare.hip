@@ -1,0 +1,375 @@
+// Stages 2-3: damping, act-order and the inverse factor U (UᵀU = H_p⁻¹).
+//
+// The page "模型量化实战：从 INT8 PTQ 到 GPTQ…" §3.2 (prepare) damps H by
+// 1% of its mean diagonal, factors it, inverts it and takes the upper
+// Cholesky factor of the inverse.  Here the same U is reached with half the
+// work: let J be the exchange matrix and H_f = J H_p J (the permuted matrix
+// read back to front).  With H_f = L Lᵀ (ordinary lower Cholesky) and
+// M = L⁻¹, H_p⁻¹ = (J M J)ᵀ (J M J), and J M J is upper triangular with a
+// positive diagonal, so it is the unique upper Cholesky factor of H_p⁻¹:
+//     U[i][j] = M[n-1-i][n-1-j].
+// Cost: n³/3 (Cholesky) + n³/3 (triangular inverse), both on fp32 MFMA.
+//
+// Data flow (all fp32, row-major, n_pad = n rounded up to 128):
+//   stats     : λ = p · mean(diag H) in fp64, non-finite check
+//   rank      : perm = stable descending order of the key (O(n²) ranks)
+//   permute   : A[a][b] = H[perm[n-1-a]][perm[n-1-b]] + λ δ_ab, identity pad
+//   cholesky  : per 128-column panel: leaf (factor + invert the diagonal
+//               block in LDS), panel solve as a GEMM with the leaf inverse,
+//               trailing update on lower tiles (all MFMA)
+//   trtri     : bottom-up doubling on the leaf inverses (2 GEMMs per level)
+//   flip      : U = J M J written over H, lower triangle zeroed
+#include <algorithm>
+
+#include "gptq_internal.hpp"
+
+namespace gptq {
+namespace {
+
+constexpr int NB = kNb;
+
+// flag bits
+constexpr int kFlagNotPD = 1;
+constexpr int kFlagNonFinite = 2;
+
+__device__ __forceinline__ double key_of(const double* key, const float* H, int64_t n, int64_t j) {
+  return key ? key[j] : (double)H[j * n + j];
+}
+
+// λ = damp * mean(diag); one workgroup, fixed reduction order.
+__global__ __launch_bounds__(1024) void stats_kernel(const double* key, const float* H, int64_t n,
+                                                     float damp, double* lam_out, int* flag) {
+  __shared__ double red[1024];
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  double s = 0.0;
+  int b = 0;
+  for (int64_t j = threadIdx.x; j < n; j += 1024) {
+    const double k = key_of(key, H, n, j);
+    if (!isfinite(k)) b = 1;
+    s += k;
+  }
+  red[threadIdx.x] = s;
+  if (b) atomicOr(&bad, 1);
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double mean = red[0] / (double)n;
+    *lam_out = (double)damp * mean;
+    if (bad || !isfinite(mean)) atomicOr(flag, kFlagNonFinite);
+  }
+}
+
+// perm[rank(j)] = j, rank = #{i: k_i > k_j} + #{i < j: k_i == k_j}.  NaN keys
+// sort as -inf, so the result is always a permutation.
+__global__ __launch_bounds__(256) void rank_kernel(const double* key, const float* H, int64_t n,
+                                                   int desc_act, int32_t* perm) {
+  __shared__ double ks[2048];
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (!desc_act) {
+    if (j < n) perm[j] = (int32_t)j;
+    return;
+  }
+  double kj = -INFINITY;
+  if (j < n) {
+    kj = key_of(key, H, n, j);
+    if (isnan(kj)) kj = -INFINITY;
+  }
+  int64_t rank = 0;
+  for (int64_t c0 = 0; c0 < n; c0 += 2048) {
+    __syncthreads();
+    for (int t = threadIdx.x; t < 2048; t += 256) {
+      const int64_t i = c0 + t;
+      double k = -INFINITY;
+      if (i < n) {
+        k = key_of(key, H, n, i);
+        if (isnan(k)) k = -INFINITY;
+      }
+      ks[t] = k;
+    }
+    __syncthreads();
+    const int64_t lim = std::min<int64_t>(2048, n - c0);
+    for (int64_t t = 0; t < lim; ++t) {
+      const double ki = ks[t];
+      const int64_t i = c0 + t;
+      rank += (ki > kj) || (ki == kj && i < j);
+    }
+  }
+  if (j < n) perm[rank] = (int32_t)j;
+}
+
+// One output row a of A = J P (H + λI) Pᵀ J, padded with the identity.
+__global__ __launch_bounds__(256) void permute_kernel(const float* __restrict__ H, int64_t n,
+                                                      const int32_t* __restrict__ perm,
+                                                      const double* lam, float* __restrict__ A,
+                                                      int64_t lda) {
+  extern __shared__ float row[];
+  const int64_t a = blockIdx.x;
+  float* out = A + a * lda;
+  if (a >= n) {
+    for (int64_t b = threadIdx.x; b < lda; b += 256) out[b] = (a == b) ? 1.f : 0.f;
+    return;
+  }
+  const int64_t src = perm[n - 1 - a];
+  const float* h = H + src * n;
+  for (int64_t b = threadIdx.x; b < n; b += 256) row[b] = h[b];
+  __syncthreads();
+  const float l = (float)*lam;
+  for (int64_t b = threadIdx.x; b < lda; b += 256) {
+    float v = 0.f;
+    if (b < n) {
+      v = row[perm[n - 1 - b]];
+      if (b == a) v += l;
+    }
+    out[b] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Leaf: Cholesky of the 128 x 128 diagonal block at (k0, k0), then its inverse.
+// Thread t < 136 owns the t-th lower 8 x 8 sub-block in registers; columns
+// (factorisation) and rows (inversion) are broadcast through LDS, one barrier
+// per step.  Writes L back into A and D = L⁻¹ into the same block of Mmat
+// (strict upper part of that block set to 0).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void sub_decode(int t, int& bi, int& bj) {
+  int r = 0;
+  while ((r + 1) * (r + 2) / 2 <= t) ++r;
+  bi = r;
+  bj = t - r * (r + 1) / 2;
+}
+
+__global__ __launch_bounds__(256) void chol_leaf_kernel(float* A, float* Mm, int64_t lda, int64_t k0,
+                                                        int* flag) {
+  __shared__ float colb[2][NB];
+  __shared__ float Ls[NB][NB + 1];
+  const int tid = threadIdx.x;
+  const bool owner = tid < 136;
+  int bi = 0, bj = 0;
+  if (owner) sub_decode(tid, bi, bj);
+  float* Ab = A + k0 * lda + k0;
+  float* Mb = Mm + k0 * lda + k0;
+
+  float a[8][8];
+  if (owner) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) a[r][c] = Ab[(int64_t)(8 * bi + r) * lda + 8 * bj + c];
+  }
+
+  // ---- Cholesky, right-looking, column j per step
+  bool bad = false;
+  for (int j = 0; j < NB; ++j) {
+    const int jb = j >> 3, jj = j & 7, buf = j & 1;
+    if (owner && bj == jb) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          if (c == jj) colb[buf][8 * bi + r] = a[r][c];
+    }
+    __syncthreads();
+    float d = colb[buf][j];
+    if (!(d > 0.f) || !isfinite(d)) {
+      bad = true;
+      d = 1.f;
+    }
+    const float sd = sqrtf(d);
+    const float inv = 1.f / sd;
+    if (owner && bi >= jb && bj >= jb) {
+      float li[8], lc[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) li[r] = colb[buf][8 * bi + r] * inv;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) lc[c] = colb[buf][8 * bj + c] * inv;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int gi = 8 * bi + r, gc = 8 * bj + c;
+          if (gc == j && gi >= j) a[r][c] = (gi == j) ? sd : li[r];
+          else if (gc > j && gi >= gc) a[r][c] -= li[r] * lc[c];
+        }
+    }
+  }
+  if (bad && tid == 0) atomicOr(flag, kFlagNotPD);
+
+  // ---- write L (lower) to A and LDS
+  if (owner) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int gi = 8 * bi + r, gc = 8 * bj + c;
+        if (gi >= gc) {
+          Ab[(int64_t)gi * lda + gc] = a[r][c];
+          Ls[gi][gc] = a[r][c];
+        }
+      }
+  }
+  __syncthreads();
+
+  // ---- inverse, right-looking by rows: R = I; row k of M = R[k]/L[k][k];
+  //      R[i] -= L[i][k] M[k] for i > k.
+  if (owner) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) a[r][c] = (8 * bi + r == 8 * bj + c) ? 1.f : 0.f;
+  }
+  for (int k = 0; k < NB; ++k) {
+    const int kb = k >> 3, kk = k & 7, buf = k & 1;
+    const float invd = 1.f / Ls[k][k];
+    if (owner && bi == kb) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (r == kk) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            a[r][c] *= invd;
+            colb[buf][8 * bj + c] = a[r][c];
+          }
+        }
+    }
+    __syncthreads();
+    if (owner && bi >= kb && bj <= kb) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int gi = 8 * bi + r;
+        if (gi > k) {
+          const float lik = Ls[gi][k];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) a[r][c] -= lik * colb[buf][8 * bj + c];
+        }
+      }
+    }
+  }
+
+  // ---- write D = L^{-1} (lower) and zero its strict upper part
+  if (owner) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int gi = 8 * bi + r, gc = 8 * bj + c;
+        Mb[(int64_t)gi * lda + gc] = (gi >= gc) ? a[r][c] : 0.f;
+      }
+  } else {
+    // threads 136..255 own the 120 strictly-upper sub-blocks (rb < cb):
+    // t = cb (cb - 1) / 2 + rb
+    const int t = tid - 136;
+    int cb = 1;
+    while (cb * (cb + 1) / 2 <= t) ++cb;
+    const int rb = t - cb * (cb - 1) / 2;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) Mb[(int64_t)(8 * rb + r) * lda + 8 * cb + c] = 0.f;
+  }
+}
+
+// U[a][b] = M[n-1-a][n-1-b] for a <= b, 0 below the diagonal.
+__global__ __launch_bounds__(256) void flip_kernel(const float* __restrict__ Mm, int64_t lda,
+                                                   int64_t n, float* __restrict__ U) {
+  const int64_t a = blockIdx.y;
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= n) return;
+  U[a * n + b] = (a <= b) ? Mm[(n - 1 - a) * lda + (n - 1 - b)] : 0.f;
+}
+
+}  // namespace
+
+PreparePlan plan_prepare(int64_t n) {
+  PreparePlan p;
+  p.n = n;
+  p.n_pad = round_up(std::max<int64_t>(n, 1), NB);
+  p.nblk = p.n_pad / NB;
+  const size_t mat = align256((size_t)p.n_pad * p.n_pad * sizeof(float));
+  p.a_off = 0;
+  p.m_off = mat;
+  p.lam_off = 2 * mat;
+  p.flag_off = p.lam_off + 256;
+  p.total = p.flag_off + 256;
+  return p;
+}
+
+gptq_status run_prepare(float* H, const double* key, int64_t n, float damp, int desc_act,
+                        int32_t* perm, void* ws, const PreparePlan& p, double* damp_out,
+                        hipStream_t stream) {
+  char* w = static_cast<char*>(ws);
+  float* A = reinterpret_cast<float*>(w + p.a_off);
+  float* Mm = reinterpret_cast<float*>(w + p.m_off);
+  double* lam = reinterpret_cast<double*>(w + p.lam_off);
+  int* flag = reinterpret_cast<int*>(w + p.flag_off);
+  const int64_t lda = p.n_pad;
+
+  GPTQ_HIP_CHECK(hipMemsetAsync(flag, 0, sizeof(int), stream));
+  hipLaunchKernelGGL(stats_kernel, dim3(1), dim3(1024), 0, stream, key, (const float*)H, n, damp,
+                     lam, flag);
+  GPTQ_LAUNCH_CHECK();
+  hipLaunchKernelGGL(rank_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, key,
+                     (const float*)H, n, desc_act, perm);
+  GPTQ_LAUNCH_CHECK();
+  const size_t row_bytes = (size_t)n * sizeof(float);
+  if (row_bytes > 65536)
+    GPTQ_HIP_CHECK(hipFuncSetAttribute((const void*)permute_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)row_bytes));
+  hipLaunchKernelGGL(permute_kernel, dim3((unsigned)p.n_pad), dim3(256), row_bytes, stream,
+                     (const float*)H, n, (const int32_t*)perm, (const double*)lam, A, lda);
+  GPTQ_LAUNCH_CHECK();
+
+  // blocked right-looking Cholesky of A (lower), leaf inverses into Mm
+  for (int64_t kb = 0; kb < p.nblk; ++kb) {
+    const int64_t k0 = kb * NB;
+    hipLaunchKernelGGL(chol_leaf_kernel, dim3(1), dim3(256), 0, stream, A, Mm, lda, k0, flag);
+    GPTQ_LAUNCH_CHECK();
+    const int64_t rows = p.n_pad - k0 - NB;
+    if (rows <= 0) break;
+    GemmArgs g;
+    // panel solve: P = A_panel · D_kᵀ  (D_kᵀ read column-major from D_k)
+    g.A = A + (k0 + NB) * lda + k0; g.lda = lda;
+    g.B = Mm + k0 * lda + k0; g.ldb = lda;
+    g.C = A + (k0 + NB) * lda + k0; g.ldc = lda;
+    g.M = rows; g.N = NB; g.k_begin = 0; g.k_end = NB; g.alpha = 1.f; g.beta = 0.f;
+    gptq_status st = launch_gemm_rect(g, /*b_colmajor=*/true, stream);
+    if (st != GPTQ_OK) return st;
+    // trailing update: A22 -= P Pᵀ on lower tiles
+    g.A = A + (k0 + NB) * lda + k0; g.lda = lda;
+    g.B = A + (k0 + NB) * lda + k0; g.ldb = lda;
+    g.C = A + (k0 + NB) * lda + k0 + NB; g.ldc = lda;
+    g.M = rows; g.N = rows; g.k_begin = 0; g.k_end = NB; g.alpha = -1.f; g.beta = 1.f;
+    st = launch_gemm_lower(g, /*b_colmajor=*/true, stream);
+    if (st != GPTQ_OK) return st;
+  }
+  // triangular inverse: doubling levels over the leaf inverses
+  for (int64_t half = 1; half < p.nblk; half *= 2) {
+    gptq_status st = launch_trtri_level(A, Mm, lda, p.nblk, half, stream);
+    if (st != GPTQ_OK) return st;
+  }
+  hipLaunchKernelGGL(flip_kernel, dim3((unsigned)ceil_div(n, 256), (unsigned)n), dim3(256), 0,
+                     stream, (const float*)Mm, lda, n, H);
+  GPTQ_LAUNCH_CHECK();
+
+  int hflag = 0;
+  double hlam = 0.0;
+  GPTQ_HIP_CHECK(hipMemcpyAsync(&hflag, flag, sizeof(int), hipMemcpyDeviceToHost, stream));
+  GPTQ_HIP_CHECK(hipMemcpyAsync(&hlam, lam, sizeof(double), hipMemcpyDeviceToHost, stream));
+  GPTQ_HIP_CHECK(hipStreamSynchronize(stream));
+  if (damp_out) *damp_out = hlam;
+  if (hflag & kFlagNonFinite) {
+    set_error("gptq_prepare_hinv: non-finite value on the Hessian diagonal");
+    return GPTQ_ERR_NONFINITE;
+  }
+  if (hflag & kFlagNotPD) {
+    set_error("gptq_prepare_hinv: damped Hessian is not positive definite");
+    return GPTQ_ERR_NOT_PD;
+  }
+  return GPTQ_OK;
+}
+
+}  // namespace gptq

@@ -1,0 +1,62 @@
+// Shared by the column quantizer translation units: the argument block, the
+// grid of one group, and the code of one weight on it.
+#pragma once
+
+#include "gptq_internal.hpp"
+
+namespace gptq {
+
+constexpr int QB = kQBlock;
+
+struct QArgs {
+  float* Wp;          // [m][ldw] working weights, processing order
+  int64_t ldw, m, n;
+  const float* U;     // [n][n]
+  int64_t ldu;
+  int bits, sym;
+  float* scales;      // [m][G]
+  int32_t* zeros;     // [m][G]
+  int64_t G;
+  float* err;         // [m][128]
+  uint8_t* codes;     // [m][ldw], processing order
+  double* loss_rows;  // [m]
+};
+
+// Grid of one group (page "模型量化实战：从 INT8 PTQ 到 GPTQ…" §2.1/§3.1):
+// asym -> range [min(w,0), max(w,0)] in 2^b - 1 steps, zero point = rounded
+// position of 0; sym -> scale max|w| / (2^(b-1) - 1), zero = storage offset
+// 2^(b-1).  Scales are floored at 1e-8.
+__device__ __forceinline__ void grid_params(float lo, float hi, float amax, int bits, int sym,
+                                            float& s, float& z) {
+  if (sym) {
+    s = fmaxf(amax / (float)((1 << (bits - 1)) - 1), 1e-8f);
+    z = (float)(1 << (bits - 1));
+  } else {
+    lo = fminf(lo, 0.f);
+    hi = fmaxf(hi, 0.f);
+    s = fmaxf((hi - lo) / (float)((1 << bits) - 1), 1e-8f);
+    z = rintf(-lo / s);
+  }
+}
+
+__device__ __forceinline__ float quant_code(float w, float s, float z, int bits, int sym) {
+  if (sym) {
+    const float qs = (float)((1 << (bits - 1)) - 1);
+    return fminf(fmaxf(rintf(w / s), -qs), qs) + z;
+  }
+  return fminf(fmaxf(rintf(w / s + z), 0.f), (float)((1 << bits) - 1));
+}
+
+
+// One block of 128 columns for rows [64·blockIdx, +64); GW = group width or 0
+// for one group per row.  Instantiated in block_quant_g*.hip.
+template <int GW>
+void launch_block_quant(const QArgs& a, int64_t i1, int bw, hipStream_t stream);
+template <> void launch_block_quant<0>(const QArgs&, int64_t, int, hipStream_t);
+template <> void launch_block_quant<8>(const QArgs&, int64_t, int, hipStream_t);
+template <> void launch_block_quant<16>(const QArgs&, int64_t, int, hipStream_t);
+template <> void launch_block_quant<32>(const QArgs&, int64_t, int, hipStream_t);
+template <> void launch_block_quant<64>(const QArgs&, int64_t, int, hipStream_t);
+template <> void launch_block_quant<128>(const QArgs&, int64_t, int, hipStream_t);
+
+}  // namespace gptq

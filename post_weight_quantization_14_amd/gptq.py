@@ -1,0 +1,179 @@
+"""Python binding of the C ABI: the same entry points, taking torch tensors.
+
+Argument marshalling only: tensors become device pointers, sizes and strides
+become integers, the stream is torch's current HIP stream.  Every step of the
+path runs in the HIP kernels of libgptq_mi355x.so; a non-OK status raises
+GptqError carrying the library's message.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import GptqConfig, lib
+
+
+class GptqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = lib().gptq_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {_lib.STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+@dataclass
+class QuantConfig:
+    """Quantizer settings (bits, group_size, sym, desc_act, damp_percent)."""
+    bits: int = 4
+    group_size: int = 128
+    sym: bool = False
+    desc_act: bool = True
+    damp_percent: float = 0.01
+    block_size: int = 128
+
+    def c(self) -> GptqConfig:
+        return GptqConfig(int(self.bits), int(self.group_size), int(bool(self.sym)),
+                          int(bool(self.desc_act)), int(self.block_size), float(self.damp_percent))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.GPTQ_BF16
+    if t.dtype == torch.float32:
+        return _lib.GPTQ_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != _lib.GPTQ_OK:
+        raise GptqError(status, where)
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return workspace
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- sizes
+def gptq_hessian_workspace_bytes(n: int, tokens: int, x_dtype: int = _lib.GPTQ_BF16) -> int:
+    return int(lib().gptq_hessian_workspace_bytes(n, tokens, x_dtype))
+
+
+def gptq_prepare_workspace_bytes(n: int) -> int:
+    return int(lib().gptq_prepare_workspace_bytes(n))
+
+
+def gptq_quantize_workspace_bytes(m: int, n: int, cfg: QuantConfig) -> int:
+    c = cfg.c()
+    return int(lib().gptq_quantize_workspace_bytes(m, n, ctypes.byref(c)))
+
+
+def gptq_qweight_words(n: int, bits: int) -> int:
+    return int(lib().gptq_qweight_words(n, bits))
+
+
+def gptq_num_groups(n: int, group_size: int) -> int:
+    return int(lib().gptq_num_groups(n, group_size))
+
+
+def gptq_last_error() -> str:
+    return lib().gptq_last_error().decode(errors="replace")
+
+
+# ---------------------------------------------------------------- stages
+def gptq_hessian_accumulate(H: torch.Tensor, diag_key: Optional[torch.Tensor], X: torch.Tensor,
+                            alpha: float = 2.0, workspace: Optional[torch.Tensor] = None,
+                            stream=None) -> None:
+    """H += alpha·XᵀX, diag_key += alpha·Σx² (fp64), for X [tokens, n] with unit column stride."""
+    n = H.shape[0]
+    if X.dim() != 2 or X.shape[1] != n or (X.shape[0] > 0 and X.stride(1) != 1):
+        raise ValueError("X must be [tokens, n] with contiguous rows")
+    code = _dtype_code(X)
+    ws = _workspace(gptq_hessian_workspace_bytes(n, X.shape[0], code), H.device, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().gptq_hessian_accumulate(_ptr(H), _ptr(diag_key), n, _ptr(X), code, X.shape[0],
+                                       X.stride(0) if X.shape[0] > 0 else n, float(alpha),
+                                       _ptr(ws), nbytes, _stream(stream))
+    _check(st, "gptq_hessian_accumulate")
+
+
+def gptq_prepare_hinv(H: torch.Tensor, diag_key: Optional[torch.Tensor], damp_percent: float,
+                      desc_act: bool, perm_out: torch.Tensor,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> float:
+    """H (in place) -> U; fills perm_out; returns the damping λ."""
+    n = H.shape[0]
+    ws = _workspace(gptq_prepare_workspace_bytes(n), H.device, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    lam = ctypes.c_double(0.0)
+    st = lib().gptq_prepare_hinv(_ptr(H), _ptr(diag_key), n, float(damp_percent), int(bool(desc_act)),
+                                 _ptr(perm_out), _ptr(ws), nbytes, ctypes.byref(lam), _stream(stream))
+    _check(st, "gptq_prepare_hinv")
+    return lam.value
+
+
+def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, cfg: QuantConfig,
+                        qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                        g_idx: torch.Tensor, loss: torch.Tensor,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    if not W.is_contiguous():
+        raise ValueError("W must be contiguous [m, n]")
+    m, n = W.shape
+    c = cfg.c()
+    ws = _workspace(gptq_quantize_workspace_bytes(m, n, cfg), W.device, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().gptq_quantize_layer(_ptr(W), _dtype_code(W), m, n, _ptr(U), _ptr(perm), ctypes.byref(c),
+                                   _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(g_idx), _ptr(loss),
+                                   _ptr(ws), nbytes, _stream(stream))
+    _check(st, "gptq_quantize_layer")
+
+
+# ---------------------------------------------------------------- whole layer
+def alloc_outputs(m: int, n: int, cfg: QuantConfig, device) -> dict:
+    words = gptq_qweight_words(n, cfg.bits)
+    groups = gptq_num_groups(n, cfg.group_size)
+    return dict(
+        qweight=torch.empty(m, words, dtype=torch.int32, device=device),
+        scales=torch.empty(m, groups, dtype=torch.float32, device=device),
+        zeros=torch.empty(m, groups, dtype=torch.int32, device=device),
+        g_idx=torch.empty(n, dtype=torch.int32, device=device),
+        loss=torch.zeros(2, dtype=torch.float64, device=device),
+        perm=torch.empty(n, dtype=torch.int32, device=device),
+    )
+
+
+def quantize_layer(W: torch.Tensor, x_tiles, cfg: QuantConfig, alpha: float = 2.0,
+                   keep_hessian: bool = False) -> dict:
+    """The three calls in order on one layer: accumulate every X tile into H,
+    prepare U, quantize W.  Returns the outputs (and H/key if keep_hessian)."""
+    m, n = W.shape
+    dev = W.device
+    H = torch.zeros(n, n, dtype=torch.float32, device=dev)
+    key = torch.zeros(n, dtype=torch.float64, device=dev)
+    for X in x_tiles:
+        gptq_hessian_accumulate(H, key, X, alpha)
+    out = alloc_outputs(m, n, cfg, dev)
+    if keep_hessian:
+        out["H"] = H.clone()
+        out["key"] = key.clone()
+    lam = gptq_prepare_hinv(H, key, cfg.damp_percent, cfg.desc_act, out["perm"])
+    out["U"] = H
+    out["lam"] = lam
+    gptq_quantize_layer(W, H, out["perm"], cfg, out["qweight"], out["scales"], out["zeros"],
+                        out["g_idx"], out["loss"])
+    return out

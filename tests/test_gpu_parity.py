@@ -1,0 +1,224 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded bytes.  Stage-wise (each GPU stage fed the GPU's own inputs into
+the oracle) and end to end (both sides free-running)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import (CODE_AGREE, H_REL_FROB, LOSS_REL, SCALE_REL, assert_codes, compare_codes,
+                         f64, rel_frob, spec, unpack_u32)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import post_weight_quantization_14_amd as pq
+    pq.lib()
+    return pq
+
+
+def _gpu_layer(pq, sp, cfg):
+    W = workloads.gen_weight(sp, "cuda")
+    tiles = list(workloads.x_tiles(sp, "cuda"))
+    out = pq.quantize_layer(W, tiles, cfg, keep_hessian=True)
+    torch.cuda.synchronize()
+    return W, tiles, out
+
+
+def _cfg(pq, sp):
+    return pq.QuantConfig(bits=sp.bits, group_size=sp.group_size, sym=sp.sym,
+                          desc_act=sp.desc_act, damp_percent=sp.damp_percent)
+
+
+# ---------------------------------------------------------------- stage 1
+HESSIAN_CASES = [
+    dict(m=16, n=256, tokens=512, x_dtype="fp32", x_dist="normal", outlier_count=4),
+    dict(m=16, n=200, tokens=1000),
+    dict(m=16, n=520, tokens=777),
+    dict(m=16, n=384, tokens=70000),
+    dict(m=16, n=64, tokens=5),
+    dict(m=16, n=136, tokens=300, x_dtype="fp32"),
+]
+
+
+@pytest.mark.parametrize("case", HESSIAN_CASES, ids=lambda c: f"n{c['n']}_T{c['tokens']}_{c.get('x_dtype', 'bf16')}")
+def test_hessian_matches_oracle(pq, case):
+    sp = spec(**case)
+    tiles = list(workloads.x_tiles(sp, "cuda"))
+    n = sp.n
+    H = torch.zeros(n, n, dtype=torch.float32, device="cuda")
+    key = torch.zeros(n, dtype=torch.float64, device="cuda")
+    for X in tiles:
+        pq.gptq_hessian_accumulate(H, key, X, 2.0)
+    torch.cuda.synchronize()
+    X = np.concatenate([f64(t) for t in tiles])
+    H_ref, key_ref = oracle.hessian([X], n)
+    Hg = f64(H)
+    err = rel_frob(Hg, H_ref)
+    print(f"H rel frob {err:.3e}")
+    assert err <= H_REL_FROB
+    assert np.array_equal(Hg, Hg.T), "H must come back exactly symmetric"
+    np.testing.assert_allclose(f64(key), key_ref, rtol=1e-12)
+
+
+def test_hessian_accumulates_over_calls_and_is_deterministic(pq):
+    sp = spec(16, 640, 40000)
+    X = workloads.gen_x(sp, "cuda")
+    n = sp.n
+
+    def run(chunks):
+        H = torch.zeros(n, n, dtype=torch.float32, device="cuda")
+        key = torch.zeros(n, dtype=torch.float64, device="cuda")
+        for c in chunks:
+            pq.gptq_hessian_accumulate(H, key, c, 2.0)
+        torch.cuda.synchronize()
+        return H.clone(), key.clone()
+
+    H1, k1 = run([X])
+    H2, k2 = run([X])
+    assert torch.equal(H1, H2) and torch.equal(k1, k2), "not bitwise deterministic"
+    H3, k3 = run([X[:12345], X[12345:30000], X[30000:]])
+    H_ref, key_ref = oracle.hessian([f64(X)], n)
+    assert rel_frob(f64(H3), H_ref) <= H_REL_FROB
+    np.testing.assert_allclose(f64(k3), key_ref, rtol=1e-12)
+    # zero tokens leave H and key untouched
+    H4, k4 = H1.clone(), k1.clone()
+    pq.gptq_hessian_accumulate(H4, k4, X[:0], 2.0)
+    torch.cuda.synchronize()
+    assert torch.equal(H4, H1) and torch.equal(k4, k1)
+
+
+# ---------------------------------------------------------------- stages 2-3
+PREPARE_CASES = [(128, True), (200, True), (256, False), (384, True), (1000, True), (1, True)]
+
+
+@pytest.mark.parametrize("n,desc", PREPARE_CASES, ids=lambda v: str(v))
+def test_prepare_matches_oracle(pq, n, desc):
+    sp = spec(8, n, max(4 * n, 64))
+    tiles = list(workloads.x_tiles(sp, "cuda"))
+    H = torch.zeros(n, n, dtype=torch.float32, device="cuda")
+    key = torch.zeros(n, dtype=torch.float64, device="cuda")
+    for X in tiles:
+        pq.gptq_hessian_accumulate(H, key, X, 2.0)
+    Hin = f64(H)
+    kin = f64(key)
+    perm = torch.empty(n, dtype=torch.int32, device="cuda")
+    lam = pq.gptq_prepare_hinv(H, key, 0.01, desc, perm)
+    torch.cuda.synchronize()
+    U = f64(H)
+    U_ref, perm_ref, lam_ref = oracle.prepare(Hin, kin, 0.01, desc)
+    assert perm.cpu().numpy().tolist() == perm_ref.tolist()
+    assert lam == pytest.approx(lam_ref, rel=1e-12)
+    assert np.all(np.tril(U, -1) == 0) and np.all(np.diag(U) > 0)
+    err = rel_frob(U, U_ref)
+    Hp = (Hin + lam_ref * np.eye(n))[np.ix_(perm_ref, perm_ref)]
+    resid = float(np.abs(U @ Hp @ U.T - np.eye(n)).max())
+    print(f"U rel frob {err:.3e}, max|U Hp Uᵀ - I| {resid:.3e}")
+    assert err <= 2e-4
+    assert resid <= 2e-3
+
+
+def test_not_positive_definite_and_nonfinite(pq):
+    n = 64
+    H = torch.zeros(n, n, dtype=torch.float32, device="cuda")
+    perm = torch.empty(n, dtype=torch.int32, device="cuda")
+    with pytest.raises(pq.GptqError) as ei:
+        pq.gptq_prepare_hinv(H, None, 0.01, True, perm)
+    assert ei.value.status == -4
+    H = -torch.eye(n, dtype=torch.float32, device="cuda")
+    with pytest.raises(pq.GptqError) as ei:
+        pq.gptq_prepare_hinv(H, None, 0.0, False, perm)
+    assert ei.value.status == -4
+    # NaN activation -> NaN key -> non-finite
+    X = torch.randn(100, n, device="cuda").to(torch.bfloat16)
+    X[3, 5] = float("nan")
+    H = torch.zeros(n, n, dtype=torch.float32, device="cuda")
+    key = torch.zeros(n, dtype=torch.float64, device="cuda")
+    pq.gptq_hessian_accumulate(H, key, X, 2.0)
+    with pytest.raises(pq.GptqError) as ei:
+        pq.gptq_prepare_hinv(H, key, 0.01, True, perm)
+    assert ei.value.status == -5
+    # NaN weight -> non-finite from the quantizer
+    X = torch.randn(300, n, device="cuda").to(torch.bfloat16)
+    W = (0.02 * torch.randn(32, n, device="cuda")).to(torch.bfloat16)
+    W[7, 9] = float("inf")
+    cfg = pq.QuantConfig(bits=4, group_size=32)
+    with pytest.raises(pq.GptqError) as ei:
+        pq.quantize_layer(W, [X], cfg)
+    assert ei.value.status == -5
+
+
+# ---------------------------------------------------------------- stages 4-5
+QUANT_CASES = [
+    dict(m=64, n=256, tokens=2048, bits=4, group_size=128, sym=False, desc_act=True),
+    dict(m=70, n=200, tokens=1600, bits=4, group_size=64, sym=False, desc_act=True),
+    dict(m=33, n=300, tokens=2400, bits=3, group_size=32, sym=False, desc_act=False),
+    dict(m=96, n=384, tokens=3000, bits=2, group_size=128, sym=False, desc_act=True),
+    dict(m=64, n=512, tokens=4096, bits=8, group_size=64, sym=False, desc_act=True),
+    dict(m=64, n=256, tokens=2048, bits=4, group_size=128, sym=True, desc_act=True),
+    dict(m=40, n=130, tokens=1200, bits=4, group_size=-1, sym=False, desc_act=True),
+    dict(m=40, n=130, tokens=1200, bits=3, group_size=16, sym=True, desc_act=False),
+    dict(m=1, n=72, tokens=500, bits=4, group_size=8, sym=False, desc_act=True),
+]
+
+
+def _ids(c):
+    return f"m{c['m']}_n{c['n']}_b{c['bits']}_g{c['group_size']}_{'sym' if c['sym'] else 'asym'}_{'act' if c['desc_act'] else 'noact'}"
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=_ids)
+def test_quantize_stage_matches_oracle(pq, case):
+    sp = spec(**case)
+    cfg = _cfg(pq, sp)
+    W, tiles, out = _gpu_layer(pq, sp, cfg)
+    m, n = sp.m, sp.n
+    Wf = f64(W)
+    U = f64(out["U"])
+    perm = out["perm"].cpu().numpy().astype(np.int64)
+    # oracle fed the GPU's own factor and order
+    ref = oracle.gptq_quantize(Wf[:, perm], U, sp.bits, sp.group_size, sp.sym)
+    Q_ref = oracle.unpermute_codes(ref["codes"], perm)
+    Q = unpack_u32(out["qweight"], n, sp.bits)
+    agree, mx = assert_codes(Q, Q_ref)
+    gidx = out["g_idx"].cpu().numpy()
+    assert gidx.tolist() == oracle.g_index(perm, sp.group_size).tolist()
+    sc = out["scales"].cpu().numpy().astype(np.float64)
+    zr = out["zeros"].cpu().numpy()
+    clean = np.all(Q == Q_ref, axis=1)
+    np.testing.assert_allclose(sc[clean], ref["scales"][clean], rtol=SCALE_REL)
+    assert np.array_equal(zr[clean], ref["zeros"][clean])
+    loss = out["loss"].cpu().numpy()
+    Qhat = oracle.dequantize_layer(Q, sc, zr, gidx)
+    loss1_ref = float(np.sum((Wf - Qhat) ** 2))
+    print(f"codes agree {agree:.6f} max {mx}; loss0 {loss[0]:.6e} ref {ref['loss0']:.6e}; loss1 {loss[1]:.6e} ref {loss1_ref:.6e}")
+    assert loss[0] == pytest.approx(ref["loss0"], rel=LOSS_REL)
+    assert loss[1] == pytest.approx(loss1_ref, rel=1e-6)
+    assert Q.min() >= (1 if sp.sym else 0) and Q.max() <= 2 ** sp.bits - 1
+
+
+def test_end_to_end_tiny_layer_config(pq):
+    """The 256 x 256 fp32 layer, 512 tokens, 4-bit asym g128, no act-order:
+    both sides free-running from W and X."""
+    sp = workloads.CONFIGS["c1_tiny_256"]
+    cfg = _cfg(pq, sp)
+    W, tiles, out = _gpu_layer(pq, sp, cfg)
+    X = np.concatenate([f64(t) for t in tiles])
+    H_ref, key_ref = oracle.hessian([X], sp.n)
+    assert rel_frob(f64(out["H"]), H_ref) <= H_REL_FROB
+    ref = oracle.gptq_layer(f64(W), H_ref, key_ref, sp.bits, sp.group_size, sp.sym, sp.desc_act,
+                            sp.damp_percent)
+    assert out["perm"].cpu().numpy().tolist() == ref["perm"].tolist()
+    Q = unpack_u32(out["qweight"], sp.n, sp.bits)
+    agree, mx = assert_codes(Q, ref["codes"])
+    clean = np.all(Q == ref["codes"], axis=1)
+    np.testing.assert_allclose(out["scales"].cpu().numpy()[clean], ref["scales"][clean], rtol=SCALE_REL)
+    loss = out["loss"].cpu().numpy()
+    print(f"C1 codes agree {agree:.6f}; loss0 {loss[0]:.6e} vs {ref['loss0']:.6e}")
+    assert loss[0] == pytest.approx(ref["loss0"], rel=LOSS_REL)
+    assert loss[1] == pytest.approx(ref["loss1"], rel=LOSS_REL)
+    assert out["lam"] == pytest.approx(ref["lam"], rel=1e-9)
