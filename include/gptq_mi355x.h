@@ -60,7 +60,7 @@ typedef struct {
   int32_t sym;
   int32_t desc_act;
   int32_t block_size;
-  float damp_percent;
+  double damp_percent;
 } gptq_config;
 
 /* ------------------------------------------------------------------------
@@ -116,7 +116,7 @@ gptq_status gptq_hessian_accumulate(float* H, double* diag_key, int64_t n, const
  * ---------------------------------------------------------------------- */
 size_t gptq_prepare_workspace_bytes(int64_t n);
 gptq_status gptq_prepare_hinv(float* H_inout, const double* diag_key, int64_t n,
-                              float damp_percent, int32_t desc_act, int32_t* perm_out,
+                              double damp_percent, int32_t desc_act, int32_t* perm_out,
                               void* workspace, size_t ws_bytes, double* damp_out, void* stream);
 
 /* ------------------------------------------------------------------------

@@ -29,7 +29,7 @@ GPTQ_FP32 = 1
 class GptqConfig(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32), ("sym", ctypes.c_int32),
                 ("desc_act", ctypes.c_int32), ("block_size", ctypes.c_int32),
-                ("damp_percent", ctypes.c_float)]
+                ("damp_percent", ctypes.c_double)]
 
 
 _P = ctypes.c_void_p
@@ -42,7 +42,7 @@ SIGNATURES = {
     "gptq_hessian_workspace_bytes": (_SZ, [_I64, _I64, _I32]),
     "gptq_hessian_accumulate": (_ST, [_P, _P, _I64, _P, _I32, _I64, _I64, ctypes.c_float, _P, _SZ, _P]),
     "gptq_prepare_workspace_bytes": (_SZ, [_I64]),
-    "gptq_prepare_hinv": (_ST, [_P, _P, _I64, ctypes.c_float, _I32, _P, _P, _SZ,
+    "gptq_prepare_hinv": (_ST, [_P, _P, _I64, ctypes.c_double, _I32, _P, _P, _SZ,
                                 ctypes.POINTER(ctypes.c_double), _P]),
     "gptq_quantize_workspace_bytes": (_SZ, [_I64, _I64, ctypes.POINTER(GptqConfig)]),
     "gptq_quantize_layer": (_ST, [_P, _I32, _I64, _I64, _P, _P, ctypes.POINTER(GptqConfig), _P, _P,

@@ -112,7 +112,7 @@ size_t gptq_prepare_workspace_bytes(int64_t n) {
 }
 
 gptq_status gptq_prepare_hinv(float* H_inout, const double* diag_key, int64_t n,
-                              float damp_percent, int32_t desc_act, int32_t* perm_out,
+                              double damp_percent, int32_t desc_act, int32_t* perm_out,
                               void* workspace, size_t ws_bytes, double* damp_out, void* stream) {
   clear_error();
   if (n < 0) return fail(GPTQ_ERR_INVALID_ARG, "n=%lld", (long long)n);
@@ -123,7 +123,7 @@ gptq_status gptq_prepare_hinv(float* H_inout, const double* diag_key, int64_t n,
   if (diag_key && bad_ptr(diag_key, 8)) return fail(GPTQ_ERR_INVALID_ARG, "diag_key misaligned");
   if (bad_ptr(perm_out, 4)) return fail(GPTQ_ERR_INVALID_ARG, "perm_out is NULL or misaligned");
   if (desc_act != 0 && desc_act != 1) return fail(GPTQ_ERR_INVALID_ARG, "desc_act=%d", desc_act);
-  if (!std::isfinite(damp_percent) || damp_percent < 0.f)
+  if (!std::isfinite(damp_percent) || damp_percent < 0.0)
     return fail(GPTQ_ERR_INVALID_ARG, "damp_percent=%g", (double)damp_percent);
   const PreparePlan plan = plan_prepare(n);
   if (workspace == nullptr || ws_bytes < plan.total || bad_ptr(workspace, 256))

@@ -75,7 +75,7 @@ struct PreparePlan {
   size_t a_off = 0, m_off = 0, lam_off = 0, flag_off = 0, total = 0;
 };
 PreparePlan plan_prepare(int64_t n);
-gptq_status run_prepare(float* H, const double* key, int64_t n, float damp, int desc_act,
+gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int desc_act,
                         int32_t* perm, void* ws, const PreparePlan& plan, double* damp_out,
                         hipStream_t stream);
 

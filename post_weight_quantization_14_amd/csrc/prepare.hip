@@ -38,7 +38,7 @@ __device__ __forceinline__ double key_of(const double* key, const float* H, int6
 
 // λ = damp * mean(diag); one workgroup, fixed reduction order.
 __global__ __launch_bounds__(1024) void stats_kernel(const double* key, const float* H, int64_t n,
-                                                     float damp, double* lam_out, int* flag) {
+                                                     double damp, double* lam_out, int* flag) {
   __shared__ double red[1024];
   __shared__ int bad;
   if (threadIdx.x == 0) bad = 0;
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(1024) void stats_kernel(const double* key, const fl
   }
   if (threadIdx.x == 0) {
     const double mean = red[0] / (double)n;
-    *lam_out = (double)damp * mean;
+    *lam_out = damp * mean;
     if (bad || !isfinite(mean)) atomicOr(flag, kFlagNonFinite);
   }
 }
@@ -298,7 +298,7 @@ PreparePlan plan_prepare(int64_t n) {
   return p;
 }
 
-gptq_status run_prepare(float* H, const double* key, int64_t n, float damp, int desc_act,
+gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int desc_act,
                         int32_t* perm, void* ws, const PreparePlan& p, double* damp_out,
                         hipStream_t stream) {
   char* w = static_cast<char*>(ws);
