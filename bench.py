@@ -88,6 +88,7 @@ class Layer:
         self.ev[3].record()
 
     def stage_ms(self):
+        self.ev[3].synchronize()
         return [self.ev[i].elapsed_time(self.ev[i + 1]) for i in range(3)]
 
 

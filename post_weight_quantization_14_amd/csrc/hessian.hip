@@ -7,19 +7,21 @@
 // mirrored to the upper triangle.
 //
 // bf16 path: v_mfma_f32_32x32x16_bf16.  X is token-major, so the reduction
-// axis (tokens) is the strided one; each thread loads an 8-token x 8-channel
-// block with eight 16-byte reads, transposes it in registers (v_perm), and
-// stores eight channel rows of 8 tokens into LDS.  The LDS layout is
-// [token octet][256 channels] x 16 bytes with the channel slot swizzled by
-// ch ^ ((ch >> 4) & 7), which keeps both the transposing stores and the MFMA
-// operand reads free of bank conflicts.
+// axis (tokens) is the strided one.  Each 32-token stage of the two 256-channel
+// panels is copied into LDS as is (16-byte loads, token-major rows, octet slot
+// swizzled), and the MFMA operands -- 8 consecutive tokens of one channel per
+// lane -- come out of LDS through gfx950's transposing ds_read_b64_tr_b16.
+// The fp64 diagonal key of a diagonal tile is summed from the staged panel.
 //
-// Tiles are 256 x 256 (4 waves, 128 x 128 each).  Long token ranges are cut
-// into `splits` slices (split-K) so the grid fills 256 CUs and every fp32
-// register chain stays <= 32768 tokens long; with splits a multiple of 8 all
-// workgroups of one XCD share a token slice.  Slices meet in a partial buffer
-// and the last workgroup of a tile to finish (an atomic ticket) sums the
-// partials in slice order, so the result is deterministic.
+// Tiles are 256 x 256 with 8 waves (two per SIMD), each 64 x 128 = 2 x 4
+// MFMA blocks (128 accumulator registers), so a second wave hides each
+// wave's LDS and barrier latency.
+// Long token ranges are cut into `splits` slices (split-K) so the grid fills
+// 256 CUs and every fp32 register chain stays <= 32768 tokens long; with
+// splits a multiple of 8 all workgroups of one XCD share a token slice.
+// Slices meet in a partial buffer and the last workgroup of a tile to finish
+// (an atomic ticket) sums the partials in slice order, so the result is
+// deterministic.
 #include <algorithm>
 
 #include "gptq_internal.hpp"
@@ -40,9 +42,18 @@ struct SyrkArgs {
   int* counters;
 };
 
-constexpr int kOcts = kSyrkStage / 8;   // token octets per stage
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
-__device__ __forceinline__ int swz(int ch) { return ch ^ ((ch >> 4) & 7); }
+constexpr int kRowBytes = 512;                       // one token of a 256-channel panel
+constexpr int kPanelBytes = kSyrkStage * kRowBytes;  // 16 KB per panel per stage
+
+// Byte offset of (token t, channel octet o) in a panel stage: token-major rows
+// of 32 octets, octet slot swizzled by 4·(t mod 4).  The transposing reads
+// below touch 4 consecutive tokens x 2 octets per 16-lane group; the swizzle
+// spreads them over 8 distinct bank quads, and the paired group (16 channels
+// further) over the other 8, so a 32-lane half reads all 64 banks once.
+__device__ __forceinline__ int lds_off(int t, int o) { return t * kRowBytes + ((o ^ ((t & 3) << 2)) << 4); }
 
 __device__ __forceinline__ void tri_decode(int64_t t, int64_t& ti, int64_t& tj) {
   int64_t r = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
@@ -52,84 +63,39 @@ __device__ __forceinline__ void tri_decode(int64_t t, int64_t& ti, int64_t& tj) 
   tj = t - r * (r + 1) / 2;
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// 8 tokens (rows) x 8 channels starting at (t0, c0); zero outside [.., t_end) x [.., n).
-template <bool VEC>
-__device__ __forceinline__ void load_block(const uint16_t* __restrict__ X, int64_t ldx, int64_t t0,
-                                           int64_t t_end, int64_t c0, int64_t n, uint4 (&v)[8]) {
-  if (VEC && t0 + 8 <= t_end && c0 + 8 <= n) {
-    const uint16_t* p = X + t0 * ldx + c0;
+// 16 bytes = channels [c, c+8) of token t; zero where t >= t_lim or c + e >= n.
+__device__ __forceinline__ uint4 load16(const uint16_t* __restrict__ X, int64_t ldx, int64_t t,
+                                        int64_t t_lim, int64_t c, int64_t n) {
+  uint32_t h[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) v[r] = *reinterpret_cast<const uint4*>(p + r * ldx);
-    return;
-  }
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int64_t t = t0 + r;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (t < t_end && c0 < n) {
-      const uint16_t* p = X + t * ldx + c0;
-      if (VEC && c0 + 8 <= n) {
-        x = *reinterpret_cast<const uint4*>(p);
-      } else {
-        uint32_t h[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = (c0 + e < n) ? (uint32_t)p[e] : 0u;
-        x.x = h[0] | (h[1] << 16);
-        x.y = h[2] | (h[3] << 16);
-        x.z = h[4] | (h[5] << 16);
-        x.w = h[6] | (h[7] << 16);
-      }
-    }
-    v[r] = x;
-  }
+  for (int e = 0; e < 8; ++e) h[e] = (t < t_lim && c + e < n) ? (uint32_t)X[t * ldx + c + e] : 0u;
+  return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
 }
 
-__device__ __forceinline__ uint32_t dw(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-// Transpose the 8x8 block (rows = tokens) into 8 channel vectors of 8 tokens and
-// store them at LDS [oct][swz(ch)].  With KEY, add each channel's Σx² (fp64).
-template <bool KEY>
-__device__ __forceinline__ void transpose_store(const uint4 (&v)[8], uint4* __restrict__ panel,
-                                                int oct, int ch0, double (&keyacc)[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    uint4 o;
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t a = dw(v[2 * k], e >> 1), b = dw(v[2 * k + 1], e >> 1);
-      w[k] = (e & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-    o.x = w[0]; o.y = w[1]; o.z = w[2]; o.w = w[3];
-    panel[oct * 256 + swz(ch0 + e)] = o;
-    if (KEY) {
-      double s = 0.0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float lo = bf16_lo(w[k]), hi = bf16_hi(w[k]);
-        s += (double)(lo * lo);   // a bf16 square is exact in fp32
-        s += (double)(hi * hi);
-      }
-      keyacc[e] += s;
-    }
-  }
+// MFMA operand of 32 channels [c0, c0+32) for the 16-token step at token k0:
+// lane l gets channel c0 + l%32 at tokens k0 + 8·(l/32) + e, e = 0..7, via two
+// ds_read_b64_tr_b16 (each 16-lane group points at 4 tokens x 16 channels).
+__device__ __forceinline__ bf16x8_t tr_frag(const uint8_t* panel, int k0, int c0, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int c = c0 + ((g & 1) << 4) + ((s & 3) << 2);
+  const int t = k0 + ((g >> 1) << 3) + (s >> 2);
+  const uint8_t* p0 = panel + lds_off(t, c >> 3) + ((c & 7) << 1);
+  const uint8_t* p1 = panel + lds_off(t + 4, c >> 3) + ((c & 7) << 1);
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p0));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p1));
+  const auto v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
 }
 
 template <bool VEC>
-__global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(SyrkArgs a) {
-  // [buffer][panel I/J][token octet * 256 + channel slot]: 2 x 2 x 4 x 256 x 16 B = 64 KB
-  __shared__ uint4 lds[2][2][kOcts * 256];
-  __shared__ double red[kOcts][256];
+__global__ __launch_bounds__(512, 1) void syrk_bf16_kernel(SyrkArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kPanelBytes];   // [buffer][panel]: 64 KB
+  __shared__ double kred[256];
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave >> 1, wc = wave & 1;   // wave tile: rows wr*64 (+64), cols wc*128 (+128)
 
   // workgroup -> (tile, slice); without slices-per-XCD, spread contiguous
   // logical ranges over the 8 XCDs (dispatch is round-robin over XCDs).
@@ -144,100 +110,131 @@ __global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(SyrkArgs a) {
   int64_t ti, tj;
   tri_decode(tile, ti, tj);
   const bool diag = (ti == tj);
-  const bool idle_wave = diag && wr == 0 && wc == 1;   // strictly upper quarter
+  const bool idle_wave = diag && wc == 1 && wr < 2;   // strictly above the diagonal
+  const int64_t n = a.n;
 
   const int64_t t_begin = s * a.slice_tokens;
   const int64_t t_end = (t_begin + a.slice_tokens < a.T) ? t_begin + a.slice_tokens : a.T;
   const int64_t nst = (t_end > t_begin) ? (t_end - t_begin + kSyrkStage - 1) / kSyrkStage : 0;
 
-  // staging role: one 8-token x 8-channel block of panel I (threads 0-127) or J
-  const int panel = tid >> 7;
-  const int ch_oct = tid & 31, tok_oct = (tid >> 5) & 3;
-  const bool stager = !(diag && panel == 1);
-  const bool keyer = diag && panel == 0;
-  const int64_t cbase = (panel == 0 ? ti : tj) * kSyrkTile + ch_oct * 8;
+  // staging: thread loads octet o of tokens tr and tr + 16 of both panels
+  const int o = tid & 31, tr = tid >> 5;
+  const int64_t cI = ti * kSyrkTile + 8 * o, cJ = tj * kSyrkTile + 8 * o;
+  const bool okI = cI < n, okJ = cJ < n;   // (VEC: n % 8 == 0, so cI < n covers the octet)
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  double keyacc[8];
+  double ksum = 0.0;   // diagonal tiles: Σx² of channel tid % 256 over half the tokens
+
+  // VEC: buffer loads off a per-stage scalar base, one 32-bit lane offset per
+  // panel and the 16-token row step in an SGPR.  The descriptor's size ends at
+  // the slice's last token, so rows past it read as zeros; channel octets past
+  // n read a valid octet and are zeroed in put().  Every stage issues the same
+  // 4 loads, so the loop needs no per-path wait bookkeeping.
+  uint4 vI[2], vJ[2];
+  const int32_t rowb = (int32_t)(a.ldx * 2);
+  const int32_t vofsI = tr * rowb + (int32_t)((okI ? cI : n - 8) * 2);
+  const int32_t vofsJ = tr * rowb + (int32_t)((okJ ? cJ : n - 8) * 2);
+  auto load = [&](int64_t t0) {
+    if (VEC) {
+      const int64_t bytes = (t_end - t0) * a.ldx * 2;
+      const int32_t nrec = bytes > 0x7fffffff ? 0x7fffffff : (int32_t)bytes;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.X + t0 * a.ldx), 0, nrec, 0x00020000);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) keyacc[e] = 0.0;
-
-  uint4 vb[8];
-  if (nst > 0 && stager) {
-    load_block<VEC>(a.X, a.ldx, t_begin + tok_oct * 8, t_end, cbase, a.n, vb);
-    if (keyer) transpose_store<true>(vb, lds[0][0], tok_oct, ch_oct * 8, keyacc);
-    else transpose_store<false>(vb, lds[0][panel], tok_oct, ch_oct * 8, keyacc);
-  }
-  __syncthreads();
-
-  for (int64_t st = 0; st < nst; ++st) {
-    const int cur = (int)(st & 1);
-    const bool more = st + 1 < nst;
-    if (more && stager)
-      load_block<VEC>(a.X, a.ldx, t_begin + (st + 1) * kSyrkStage + tok_oct * 8, t_end, cbase, a.n, vb);
+      for (int u = 0; u < 2; ++u) {
+        vI[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, vofsI, 16 * u * rowb, 0));
+        vJ[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, vofsJ, 16 * u * rowb, 0));
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        vI[u] = load16(a.X, a.ldx, t0 + tr + 16 * u, t_end, cI, n);
+        vJ[u] = load16(a.X, a.ldx, t0 + tr + 16 * u, t_end, cJ, n);
+      }
+    }
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int off = lds_off(tr + 16 * u, o);
+      *reinterpret_cast<uint4*>(&lds[buf][0][off]) = okI ? vI[u] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&lds[buf][1][off]) = okJ ? vJ[u] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto mma = [&](int buf) {
     if (!idle_wave) {
-      const uint4* pI = lds[cur][0];
-      const uint4* pJ = diag ? lds[cur][0] : lds[cur][1];
+      const uint8_t* pI = lds[buf][0];
+      const uint8_t* pJ = lds[buf][1];
 #pragma unroll
       for (int kk = 0; kk < kSyrkStage / 16; ++kk) {
-        const int oct = 2 * kk + (lane >> 5);
-        bf16x8_t af[4], bfm[4];
+        bf16x8_t af[2], bfm[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[i] = __builtin_bit_cast(bf16x8_t, pI[oct * 256 + swz(wr * 128 + i * 32 + (lane & 31))]);
+        for (int i = 0; i < 2; ++i) af[i] = tr_frag(pI, 16 * kk, wr * 64 + i * 32, lane);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bfm[j] = __builtin_bit_cast(bf16x8_t, pJ[oct * 256 + swz(wc * 128 + j * 32 + (lane & 31))]);
+        for (int j = 0; j < 4; ++j) bfm[j] = tr_frag(pJ, 16 * kk, wc * 128 + j * 32, lane);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfm[j], acc[i][j], 0, 0, 0);
       }
     }
-    if (more && stager) {
-      if (keyer) transpose_store<true>(vb, lds[cur ^ 1][0], tok_oct, ch_oct * 8, keyacc);
-      else transpose_store<false>(vb, lds[cur ^ 1][panel], tok_oct, ch_oct * 8, keyacc);
+    if (diag) {   // fp64 key: channel tid % 256, tokens [16·(tid / 256), +16) of the stage
+      const uint8_t* pI = lds[buf][0];
+      const int c = tid & 255, t0 = (tid >> 8) * 16;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const uint16_t hv = *reinterpret_cast<const uint16_t*>(pI + lds_off(t0 + t, c >> 3) + ((c & 7) << 1));
+        const float x = __uint_as_float((uint32_t)hv << 16);
+        ksum += (double)(x * x);   // a bf16 square is exact in fp32
+      }
     }
+  };
+
+  if (nst > 0) {
+    load(t_begin);
+    put(0);
     __syncthreads();
+    // stage st sits in lds[st & 1]; the loads of stage st + 1 are in flight
+    // while its MFMAs run (the last iteration re-reads the last stage)
+    for (int64_t st = 0; st < nst; ++st) {
+      const int64_t nx = (st + 1 < nst) ? st + 1 : st;
+      load(t_begin + nx * kSyrkStage);
+      mma((int)(st & 1));
+      if (st + 1 < nst) put((int)((st + 1) & 1));
+      __syncthreads();
+    }
+  }
+  if (diag) {   // combine the two token halves of each channel
+    if (tid >= 256) kred[tid - 256] = ksum;
+    __syncthreads();
+    if (tid < 256) ksum += kred[tid];
   }
 
-  // ---- per-channel key of a diagonal tile: reduce the token-octet partials
-  double ksum = 0.0;
-  if (diag) {
-    if (keyer) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red[tok_oct][ch_oct * 8 + e] = keyacc[e];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int o = 0; o < kOcts; ++o) ksum += red[o][tid];
-  }
-
-  const int64_t n = a.n;
-  const int64_t gi0 = ti * kSyrkTile + wr * 128 + 4 * (lane >> 5);
+  const int64_t gi0 = ti * kSyrkTile + wr * 64 + 4 * (lane >> 5);
   const int64_t gj0 = tj * kSyrkTile + wc * 128 + (lane & 31);
+  constexpr int kRegs = 2 * 4 * 16;   // accumulator registers per lane
 
   if (a.splits > 1) {
     // ---- split-K: publish the partial, take a ticket; the last workgroup of
     // the tile re-reads all slices (its own included) and sums them in slice
     // order, so the result does not depend on which one finishes last.
-    float* mine = a.partials + ((tile * a.splits + s) * 256) * 256;
+    float* mine = a.partials + (tile * a.splits + s) * (int64_t)(kRegs * 512);
     if (!idle_wave) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) mine[((i * 4 + j) * 16 + v) * 256 + tid] = acc[i][j][v];
+          for (int v = 0; v < 16; ++v) mine[((i * 4 + j) * 16 + v) * 512 + tid] = acc[i][j][v];
     }
-    if (diag) {
+    if (diag && tid < 256) {
       const int64_t c = ti * kSyrkTile + tid;
       if (c < n) a.keyparts[s * n + c] = ksum;
     }
@@ -252,21 +249,21 @@ __global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(SyrkArgs a) {
     if (!s_last) return;
     __threadfence();
     if (!idle_wave) {
-      const float* base = a.partials + (tile * a.splits) * 256 * 256;
+      const float* base = a.partials + (tile * a.splits) * (int64_t)(kRegs * 512);
       for (int64_t q = 0; q < a.splits; ++q) {
-        const float* pq = base + q * 256 * 256;
+        const float* pq = base + q * (int64_t)(kRegs * 512);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              const float x = pq[((i * 4 + j) * 16 + v) * 256 + tid];
+              const float x = pq[((i * 4 + j) * 16 + v) * 512 + tid];
               acc[i][j][v] = (q == 0) ? x : acc[i][j][v] + x;
             }
       }
     }
-    if (diag) {
+    if (diag && tid < 256) {
       const int64_t c = ti * kSyrkTile + tid;
       double sum = 0.0;
       if (c < n)
@@ -278,7 +275,7 @@ __global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(SyrkArgs a) {
   // ---- H (lower tile, mirrored) and key
   if (!idle_wave) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -292,7 +289,7 @@ __global__ __launch_bounds__(256, 1) void syrk_bf16_kernel(SyrkArgs a) {
           }
         }
   }
-  if (diag && a.key) {
+  if (diag && a.key && tid < 256) {
     const int64_t c = ti * kSyrkTile + tid;
     if (c < n) a.key[c] += (double)a.alpha * ksum;
   }
@@ -462,9 +459,10 @@ gptq_status launch_hessian_bf16(float* H, double* key, int64_t n, const uint16_t
   }
   int64_t grid = plan.tiles * plan.splits;
   if (plan.splits % 8 != 0) grid = round_up(grid, 8);
-  const bool vec = (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
-  if (vec) hipLaunchKernelGGL(syrk_bf16_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(syrk_bf16_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  // the vector path needs 16-byte rows and whole channel octets
+  const bool vec = (ldx % 8 == 0) && (n % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+  if (vec) hipLaunchKernelGGL(syrk_bf16_kernel<true>, dim3((unsigned)grid), dim3(512), 0, stream, a);
+  else hipLaunchKernelGGL(syrk_bf16_kernel<false>, dim3((unsigned)grid), dim3(512), 0, stream, a);
   GPTQ_LAUNCH_CHECK();
   return GPTQ_OK;
 }

@@ -131,11 +131,21 @@ __global__ __launch_bounds__(256) void permute_kernel(const float* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // Leaf: Cholesky of the 128 x 128 diagonal block at (k0, k0), then its inverse.
-// Thread t < 136 owns the t-th lower 8 x 8 sub-block in registers; columns
-// (factorisation) and rows (inversion) are broadcast through LDS, one barrier
-// per step.  Writes L back into A and D = L⁻¹ into the same block of Mmat
-// (strict upper part of that block set to 0).
+// The block is cut into 16 x 16 sub-blocks of 8 x 8; thread t < 136 owns the
+// t-th lower sub-block (bi, bj) in registers.  Both phases run 16 block steps
+// with static 8 x 8 kernels in registers and 8 x 8 operands shared through
+// LDS (sub-block stride 68 floats: distinct bank groups per sub-block row):
+//   Cholesky, step jb: the owner of (jb, jb) factors it; owners of (bi, jb)
+//     solve X · L_jbᵀ = A_bi,jb; owners of (bi, bj), jb < bj <= bi, subtract
+//     L_bi,jb · L_bj,jbᵀ.
+//   Inverse (R = I, row block kb per step): owners of (kb, bj) solve
+//     L_kb,kb · M_kb,bj = R_kb,bj; owners of (bi, bj), bi > kb, bj <= kb,
+//     subtract L_bi,kb · M_kb,bj.
+// Writes L back into A and D = L⁻¹ into the same block of Mmat (strict upper
+// part of that block set to 0).
 // ---------------------------------------------------------------------------
+constexpr int SB = 68;   // LDS stride of one 8 x 8 sub-block (floats)
+
 __device__ __forceinline__ void sub_decode(int t, int& bi, int& bj) {
   int r = 0;
   while ((r + 1) * (r + 2) / 2 <= t) ++r;
@@ -143,10 +153,30 @@ __device__ __forceinline__ void sub_decode(int t, int& bi, int& bj) {
   bj = t - r * (r + 1) / 2;
 }
 
+__device__ __forceinline__ int lsub(int bi, int bj) { return (bi * 17 + bj) * SB; }
+
+__device__ __forceinline__ void lds_store8x8(float* dst, const float (&x)[8][8]) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    *reinterpret_cast<f32x4_t*>(dst + 8 * r) = f32x4_t{x[r][0], x[r][1], x[r][2], x[r][3]};
+    *reinterpret_cast<f32x4_t*>(dst + 8 * r + 4) = f32x4_t{x[r][4], x[r][5], x[r][6], x[r][7]};
+  }
+}
+
+__device__ __forceinline__ void lds_load8x8(const float* src, float (&x)[8][8]) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const f32x4_t u = *reinterpret_cast<const f32x4_t*>(src + 8 * r);
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + 8 * r + 4);
+    x[r][0] = u[0]; x[r][1] = u[1]; x[r][2] = u[2]; x[r][3] = u[3];
+    x[r][4] = v[0]; x[r][5] = v[1]; x[r][6] = v[2]; x[r][7] = v[3];
+  }
+}
+
 __global__ __launch_bounds__(256) void chol_leaf_kernel(float* A, float* Mm, int64_t lda, int64_t k0,
                                                         int* flag) {
-  __shared__ float colb[2][NB];
-  __shared__ float Ls[NB][NB + 1];
+  __shared__ __attribute__((aligned(16))) float Lsub[16 * 17 * SB];   // L by sub-block
+  __shared__ __attribute__((aligned(16))) float Pan[2][16 * SB];      // step operands
   const int tid = threadIdx.x;
   const bool owner = tid < 136;
   int bi = 0, bj = 0;
@@ -162,103 +192,138 @@ __global__ __launch_bounds__(256) void chol_leaf_kernel(float* A, float* Mm, int
       for (int c = 0; c < 8; ++c) a[r][c] = Ab[(int64_t)(8 * bi + r) * lda + 8 * bj + c];
   }
 
-  // ---- Cholesky, right-looking, column j per step
+  // ---- Cholesky by 8-column block steps
   bool bad = false;
-  for (int j = 0; j < NB; ++j) {
-    const int jb = j >> 3, jj = j & 7, buf = j & 1;
-    if (owner && bj == jb) {
+#pragma unroll 1
+  for (int jb = 0; jb < 16; ++jb) {
+    if (owner && bi == jb && bj == jb) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float d = a[c][c];
+        if (!(d > 0.f) || !isfinite(d)) {
+          bad = true;
+          d = 1.f;
+        }
+        const float sd = sqrtf(d);
+        const float inv = 1.f / sd;
+        a[c][c] = sd;
+#pragma unroll
+        for (int r = c + 1; r < 8; ++r) a[r][c] *= inv;
+#pragma unroll
+        for (int c2 = c + 1; c2 < 8; ++c2)
+#pragma unroll
+          for (int r = c2; r < 8; ++r) a[r][c2] -= a[r][c] * a[c2][c];
+      }
 #pragma unroll
       for (int r = 0; r < 8; ++r)
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-          if (c == jj) colb[buf][8 * bi + r] = a[r][c];
+        for (int c = r + 1; c < 8; ++c) a[r][c] = 0.f;
+      lds_store8x8(&Pan[0][jb * SB], a);
     }
     __syncthreads();
-    float d = colb[buf][j];
-    if (!(d > 0.f) || !isfinite(d)) {
-      bad = true;
-      d = 1.f;
+    if (owner && bj == jb && bi > jb) {
+      float l[8][8];
+      lds_load8x8(&Pan[0][jb * SB], l);
+      // X · Lᵀ = A, row by row: x[r][c] = (a[r][c] - Σ_{k<c} x[r][k] l[c][k]) / l[c][c]
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float inv = 1.f / l[c][c];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          float v = a[r][c];
+#pragma unroll
+          for (int k = 0; k < c; ++k) v -= a[r][k] * l[c][k];
+          a[r][c] = v * inv;
+        }
+      }
+      lds_store8x8(&Pan[1][bi * SB], a);
     }
-    const float sd = sqrtf(d);
-    const float inv = 1.f / sd;
-    if (owner && bi >= jb && bj >= jb) {
-      float li[8], lc[8];
+    __syncthreads();
+    if (owner && bj > jb) {
+      float lb[8][8];
+      lds_load8x8(&Pan[1][bj * SB], lb);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) li[r] = colb[buf][8 * bi + r] * inv;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) lc[c] = colb[buf][8 * bj + c] * inv;
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
+      for (int r = 0; r < 8; ++r) {
+        const f32x4_t u = *reinterpret_cast<const f32x4_t*>(&Pan[1][bi * SB + 8 * r]);
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&Pan[1][bi * SB + 8 * r + 4]);
+        const float li[8] = {u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          const int gi = 8 * bi + r, gc = 8 * bj + c;
-          if (gc == j && gi >= j) a[r][c] = (gi == j) ? sd : li[r];
-          else if (gc > j && gi >= gc) a[r][c] -= li[r] * lc[c];
+          float acc = a[r][c];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc -= li[k] * lb[c][k];
+          a[r][c] = acc;
         }
+      }
     }
   }
-  if (bad && tid == 0) atomicOr(flag, kFlagNotPD);
+  if (bad) atomicOr(flag, kFlagNotPD);
 
-  // ---- write L (lower) to A and LDS
+  // ---- L to A (lower) and to LDS
   if (owner) {
 #pragma unroll
     for (int r = 0; r < 8; ++r)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int gi = 8 * bi + r, gc = 8 * bj + c;
-        if (gi >= gc) {
-          Ab[(int64_t)gi * lda + gc] = a[r][c];
-          Ls[gi][gc] = a[r][c];
-        }
-      }
+      for (int c = 0; c < 8; ++c)
+        if (bi != bj || r >= c) Ab[(int64_t)(8 * bi + r) * lda + 8 * bj + c] = a[r][c];
+    lds_store8x8(&Lsub[lsub(bi, bj)], a);
   }
   __syncthreads();
 
-  // ---- inverse, right-looking by rows: R = I; row k of M = R[k]/L[k][k];
-  //      R[i] -= L[i][k] M[k] for i > k.
+  // ---- inverse by 8-row block steps (R starts as I)
   if (owner) {
 #pragma unroll
     for (int r = 0; r < 8; ++r)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) a[r][c] = (8 * bi + r == 8 * bj + c) ? 1.f : 0.f;
+      for (int c = 0; c < 8; ++c) a[r][c] = (bi == bj && r == c) ? 1.f : 0.f;
   }
-  for (int k = 0; k < NB; ++k) {
-    const int kb = k >> 3, kk = k & 7, buf = k & 1;
-    const float invd = 1.f / Ls[k][k];
+#pragma unroll 1
+  for (int kb = 0; kb < 16; ++kb) {
+    float* P = Pan[kb & 1];
     if (owner && bi == kb) {
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        if (r == kk) {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            a[r][c] *= invd;
-            colb[buf][8 * bj + c] = a[r][c];
-          }
-        }
-    }
-    __syncthreads();
-    if (owner && bi >= kb && bj <= kb) {
+      float l[8][8];
+      lds_load8x8(&Lsub[lsub(kb, kb)], l);
+      // L · M = R, column by column (forward substitution)
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const int gi = 8 * bi + r;
-        if (gi > k) {
-          const float lik = Ls[gi][k];
+        const float inv = 1.f / l[r][r];
 #pragma unroll
-          for (int c = 0; c < 8; ++c) a[r][c] -= lik * colb[buf][8 * bj + c];
+        for (int c = 0; c < 8; ++c) {
+          float v = a[r][c];
+#pragma unroll
+          for (int k = 0; k < r; ++k) v -= l[r][k] * a[k][c];
+          a[r][c] = v * inv;
+        }
+      }
+      lds_store8x8(&P[bj * SB], a);
+    }
+    __syncthreads();
+    if (owner && bi > kb && bj <= kb) {
+      float mk[8][8];
+      lds_load8x8(&P[bj * SB], mk);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const f32x4_t u = *reinterpret_cast<const f32x4_t*>(&Lsub[lsub(bi, kb) + 8 * r]);
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&Lsub[lsub(bi, kb) + 8 * r + 4]);
+        const float li[8] = {u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          float acc = a[r][c];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc -= li[k] * mk[k][c];
+          a[r][c] = acc;
         }
       }
     }
   }
 
-  // ---- write D = L^{-1} (lower) and zero its strict upper part
+  // ---- D = L^{-1} (lower) to Mmat; zero the strict upper part of the block
   if (owner) {
 #pragma unroll
     for (int r = 0; r < 8; ++r)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int gi = 8 * bi + r, gc = 8 * bj + c;
-        Mb[(int64_t)gi * lda + gc] = (gi >= gc) ? a[r][c] : 0.f;
-      }
+      for (int c = 0; c < 8; ++c)
+        Mb[(int64_t)(8 * bi + r) * lda + 8 * bj + c] = (bi != bj || r >= c) ? a[r][c] : 0.f;
   } else {
     // threads 136..255 own the 120 strictly-upper sub-blocks (rb < cb):
     // t = cb (cb - 1) / 2 + rb

@@ -49,14 +49,16 @@ __device__ __forceinline__ float quant_code(float w, float s, float z, int bits,
 
 
 // One block of 128 columns for rows [64·blockIdx, +64); GW = group width or 0
-// for one group per row.  Instantiated in block_quant_g*.hip.
+// for one group per row.  ublk points at U[i1][i1] with row stride ldu and
+// must allow 128 reads per row.  Instantiated in block_quant_g*.hip.
 template <int GW>
-void launch_block_quant(const QArgs& a, int64_t i1, int bw, hipStream_t stream);
-template <> void launch_block_quant<0>(const QArgs&, int64_t, int, hipStream_t);
-template <> void launch_block_quant<8>(const QArgs&, int64_t, int, hipStream_t);
-template <> void launch_block_quant<16>(const QArgs&, int64_t, int, hipStream_t);
-template <> void launch_block_quant<32>(const QArgs&, int64_t, int, hipStream_t);
-template <> void launch_block_quant<64>(const QArgs&, int64_t, int, hipStream_t);
-template <> void launch_block_quant<128>(const QArgs&, int64_t, int, hipStream_t);
+void launch_block_quant(const QArgs& a, const float* ublk, int64_t ldu, int64_t i1, int bw,
+                        hipStream_t stream);
+template <> void launch_block_quant<0>(const QArgs&, const float*, int64_t, int64_t, int, hipStream_t);
+template <> void launch_block_quant<8>(const QArgs&, const float*, int64_t, int64_t, int, hipStream_t);
+template <> void launch_block_quant<16>(const QArgs&, const float*, int64_t, int64_t, int, hipStream_t);
+template <> void launch_block_quant<32>(const QArgs&, const float*, int64_t, int64_t, int, hipStream_t);
+template <> void launch_block_quant<64>(const QArgs&, const float*, int64_t, int64_t, int, hipStream_t);
+template <> void launch_block_quant<128>(const QArgs&, const float*, int64_t, int64_t, int, hipStream_t);
 
 }  // namespace gptq
