@@ -168,6 +168,9 @@ def main():
     ap.add_argument("--workload", default="c3_down_proj_4096x11008")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also time the 7B-shaped 224-linear sweep")
+    ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; "
+                         "the reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this path runs on one GPU "
@@ -176,6 +179,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_check:
+        nbytes = args.copy_check << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_check_bytes": nbytes, "copies": 3}), flush=True)
+        return
 
     import post_weight_quantization_14_amd as pq
     import workloads

@@ -47,7 +47,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------- Hessian (stage 1)
 constexpr int kSyrkTile = 256;      // output tile edge of the bf16 SYRK
-constexpr int kSyrkStage = 32;      // tokens per LDS stage
+constexpr int kSyrkStage = 64;      // tokens per LDS stage
 constexpr int kSyrkMaxSliceTokens = 32768;  // fp32 register chains stay this short
 
 struct SyrkPlan {

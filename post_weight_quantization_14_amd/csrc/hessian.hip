@@ -33,7 +33,7 @@ struct SyrkArgs {
   const uint16_t* X;
   int64_t ldx, T;
   int64_t n;
-  int64_t tiles, splits, slice_tokens;
+  int64_t panels, tiles, splits, slice_tokens;
   float* H;
   double* key;
   float alpha;
@@ -46,7 +46,7 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 constexpr int kRowBytes = 512;                       // one token of a 256-channel panel
-constexpr int kPanelBytes = kSyrkStage * kRowBytes;  // 16 KB per panel per stage
+constexpr int kPanelBytes = kSyrkStage * kRowBytes;  // 32 KB per panel per stage
 
 // Byte offset of (token t, channel octet o) in a panel stage: token-major rows
 // of 32 octets, octet slot swizzled by 4·(t mod 4).  The transposing reads
@@ -61,6 +61,39 @@ __device__ __forceinline__ void tri_decode(int64_t t, int64_t& ti, int64_t& tj) 
   while ((r + 1) * (r + 2) / 2 <= t) ++r;
   ti = r;
   tj = t - r * (r + 1) / 2;
+}
+
+// Lower-triangle tile number t -> (ti, tj) in a grouped order: super-blocks of
+// 8 x 8 tiles, super-blocks row by row, tiles row by row inside each.  The 32
+// workgroups an XCD runs at once then cover about 4 x 8 tiles (12 panels of X)
+// instead of a long tile row, so more of their panel reads hit the XCD's L2.
+constexpr int kGroup = 8;
+__device__ __forceinline__ void tile_decode_grouped(int64_t t, int64_t panels, int64_t& ti,
+                                                    int64_t& tj) {
+  const int64_t nr = (panels + kGroup - 1) / kGroup;
+  int64_t rem = t;
+  for (int64_t R = 0; R < nr; ++R) {
+    const int64_t r0 = R * kGroup, r1 = (r0 + kGroup < panels) ? r0 + kGroup : panels;
+    for (int64_t C = 0; C <= R; ++C) {
+      const int64_t c0 = C * kGroup, c1 = (c0 + kGroup < panels) ? c0 + kGroup : panels;
+      const int64_t w = c1 - c0, h = r1 - r0;
+      const int64_t cnt = (C < R) ? h * w : h * (h + 1) / 2;
+      if (rem < cnt) {
+        if (C < R) {
+          ti = r0 + rem / w;
+          tj = c0 + rem % w;
+        } else {
+          int64_t li, lj;
+          tri_decode(rem, li, lj);
+          ti = r0 + li;
+          tj = c0 + lj;
+        }
+        return;
+      }
+      rem -= cnt;
+    }
+  }
+  ti = tj = 0;   // not reached for t < tiles
 }
 
 // 16 bytes = channels [c, c+8) of token t; zero where t >= t_lim or c + e >= n.
@@ -89,7 +122,7 @@ __device__ __forceinline__ bf16x8_t tr_frag(const uint8_t* panel, int k0, int c0
 
 template <bool VEC>
 __global__ __launch_bounds__(512, 1) void syrk_bf16_kernel(SyrkArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kPanelBytes];   // [buffer][panel]: 64 KB
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kPanelBytes];   // [buffer][panel]: 128 KB
   __shared__ double kred[256];
   __shared__ int s_last;
 
@@ -108,7 +141,7 @@ __global__ __launch_bounds__(512, 1) void syrk_bf16_kernel(SyrkArgs a) {
   }
   const int64_t tile = b / a.splits, s = b % a.splits;
   int64_t ti, tj;
-  tri_decode(tile, ti, tj);
+  tile_decode_grouped(tile, a.panels, ti, tj);
   const bool diag = (ti == tj);
   const bool idle_wave = diag && wc == 1 && wr < 2;   // strictly above the diagonal
   const int64_t n = a.n;
@@ -117,7 +150,7 @@ __global__ __launch_bounds__(512, 1) void syrk_bf16_kernel(SyrkArgs a) {
   const int64_t t_end = (t_begin + a.slice_tokens < a.T) ? t_begin + a.slice_tokens : a.T;
   const int64_t nst = (t_end > t_begin) ? (t_end - t_begin + kSyrkStage - 1) / kSyrkStage : 0;
 
-  // staging: thread loads octet o of tokens tr and tr + 16 of both panels
+  // staging: thread loads octet o of tokens tr + 16u (u = 0..3) of both panels
   const int o = tid & 31, tr = tid >> 5;
   const int64_t cI = ti * kSyrkTile + 8 * o, cJ = tj * kSyrkTile + 8 * o;
   const bool okI = cI < n, okJ = cJ < n;   // (VEC: n % 8 == 0, so cI < n covers the octet)
@@ -129,14 +162,15 @@ __global__ __launch_bounds__(512, 1) void syrk_bf16_kernel(SyrkArgs a) {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  double ksum = 0.0;   // diagonal tiles: Σx² of channel tid % 256 over half the tokens
+  double ksum = 0.0;   // diagonal tiles: Σx² of channel tid % 256 over half of each stage
 
   // VEC: buffer loads off a per-stage scalar base, one 32-bit lane offset per
   // panel and the 16-token row step in an SGPR.  The descriptor's size ends at
   // the slice's last token, so rows past it read as zeros; channel octets past
   // n read a valid octet and are zeroed in put().  Every stage issues the same
-  // 4 loads, so the loop needs no per-path wait bookkeeping.
-  uint4 vI[2], vJ[2];
+  // 8 loads, so the loop needs no per-path wait bookkeeping.
+  constexpr int kU = kSyrkStage / 16;   // loads per panel per thread and stage
+  uint4 vI[kU], vJ[kU];
   const int32_t rowb = (int32_t)(a.ldx * 2);
   const int32_t vofsI = tr * rowb + (int32_t)((okI ? cI : n - 8) * 2);
   const int32_t vofsJ = tr * rowb + (int32_t)((okJ ? cJ : n - 8) * 2);
@@ -147,13 +181,13 @@ __global__ __launch_bounds__(512, 1) void syrk_bf16_kernel(SyrkArgs a) {
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.X + t0 * a.ldx), 0, nrec, 0x00020000);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < kU; ++u) {
         vI[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, vofsI, 16 * u * rowb, 0));
         vJ[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, vofsJ, 16 * u * rowb, 0));
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < kU; ++u) {
         vI[u] = load16(a.X, a.ldx, t0 + tr + 16 * u, t_end, cI, n);
         vJ[u] = load16(a.X, a.ldx, t0 + tr + 16 * u, t_end, cJ, n);
       }
@@ -161,7 +195,7 @@ __global__ __launch_bounds__(512, 1) void syrk_bf16_kernel(SyrkArgs a) {
   };
   auto put = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int off = lds_off(tr + 16 * u, o);
       *reinterpret_cast<uint4*>(&lds[buf][0][off]) = okI ? vI[u] : make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(&lds[buf][1][off]) = okJ ? vJ[u] : make_uint4(0, 0, 0, 0);
@@ -185,11 +219,11 @@ __global__ __launch_bounds__(512, 1) void syrk_bf16_kernel(SyrkArgs a) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfm[j], acc[i][j], 0, 0, 0);
       }
     }
-    if (diag) {   // fp64 key: channel tid % 256, tokens [16·(tid / 256), +16) of the stage
+    if (diag) {   // fp64 key: channel tid % 256, one half of the stage's tokens
       const uint8_t* pI = lds[buf][0];
-      const int c = tid & 255, t0 = (tid >> 8) * 16;
+      const int c = tid & 255, t0 = (tid >> 8) * (kSyrkStage / 2);
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
+      for (int t = 0; t < kSyrkStage / 2; ++t) {
         const uint16_t hv = *reinterpret_cast<const uint16_t*>(pI + lds_off(t0 + t, c >> 3) + ((c & 7) << 1));
         const float x = __uint_as_float((uint32_t)hv << 16);
         ksum += (double)(x * x);   // a bf16 square is exact in fp32
@@ -445,7 +479,8 @@ gptq_status launch_hessian_bf16(float* H, double* key, int64_t n, const uint16_t
                                 hipStream_t stream) {
   SyrkArgs a;
   a.X = X; a.ldx = ldx; a.T = tokens; a.n = n;
-  a.tiles = plan.tiles; a.splits = plan.splits; a.slice_tokens = plan.slice_tokens;
+  a.panels = plan.panels; a.tiles = plan.tiles; a.splits = plan.splits;
+  a.slice_tokens = plan.slice_tokens;
   a.H = H; a.key = key; a.alpha = alpha;
   char* w = static_cast<char*>(ws);
   a.partials = plan.splits > 1 ? reinterpret_cast<float*>(w) : nullptr;
