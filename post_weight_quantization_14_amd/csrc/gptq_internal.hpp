@@ -47,7 +47,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------- Hessian (stage 1)
 constexpr int kSyrkTile = 256;      // output tile edge of the bf16 SYRK
-constexpr int kSyrkStage = 64;      // tokens per LDS stage
+constexpr int kSyrkStage = 32;      // tokens per LDS ring slot
 constexpr int kSyrkMaxSliceTokens = 32768;  // fp32 register chains stay this short
 
 struct SyrkPlan {
@@ -55,7 +55,7 @@ struct SyrkPlan {
   int64_t tiles = 0;    // lower-triangle tiles
   int64_t splits = 1;   // token slices (split-K)
   int64_t slice_tokens = 0;
-  size_t partial_bytes = 0, keypart_bytes = 0, counter_bytes = 0;
+  size_t partial_bytes = 0, keypart_bytes = 0;
   size_t total_bytes = 0;
 };
 SyrkPlan plan_syrk_bf16(int64_t n, int64_t tokens);

@@ -6,22 +6,30 @@
 // update, so only lower-triangle tiles are computed and each result is
 // mirrored to the upper triangle.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16.  X is token-major, so the reduction
-// axis (tokens) is the strided one.  Each 32-token stage of the two 256-channel
-// panels is copied into LDS as is (16-byte loads, token-major rows, octet slot
-// swizzled), and the MFMA operands -- 8 consecutive tokens of one channel per
-// lane -- come out of LDS through gfx950's transposing ds_read_b64_tr_b16.
-// The fp64 diagonal key of a diagonal tile is summed from the staged panel.
+// bf16 path: v_mfma_f32_32x32x16_bf16 on 256 x 256 tiles, 8 waves (two per
+// SIMD) of 64 x 128 each, so one wave's LDS waits hide behind the other's
+// MFMAs.  X is token-major, so the reduction axis (tokens) is the strided one:
+// each 32-token stage of the tile's two 256-channel panels is copied into LDS
+// as is (token-major rows, octet slot swizzled) and the MFMA operands -- 8
+// consecutive tokens of one channel per lane -- come out through gfx950's
+// transposing ds_read_b64_tr_b16.
 //
-// Tiles are 256 x 256 with 8 waves (two per SIMD), each 64 x 128 = 2 x 4
-// MFMA blocks (128 accumulator registers), so a second wave hides each
-// wave's LDS and barrier latency.
+// Aligned X (the usual case) is streamed with buffer loads that write LDS
+// directly, into a ring of kRing stage slots: kRing - 1 stages are in flight
+// while one is multiplied, enough bytes to cover HBM latency at MFMA rate
+// without holding any of them in registers.  The ring is driven by explicit
+// vmcnt waits and a bare s_barrier (a __syncthreads would drain every load in
+// flight).  Rows past the token range and channels past n lie outside the
+// buffer descriptor and land in LDS as zeros.
+//
 // Long token ranges are cut into `splits` slices (split-K) so the grid fills
 // 256 CUs and every fp32 register chain stays <= 32768 tokens long; with
-// splits a multiple of 8 all workgroups of one XCD share a token slice.
-// Slices meet in a partial buffer and the last workgroup of a tile to finish
-// (an atomic ticket) sums the partials in slice order, so the result is
-// deterministic.
+// splits a multiple of 8 all workgroups of one XCD share a token slice.  Each
+// workgroup writes its fp32 tile to a partial buffer and a second kernel sums
+// the slices in slice order (deterministic), adds the result into H's lower
+// triangle and writes the mirror, coalesced through an LDS transpose.  No
+// cross-workgroup synchronisation is needed: on gfx950 that would take an L2
+// write-back and invalidate per workgroup.
 #include <algorithm>
 
 #include "gptq_internal.hpp"
@@ -34,19 +42,19 @@ struct SyrkArgs {
   int64_t ldx, T;
   int64_t n;
   int64_t panels, tiles, splits, slice_tokens;
-  float* H;
-  double* key;
-  float alpha;
-  float* partials;
-  double* keyparts;
-  int* counters;
+  float* partials;    // [splits][tiles][256][256] fp32, row-major tiles
+  double* keyparts;   // [splits][n]
 };
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kRowBytes = 512;                       // one token of a 256-channel panel
-constexpr int kPanelBytes = kSyrkStage * kRowBytes;  // 32 KB per panel per stage
+constexpr int kRowBytes = 512;                        // one token of a 256-channel panel
+constexpr int kPanelBytes = kSyrkStage * kRowBytes;   // 16 KB: one panel, one stage
+constexpr int kSlotBytes = 2 * kPanelBytes;           // 32 KB: both panels
+constexpr int kRing = 4;                              // ring slots (128 KB)
+constexpr int kTilePartial = kSyrkTile * kSyrkTile;   // floats per partial tile
 
 // Byte offset of (token t, channel octet o) in a panel stage: token-major rows
 // of 32 octets, octet slot swizzled by 4·(t mod 4).  The transposing reads
@@ -96,6 +104,29 @@ __device__ __forceinline__ void tile_decode_grouped(int64_t t, int64_t panels, i
   ti = tj = 0;   // not reached for t < tiles
 }
 
+// Workgroup -> (tile, slice, tile coordinates).  Without slices-per-XCD,
+// contiguous logical ranges are spread over the 8 XCDs (dispatch is
+// round-robin over XCDs).  Returns false for padding workgroups.
+struct TileJob {
+  int64_t tile, s, ti, tj, t_begin, t_end;
+};
+__device__ __forceinline__ bool decode_job(const SyrkArgs& a, TileJob& j) {
+  const int64_t total = a.tiles * a.splits;
+  int64_t b = blockIdx.x;
+  if (a.splits % 8 != 0) {
+    const int64_t per = (total + 7) / 8;
+    b = (b % 8) * per + b / 8;
+    if (b >= total) return false;
+  }
+  j.tile = b / a.splits;
+  j.s = b % a.splits;
+  tile_decode_grouped(j.tile, a.panels, j.ti, j.tj);
+  j.t_begin = j.s * a.slice_tokens;
+  j.t_end = (j.t_begin + a.slice_tokens < a.T) ? j.t_begin + a.slice_tokens : a.T;
+  if (j.t_end < j.t_begin) j.t_end = j.t_begin;
+  return true;
+}
+
 // 16 bytes = channels [c, c+8) of token t; zero where t >= t_lim or c + e >= n.
 __device__ __forceinline__ uint4 load16(const uint16_t* __restrict__ X, int64_t ldx, int64_t t,
                                         int64_t t_lim, int64_t c, int64_t n) {
@@ -120,219 +151,290 @@ __device__ __forceinline__ bf16x8_t tr_frag(const uint8_t* panel, int k0, int c0
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-template <bool VEC>
-__global__ __launch_bounds__(512, 1) void syrk_bf16_kernel(SyrkArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kPanelBytes];   // [buffer][panel]: 128 KB
-  __shared__ double kred[256];
-  __shared__ int s_last;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;   // wave tile: rows wr*64 (+64), cols wc*128 (+128)
-
-  // workgroup -> (tile, slice); without slices-per-XCD, spread contiguous
-  // logical ranges over the 8 XCDs (dispatch is round-robin over XCDs).
-  const int64_t total = a.tiles * a.splits;
-  int64_t b = blockIdx.x;
-  if (a.splits % 8 != 0) {
-    const int64_t per = (total + 7) / 8;
-    b = (b % 8) * per + b / 8;
-    if (b >= total) return;
-  }
-  const int64_t tile = b / a.splits, s = b % a.splits;
-  int64_t ti, tj;
-  tile_decode_grouped(tile, a.panels, ti, tj);
-  const bool diag = (ti == tj);
-  const bool idle_wave = diag && wc == 1 && wr < 2;   // strictly above the diagonal
-  const int64_t n = a.n;
-
-  const int64_t t_begin = s * a.slice_tokens;
-  const int64_t t_end = (t_begin + a.slice_tokens < a.T) ? t_begin + a.slice_tokens : a.T;
-  const int64_t nst = (t_end > t_begin) ? (t_end - t_begin + kSyrkStage - 1) / kSyrkStage : 0;
-
-  // staging: thread loads octet o of tokens tr + 16u (u = 0..3) of both panels
-  const int o = tid & 31, tr = tid >> 5;
-  const int64_t cI = ti * kSyrkTile + 8 * o, cJ = tj * kSyrkTile + 8 * o;
-  const bool okI = cI < n, okJ = cJ < n;   // (VEC: n % 8 == 0, so cI < n covers the octet)
-
+// The per-wave tile work shared by both bf16 kernels.
+struct WaveTile {
   f32x16_t acc[2][4];
+  double ksum;   // diagonal tiles: Σx² of channel tid % 256 over half of each stage
+};
+
+__device__ __forceinline__ void wave_tile_init(WaveTile& w) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  double ksum = 0.0;   // diagonal tiles: Σx² of channel tid % 256 over half of each stage
+      for (int v = 0; v < 16; ++v) w.acc[i][j][v] = 0.f;
+  w.ksum = 0.0;
+}
 
-  // VEC: buffer loads off a per-stage scalar base, one 32-bit lane offset per
-  // panel and the 16-token row step in an SGPR.  The descriptor's size ends at
-  // the slice's last token, so rows past it read as zeros; channel octets past
-  // n read a valid octet and are zeroed in put().  Every stage issues the same
-  // 8 loads, so the loop needs no per-path wait bookkeeping.
-  constexpr int kU = kSyrkStage / 16;   // loads per panel per thread and stage
-  uint4 vI[kU], vJ[kU];
-  const int32_t rowb = (int32_t)(a.ldx * 2);
-  const int32_t vofsI = tr * rowb + (int32_t)((okI ? cI : n - 8) * 2);
-  const int32_t vofsJ = tr * rowb + (int32_t)((okJ ? cJ : n - 8) * 2);
-  auto load = [&](int64_t t0) {
-    if (VEC) {
-      const int64_t bytes = (t_end - t0) * a.ldx * 2;
-      const int32_t nrec = bytes > 0x7fffffff ? 0x7fffffff : (int32_t)bytes;
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.X + t0 * a.ldx), 0, nrec, 0x00020000);
+// One 32-token stage: 2 k-steps of 2 x 4 MFMAs per wave; diagonal tiles also
+// add the stage's squares to the fp64 key.
+__device__ __forceinline__ void stage_mma(WaveTile& w, const uint8_t* pI, const uint8_t* pJ, bool active,
+                                          bool diag, int wr, int wc, int lane, int tid) {
+  if (active) {
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        vI[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, vofsI, 16 * u * rowb, 0));
-        vJ[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, vofsJ, 16 * u * rowb, 0));
-      }
-    } else {
+    for (int kk = 0; kk < kSyrkStage / 16; ++kk) {
+      bf16x8_t af[2], bfm[4];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        vI[u] = load16(a.X, a.ldx, t0 + tr + 16 * u, t_end, cI, n);
-        vJ[u] = load16(a.X, a.ldx, t0 + tr + 16 * u, t_end, cJ, n);
-      }
-    }
-  };
-  auto put = [&](int buf) {
+      for (int i = 0; i < 2; ++i) af[i] = tr_frag(pI, 16 * kk, wr * 64 + i * 32, lane);
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int off = lds_off(tr + 16 * u, o);
-      *reinterpret_cast<uint4*>(&lds[buf][0][off]) = okI ? vI[u] : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&lds[buf][1][off]) = okJ ? vJ[u] : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto mma = [&](int buf) {
-    if (!idle_wave) {
-      const uint8_t* pI = lds[buf][0];
-      const uint8_t* pJ = lds[buf][1];
-#pragma unroll
-      for (int kk = 0; kk < kSyrkStage / 16; ++kk) {
-        bf16x8_t af[2], bfm[4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) af[i] = tr_frag(pI, 16 * kk, wr * 64 + i * 32, lane);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bfm[j] = tr_frag(pJ, 16 * kk, wc * 128 + j * 32, lane);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfm[j], acc[i][j], 0, 0, 0);
-      }
-    }
-    if (diag) {   // fp64 key: channel tid % 256, one half of the stage's tokens
-      const uint8_t* pI = lds[buf][0];
-      const int c = tid & 255, t0 = (tid >> 8) * (kSyrkStage / 2);
-#pragma unroll
-      for (int t = 0; t < kSyrkStage / 2; ++t) {
-        const uint16_t hv = *reinterpret_cast<const uint16_t*>(pI + lds_off(t0 + t, c >> 3) + ((c & 7) << 1));
-        const float x = __uint_as_float((uint32_t)hv << 16);
-        ksum += (double)(x * x);   // a bf16 square is exact in fp32
-      }
-    }
-  };
-
-  if (nst > 0) {
-    load(t_begin);
-    put(0);
-    __syncthreads();
-    // stage st sits in lds[st & 1]; the loads of stage st + 1 are in flight
-    // while its MFMAs run (the last iteration re-reads the last stage)
-    for (int64_t st = 0; st < nst; ++st) {
-      const int64_t nx = (st + 1 < nst) ? st + 1 : st;
-      load(t_begin + nx * kSyrkStage);
-      mma((int)(st & 1));
-      if (st + 1 < nst) put((int)((st + 1) & 1));
-      __syncthreads();
-    }
-  }
-  if (diag) {   // combine the two token halves of each channel
-    if (tid >= 256) kred[tid - 256] = ksum;
-    __syncthreads();
-    if (tid < 256) ksum += kred[tid];
-  }
-
-  const int64_t gi0 = ti * kSyrkTile + wr * 64 + 4 * (lane >> 5);
-  const int64_t gj0 = tj * kSyrkTile + wc * 128 + (lane & 31);
-  constexpr int kRegs = 2 * 4 * 16;   // accumulator registers per lane
-
-  if (a.splits > 1) {
-    // ---- split-K: publish the partial, take a ticket; the last workgroup of
-    // the tile re-reads all slices (its own included) and sums them in slice
-    // order, so the result does not depend on which one finishes last.
-    float* mine = a.partials + (tile * a.splits + s) * (int64_t)(kRegs * 512);
-    if (!idle_wave) {
+      for (int j = 0; j < 4; ++j) bfm[j] = tr_frag(pJ, 16 * kk, wc * 128 + j * 32, lane);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mine[((i * 4 + j) * 16 + v) * 512 + tid] = acc[i][j][v];
-    }
-    if (diag && tid < 256) {
-      const int64_t c = ti * kSyrkTile + tid;
-      if (c < n) a.keyparts[s * n + c] = ksum;
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const int old = __hip_atomic_fetch_add(&a.counters[tile], 1, __ATOMIC_ACQ_REL,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-      s_last = (old == (int)a.splits - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (!idle_wave) {
-      const float* base = a.partials + (tile * a.splits) * (int64_t)(kRegs * 512);
-      for (int64_t q = 0; q < a.splits; ++q) {
-        const float* pq = base + q * (int64_t)(kRegs * 512);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const float x = pq[((i * 4 + j) * 16 + v) * 512 + tid];
-              acc[i][j][v] = (q == 0) ? x : acc[i][j][v] + x;
-            }
-      }
-    }
-    if (diag && tid < 256) {
-      const int64_t c = ti * kSyrkTile + tid;
-      double sum = 0.0;
-      if (c < n)
-        for (int64_t q = 0; q < a.splits; ++q) sum += a.keyparts[q * n + c];
-      ksum = sum;
+          w.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfm[j], w.acc[i][j], 0, 0, 0);
     }
   }
-
-  // ---- H (lower tile, mirrored) and key
-  if (!idle_wave) {
+  if (diag) {
+    const int c = tid & 255, t0 = (tid >> 8) * (kSyrkStage / 2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t gi = gi0 + i * 32 + 8 * (v >> 2) + (v & 3);
-          const int64_t gj = gj0 + j * 32;
-          if (gi < n && gj < n && (!diag || gi >= gj)) {
-            const float val = a.H[gi * n + gj] + a.alpha * acc[i][j][v];
-            a.H[gi * n + gj] = val;
-            if (gi != gj) a.H[gj * n + gi] = val;
-          }
-        }
-  }
-  if (diag && a.key && tid < 256) {
-    const int64_t c = ti * kSyrkTile + tid;
-    if (c < n) a.key[c] += (double)a.alpha * ksum;
+    for (int t = 0; t < kSyrkStage / 2; ++t) {
+      const uint16_t hv = *reinterpret_cast<const uint16_t*>(pI + lds_off(t0 + t, c >> 3) + ((c & 7) << 1));
+      const float x = __uint_as_float((uint32_t)hv << 16);
+      w.ksum += (double)(x * x);   // a bf16 square is exact in fp32
+    }
   }
 }
 
-__global__ void fill_i32_kernel(int* p, int64_t count, int val) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
-       i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = val;
+// Partial tile (row-major 256 x 256 fp32) and key part of one slice.  `kred`
+// is 256 doubles of LDS that no wave reads or writes any more.
+__device__ __forceinline__ void store_partial(const SyrkArgs& a, const TileJob& jb, WaveTile& w,
+                                              bool active, bool diag, int wr, int wc, int lane,
+                                              int tid, double* kred) {
+  if (diag) {   // combine the two token halves of each channel
+    if (tid >= 256) kred[tid - 256] = w.ksum;
+    __syncthreads();
+    if (tid < 256) {
+      const int64_t c = jb.ti * kSyrkTile + tid;
+      if (c < a.n) a.keyparts[jb.s * a.n + c] = w.ksum + kred[tid];
+    }
+  }
+  if (!active) return;
+  float* P = a.partials + (jb.s * a.tiles + jb.tile) * (int64_t)kTilePartial;
+  const int r0 = wr * 64 + 4 * (lane >> 5), c0 = wc * 128 + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        P[(r0 + i * 32 + 8 * (v >> 2) + (v & 3)) * kSyrkTile + c0 + j * 32] = w.acc[i][j][v];
+}
+
+__device__ __forceinline__ constexpr int vmcnt_only(int n) {   // s_waitcnt vmcnt(n), other counters free
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
+// ---------------------------------------------------------------------------
+// Aligned X: direct-to-LDS ring.  Needs ldx % 8 == 0, n % 8 == 0 and a
+// 16-byte aligned X (every 16-byte chunk is 8 whole channels of one token).
+// ---------------------------------------------------------------------------
+// The streaming loop over one slice.  The four slots come in as distinct
+// __restrict__ pointers, so every LDS access below carries no-alias scopes
+// that tell the compiler a read of one slot cannot see a copy into another:
+// it then waits only for the copies the explicit vmcnt below names.
+__device__ __forceinline__ void ring_stream(const SyrkArgs& a, const TileJob& jb, WaveTile& w,
+                                            bool active, bool diag, uint8_t* __restrict__ s0,
+                                            uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
+                                            uint8_t* __restrict__ s3) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int64_t n = a.n;
+  const int64_t nst = (jb.t_end - jb.t_begin + kSyrkStage - 1) / kSyrkStage;
+
+  // Direct-to-LDS copy: instruction (panel p, half h) of wave w writes 1 KB at
+  // slot + p·16K + h·8K + w·1K, lane l at +16·l: token row 16h + 2w + l/32,
+  // slot position l % 32, which holds channel octet o = (l%32) ^ 4·(row%4).
+  const int row0 = 2 * wave + (lane >> 5);
+  const int oct = (lane & 31) ^ ((row0 & 3) << 2);   // (row0 + 16) % 4 == row0 % 4
+  const int32_t rowb = (int32_t)(a.ldx * 2);
+  constexpr int32_t kOut = 0x7ffffff0;   // beyond any descriptor size: reads as zero
+  const int64_t cI = jb.ti * kSyrkTile + 8 * oct, cJ = jb.tj * kSyrkTile + 8 * oct;
+  const int32_t vI0 = cI < n ? row0 * rowb + (int32_t)(cI * 2) : kOut;
+  const int32_t vJ0 = cJ < n ? row0 * rowb + (int32_t)(cJ * 2) : kOut;
+  const int32_t vI1 = cI < n ? vI0 + 16 * rowb : kOut;
+  const int32_t vJ1 = cJ < n ? vJ0 + 16 * rowb : kOut;
+
+  // Stage st (possibly past the end: then the descriptor is empty and the slot
+  // fills with zeros nobody reads) -> `slot`.  Always 4 loads, so the vmcnt
+  // bookkeeping below is the same on every step.
+  auto issue = [&](int64_t st, uint8_t* slot) {
+    const int64_t t0 = jb.t_begin + st * kSyrkStage;
+    const int64_t bytes = (jb.t_end - t0) * (int64_t)rowb;
+    const int32_t nrec = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int32_t)bytes);
+    const uint16_t* base = a.X + (bytes <= 0 ? 0 : t0 * a.ldx);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, nrec, 0x00020000);
+    uint8_t* d = slot + wave * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(d), 16, vI0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(d + 8192), 16, vI1, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(d + kPanelBytes), 16, vJ0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(d + kPanelBytes + 8192), 16, vJ1, 0, 0, 0);
+  };
+  // One step: this wave's loads of stage st are the oldest 4 of the 12 in
+  // flight; after the barrier every wave's are in LDS and every wave has
+  // finished reading the slot of stage st - 1, which stage st + 3 now refills.
+  auto step = [&](int64_t st, const uint8_t* cur, uint8_t* refill) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(4 * (kRing - 2)));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    issue(st + kRing - 1, refill);
+    stage_mma(w, cur, cur + kPanelBytes, active, diag, wr, wc, lane, tid);
+  };
+  issue(0, s0);
+  issue(1, s1);
+  issue(2, s2);
+  // the stage count is rounded up to whole turns of the ring: stages past the
+  // slice read zero-filled slots and add nothing
+  for (int64_t st = 0; st < nst; st += 4) {
+    step(st, s0, s3);
+    step(st + 1, s1, s0);
+    step(st + 2, s2, s1);
+    step(st + 3, s3, s2);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));   // no copy may land after the workgroup ends
+}
+
+__global__ __launch_bounds__(512, 1) void syrk_bf16_ring_kernel(SyrkArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t slot0[kSlotBytes], slot1[kSlotBytes],
+      slot2[kSlotBytes], slot3[kSlotBytes];
+  __shared__ double kred[256];
+  static_assert(kRing == 4, "the stream loop is unrolled over four slot arrays");
+
+  TileJob jb;
+  if (!decode_job(a, jb)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;   // wave tile: rows wr*64 (+64), cols wc*128 (+128)
+  const bool diag = jb.ti == jb.tj;
+  const bool active = !(diag && wc == 1 && wr < 2);   // idle waves sit strictly above the diagonal
+  WaveTile w;
+  wave_tile_init(w);
+  ring_stream(a, jb, w, active, diag, slot0, slot1, slot2, slot3);
+  __syncthreads();
+  store_partial(a, jb, w, active, diag, wr, wc, lane, tid, kred);
+}
+
+// ---------------------------------------------------------------------------
+// Any X (unaligned rows or n % 8 != 0): element loads into registers, zero
+// outside [t_begin, t_end) x [0, n), double-buffered LDS stages.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(512, 1) void syrk_bf16_any_kernel(SyrkArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kSlotBytes];
+  __shared__ double kred[256];
+
+  TileJob jb;
+  if (!decode_job(a, jb)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const bool diag = jb.ti == jb.tj;
+  const bool active = !(diag && wc == 1 && wr < 2);
+  const int64_t n = a.n;
+  const int64_t nst = (jb.t_end - jb.t_begin + kSyrkStage - 1) / kSyrkStage;
+
+  // thread loads octet o of tokens tr + 16u (u = 0, 1) of both panels
+  const int o = tid & 31, tr = tid >> 5;
+  const int64_t cI = jb.ti * kSyrkTile + 8 * o, cJ = jb.tj * kSyrkTile + 8 * o;
+  uint4 vI[2], vJ[2];
+  auto load = [&](int64_t t0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      vI[u] = load16(a.X, a.ldx, t0 + tr + 16 * u, jb.t_end, cI, n);
+      vJ[u] = load16(a.X, a.ldx, t0 + tr + 16 * u, jb.t_end, cJ, n);
+    }
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int off = lds_off(tr + 16 * u, o);
+      *reinterpret_cast<uint4*>(&lds[buf][off]) = vI[u];
+      *reinterpret_cast<uint4*>(&lds[buf][kPanelBytes + off]) = vJ[u];
+    }
+  };
+
+  WaveTile w;
+  wave_tile_init(w);
+  if (nst > 0) {
+    load(jb.t_begin);
+    put(0);
+    __syncthreads();
+    for (int64_t st = 0; st < nst; ++st) {
+      const bool more = st + 1 < nst;
+      if (more) load(jb.t_begin + (st + 1) * kSyrkStage);
+      stage_mma(w, lds[st & 1], lds[st & 1] + kPanelBytes, active, diag, wr, wc, lane, tid);
+      if (more) put((int)((st + 1) & 1));
+      __syncthreads();
+    }
+  }
+  store_partial(a, jb, w, active, diag, wr, wc, lane, tid, kred);
+}
+
+// ---------------------------------------------------------------------------
+// Slice reduction: one workgroup per 64 x 64 block of a lower tile.  Sums the
+// slices in order, H[gi][gj] += alpha·sum for gi >= gj, then writes the mirror
+// H[gj][gi] (gi > gj) from an LDS transpose so both writes are row segments.
+// Diagonal blocks of diagonal tiles also reduce the key of their 64 channels.
+// ---------------------------------------------------------------------------
+struct ReduceArgs {
+  const float* partials;
+  const double* keyparts;
+  int64_t n, panels, tiles, splits;
+  float* H;
+  double* key;
+  float alpha;
+};
+
+__global__ __launch_bounds__(256) void syrk_reduce_kernel(ReduceArgs r) {
+  __shared__ float tb[64][65];
+  const int64_t tile = blockIdx.x >> 4;
+  const int bi = (blockIdx.x >> 2) & 3, bj = blockIdx.x & 3;
+  int64_t ti, tj;
+  tile_decode_grouped(tile, r.panels, ti, tj);
+  const bool diag = ti == tj;
+  if (diag && bj > bi) return;
+  const int tid = threadIdx.x, c = tid & 63, rq = tid >> 6;
+  const int64_t n = r.n;
+  const int64_t row0 = ti * kSyrkTile + bi * 64, col0 = tj * kSyrkTile + bj * 64;
+  const int64_t gj = col0 + c;
+
+  float sum[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) sum[k] = 0.f;
+  const float* P = r.partials + tile * (int64_t)kTilePartial + (bi * 64) * kSyrkTile + bj * 64 + c;
+  for (int64_t s = 0; s < r.splits; ++s) {
+    const float* Ps = P + s * r.tiles * (int64_t)kTilePartial;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float x = Ps[(rq + 4 * k) * kSyrkTile];
+      sum[k] = (s == 0) ? x : sum[k] + x;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int lr = rq + 4 * k;
+    const int64_t gi = row0 + lr;
+    float val = 0.f;
+    if (gi < n && gj < n && (!diag || gi >= gj)) {
+      val = r.H[gi * n + gj] + r.alpha * sum[k];
+      r.H[gi * n + gj] = val;
+    }
+    tb[lr][c] = val;
+  }
+  __syncthreads();
+  // mirror block: row gj' = col0 + lr, column gi' = row0 + c holds H[gi'][gj']
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int lr = rq + 4 * k;
+    const int64_t mrow = col0 + lr, mcol = row0 + c;   // (gj, gi) of the source element
+    if (mrow < n && mcol < n && mcol > mrow) r.H[mrow * n + mcol] = tb[c][lr];
+  }
+  if (diag && bi == bj && r.key && tid < 64) {
+    const int64_t ch = row0 + tid;
+    if (ch < n) {
+      double s = 0.0;
+      for (int64_t q = 0; q < r.splits; ++q) s += r.keyparts[q * n + ch];
+      r.key[ch] += (double)r.alpha * s;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -440,6 +542,7 @@ __global__ __launch_bounds__(256) void syrk_f32_kernel(const float* __restrict__
   }
 }
 
+
 }  // namespace
 
 SyrkPlan plan_syrk_bf16(int64_t n, int64_t tokens) {
@@ -449,8 +552,8 @@ SyrkPlan plan_syrk_bf16(int64_t n, int64_t tokens) {
   const int64_t smin = tokens > 0 ? ceil_div(tokens, kSyrkMaxSliceTokens) : 1;
   // Pick the slice count that minimises a simple time model: rounds of 256
   // resident workgroups times the per-slice MFMA time, plus the partial-tile
-  // traffic of split-K.
-  const double per_tok = (double)kSyrkTile * kSyrkTile * 2.0 / 9.8e12;   // one CU at peak
+  // traffic of the slice reduction.
+  const double per_tok = (double)kSyrkTile * kSyrkTile * 2.0 / 8.4e12;   // one CU near peak
   double best = 1e300;
   int64_t best_s = smin;
   const int64_t cands[] = {1, 2, 4, 8, 16, 24, 32, 40, 48, 56, 64};
@@ -459,18 +562,15 @@ SyrkPlan plan_syrk_bf16(int64_t n, int64_t tokens) {
     const int64_t slice = round_up(ceil_div(std::max<int64_t>(tokens, 1), c), kSyrkStage);
     const double rounds = (double)ceil_div(p.tiles * c, 256);
     double t = rounds * (double)slice * per_tok;
-    if (c > 1) t += 2.0 * (double)c * (double)p.tiles * 256.0 * 1024.0 / 4e12;
+    t += 2.0 * (double)c * (double)p.tiles * 256.0 * 1024.0 / 4e12;
     if (t < best * 0.999) { best = t; best_s = c; }
   }
   if (best_s < smin) best_s = smin;
   p.splits = best_s;
   p.slice_tokens = round_up(ceil_div(std::max<int64_t>(tokens, 1), p.splits), kSyrkStage);
-  if (p.splits > 1) {
-    p.partial_bytes = align256((size_t)p.splits * p.tiles * 256 * 256 * sizeof(float));
-    p.keypart_bytes = align256((size_t)p.splits * n * sizeof(double));
-    p.counter_bytes = align256((size_t)p.tiles * sizeof(int));
-  }
-  p.total_bytes = p.partial_bytes + p.keypart_bytes + p.counter_bytes;
+  p.partial_bytes = align256((size_t)p.splits * p.tiles * kTilePartial * sizeof(float));
+  p.keypart_bytes = align256((size_t)p.splits * n * sizeof(double));
+  p.total_bytes = p.partial_bytes + p.keypart_bytes;
   return p;
 }
 
@@ -481,23 +581,22 @@ gptq_status launch_hessian_bf16(float* H, double* key, int64_t n, const uint16_t
   a.X = X; a.ldx = ldx; a.T = tokens; a.n = n;
   a.panels = plan.panels; a.tiles = plan.tiles; a.splits = plan.splits;
   a.slice_tokens = plan.slice_tokens;
-  a.H = H; a.key = key; a.alpha = alpha;
   char* w = static_cast<char*>(ws);
-  a.partials = plan.splits > 1 ? reinterpret_cast<float*>(w) : nullptr;
-  a.keyparts = plan.splits > 1 ? reinterpret_cast<double*>(w + plan.partial_bytes) : nullptr;
-  a.counters = plan.splits > 1 ? reinterpret_cast<int*>(w + plan.partial_bytes + plan.keypart_bytes)
-                               : nullptr;
-  if (plan.splits > 1) {
-    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(plan.tiles, 256), 1024)),
-                       dim3(256), 0, stream, a.counters, plan.tiles, 0);
-    GPTQ_LAUNCH_CHECK();
-  }
+  a.partials = reinterpret_cast<float*>(w);
+  a.keyparts = reinterpret_cast<double*>(w + plan.partial_bytes);
   int64_t grid = plan.tiles * plan.splits;
   if (plan.splits % 8 != 0) grid = round_up(grid, 8);
-  // the vector path needs 16-byte rows and whole channel octets
-  const bool vec = (ldx % 8 == 0) && (n % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
-  if (vec) hipLaunchKernelGGL(syrk_bf16_kernel<true>, dim3((unsigned)grid), dim3(512), 0, stream, a);
-  else hipLaunchKernelGGL(syrk_bf16_kernel<false>, dim3((unsigned)grid), dim3(512), 0, stream, a);
+  // the ring path copies whole 16-byte channel octets with 32-bit offsets
+  const bool ring = (ldx % 8 == 0) && (n % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0) &&
+                    ldx <= (int64_t(1) << 24);
+  if (ring) hipLaunchKernelGGL(syrk_bf16_ring_kernel, dim3((unsigned)grid), dim3(512), 0, stream, a);
+  else hipLaunchKernelGGL(syrk_bf16_any_kernel, dim3((unsigned)grid), dim3(512), 0, stream, a);
+  GPTQ_LAUNCH_CHECK();
+  ReduceArgs r;
+  r.partials = a.partials; r.keyparts = a.keyparts;
+  r.n = n; r.panels = plan.panels; r.tiles = plan.tiles; r.splits = plan.splits;
+  r.H = H; r.key = key; r.alpha = alpha;
+  hipLaunchKernelGGL(syrk_reduce_kernel, dim3((unsigned)(plan.tiles * 16)), dim3(256), 0, stream, r);
   GPTQ_LAUNCH_CHECK();
   return GPTQ_OK;
 }
