@@ -1,15 +1,24 @@
 // Column quantizer for one block of 128 columns; included once per group
-// width by block_quant_g*.hip (the fully unrolled kernel takes long to
+// width by block_quant_g*.hip (the unrolled column loop takes a while to
 // compile, so each width is its own translation unit).
 //
-// One lane owns one output row.  Its 128-column slab of the working weights
-// is held in VGPRs -- every index is a template constant, generated by an
-// integer sequence -- and the rows of U's 128 x 128 diagonal block are read
-// with uniform (scalar) loads, so every update takes U from an SGPR.  Per column: the group grid at the group's first column (from
-// the current, already compensated weights), the code, e = (w - x̂)/U[c][c],
-// and w_k -= e·U[c][k] for the rest of the block.  Codes, the error block
-// and ½Σe² are written out; the columns after the block are updated by the
-// trailing GEMM.
+// GPTQ's in-block step (page "模型量化实战：从 INT8 PTQ 到 GPTQ…" §3.2,
+// quantize_block; page "大模型量化：GPTQ/AWQ/GGUF 原理对比…", section on
+// Hessian-based error compensation, for the column-by-column flow): per
+// column c, the group grid at the group's first column (from the current,
+// already compensated weights), the code, e = (w - x̂)/U[c][c], and
+// w_k -= e·U[c][k] for the rest of the block.
+//
+// Layout: 16 lanes per output row, lane j of a row holding columns 8j..8j+7
+// of the row's 128-column slab in VGPRs; a 256-thread workgroup covers 16
+// rows, so an m-row layer runs m/16 workgroups (one wave per SIMD at
+// m = 4096).  U's 128 x 128 diagonal block is staged in LDS with its strict
+// lower triangle zeroed, so every lane updates all eight of its columns with
+// no mask: columns already quantized see U[c][k] = 0 (k < c) or are never read
+// again (k = c).  The weight of column c is broadcast from its owner lane by
+// DPP row_newbcast, the group min/max is a 16-lane butterfly.  Codes, the
+// error block and ½Σe² are written out; the columns after the block are
+// updated by the trailing GEMM.
 #include <utility>
 
 #include "quant_common.hpp"
@@ -21,121 +30,146 @@
 namespace gptq {
 namespace {
 
-// Per-lane state of the column loop.  Every index into w[] is a template
-// constant, so the whole slab stays in VGPRs.
-struct ColCtx {
-  float w[QB];
+constexpr int kBqRows = 16;   // rows per workgroup: 4 waves x 4 rows
+
+// value of lane K of this lane's 16-lane row
+template <int K>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + K, 0xf, 0xf, false));
+}
+
+struct BqCtx {
+  float w[8];      // columns 8j .. 8j+7 of this lane's row
+  float e8[8];     // errors of the owned columns (lane j owns columns 8j..8j+7)
+  uint32_t c8[2];  // codes of the owned columns, one per byte
+  f32x4_t u0, u1;  // U[c][8j .. 8j+7] of the current column c (prefetched one step ahead)
+  float ud;        // U[c][c]
   float s, z, lacc;
-  uint32_t cw;
-  f32x4_t ev;
-  int bits, sym, bw;
+  int bits, sym, bw, j;
   bool act;
-  uint8_t* crow;
-  float* erow;
   float* srow;
   int32_t* zrow;
   int64_t g_base;
-  // row c of U's diagonal block at urow0 + c * ldu, 128 readable floats per
-  // row (a ragged last block reads a zero-padded copy)
-  const float* __restrict__ urow0;
-  int64_t ldu;
+  const float* us;   // LDS U block [128][128]
 };
 
 template <int GW, int C>
-__device__ __forceinline__ void col_step(ColCtx& x) {
-  if (C >= x.bw) return;
+__device__ __forceinline__ void bq_col(BqCtx& x) {
+  if (C >= x.bw) return;   // uniform: ragged last block
+  constexpr int J = C >> 3, P = C & 7;
   if constexpr (GW > 0 && C % GW == 0) {
-    float lo = x.w[C], hi = x.w[C], am = fabsf(x.w[C]);
+    // group = columns [C, C + GW) ∩ [0, bw), spread over lanes C/8 ..
+    float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf(), am = 0.f;
 #pragma unroll
-    for (int k = C + 1; k < C + GW; ++k) {
-      if (k < x.bw) {
-        lo = fminf(lo, x.w[k]);
-        hi = fmaxf(hi, x.w[k]);
-        am = fmaxf(am, fabsf(x.w[k]));
+    for (int p = 0; p < 8; ++p) {
+      const int col = 8 * x.j + p;
+      if (col >= C && col < C + GW && col < x.bw) {
+        lo = fminf(lo, x.w[p]);
+        hi = fmaxf(hi, x.w[p]);
+        am = fmaxf(am, fabsf(x.w[p]));
       }
     }
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      lo = fminf(lo, __shfl_xor(lo, d, 16));
+      hi = fmaxf(hi, __shfl_xor(hi, d, 16));
+      am = fmaxf(am, __shfl_xor(am, d, 16));
+    }
     grid_params(lo, hi, am, x.bits, x.sym, x.s, x.z);
-    if (x.act) {
+    if (x.act && x.j == 0) {
       const int64_t g = (x.g_base + C) / GW;
       x.srow[g] = x.s;
       x.zrow[g] = (int32_t)x.z;
     }
   }
-  // row C of U's diagonal block: a uniform address, so these become scalar
-  // loads and the updates below take their U operand from SGPRs
-  const float* __restrict__ urow = x.urow0 + C * x.ldu;
-  const float v = x.w[C];
+  // U of the next column, in flight while this one is quantized
+  constexpr int CN = (C + 1 < QB) ? C + 1 : C;
+  const f32x4_t n0 = *reinterpret_cast<const f32x4_t*>(x.us + CN * QB + 8 * x.j);
+  const f32x4_t n1 = *reinterpret_cast<const f32x4_t*>(x.us + CN * QB + 8 * x.j + 4);
+  const float nd = x.us[CN * QB + CN];
+  const float v = row_bcast<J>(x.w[P]);
   const float code = quant_code(v, x.s, x.z, x.bits, x.sym);
-  const float e = (v - (code - x.z) * x.s) / urow[C];
-  x.lacc += e * e;
-  x.cw |= ((uint32_t)code) << (8 * (C & 3));
-  x.ev[C & 3] = e;
-  if constexpr ((C & 3) == 3) {
-    if (x.act) {
-      *reinterpret_cast<uint32_t*>(x.crow + (C - 3)) = x.cw;
-      *reinterpret_cast<f32x4_t*>(x.erow + (C - 3)) = x.ev;
-    }
-    x.cw = 0u;
+  const float e = (v - (code - x.z) * x.s) / x.ud;
+  if (x.j == J) {
+    x.e8[P] = e;
+    x.c8[P >> 2] |= ((uint32_t)code) << (8 * (P & 3));
+    x.lacc += e * e;
   }
 #pragma unroll
-  for (int k = C + 1; k < QB; ++k) x.w[k] -= e * urow[k];
+  for (int p = 0; p < 4; ++p) {
+    x.w[p] -= e * x.u0[p];
+    x.w[p + 4] -= e * x.u1[p];
+  }
+  x.u0 = n0;
+  x.u1 = n1;
+  x.ud = nd;
 }
 
 template <int GW, int... Cs>
-__device__ __forceinline__ void run_cols(std::integer_sequence<int, Cs...>, ColCtx& x) {
-  (col_step<GW, Cs>(x), ...);
+__device__ __forceinline__ void bq_cols(std::integer_sequence<int, Cs...>, BqCtx& x) {
+  (bq_col<GW, Cs>(x), ...);
 }
 
 // GW > 0: group width (a power of two dividing 128); GW == 0: one group per
 // row, its grid already in scales/zeros.
 template <int GW>
-__global__ __launch_bounds__(64) void block_quant_kernel(QArgs q, const float* __restrict__ ublk,
+__global__ __launch_bounds__(256) void block_quant_kernel(QArgs q, const float* __restrict__ ublk,
                                                          int64_t ldu, int64_t i1, int bw) {
-  const int lane = threadIdx.x;
-  const int64_t r = (int64_t)blockIdx.x * 64 + lane;
-  const bool act = r < q.m;
-  float w[QB];
+  __shared__ __attribute__((aligned(16))) float us[QB * QB];
+  const int tid = threadIdx.x;
+  // U block: rows and columns < bw, upper triangle only (the rest zero)
+  for (int idx = tid; idx < QB * QB; idx += 256) {
+    const int r = idx >> 7, c = idx & (QB - 1);
+    us[idx] = (r < bw && c < bw && c >= r) ? ublk[r * ldu + c] : 0.f;
+  }
+
+  const int lane = tid & 63, wave = tid >> 6;
+  BqCtx x;
+  x.j = lane & 15;
+  const int64_t r = (int64_t)blockIdx.x * kBqRows + wave * 4 + (lane >> 4);
+  x.act = r < q.m;
+  const int64_t rr = x.act ? r : 0;
   {
-    const float* src = q.Wp + (act ? r : 0) * q.ldw + i1;
+    const float* src = q.Wp + rr * q.ldw + i1 + 8 * x.j;
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(src);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(src + 4);
 #pragma unroll
-    for (int c = 0; c < QB; c += 4) {
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + c);
-      w[c] = v[0]; w[c + 1] = v[1]; w[c + 2] = v[2]; w[c + 3] = v[3];
+    for (int p = 0; p < 4; ++p) {
+      x.w[p] = a[p];
+      x.w[p + 4] = b[p];
     }
   }
-  ColCtx x;
 #pragma unroll
-  for (int c = 0; c < QB; ++c) x.w[c] = w[c];
-  x.bits = q.bits; x.sym = q.sym; x.bw = bw; x.act = act;
+  for (int p = 0; p < 8; ++p) x.e8[p] = 0.f;
+  x.c8[0] = x.c8[1] = 0u;
+  x.bits = q.bits; x.sym = q.sym; x.bw = bw;
   x.s = 1.f; x.z = 0.f;
-  if (GW == 0 && act) {
-    x.s = q.scales[r * q.G];
-    x.z = (float)q.zeros[r * q.G];
+  if (GW == 0) {
+    x.s = q.scales[rr * q.G];
+    x.z = (float)q.zeros[rr * q.G];
   }
-  x.lacc = 0.f; x.cw = 0u;
-  x.ev = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  x.crow = q.codes + (act ? r : 0) * q.ldw + i1;
-  x.erow = q.err + (act ? r : 0) * QB;
-  x.srow = q.scales + (act ? r : 0) * q.G;
-  x.zrow = q.zeros + (act ? r : 0) * q.G;
+  x.lacc = 0.f;
+  x.srow = q.scales + rr * q.G;
+  x.zrow = q.zeros + rr * q.G;
   x.g_base = i1;
-  x.urow0 = ublk;
-  x.ldu = ldu;
-  run_cols<GW>(std::make_integer_sequence<int, QB>{}, x);
-  uint32_t cw = x.cw;
-  f32x4_t ev = x.ev;
+  x.us = us;
+  __syncthreads();
+  x.u0 = *reinterpret_cast<const f32x4_t*>(us + 8 * x.j);
+  x.u1 = *reinterpret_cast<const f32x4_t*>(us + 8 * x.j + 4);
+  x.ud = us[0];
+  bq_cols<GW>(std::make_integer_sequence<int, QB>{}, x);
+
   float lacc = x.lacc;
-  uint8_t* crow = x.crow;
-  float* erow = x.erow;
-  if ((bw & 3) != 0 && act) {
-    const int c0 = bw & ~3;
-    *reinterpret_cast<uint32_t*>(crow + c0) = cw;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (c0 + e >= bw) ev[e] = 0.f;
-    *reinterpret_cast<f32x4_t*>(erow + c0) = ev;
+  for (int d = 1; d < 16; d <<= 1) lacc += __shfl_xor(lacc, d, 16);
+  if (x.act) {
+    // columns >= bw carry code 0 and error 0
+    *reinterpret_cast<uint2*>(q.codes + r * q.ldw + i1 + 8 * x.j) = make_uint2(x.c8[0], x.c8[1]);
+    float* erow = q.err + r * QB + 8 * x.j;
+    *reinterpret_cast<f32x4_t*>(erow) = f32x4_t{x.e8[0], x.e8[1], x.e8[2], x.e8[3]};
+    *reinterpret_cast<f32x4_t*>(erow + 4) = f32x4_t{x.e8[4], x.e8[5], x.e8[6], x.e8[7]};
+    if (x.j == 0) q.loss_rows[r] += 0.5 * (double)lacc;
   }
-  if (act) q.loss_rows[r] += 0.5 * (double)lacc;
 }
 
 }  // namespace
@@ -143,7 +177,7 @@ __global__ __launch_bounds__(64) void block_quant_kernel(QArgs q, const float* _
 template <>
 void launch_block_quant<GPTQ_BQ_GW>(const QArgs& a, const float* ublk, int64_t ldu, int64_t i1,
                                     int bw, hipStream_t stream) {
-  hipLaunchKernelGGL(block_quant_kernel<GPTQ_BQ_GW>, dim3((unsigned)ceil_div(a.m, 64)), dim3(64), 0,
+  hipLaunchKernelGGL(block_quant_kernel<GPTQ_BQ_GW>, dim3((unsigned)ceil_div(a.m, kBqRows)), dim3(256), 0,
                      stream, a, ublk, ldu, i1, bw);
 }
 

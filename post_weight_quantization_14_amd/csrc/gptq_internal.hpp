@@ -85,7 +85,7 @@ constexpr int kQBlock = 128;
 struct QuantPlan {
   int64_t m = 0, n = 0, ldw = 0, groups = 0, words = 0;
   size_t wp_off = 0, part_off = 0, codes_off = 0, err_off = 0, loss_off = 0, inv_off = 0,
-         ublk_off = 0, flag_off = 0, total = 0;
+         flag_off = 0, total = 0;
 };
 QuantPlan plan_quantize(int64_t m, int64_t n, const gptq_config& cfg);
 gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const float* U,

@@ -23,8 +23,7 @@
 // buffer descriptor and land in LDS as zeros.
 //
 // Long token ranges are cut into `splits` slices (split-K) so the grid fills
-// 256 CUs and every fp32 register chain stays <= 32768 tokens long; with
-// splits a multiple of 8 all workgroups of one XCD share a token slice.  Each
+// 256 CUs and every fp32 register chain stays <= 32768 tokens long.  Each
 // workgroup writes its fp32 tile to a partial buffer and a second kernel sums
 // the slices in slice order (deterministic), adds the result into H's lower
 // triangle and writes the mirror, coalesced through an LDS transpose.  No
@@ -104,22 +103,29 @@ __device__ __forceinline__ void tile_decode_grouped(int64_t t, int64_t panels, i
   ti = tj = 0;   // not reached for t < tiles
 }
 
-// Workgroup -> (tile, slice, tile coordinates).  Without slices-per-XCD,
-// contiguous logical ranges are spread over the 8 XCDs (dispatch is
-// round-robin over XCDs).  Returns false for padding workgroups.
+// Workgroup -> (tile, slice, tile coordinates).  Jobs run in rounds of 256
+// workgroups (one per CU) that stream the same token slice: chunks of 256
+// tiles, and within a chunk one slice after the other.  Dispatch is
+// round-robin over the 8 XCDs, so inside a round XCD x gets the 32
+// consecutive tiles 32x .. 32x + 31 of the chunk (in the grouped order about a
+// 4 x 8 block, 12 panels), which share panel reads in that XCD's L2; the
+// other XCDs read other panels of the same tokens, which the shared memory-side
+// cache can serve.  Returns false for padding workgroups.
 struct TileJob {
   int64_t tile, s, ti, tj, t_begin, t_end;
 };
 __device__ __forceinline__ bool decode_job(const SyrkArgs& a, TileJob& j) {
-  const int64_t total = a.tiles * a.splits;
-  int64_t b = blockIdx.x;
-  if (a.splits % 8 != 0) {
-    const int64_t per = (total + 7) / 8;
-    b = (b % 8) * per + b / 8;
-    if (b >= total) return false;
-  }
-  j.tile = b / a.splits;
-  j.s = b % a.splits;
+  const int64_t L = blockIdx.x;
+  if (L >= a.tiles * a.splits) return false;
+  const int64_t per_chunk = 256 * a.splits;
+  const int64_t c = L / per_chunk, cb = c * 256;
+  const int64_t csz = (a.tiles - cb < 256) ? a.tiles - cb : 256;
+  const int64_t rem = L - c * per_chunk;
+  j.s = rem / csz;
+  const int64_t q = rem % csz;
+  // with csz % 8 == 0 the round starts on an XCD boundary: position q runs on
+  // XCD q % 8 and takes tile (q % 8)·csz/8 + q/8 of the chunk
+  j.tile = cb + ((csz % 8 == 0) ? (q % 8) * (csz / 8) + q / 8 : q);
   tile_decode_grouped(j.tile, a.panels, j.ti, j.tj);
   j.t_begin = j.s * a.slice_tokens;
   j.t_end = (j.t_begin + a.slice_tokens < a.T) ? j.t_begin + a.slice_tokens : a.T;
@@ -584,8 +590,7 @@ gptq_status launch_hessian_bf16(float* H, double* key, int64_t n, const uint16_t
   char* w = static_cast<char*>(ws);
   a.partials = reinterpret_cast<float*>(w);
   a.keyparts = reinterpret_cast<double*>(w + plan.partial_bytes);
-  int64_t grid = plan.tiles * plan.splits;
-  if (plan.splits % 8 != 0) grid = round_up(grid, 8);
+  const int64_t grid = plan.tiles * plan.splits;
   // the ring path copies whole 16-byte channel octets with 32-bit offsets
   const bool ring = (ldx % 8 == 0) && (n % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0) &&
                     ldx <= (int64_t(1) << 24);

@@ -48,9 +48,10 @@ __device__ __forceinline__ float quant_code(float w, float s, float z, int bits,
 }
 
 
-// One block of 128 columns for rows [64·blockIdx, +64); GW = group width or 0
-// for one group per row.  ublk points at U[i1][i1] with row stride ldu and
-// must allow 128 reads per row.  Instantiated in block_quant_g*.hip.
+// One block of bw <= 128 columns starting at processed column i1, all rows;
+// GW = group width or 0 for one group per row.  ublk points at U[i1][i1] with
+// row stride ldu; only rows and columns < bw of the block are read.
+// Instantiated in block_quant_g*.hip.
 template <int GW>
 void launch_block_quant(const QArgs& a, const float* ublk, int64_t ldu, int64_t i1, int bw,
                         hipStream_t stream);

@@ -162,13 +162,6 @@ __global__ __launch_bounds__(1024) void loss_reduce_kernel(const double* loss_ro
   }
 }
 
-// out[c][k] = U[i1 + c][i1 + k] inside the bw x bw block, 0 elsewhere (128 x 128).
-__global__ __launch_bounds__(128) void pad_block_kernel(const float* __restrict__ U, int64_t ldu,
-                                                        int64_t i1, int bw, float* __restrict__ out) {
-  const int c = blockIdx.x, k = threadIdx.x;
-  out[c * QB + k] = (c < bw && k < bw) ? U[(i1 + c) * ldu + i1 + k] : 0.f;
-}
-
 __global__ void zero_f64_kernel(double* p, int64_t count) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -194,7 +187,6 @@ QuantPlan plan_quantize(int64_t m, int64_t n, const gptq_config& cfg) {
   p.err_off = off; off += align256((size_t)m * QB * sizeof(float));
   p.loss_off = off; off += align256((size_t)m * sizeof(double));
   p.inv_off = off; off += align256((size_t)n * sizeof(int32_t));
-  p.ublk_off = off; off += align256((size_t)QB * QB * sizeof(float));
   p.flag_off = off; off += 256;
   p.total = off;
   return p;
@@ -212,7 +204,6 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
   double* loss_rows = reinterpret_cast<double*>(w + p.loss_off);
   int32_t* invperm = reinterpret_cast<int32_t*>(w + p.inv_off);
   int* flag = reinterpret_cast<int*>(w + p.flag_off);
-  float* ubuf = reinterpret_cast<float*>(w + p.ublk_off);
 
   GPTQ_HIP_CHECK(hipMemsetAsync(flag, 0, sizeof(int), stream));
   hipLaunchKernelGGL(zero_f64_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(m, 256), 1024)),
@@ -249,16 +240,9 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
 
   for (int64_t i1 = 0; i1 < n; i1 += QB) {
     const int bw = (int)std::min<int64_t>(QB, n - i1);
-    // the quantizer reads 128 values per row of U's diagonal block; a ragged
-    // last block reads a zero-padded copy instead of running past U's end
+    // the quantizer reads only rows and columns < bw of U's diagonal block
     const float* ublk = U + i1 * n + i1;
-    int64_t ldub = n;
-    if (bw < QB) {
-      hipLaunchKernelGGL(pad_block_kernel, dim3(QB), dim3(QB), 0, stream, U, n, i1, bw, ubuf);
-      GPTQ_LAUNCH_CHECK();
-      ublk = ubuf;
-      ldub = QB;
-    }
+    const int64_t ldub = n;
     switch (gw) {
       case -1: launch_block_quant<0>(a, ublk, ldub, i1, bw, stream); break;
       case 8: launch_block_quant<8>(a, ublk, ldub, i1, bw, stream); break;
