@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs q, const float* 
   if (x.act) {
     // columns >= bw carry code 0 and error 0
     *reinterpret_cast<uint2*>(q.codes + r * q.ldw + i1 + 8 * x.j) = make_uint2(x.c8[0], x.c8[1]);
-    float* erow = q.err + r * QB + 8 * x.j;
+    float* erow = q.err + r * q.lde + 8 * x.j;
     *reinterpret_cast<f32x4_t*>(erow) = f32x4_t{x.e8[0], x.e8[1], x.e8[2], x.e8[3]};
     *reinterpret_cast<f32x4_t*>(erow + 4) = f32x4_t{x.e8[4], x.e8[5], x.e8[6], x.e8[7]};
     if (x.j == 0) q.loss_rows[r] += 0.5 * (double)lacc;

@@ -131,6 +131,9 @@ __device__ __forceinline__ void gemm_tile_acc(const float* __restrict__ A, int64
 
 // C tile update.  Element (i, j) of the tile sits in lane j % 32 + 32 * ((i / 4) % 2),
 // register (i % 4) + 4 * (i / 8) of the 32 x 32 block (the MFMA output layout).
+// Per 32 x 32 block, the 16 reads of C are issued before its 16 writes:
+// interleaved, each read would wait for the store before it (same base
+// pointer), serialising one memory latency per element.
 template <bool LOWER>
 __device__ __forceinline__ void gemm_tile_store(float* __restrict__ C, int64_t ldc, int64_t c_rows,
                                                 int64_t c_cols, int64_t diag_off, float alpha,
@@ -143,17 +146,23 @@ __device__ __forceinline__ void gemm_tile_store(float* __restrict__ C, int64_t l
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
+    for (int bj = 0; bj < 2; ++bj) {
+      const int j = wc * 64 + bj * 32 + li;
+      const int ib = wr * 64 + bi * 32 + 4 * lk;
+      float old[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int i = wr * 64 + bi * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
-        const int j = wc * 64 + bj * 32 + li;
-        if (i < c_rows && j < c_cols && (!LOWER || i + diag_off >= j)) {
-          float* p = C + (int64_t)i * ldc + j;
-          const float x = alpha * acc[bi][bj][v];
-          *p = (beta == 0.f) ? x : x + beta * *p;
-        }
+        const int i = ib + 8 * (v >> 2) + (v & 3);
+        const bool in = i < c_rows && j < c_cols && (!LOWER || i + diag_off >= j);
+        old[v] = (beta != 0.f && in) ? C[(int64_t)i * ldc + j] : 0.f;
       }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int i = ib + 8 * (v >> 2) + (v & 3);
+        const bool in = i < c_rows && j < c_cols && (!LOWER || i + diag_off >= j);
+        if (in) C[(int64_t)i * ldc + j] = alpha * acc[bi][bj][v] + beta * old[v];
+      }
+    }
 }
 
 template <bool BCOL, bool VEC>
@@ -177,11 +186,21 @@ __device__ __forceinline__ void tri_decode(int64_t t, int64_t& ti, int64_t& tj) 
   tj = t - r * (r + 1) / 2;
 }
 
+// Lower part (i >= j) of an M x N result with M >= N: first the triangle of
+// tiles over the top N rows, then the full tiles of the rows below.
 template <bool BCOL, bool VEC>
 __global__ __launch_bounds__(256) void gemm_lower_kernel(GemmArgs g) {
   __shared__ GemmSmem sm;
+  const int64_t nt = (g.N + GT - 1) / GT;
+  const int64_t tri = nt * (nt + 1) / 2;
   int64_t ti, tj;
-  tri_decode(blockIdx.x, ti, tj);
+  if ((int64_t)blockIdx.x < tri) {
+    tri_decode(blockIdx.x, ti, tj);
+  } else {
+    const int64_t r = (int64_t)blockIdx.x - tri;
+    ti = nt + r / nt;
+    tj = r % nt;
+  }
   const int64_t i0 = ti * GT, j0 = tj * GT;
   const float* A = g.A + i0 * g.lda;
   const float* B = BCOL ? g.B + j0 * g.ldb : g.B + j0;
@@ -274,8 +293,12 @@ gptq_status launch_gemm_rect(const GemmArgs& g, bool b_colmajor, hipStream_t str
 
 gptq_status launch_gemm_lower(const GemmArgs& g, bool b_colmajor, hipStream_t stream) {
   if (g.M <= 0 || g.N <= 0) return GPTQ_OK;
-  const int64_t t = ceil_div(g.M, GT);
-  dim3 grid((unsigned)(t * (t + 1) / 2));
+  if (g.M < g.N) {
+    set_error("launch_gemm_lower: M (%lld) < N (%lld)", (long long)g.M, (long long)g.N);
+    return GPTQ_ERR_INVALID_ARG;
+  }
+  const int64_t mt = ceil_div(g.M, GT), nt = ceil_div(g.N, GT);
+  dim3 grid((unsigned)(nt * (nt + 1) / 2 + (mt - nt) * nt));
   const bool v = vec_ok(g, b_colmajor);
   if (b_colmajor) {
     if (v) hipLaunchKernelGGL((gemm_lower_kernel<true, true>), grid, dim3(256), 0, stream, g);

@@ -105,8 +105,9 @@ struct GemmArgs {
   float alpha, beta;
 };
 gptq_status launch_gemm_rect(const GemmArgs& g, bool b_colmajor, hipStream_t stream);
-// Lower-triangular output tiles only (tile row >= tile column), M == N: the
-// trailing update of a right-looking Cholesky.
+// Lower part only (element row >= column) of an M x N result, M >= N: the
+// trailing updates of the blocked Cholesky (a triangle, or a triangle over a
+// rectangle of full tiles).
 gptq_status launch_gemm_lower(const GemmArgs& g, bool b_colmajor, hipStream_t stream);
 // One level of the blocked triangular inverse (see prepare.hip).
 gptq_status launch_trtri_level(float* Amat, float* Mmat, int64_t lda, int64_t nblk, int64_t half,

@@ -388,28 +388,50 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
                      (const float*)H, n, (const int32_t*)perm, (const double*)lam, A, lda);
   GPTQ_LAUNCH_CHECK();
 
-  // blocked right-looking Cholesky of A (lower), leaf inverses into Mm
-  for (int64_t kb = 0; kb < p.nblk; ++kb) {
-    const int64_t k0 = kb * NB;
-    hipLaunchKernelGGL(chol_leaf_kernel, dim3(1), dim3(256), 0, stream, A, Mm, lda, k0, flag);
-    GPTQ_LAUNCH_CHECK();
-    const int64_t rows = p.n_pad - k0 - NB;
-    if (rows <= 0) break;
-    GemmArgs g;
-    // panel solve: P = A_panel · D_kᵀ  (D_kᵀ read column-major from D_k)
-    g.A = A + (k0 + NB) * lda + k0; g.lda = lda;
-    g.B = Mm + k0 * lda + k0; g.ldb = lda;
-    g.C = A + (k0 + NB) * lda + k0; g.ldc = lda;
-    g.M = rows; g.N = NB; g.k_begin = 0; g.k_end = NB; g.alpha = 1.f; g.beta = 0.f;
-    gptq_status st = launch_gemm_rect(g, /*b_colmajor=*/true, stream);
-    if (st != GPTQ_OK) return st;
-    // trailing update: A22 -= P Pᵀ on lower tiles
-    g.A = A + (k0 + NB) * lda + k0; g.lda = lda;
-    g.B = A + (k0 + NB) * lda + k0; g.ldb = lda;
-    g.C = A + (k0 + NB) * lda + k0 + NB; g.ldc = lda;
-    g.M = rows; g.N = rows; g.k_begin = 0; g.k_end = NB; g.alpha = -1.f; g.beta = 1.f;
-    st = launch_gemm_lower(g, /*b_colmajor=*/true, stream);
-    if (st != GPTQ_OK) return st;
+  // Blocked right-looking Cholesky of A (lower), leaf inverses into Mm, with
+  // two levels of trailing update (exact: the same products, grouped).  A
+  // 128-panel updates only the rest of its 512-column outer block (all rows
+  // below, K = 128); the columns after the outer block are updated once per
+  // outer block from its four panels (K = 512), so the trailing matrix is read
+  // and written a quarter as often.
+  constexpr int64_t OB = 4 * NB;
+  for (int64_t K0 = 0; K0 < p.n_pad; K0 += OB) {
+    const int64_t K1 = std::min<int64_t>(K0 + OB, p.n_pad);
+    for (int64_t k0 = K0; k0 < K1; k0 += NB) {
+      hipLaunchKernelGGL(chol_leaf_kernel, dim3(1), dim3(256), 0, stream, A, Mm, lda, k0, flag);
+      GPTQ_LAUNCH_CHECK();
+      const int64_t rows = p.n_pad - k0 - NB;
+      if (rows <= 0) break;
+      GemmArgs g;
+      // panel solve: P = A_panel · D_kᵀ  (D_kᵀ read column-major from D_k)
+      g.A = A + (k0 + NB) * lda + k0; g.lda = lda;
+      g.B = Mm + k0 * lda + k0; g.ldb = lda;
+      g.C = A + (k0 + NB) * lda + k0; g.ldc = lda;
+      g.M = rows; g.N = NB; g.k_begin = 0; g.k_end = NB; g.alpha = 1.f; g.beta = 0.f;
+      gptq_status st = launch_gemm_rect(g, /*b_colmajor=*/true, stream);
+      if (st != GPTQ_OK) return st;
+      // inner update: A[k0+NB:, k0+NB:K1] -= P · P[k0+NB:K1]ᵀ (lower part)
+      const int64_t cols = K1 - k0 - NB;
+      if (cols > 0) {
+        g.A = A + (k0 + NB) * lda + k0; g.lda = lda;
+        g.B = A + (k0 + NB) * lda + k0; g.ldb = lda;
+        g.C = A + (k0 + NB) * lda + k0 + NB; g.ldc = lda;
+        g.M = rows; g.N = cols; g.k_begin = 0; g.k_end = NB; g.alpha = -1.f; g.beta = 1.f;
+        st = launch_gemm_lower(g, /*b_colmajor=*/true, stream);
+        if (st != GPTQ_OK) return st;
+      }
+    }
+    // outer update: A[K1:, K1:] -= L[K1:, K0:K1] · L[K1:, K0:K1]ᵀ (lower part)
+    const int64_t rest = p.n_pad - K1;
+    if (rest > 0) {
+      GemmArgs g;
+      g.A = A + K1 * lda + K0; g.lda = lda;
+      g.B = A + K1 * lda + K0; g.ldb = lda;
+      g.C = A + K1 * lda + K1; g.ldc = lda;
+      g.M = rest; g.N = rest; g.k_begin = 0; g.k_end = K1 - K0; g.alpha = -1.f; g.beta = 1.f;
+      gptq_status st = launch_gemm_lower(g, /*b_colmajor=*/true, stream);
+      if (st != GPTQ_OK) return st;
+    }
   }
   // triangular inverse: doubling levels over the leaf inverses
   for (int64_t half = 1; half < p.nblk; half *= 2) {

@@ -7,6 +7,10 @@
 namespace gptq {
 
 constexpr int QB = kQBlock;
+// Columns per superblock of the two-level lazy update: inside a superblock a
+// block's errors update only the superblock's later columns; the columns after
+// it are updated once, from all of its errors (K = 512).
+constexpr int kQSuper = 4 * QB;
 
 struct QArgs {
   float* Wp;          // [m][ldw] working weights, processing order
@@ -17,7 +21,8 @@ struct QArgs {
   float* scales;      // [m][G]
   int32_t* zeros;     // [m][G]
   int64_t G;
-  float* err;         // [m][128]
+  float* err;         // [m][lde]: errors of the current block start here
+  int64_t lde;
   uint8_t* codes;     // [m][ldw], processing order
   double* loss_rows;  // [m]
 };

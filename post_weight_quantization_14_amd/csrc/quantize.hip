@@ -184,7 +184,7 @@ QuantPlan plan_quantize(int64_t m, int64_t n, const gptq_config& cfg) {
   p.part_off = off;  // pack partials: one double per (row, word-block)
   off += align256((size_t)m * bpr * sizeof(double));
   p.codes_off = off; off += align256((size_t)m * p.ldw);
-  p.err_off = off; off += align256((size_t)m * QB * sizeof(float));
+  p.err_off = off; off += align256((size_t)m * kQSuper * sizeof(float));
   p.loss_off = off; off += align256((size_t)m * sizeof(double));
   p.inv_off = off; off += align256((size_t)n * sizeof(int32_t));
   p.flag_off = off; off += 256;
@@ -236,32 +236,50 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
   QArgs a;
   a.Wp = Wp; a.ldw = p.ldw; a.m = m; a.n = n; a.U = U; a.ldu = n;
   a.bits = cfg.bits; a.sym = cfg.sym; a.scales = scales; a.zeros = zeros; a.G = p.groups;
-  a.err = err; a.codes = codes; a.loss_rows = loss_rows;
+  a.err = err; a.lde = kQSuper; a.codes = codes; a.loss_rows = loss_rows;
 
-  for (int64_t i1 = 0; i1 < n; i1 += QB) {
-    const int bw = (int)std::min<int64_t>(QB, n - i1);
-    // the quantizer reads only rows and columns < bw of U's diagonal block
-    const float* ublk = U + i1 * n + i1;
-    const int64_t ldub = n;
-    switch (gw) {
-      case -1: launch_block_quant<0>(a, ublk, ldub, i1, bw, stream); break;
-      case 8: launch_block_quant<8>(a, ublk, ldub, i1, bw, stream); break;
-      case 16: launch_block_quant<16>(a, ublk, ldub, i1, bw, stream); break;
-      case 32: launch_block_quant<32>(a, ublk, ldub, i1, bw, stream); break;
-      case 64: launch_block_quant<64>(a, ublk, ldub, i1, bw, stream); break;
-      case 128: launch_block_quant<128>(a, ublk, ldub, i1, bw, stream); break;
-      default:
-        set_error("group_size %d not built", gw);
-        return GPTQ_ERR_UNSUPPORTED;
+  // Two-level lazy update (exact: the same rank-1 corrections, grouped).  A
+  // block's errors update the rest of its 512-column superblock at once
+  // (K = 128); the columns after the superblock are updated once per
+  // superblock from all of its errors (K = 512), so the working weights are
+  // read and written a quarter as often as with per-block updates.
+  for (int64_t s1 = 0; s1 < n; s1 += kQSuper) {
+    const int64_t s2 = std::min<int64_t>(s1 + kQSuper, n);
+    for (int64_t i1 = s1; i1 < s2; i1 += QB) {
+      const int bw = (int)std::min<int64_t>(QB, s2 - i1);
+      // the quantizer reads only rows and columns < bw of U's diagonal block
+      const float* ublk = U + i1 * n + i1;
+      const int64_t ldub = n;
+      a.err = err + (i1 - s1);
+      switch (gw) {
+        case -1: launch_block_quant<0>(a, ublk, ldub, i1, bw, stream); break;
+        case 8: launch_block_quant<8>(a, ublk, ldub, i1, bw, stream); break;
+        case 16: launch_block_quant<16>(a, ublk, ldub, i1, bw, stream); break;
+        case 32: launch_block_quant<32>(a, ublk, ldub, i1, bw, stream); break;
+        case 64: launch_block_quant<64>(a, ublk, ldub, i1, bw, stream); break;
+        case 128: launch_block_quant<128>(a, ublk, ldub, i1, bw, stream); break;
+        default:
+          set_error("group_size %d not built", gw);
+          return GPTQ_ERR_UNSUPPORTED;
+      }
+      GPTQ_LAUNCH_CHECK();
+      const int64_t i2 = i1 + bw;
+      if (i2 < s2) {   // W_p[:, i2:s2] -= Err_block · U[i1:i2, i2:s2]
+        GemmArgs g;
+        g.A = a.err; g.lda = kQSuper;
+        g.B = U + i1 * n + i2; g.ldb = n;
+        g.C = Wp + i2; g.ldc = p.ldw;
+        g.M = m; g.N = s2 - i2; g.k_begin = 0; g.k_end = bw; g.alpha = -1.f; g.beta = 1.f;
+        gptq_status st = launch_gemm_rect(g, /*b_colmajor=*/false, stream);
+        if (st != GPTQ_OK) return st;
+      }
     }
-    GPTQ_LAUNCH_CHECK();
-    const int64_t i2 = i1 + bw;
-    if (i2 < n) {
+    if (s2 < n) {   // W_p[:, s2:] -= Err_super · U[s1:s2, s2:]
       GemmArgs g;
-      g.A = err; g.lda = QB;
-      g.B = U + i1 * n + i2; g.ldb = n;
-      g.C = Wp + i2; g.ldc = p.ldw;
-      g.M = m; g.N = n - i2; g.k_begin = 0; g.k_end = bw; g.alpha = -1.f; g.beta = 1.f;
+      g.A = err; g.lda = kQSuper;
+      g.B = U + s1 * n + s2; g.ldb = n;
+      g.C = Wp + s2; g.ldc = p.ldw;
+      g.M = m; g.N = n - s2; g.k_begin = 0; g.k_end = s2 - s1; g.alpha = -1.f; g.beta = 1.f;
       gptq_status st = launch_gemm_rect(g, /*b_colmajor=*/false, stream);
       if (st != GPTQ_OK) return st;
     }
