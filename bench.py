@@ -245,7 +245,7 @@ def main():
         "xtx_tflops": syrk_tflops,
         "roofline": {
             "bound": "mfma",
-            "kernel": "syrk_bf16_kernel (H += 2·XᵀX)",
+            "kernel": "gptq_hessian_accumulate = syrk_bf16_ring_kernel + syrk_reduce_kernel (H += 2·XᵀX)",
             "achieved": syrk_tflops,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
