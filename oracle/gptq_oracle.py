@@ -199,7 +199,7 @@ def _group_width(g, n):
     return n if g == -1 else g
 
 
-def gptq_quantize(Wp, U, bits, group_size, sym, block=None):
+def gptq_quantize(Wp, U, bits, group_size, sym, block=None, forced=None, tie_tol=1e-3):
     """GPTQ on permuted weights Wp [m, n] with the inverse factor U [n, n].
 
     For each processed column c in order:
@@ -211,6 +211,13 @@ def gptq_quantize(Wp, U, bits, group_size, sym, block=None):
     block=B defers updates beyond the current B-column block and applies them
     with one matrix product when the block ends; it computes the same thing
     (only the order of the additions to each w_k changes).
+
+    forced (codes [m,n], processed order) replays another implementation's
+    decisions: at every column where its code differs from this one, the
+    difference must be one step at a rounding boundary (the unrounded grid
+    position within tie_tol steps of the half-way point), and the forced code is
+    used from there on, so both sides stay on the same trajectory.  The result
+    then also holds replay = dict(flips, bad, max_tie_dist).
 
     Returns dict(codes [m,n] processed order, scales [m,G], zeros [m,G],
     err [m,n], loss0 = ½Σe²).
@@ -229,6 +236,7 @@ def gptq_quantize(Wp, U, bits, group_size, sym, block=None):
     if block is not None and group_size != -1 and block % group_size != 0:
         raise ValueError("block must be a multiple of group_size")
     s = z = None
+    replay = dict(flips=0, bad=0, max_tie_dist=0.0)
     for i1 in range(0, n, max(B, 1)):
         i2 = min(i1 + B, n)
         for c in range(i1, i2):
@@ -237,6 +245,19 @@ def gptq_quantize(Wp, U, bits, group_size, sym, block=None):
                 scales[:, c // gw] = s
                 zeros[:, c // gw] = z
             q = quantize_values(W[:, c], s, z, bits, sym)
+            if forced is not None:
+                qf = np.asarray(forced[:, c], dtype=np.float64)
+                d = qf != q
+                if d.any():
+                    # position on the grid before rounding, in code units
+                    x = W[d, c] / s[d] + (0.0 if sym else z[d])
+                    lo = np.minimum(q[d], qf[d]) - (z[d] if sym else 0.0)
+                    dist = np.abs(x - (lo + 0.5))
+                    ok = (np.abs(qf[d] - q[d]) == 1) & (dist <= tie_tol)
+                    replay["flips"] += int(d.sum())
+                    replay["bad"] += int((~ok).sum())
+                    replay["max_tie_dist"] = max(replay["max_tie_dist"], float(dist.max()))
+                q = qf
             e = (W[:, c] - dequantize_values(q, s, z)) / U[c, c]
             codes[:, c] = q
             err[:, c] = e
@@ -244,8 +265,11 @@ def gptq_quantize(Wp, U, bits, group_size, sym, block=None):
             W[:, c + 1:i2] -= np.outer(e, U[c, c + 1:i2])
         if i2 < n:
             W[:, i2:] -= err[:, i1:i2] @ U[i1:i2, i2:]
-    return dict(codes=codes.astype(np.int64), scales=scales,
-                zeros=zeros.astype(np.int64), err=err, loss0=loss0)
+    out = dict(codes=codes.astype(np.int64), scales=scales,
+               zeros=zeros.astype(np.int64), err=err, loss0=loss0)
+    if forced is not None:
+        out["replay"] = replay
+    return out
 
 
 def rtn_quantize(Wp, bits, group_size, sym):
@@ -321,7 +345,7 @@ def loss_terms(W, Qhat, H, lam):
     """(½·tr(ΔW H_d ΔWᵀ), ‖ΔW‖²_F) with ΔW = W - Q̂ in original order, H_d = H + λI."""
     dW = np.asarray(W, dtype=np.float64) - Qhat
     Hd = np.asarray(H, dtype=np.float64) + lam * np.eye(dW.shape[1])
-    return 0.5 * float(np.einsum("ij,jk,ik->", dW, Hd, dW)), float(np.sum(dW * dW))
+    return 0.5 * float(np.sum((dW @ Hd) * dW)), float(np.sum(dW * dW))
 
 
 # ---------------------------------------------------------------------------

@@ -43,6 +43,7 @@ HESSIAN_CASES = [
     dict(m=16, n=384, tokens=70000),
     dict(m=16, n=64, tokens=5),
     dict(m=16, n=136, tokens=300, x_dtype="fp32"),
+    dict(m=16, n=2600, tokens=70000),
 ]
 
 
@@ -94,7 +95,8 @@ def test_hessian_accumulates_over_calls_and_is_deterministic(pq):
 
 
 # ---------------------------------------------------------------- stages 2-3
-PREPARE_CASES = [(128, True), (200, True), (256, False), (384, True), (1000, True), (1, True)]
+PREPARE_CASES = [(128, True), (200, True), (256, False), (384, True), (1000, True), (1, True),
+                 (1500, True)]
 
 
 @pytest.mark.parametrize("n,desc", PREPARE_CASES, ids=lambda v: str(v))
@@ -164,6 +166,9 @@ QUANT_CASES = [
     dict(m=40, n=130, tokens=1200, bits=4, group_size=-1, sym=False, desc_act=True),
     dict(m=40, n=130, tokens=1200, bits=3, group_size=16, sym=True, desc_act=False),
     dict(m=1, n=72, tokens=500, bits=4, group_size=8, sym=False, desc_act=True),
+    # several 512-column superblocks, ragged last block
+    dict(m=48, n=1100, tokens=4400, bits=4, group_size=128, sym=False, desc_act=True),
+    dict(m=40, n=1540, tokens=6000, bits=3, group_size=64, sym=True, desc_act=True),
 ]
 
 

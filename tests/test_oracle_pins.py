@@ -362,3 +362,40 @@ def test_pack_layout():
     for bits in (2, 3, 4, 8):
         Q = rng.integers(0, 2 ** bits, size=(3, 21))
         assert np.array_equal(oracle.unpack_codes(oracle.pack_codes(Q, bits), 21, bits), Q)
+
+
+# ---------------------------------------------------------------------------
+# Replay of another implementation's decisions (used by the full-size GPU
+# parity): hand case with an exact half-way point.
+#   row [1.25, -1.5, 6.0], 4-bit asym, one group: s = 7.5/15 = 0.5,
+#   z = rne(1.5/0.5) = 3; column 0 sits at 1.25/0.5 + 3 = 5.5 exactly, which
+#   rounds half-to-even to 6.  With U = [[1, .5, .25], [0, 1, .5], [0, 0, 1]]:
+#   code 6 -> e0 = -0.25, column 1 at 0.25 -> 0, column 2 at 15 -> codes [6, 0, 15];
+#   code 5 -> e0 = +0.25, column 1 at -0.25 -> 0, column 2 at 15 -> codes [5, 0, 15].
+# ---------------------------------------------------------------------------
+_TIE_W = np.array([[1.25, -1.5, 6.0]])
+_TIE_U = np.array([[1.0, 0.5, 0.25], [0.0, 1.0, 0.5], [0.0, 0.0, 1.0]])
+
+
+def test_replay_hand_tie():
+    own = go.gptq_quantize(_TIE_W, _TIE_U, 4, -1, False)
+    assert own["codes"].tolist() == [[6, 0, 15]]
+    rep = go.gptq_quantize(_TIE_W, _TIE_U, 4, -1, False, forced=np.array([[5, 0, 15]]))
+    assert rep["codes"].tolist() == [[5, 0, 15]]
+    assert rep["replay"] == dict(flips=1, bad=0, max_tie_dist=0.0)
+    assert rep["err"][0].tolist() == [0.25, -0.125, 0.0]
+    for wrong in ([[7, 0, 15]], [[4, 0, 15]], [[6, 1, 15]]):
+        r = go.gptq_quantize(_TIE_W, _TIE_U, 4, -1, False, forced=np.array(wrong))
+        assert r["replay"]["bad"] >= 1, wrong
+
+
+def test_replay_of_own_codes_changes_nothing():
+    rng = np.random.default_rng(3)
+    m, n = 6, 40
+    A = rng.standard_normal((n, 2 * n))
+    U, perm, lam = oracle.prepare(A @ A.T, None, 0.01, True)
+    Wp = 0.02 * rng.standard_normal((m, n))
+    own = go.gptq_quantize(Wp, U, 3, 8, True)
+    rep = go.gptq_quantize(Wp, U, 3, 8, True, forced=own["codes"])
+    assert rep["replay"] == dict(flips=0, bad=0, max_tie_dist=0.0)
+    assert np.array_equal(rep["codes"], own["codes"]) and rep["loss0"] == own["loss0"]
