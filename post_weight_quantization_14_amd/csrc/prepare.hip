@@ -131,20 +131,28 @@ __global__ __launch_bounds__(256) void permute_kernel(const float* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // Leaf: Cholesky of the 128 x 128 diagonal block at (k0, k0), then its inverse.
-// The block is cut into 16 x 16 sub-blocks of 8 x 8; thread t < 136 owns the
-// t-th lower sub-block (bi, bj) in registers.  Both phases run 16 block steps
-// with static 8 x 8 kernels in registers and 8 x 8 operands shared through
-// LDS (sub-block stride 68 floats: distinct bank groups per sub-block row):
-//   Cholesky, step jb: the owner of (jb, jb) factors it; owners of (bi, jb)
-//     solve X · L_jbᵀ = A_bi,jb; owners of (bi, bj), jb < bj <= bi, subtract
-//     L_bi,jb · L_bj,jbᵀ.
+// The block is cut into 8 x 8 sub-blocks of 16 x 16; threads 16t .. 16t+15
+// (t < 36) serve the t-th lower sub-block (bi, bj), thread 16t + r holding its
+// row r (Cholesky) or column r (inverse) in registers.  The 16 threads of a
+// sub-block are one 16-lane row of a wave.  Both phases run 8 block steps with
+// operands through LDS (row pitch 20 floats: 16-byte aligned rows, and the 16
+// rows of a sub-block on distinct bank quads):
+//   Cholesky, step jb: the lanes of (jb, jb) factor it column by column,
+//     broadcasting within their row by DPP row_newbcast; owners of (bi, jb)
+//     solve X · L_jbᵀ = A_bi,jb along their row; owners of (bi, bj),
+//     jb < bj <= bi, subtract L_bi,jb · L_bj,jbᵀ.
 //   Inverse (R = I, row block kb per step): owners of (kb, bj) solve
-//     L_kb,kb · M_kb,bj = R_kb,bj; owners of (bi, bj), bi > kb, bj <= kb,
-//     subtract L_bi,kb · M_kb,bj.
-// Writes L back into A and D = L⁻¹ into the same block of Mmat (strict upper
-// part of that block set to 0).
+//     L_kb,kb · M_kb,bj = R_kb,bj down their column; owners of (bi, bj),
+//     bi > kb, bj <= kb, subtract L_bi,kb · M_kb,bj.
+// Writes L back into A (lower triangle of the block) and D = L⁻¹ into the same
+// block of Mmat (strict upper part of that block set to 0).
 // ---------------------------------------------------------------------------
-constexpr int SB = 68;   // LDS stride of one 8 x 8 sub-block (floats)
+constexpr int LE = 16;                  // sub-block edge
+constexpr int LN = NB / LE;             // sub-blocks per side
+constexpr int LT = LN * (LN + 1) / 2;   // lower sub-blocks
+constexpr int LP = 20;                  // LDS row pitch (floats)
+constexpr int LSZ = LE * LP;            // floats per stored sub-block
+constexpr int kLeafThreads = LT * LE;   // 576
 
 __device__ __forceinline__ void sub_decode(int t, int& bi, int& bj) {
   int r = 0;
@@ -152,189 +160,151 @@ __device__ __forceinline__ void sub_decode(int t, int& bi, int& bj) {
   bi = r;
   bj = t - r * (r + 1) / 2;
 }
+__device__ __forceinline__ int lblk(int bi, int bj) { return (bi * (bi + 1) / 2 + bj) * LSZ; }
 
-__device__ __forceinline__ int lsub(int bi, int bj) { return (bi * 17 + bj) * SB; }
+// value of lane K of this lane's 16-lane row
+template <int K>
+__device__ __forceinline__ float row_bcast16(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + K, 0xf, 0xf, false));
+}
 
-__device__ __forceinline__ void lds_store8x8(float* dst, const float (&x)[8][8]) {
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    *reinterpret_cast<f32x4_t*>(dst + 8 * r) = f32x4_t{x[r][0], x[r][1], x[r][2], x[r][3]};
-    *reinterpret_cast<f32x4_t*>(dst + 8 * r + 4) = f32x4_t{x[r][4], x[r][5], x[r][6], x[r][7]};
+template <int J>
+__device__ __forceinline__ void diag_update(float (&a)[LE], float lc) {
+  if constexpr (J < LE) {
+    a[J] -= lc * row_bcast16<J>(lc);   // a[r][J] -= L[r][C] · L[J][C]
+    diag_update<J + 1>(a, lc);
   }
 }
 
-__device__ __forceinline__ void lds_load8x8(const float* src, float (&x)[8][8]) {
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const f32x4_t u = *reinterpret_cast<const f32x4_t*>(src + 8 * r);
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + 8 * r + 4);
-    x[r][0] = u[0]; x[r][1] = u[1]; x[r][2] = u[2]; x[r][3] = u[3];
-    x[r][4] = v[0]; x[r][5] = v[1]; x[r][6] = v[2]; x[r][7] = v[3];
+// Column C of the 16 x 16 diagonal Cholesky; lane r holds row r.
+template <int C>
+__device__ __forceinline__ void diag_factor(float (&a)[LE], int r, bool& bad) {
+  if constexpr (C < LE) {
+    float d = row_bcast16<C>(a[C]);
+    if (!(d > 0.f) || !isfinite(d)) {
+      bad = true;
+      d = 1.f;
+    }
+    const float sd = sqrtf(d);
+    const float lc = (r > C) ? a[C] / sd : (r == C ? sd : 0.f);
+    a[C] = lc;
+    diag_update<C + 1>(a, lc);
+    diag_factor<C + 1>(a, r, bad);
   }
 }
 
-__global__ __launch_bounds__(256) void chol_leaf_kernel(float* A, float* Mm, int64_t lda, int64_t k0,
-                                                        int* flag) {
-  __shared__ __attribute__((aligned(16))) float Lsub[16 * 17 * SB];   // L by sub-block
-  __shared__ __attribute__((aligned(16))) float Pan[2][16 * SB];      // step operands
+__global__ __launch_bounds__(kLeafThreads) void chol_leaf_kernel(float* A, float* Mm, int64_t lda,
+                                                                 int64_t k0, int* flag) {
+  __shared__ __attribute__((aligned(16))) float Ls[LT * LSZ];   // L by lower sub-block
+  __shared__ __attribute__((aligned(16))) float Ms[LN * LSZ];   // M row block of the step
   const int tid = threadIdx.x;
-  const bool owner = tid < 136;
-  int bi = 0, bj = 0;
-  if (owner) sub_decode(tid, bi, bj);
+  const int t = tid >> 4, r = tid & (LE - 1);
+  int bi, bj;
+  sub_decode(t, bi, bj);
   float* Ab = A + k0 * lda + k0;
   float* Mb = Mm + k0 * lda + k0;
 
-  float a[8][8];
-  if (owner) {
+  float a[LE];
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) a[r][c] = Ab[(int64_t)(8 * bi + r) * lda + 8 * bj + c];
-  }
+  for (int c = 0; c < LE; ++c) a[c] = Ab[(int64_t)(LE * bi + r) * lda + LE * bj + c];
 
-  // ---- Cholesky by 8-column block steps
+  // ---- Cholesky by 16-column block steps; thread = row r of (bi, bj)
   bool bad = false;
 #pragma unroll 1
-  for (int jb = 0; jb < 16; ++jb) {
-    if (owner && bi == jb && bj == jb) {
+  for (int jb = 0; jb < LN; ++jb) {
+    if (bi == jb && bj == jb) {
+      diag_factor<0>(a, r, bad);
+      float* dst = Ls + lblk(jb, jb) + r * LP;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float d = a[c][c];
-        if (!(d > 0.f) || !isfinite(d)) {
-          bad = true;
-          d = 1.f;
-        }
-        const float sd = sqrtf(d);
-        const float inv = 1.f / sd;
-        a[c][c] = sd;
-#pragma unroll
-        for (int r = c + 1; r < 8; ++r) a[r][c] *= inv;
-#pragma unroll
-        for (int c2 = c + 1; c2 < 8; ++c2)
-#pragma unroll
-          for (int r = c2; r < 8; ++r) a[r][c2] -= a[r][c] * a[c2][c];
+      for (int c = 0; c < LE; ++c) {
+        if (c > r) a[c] = 0.f;
+        dst[c] = a[c];
       }
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int c = r + 1; c < 8; ++c) a[r][c] = 0.f;
-      lds_store8x8(&Pan[0][jb * SB], a);
     }
     __syncthreads();
-    if (owner && bj == jb && bi > jb) {
-      float l[8][8];
-      lds_load8x8(&Pan[0][jb * SB], l);
-      // X · Lᵀ = A, row by row: x[r][c] = (a[r][c] - Σ_{k<c} x[r][k] l[c][k]) / l[c][c]
+    if (bj == jb && bi > jb) {
+      // X · Lᵀ = A along the row: x[c] = (a[c] - Σ_{k<c} x[k] L[c][k]) / L[c][c]
+      const float* L = Ls + lblk(jb, jb);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float inv = 1.f / l[c][c];
+      for (int c = 0; c < LE; ++c) {
+        float v = a[c];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          float v = a[r][c];
-#pragma unroll
-          for (int k = 0; k < c; ++k) v -= a[r][k] * l[c][k];
-          a[r][c] = v * inv;
-        }
+        for (int k = 0; k < c; ++k) v -= a[k] * L[c * LP + k];
+        a[c] = v / L[c * LP + c];
       }
-      lds_store8x8(&Pan[1][bi * SB], a);
+      float* dst = Ls + lblk(bi, jb) + r * LP;
+#pragma unroll
+      for (int c = 0; c < LE; ++c) dst[c] = a[c];
     }
     __syncthreads();
-    if (owner && bj > jb) {
-      float lb[8][8];
-      lds_load8x8(&Pan[1][bj * SB], lb);
+    if (bj > jb && bi >= bj) {
+      const float* X = Ls + lblk(bi, jb) + r * LP;
+      const float* Y = Ls + lblk(bj, jb);
+      float x[LE];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const f32x4_t u = *reinterpret_cast<const f32x4_t*>(&Pan[1][bi * SB + 8 * r]);
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&Pan[1][bi * SB + 8 * r + 4]);
-        const float li[8] = {u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
+      for (int k = 0; k < LE; ++k) x[k] = X[k];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          float acc = a[r][c];
+      for (int c = 0; c < LE; ++c) {
+        float acc = a[c];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) acc -= li[k] * lb[c][k];
-          a[r][c] = acc;
-        }
+        for (int k = 0; k < LE; ++k) acc -= x[k] * Y[c * LP + k];
+        a[c] = acc;
       }
     }
+    // the next step's diagonal factor uses only its own registers, and its
+    // writes go to a sub-block no thread reads in this step
   }
   if (bad) atomicOr(flag, kFlagNotPD);
 
-  // ---- L to A (lower) and to LDS
-  if (owner) {
+  // ---- L to A (lower triangle of the block)
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        if (bi != bj || r >= c) Ab[(int64_t)(8 * bi + r) * lda + 8 * bj + c] = a[r][c];
-    lds_store8x8(&Lsub[lsub(bi, bj)], a);
-  }
-  __syncthreads();
+  for (int c = 0; c < LE; ++c)
+    if (bi != bj || c <= r) Ab[(int64_t)(LE * bi + r) * lda + LE * bj + c] = a[c];
 
-  // ---- inverse by 8-row block steps (R starts as I)
-  if (owner) {
+  // ---- inverse by 16-row block steps (R starts as I); thread = column r of (bi, bj)
+  float m[LE];
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) a[r][c] = (bi == bj && r == c) ? 1.f : 0.f;
-  }
+  for (int i = 0; i < LE; ++i) m[i] = (bi == bj && i == r) ? 1.f : 0.f;
 #pragma unroll 1
-  for (int kb = 0; kb < 16; ++kb) {
-    float* P = Pan[kb & 1];
-    if (owner && bi == kb) {
-      float l[8][8];
-      lds_load8x8(&Lsub[lsub(kb, kb)], l);
-      // L · M = R, column by column (forward substitution)
+  for (int kb = 0; kb < LN; ++kb) {
+    if (bi == kb) {
+      // L · M = R down the column: m[i] = (m[i] - Σ_{k<i} L[i][k] m[k]) / L[i][i]
+      const float* L = Ls + lblk(kb, kb);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float inv = 1.f / l[r][r];
+      for (int i = 0; i < LE; ++i) {
+        float v = m[i];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          float v = a[r][c];
-#pragma unroll
-          for (int k = 0; k < r; ++k) v -= l[r][k] * a[k][c];
-          a[r][c] = v * inv;
-        }
+        for (int k = 0; k < i; ++k) v -= L[i * LP + k] * m[k];
+        m[i] = v / L[i * LP + i];
       }
-      lds_store8x8(&P[bj * SB], a);
+      float* dst = Ms + bj * LSZ + r;
+#pragma unroll
+      for (int i = 0; i < LE; ++i) dst[i * LP] = m[i];
     }
     __syncthreads();
-    if (owner && bi > kb && bj <= kb) {
-      float mk[8][8];
-      lds_load8x8(&P[bj * SB], mk);
+    if (bi > kb && bj <= kb) {
+      const float* L = Ls + lblk(bi, kb);
+      const float* Mk = Ms + bj * LSZ + r;
+      float mk[LE];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const f32x4_t u = *reinterpret_cast<const f32x4_t*>(&Lsub[lsub(bi, kb) + 8 * r]);
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&Lsub[lsub(bi, kb) + 8 * r + 4]);
-        const float li[8] = {u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
+      for (int k = 0; k < LE; ++k) mk[k] = Mk[k * LP];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          float acc = a[r][c];
+      for (int i = 0; i < LE; ++i) {
+        float acc = m[i];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) acc -= li[k] * mk[k][c];
-          a[r][c] = acc;
-        }
+        for (int k = 0; k < LE; ++k) acc -= L[i * LP + k] * mk[k];
+        m[i] = acc;
       }
     }
+    __syncthreads();   // Ms is rewritten by the next step
   }
 
-  // ---- D = L^{-1} (lower) to Mmat; zero the strict upper part of the block
-  if (owner) {
+  // ---- D = L⁻¹ (lower) to Mmat; owners of (bi, bj), bi > bj, also zero (bj, bi)
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
+  for (int i = 0; i < LE; ++i) Mb[(int64_t)(LE * bi + i) * lda + LE * bj + r] = m[i];
+  if (bi > bj) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        Mb[(int64_t)(8 * bi + r) * lda + 8 * bj + c] = (bi != bj || r >= c) ? a[r][c] : 0.f;
-  } else {
-    // threads 136..255 own the 120 strictly-upper sub-blocks (rb < cb):
-    // t = cb (cb - 1) / 2 + rb
-    const int t = tid - 136;
-    int cb = 1;
-    while (cb * (cb + 1) / 2 <= t) ++cb;
-    const int rb = t - cb * (cb - 1) / 2;
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) Mb[(int64_t)(8 * rb + r) * lda + 8 * cb + c] = 0.f;
+    for (int i = 0; i < LE; ++i) Mb[(int64_t)(LE * bj + i) * lda + LE * bi + r] = 0.f;
   }
 }
 
@@ -398,7 +368,7 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
   for (int64_t K0 = 0; K0 < p.n_pad; K0 += OB) {
     const int64_t K1 = std::min<int64_t>(K0 + OB, p.n_pad);
     for (int64_t k0 = K0; k0 < K1; k0 += NB) {
-      hipLaunchKernelGGL(chol_leaf_kernel, dim3(1), dim3(256), 0, stream, A, Mm, lda, k0, flag);
+      hipLaunchKernelGGL(chol_leaf_kernel, dim3(1), dim3(kLeafThreads), 0, stream, A, Mm, lda, k0, flag);
       GPTQ_LAUNCH_CHECK();
       const int64_t rows = p.n_pad - k0 - NB;
       if (rows <= 0) break;
