@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <vector>
 
 #include "gptq_internal.hpp"
 
@@ -55,6 +56,25 @@ gptq_status check_config(const gptq_config* cfg) {
 }  // namespace gptq
 
 using namespace gptq;
+
+namespace gptq {
+
+gptq_status get_side_stream(SideStream& out) {
+  thread_local std::vector<SideStream> per_device;
+  int dev = 0;
+  GPTQ_HIP_CHECK(hipGetDevice(&dev));
+  if ((int)per_device.size() <= dev) per_device.resize(dev + 1);
+  SideStream& s = per_device[dev];
+  if (s.stream == nullptr) {
+    GPTQ_HIP_CHECK(hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking));
+    GPTQ_HIP_CHECK(hipEventCreateWithFlags(&s.ready, hipEventDisableTiming));
+    GPTQ_HIP_CHECK(hipEventCreateWithFlags(&s.done, hipEventDisableTiming));
+  }
+  out = s;
+  return GPTQ_OK;
+}
+
+}  // namespace gptq
 
 extern "C" {
 

@@ -41,9 +41,28 @@ void clear_error();
     }                                                                                \
   } while (0)
 
+#define GPTQ_TRY(expr)                 \
+  do {                                 \
+    gptq_status _st = (expr);          \
+    if (_st != GPTQ_OK) return _st;    \
+  } while (0)
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------- side stream
+// Lookahead: work the caller's stream does not need until later runs on a
+// second stream of the same device, ordered by events.  One side stream and
+// two events per host thread and device, created on first use (default
+// priority) and kept until the process ends, so concurrent calls from
+// different host threads never share them.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t ready = nullptr;   // recorded on the caller's stream, waited on by the side stream
+  hipEvent_t done = nullptr;    // recorded on the side stream, waited on by the caller's stream
+};
+gptq_status get_side_stream(SideStream& out);
 
 // ---------------------------------------------------------------- Hessian (stage 1)
 constexpr int kSyrkTile = 256;      // output tile edge of the bf16 SYRK

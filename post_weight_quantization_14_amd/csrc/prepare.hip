@@ -365,6 +365,9 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
   // outer block from its four panels (K = 512), so the trailing matrix is read
   // and written a quarter as often.
   constexpr int64_t OB = 4 * NB;
+  SideStream side;
+  GPTQ_TRY(get_side_stream(side));
+  bool side_pending = false;
   for (int64_t K0 = 0; K0 < p.n_pad; K0 += OB) {
     const int64_t K1 = std::min<int64_t>(K0 + OB, p.n_pad);
     for (int64_t k0 = K0; k0 < K1; k0 += NB) {
@@ -391,18 +394,41 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
         if (st != GPTQ_OK) return st;
       }
     }
-    // outer update: A[K1:, K1:] -= L[K1:, K0:K1] · L[K1:, K0:K1]ᵀ (lower part)
+    // outer update: A[K1:, K1:] -= L[K1:, K0:K1] · L[K1:, K0:K1]ᵀ (lower part),
+    // split with lookahead: the next outer block's columns [K1, K1+OB) on the
+    // caller's stream, the columns after them on the side stream, where they
+    // run while the next outer block's leaf chain (which touches only its own
+    // columns) runs here.  The near part writes columns the previous far part
+    // wrote, so it waits for that first.
     const int64_t rest = p.n_pad - K1;
     if (rest > 0) {
+      const int64_t near = std::min<int64_t>(OB, rest), far = rest - near;
+      if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
+      side_pending = false;
       GemmArgs g;
       g.A = A + K1 * lda + K0; g.lda = lda;
       g.B = A + K1 * lda + K0; g.ldb = lda;
+      g.k_begin = 0; g.k_end = K1 - K0; g.alpha = -1.f; g.beta = 1.f;
+      if (far > 0) {
+        GPTQ_HIP_CHECK(hipEventRecord(side.ready, stream));
+        GPTQ_HIP_CHECK(hipStreamWaitEvent(side.stream, side.ready, 0));
+        GemmArgs f = g;
+        f.A = A + (K1 + near) * lda + K0;
+        f.B = A + (K1 + near) * lda + K0;
+        f.C = A + (K1 + near) * lda + K1 + near; f.ldc = lda;
+        f.M = far; f.N = far;
+        gptq_status st = launch_gemm_lower(f, /*b_colmajor=*/true, side.stream);
+        if (st != GPTQ_OK) return st;
+        GPTQ_HIP_CHECK(hipEventRecord(side.done, side.stream));
+        side_pending = true;
+      }
       g.C = A + K1 * lda + K1; g.ldc = lda;
-      g.M = rest; g.N = rest; g.k_begin = 0; g.k_end = K1 - K0; g.alpha = -1.f; g.beta = 1.f;
+      g.M = rest; g.N = near;
       gptq_status st = launch_gemm_lower(g, /*b_colmajor=*/true, stream);
       if (st != GPTQ_OK) return st;
     }
   }
+  if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
   // triangular inverse: doubling levels over the leaf inverses
   for (int64_t half = 1; half < p.nblk; half *= 2) {
     gptq_status st = launch_trtri_level(A, Mm, lda, p.nblk, half, stream);

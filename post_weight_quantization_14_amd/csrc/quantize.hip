@@ -184,7 +184,7 @@ QuantPlan plan_quantize(int64_t m, int64_t n, const gptq_config& cfg) {
   p.part_off = off;  // pack partials: one double per (row, word-block)
   off += align256((size_t)m * bpr * sizeof(double));
   p.codes_off = off; off += align256((size_t)m * p.ldw);
-  p.err_off = off; off += align256((size_t)m * kQSuper * sizeof(float));
+  p.err_off = off; off += align256((size_t)2 * m * kQSuper * sizeof(float));   // two superblocks
   p.loss_off = off; off += align256((size_t)m * sizeof(double));
   p.inv_off = off; off += align256((size_t)n * sizeof(int32_t));
   p.flag_off = off; off += 256;
@@ -243,14 +243,23 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
   // (K = 128); the columns after the superblock are updated once per
   // superblock from all of its errors (K = 512), so the working weights are
   // read and written a quarter as often as with per-block updates.
+  // Lookahead: of that superblock update, the next superblock's columns run on
+  // the caller's stream and the columns after them on the side stream, while
+  // the next superblock's column loop (its own columns only) runs here.  The
+  // error block alternates between two buffers, so the side stream's reads of
+  // one superblock's errors never meet the next superblock's writes.
+  SideStream side;
+  GPTQ_TRY(get_side_stream(side));
+  bool side_pending = false;
   for (int64_t s1 = 0; s1 < n; s1 += kQSuper) {
     const int64_t s2 = std::min<int64_t>(s1 + kQSuper, n);
+    float* errs = err + ((s1 / kQSuper) & 1) * m * kQSuper;
     for (int64_t i1 = s1; i1 < s2; i1 += QB) {
       const int bw = (int)std::min<int64_t>(QB, s2 - i1);
       // the quantizer reads only rows and columns < bw of U's diagonal block
       const float* ublk = U + i1 * n + i1;
       const int64_t ldub = n;
-      a.err = err + (i1 - s1);
+      a.err = errs + (i1 - s1);
       switch (gw) {
         case -1: launch_block_quant<0>(a, ublk, ldub, i1, bw, stream); break;
         case 8: launch_block_quant<8>(a, ublk, ldub, i1, bw, stream); break;
@@ -275,15 +284,33 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
       }
     }
     if (s2 < n) {   // W_p[:, s2:] -= Err_super · U[s1:s2, s2:]
+      const int64_t near = std::min<int64_t>(kQSuper, n - s2), far = n - s2 - near;
+      if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
+      side_pending = false;
       GemmArgs g;
-      g.A = err; g.lda = kQSuper;
-      g.B = U + s1 * n + s2; g.ldb = n;
-      g.C = Wp + s2; g.ldc = p.ldw;
-      g.M = m; g.N = n - s2; g.k_begin = 0; g.k_end = s2 - s1; g.alpha = -1.f; g.beta = 1.f;
+      g.A = errs; g.lda = kQSuper;
+      g.ldb = n; g.ldc = p.ldw;
+      g.M = m; g.k_begin = 0; g.k_end = s2 - s1; g.alpha = -1.f; g.beta = 1.f;
+      if (far > 0) {
+        GPTQ_HIP_CHECK(hipEventRecord(side.ready, stream));
+        GPTQ_HIP_CHECK(hipStreamWaitEvent(side.stream, side.ready, 0));
+        GemmArgs f = g;
+        f.B = U + s1 * n + s2 + near;
+        f.C = Wp + s2 + near;
+        f.N = far;
+        gptq_status st = launch_gemm_rect(f, /*b_colmajor=*/false, side.stream);
+        if (st != GPTQ_OK) return st;
+        GPTQ_HIP_CHECK(hipEventRecord(side.done, side.stream));
+        side_pending = true;
+      }
+      g.B = U + s1 * n + s2;
+      g.C = Wp + s2;
+      g.N = near;
       gptq_status st = launch_gemm_rect(g, /*b_colmajor=*/false, stream);
       if (st != GPTQ_OK) return st;
     }
   }
+  if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
 
   hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, perm, n,
                      (int64_t)(gw > 0 ? gw : 0), g_idx, invperm);
