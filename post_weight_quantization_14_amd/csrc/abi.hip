@@ -59,12 +59,12 @@ using namespace gptq;
 
 namespace gptq {
 
-gptq_status get_side_stream(SideStream& out) {
-  thread_local std::vector<SideStream> per_device;
+gptq_status get_side_stream(SideStream& out, int which) {
+  thread_local std::vector<SideStream> per_device;   // [device][which]
   int dev = 0;
   GPTQ_HIP_CHECK(hipGetDevice(&dev));
-  if ((int)per_device.size() <= dev) per_device.resize(dev + 1);
-  SideStream& s = per_device[dev];
+  if ((int)per_device.size() <= 2 * dev + 1) per_device.resize(2 * dev + 2);
+  SideStream& s = per_device[2 * dev + (which & 1)];
   if (s.stream == nullptr) {
     GPTQ_HIP_CHECK(hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking));
     GPTQ_HIP_CHECK(hipEventCreateWithFlags(&s.ready, hipEventDisableTiming));

@@ -222,9 +222,10 @@ __global__ __launch_bounds__(256) void gemm_lower_kernel(GemmArgs g) {
 // Cholesky buffer, which the factorisation never reads.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void trtri_step1_kernel(float* Amat, const float* Mmat,
-                                                          int64_t lda, int64_t nblk, int64_t half) {
+                                                          int64_t lda, int64_t nblk, int64_t half,
+                                                          int64_t p0) {
   __shared__ GemmSmem sm;
-  const int64_t p = blockIdx.y;
+  const int64_t p = p0 + blockIdx.y;
   const int64_t l0 = p * 2 * half, r0 = l0 + half;
   const int64_t r1 = (l0 + 2 * half < nblk) ? l0 + 2 * half : nblk;
   const int64_t ti = blockIdx.x / half, tj = blockIdx.x % half;
@@ -253,9 +254,10 @@ __global__ __launch_bounds__(256) void trtri_step1_kernel(float* Amat, const flo
 }
 
 __global__ __launch_bounds__(256) void trtri_step2_kernel(const float* Amat, float* Mmat,
-                                                          int64_t lda, int64_t nblk, int64_t half) {
+                                                          int64_t lda, int64_t nblk, int64_t half,
+                                                          int64_t p0) {
   __shared__ GemmSmem sm;
-  const int64_t p = blockIdx.y;
+  const int64_t p = p0 + blockIdx.y;
   const int64_t l0 = p * 2 * half, r0 = l0 + half;
   const int64_t r1 = (l0 + 2 * half < nblk) ? l0 + 2 * half : nblk;
   const int64_t ti = blockIdx.x / half, tj = blockIdx.x % half;
@@ -311,16 +313,16 @@ gptq_status launch_gemm_lower(const GemmArgs& g, bool b_colmajor, hipStream_t st
   return GPTQ_OK;
 }
 
-gptq_status launch_trtri_level(float* Amat, float* Mmat, int64_t lda, int64_t nblk, int64_t half,
-                               hipStream_t stream) {
-  const int64_t nodes = ceil_div(nblk - half, 2 * half);  // nodes with a right part
-  if (nodes <= 0) return GPTQ_OK;
-  dim3 grid((unsigned)(half * half), (unsigned)nodes);
-  hipLaunchKernelGGL(trtri_step1_kernel, grid, dim3(256), 0, stream, Amat, (const float*)Mmat, lda,
-                     nblk, half);
-  GPTQ_LAUNCH_CHECK();
-  hipLaunchKernelGGL(trtri_step2_kernel, grid, dim3(256), 0, stream, (const float*)Amat, Mmat, lda,
-                     nblk, half);
+gptq_status launch_trtri_nodes(float* Amat, float* Mmat, int64_t lda, int64_t nblk, int64_t half,
+                               int64_t p0, int64_t count, int step, hipStream_t stream) {
+  if (count <= 0) return GPTQ_OK;
+  dim3 grid((unsigned)(half * half), (unsigned)count);
+  if (step == 1)
+    hipLaunchKernelGGL(trtri_step1_kernel, grid, dim3(256), 0, stream, Amat, (const float*)Mmat, lda,
+                       nblk, half, p0);
+  else
+    hipLaunchKernelGGL(trtri_step2_kernel, grid, dim3(256), 0, stream, (const float*)Amat, Mmat, lda,
+                       nblk, half, p0);
   GPTQ_LAUNCH_CHECK();
   return GPTQ_OK;
 }

@@ -52,9 +52,9 @@ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------- side stream
-// Lookahead: work the caller's stream does not need until later runs on a
-// second stream of the same device, ordered by events.  One side stream and
-// two events per host thread and device, created on first use (default
+// Lookahead: work the caller's stream does not need until later runs on
+// other streams of the same device, ordered by events.  Two side streams with
+// two events each per host thread and device, created on first use (default
 // priority) and kept until the process ends, so concurrent calls from
 // different host threads never share them.
 struct SideStream {
@@ -62,7 +62,7 @@ struct SideStream {
   hipEvent_t ready = nullptr;   // recorded on the caller's stream, waited on by the side stream
   hipEvent_t done = nullptr;    // recorded on the side stream, waited on by the caller's stream
 };
-gptq_status get_side_stream(SideStream& out);
+gptq_status get_side_stream(SideStream& out, int which = 0);   // which: 0 or 1
 
 // ---------------------------------------------------------------- Hessian (stage 1)
 constexpr int kSyrkTile = 256;      // output tile edge of the bf16 SYRK
@@ -128,8 +128,10 @@ gptq_status launch_gemm_rect(const GemmArgs& g, bool b_colmajor, hipStream_t str
 // trailing updates of the blocked Cholesky (a triangle, or a triangle over a
 // rectangle of full tiles).
 gptq_status launch_gemm_lower(const GemmArgs& g, bool b_colmajor, hipStream_t stream);
-// One level of the blocked triangular inverse (see prepare.hip).
-gptq_status launch_trtri_level(float* Amat, float* Mmat, int64_t lda, int64_t nblk, int64_t half,
-                               hipStream_t stream);
+// Step 1 (T = L21·M11) or step 2 (M21 = -M22·T) of nodes p0 .. p0+count-1 of
+// one level (`half` blocks per side) of the blocked triangular inverse's
+// bottom-up doubling (see prepare.hip).
+gptq_status launch_trtri_nodes(float* Amat, float* Mmat, int64_t lda, int64_t nblk, int64_t half,
+                               int64_t p0, int64_t count, int step, hipStream_t stream);
 
 }  // namespace gptq

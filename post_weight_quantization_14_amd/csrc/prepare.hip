@@ -365,16 +365,48 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
   // outer block from its four panels (K = 512), so the trailing matrix is read
   // and written a quarter as often.
   constexpr int64_t OB = 4 * NB;
-  SideStream side;
-  GPTQ_TRY(get_side_stream(side));
-  bool side_pending = false;
+  SideStream side, tri;
+  GPTQ_TRY(get_side_stream(side, 0));
+  GPTQ_TRY(get_side_stream(tri, 1));
+  bool side_pending = false, tri_pending = false;
+  // Triangular inverse, overlapped with the factorisation.  A node of the
+  // bottom-up doubling joins blocks [l0, r0) and [r0, r1): its step 1
+  // (T = L21·M11) needs L rows [r0, r1) of columns [l0, r0), final once panel
+  // r0 - 1 is solved, and M11 (the child node, issued before it); its step 2
+  // (M21 = -M22·T) also needs M22, complete once panel r1 - 1 is.  Steps run in
+  // that order on their own stream (smaller levels first, so children precede
+  // parents).  Their writes (T parked in A's strict upper block triangle, M's
+  // off-diagonal blocks) touch nothing the factorisation still uses.
+  auto issue_trtri = [&](int64_t kb) -> gptq_status {
+    bool recorded = false;
+    for (int64_t half = 1; half < p.nblk; half *= 2) {
+      for (int64_t q = 0; q * 2 * half + half < p.nblk; ++q) {
+        const int64_t r0 = q * 2 * half + half;
+        const int64_t r1 = std::min<int64_t>(r0 + half, p.nblk);
+        for (int step = 1; step <= 2; ++step) {
+          if ((step == 1 ? r0 : r1) != kb + 1) continue;
+          if (!recorded) {
+            GPTQ_HIP_CHECK(hipEventRecord(tri.ready, stream));
+            GPTQ_HIP_CHECK(hipStreamWaitEvent(tri.stream, tri.ready, 0));
+            recorded = true;
+          }
+          GPTQ_TRY(launch_trtri_nodes(A, Mm, lda, p.nblk, half, q, 1, step, tri.stream));
+          tri_pending = true;
+        }
+      }
+    }
+    return GPTQ_OK;
+  };
   for (int64_t K0 = 0; K0 < p.n_pad; K0 += OB) {
     const int64_t K1 = std::min<int64_t>(K0 + OB, p.n_pad);
     for (int64_t k0 = K0; k0 < K1; k0 += NB) {
       hipLaunchKernelGGL(chol_leaf_kernel, dim3(1), dim3(kLeafThreads), 0, stream, A, Mm, lda, k0, flag);
       GPTQ_LAUNCH_CHECK();
       const int64_t rows = p.n_pad - k0 - NB;
-      if (rows <= 0) break;
+      if (rows <= 0) {
+        GPTQ_TRY(issue_trtri(k0 / NB));
+        break;
+      }
       GemmArgs g;
       // panel solve: P = A_panel · D_kᵀ  (D_kᵀ read column-major from D_k)
       g.A = A + (k0 + NB) * lda + k0; g.lda = lda;
@@ -383,6 +415,7 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
       g.M = rows; g.N = NB; g.k_begin = 0; g.k_end = NB; g.alpha = 1.f; g.beta = 0.f;
       gptq_status st = launch_gemm_rect(g, /*b_colmajor=*/true, stream);
       if (st != GPTQ_OK) return st;
+      GPTQ_TRY(issue_trtri(k0 / NB));
       // inner update: A[k0+NB:, k0+NB:K1] -= P · P[k0+NB:K1]ᵀ (lower part)
       const int64_t cols = K1 - k0 - NB;
       if (cols > 0) {
@@ -429,10 +462,9 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
     }
   }
   if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
-  // triangular inverse: doubling levels over the leaf inverses
-  for (int64_t half = 1; half < p.nblk; half *= 2) {
-    gptq_status st = launch_trtri_level(A, Mm, lda, p.nblk, half, stream);
-    if (st != GPTQ_OK) return st;
+  if (tri_pending) {
+    GPTQ_HIP_CHECK(hipEventRecord(tri.done, tri.stream));
+    GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, tri.done, 0));
   }
   hipLaunchKernelGGL(flip_kernel, dim3((unsigned)ceil_div(n, 256), (unsigned)n), dim3(256), 0,
                      stream, (const float*)Mm, lda, n, H);
