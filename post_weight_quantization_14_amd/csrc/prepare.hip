@@ -138,7 +138,8 @@ __global__ __launch_bounds__(256) void permute_kernel(const float* __restrict__ 
 // operands through LDS (row pitch 20 floats: 16-byte aligned rows, and the 16
 // rows of a sub-block on distinct bank quads):
 //   Cholesky, step jb: the lanes of (jb, jb) factor it column by column,
-//     broadcasting within their row by DPP row_newbcast; owners of (bi, jb)
+//     broadcasting within their row by DPP row_newbcast (pivots through
+//     v_rsq_f32; the solves multiply by the kept 1/L[c][c]); owners of (bi, jb)
 //     solve X · L_jbᵀ = A_bi,jb along their row; owners of (bi, bj),
 //     jb < bj <= bi, subtract L_bi,jb · L_bj,jbᵀ.
 //   Inverse (R = I, row block kb per step): owners of (kb, bj) solve
@@ -176,20 +177,23 @@ __device__ __forceinline__ void diag_update(float (&a)[LE], float lc) {
   }
 }
 
-// Column C of the 16 x 16 diagonal Cholesky; lane r holds row r.
+// Column C of the 16 x 16 diagonal Cholesky; lane r holds row r.  The pivot's
+// reciprocal square root (v_rsq_f32, within 1 ulp) scales the column, and lane
+// C keeps it as 1/L[C][C] for the solves.
 template <int C>
-__device__ __forceinline__ void diag_factor(float (&a)[LE], int r, bool& bad) {
+__device__ __forceinline__ void diag_factor(float (&a)[LE], int r, bool& bad, float& dinv) {
   if constexpr (C < LE) {
     float d = row_bcast16<C>(a[C]);
     if (!(d > 0.f) || !isfinite(d)) {
       bad = true;
       d = 1.f;
     }
-    const float sd = sqrtf(d);
-    const float lc = (r > C) ? a[C] / sd : (r == C ? sd : 0.f);
+    const float rs = __builtin_amdgcn_rsqf(d);
+    const float lc = (r > C) ? a[C] * rs : (r == C ? d * rs : 0.f);
+    if (r == C) dinv = rs;
     a[C] = lc;
     diag_update<C + 1>(a, lc);
-    diag_factor<C + 1>(a, r, bad);
+    diag_factor<C + 1>(a, r, bad, dinv);
   }
 }
 
@@ -197,6 +201,7 @@ __global__ __launch_bounds__(kLeafThreads) void chol_leaf_kernel(float* A, float
                                                                  int64_t k0, int* flag) {
   __shared__ __attribute__((aligned(16))) float Ls[LT * LSZ];   // L by lower sub-block
   __shared__ __attribute__((aligned(16))) float Ms[LN * LSZ];   // M row block of the step
+  __shared__ float Ldi[NB];                                     // 1 / L[c][c]
   const int tid = threadIdx.x;
   const int t = tid >> 4, r = tid & (LE - 1);
   int bi, bj;
@@ -213,7 +218,9 @@ __global__ __launch_bounds__(kLeafThreads) void chol_leaf_kernel(float* A, float
 #pragma unroll 1
   for (int jb = 0; jb < LN; ++jb) {
     if (bi == jb && bj == jb) {
-      diag_factor<0>(a, r, bad);
+      float dinv = 1.f;
+      diag_factor<0>(a, r, bad, dinv);
+      Ldi[LE * jb + r] = dinv;
       float* dst = Ls + lblk(jb, jb) + r * LP;
 #pragma unroll
       for (int c = 0; c < LE; ++c) {
@@ -230,7 +237,7 @@ __global__ __launch_bounds__(kLeafThreads) void chol_leaf_kernel(float* A, float
         float v = a[c];
 #pragma unroll
         for (int k = 0; k < c; ++k) v -= a[k] * L[c * LP + k];
-        a[c] = v / L[c * LP + c];
+        a[c] = v * Ldi[LE * jb + c];
       }
       float* dst = Ls + lblk(bi, jb) + r * LP;
 #pragma unroll
@@ -275,7 +282,7 @@ __global__ __launch_bounds__(kLeafThreads) void chol_leaf_kernel(float* A, float
         float v = m[i];
 #pragma unroll
         for (int k = 0; k < i; ++k) v -= L[i * LP + k] * m[k];
-        m[i] = v / L[i * LP + i];
+        m[i] = v * Ldi[LE * kb + i];
       }
       float* dst = Ms + bj * LSZ + r;
 #pragma unroll
