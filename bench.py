@@ -7,8 +7,12 @@ inverse factor, block-wise quantization with error feedback and packing.
 Default workload: the 7B MLP down projection, W 4096 x 11008 bf16, X 262144
 tokens x 11008 bf16, 4-bit asym, group 128, desc_act.
 
+With the default workload it also times the 7B-shaped sweep (32 decoder
+layers x {q, k, v, o, gate, up, down}, at 4-bit g128 and at 3-bit g64; X and W
+regenerated per linear outside the timed calls) and reports its total seconds.
+
 Prints ONE JSON line on stdout; progress goes to stderr.
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--sweep]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-sweep]
 """
 from __future__ import annotations
 
@@ -167,7 +171,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="c3_down_proj_4096x11008")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sweep", action="store_true", help="also time the 7B-shaped 224-linear sweep")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the 7B-shaped sweep (224 linears at 4-bit g128 and at 3-bit g64)")
     ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; "
                          "the reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE counters")
@@ -255,7 +260,7 @@ def main():
         },
         "loss": layer.out["loss"].cpu().tolist(),
     }
-    if args.sweep:
+    if not args.no_sweep and args.workload == "c3_down_proj_4096x11008":
         del layer
         torch.cuda.empty_cache()
         log("bench: 7B-shaped sweep")
