@@ -61,14 +61,21 @@ namespace gptq {
 
 gptq_status get_side_stream(SideStream& out, int which) {
   thread_local std::vector<SideStream> per_device;   // [device][which]
+  if (which < 0 || which >= kSideStreams) {
+    set_error("side stream %d out of range", which);
+    return GPTQ_ERR_INVALID_ARG;
+  }
   int dev = 0;
   GPTQ_HIP_CHECK(hipGetDevice(&dev));
-  if ((int)per_device.size() <= 2 * dev + 1) per_device.resize(2 * dev + 2);
-  SideStream& s = per_device[2 * dev + (which & 1)];
+  if ((int)per_device.size() < kSideStreams * (dev + 1)) per_device.resize(kSideStreams * (dev + 1));
+  SideStream& s = per_device[kSideStreams * dev + which];
   if (s.stream == nullptr) {
     GPTQ_HIP_CHECK(hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking));
-    GPTQ_HIP_CHECK(hipEventCreateWithFlags(&s.ready, hipEventDisableTiming));
-    GPTQ_HIP_CHECK(hipEventCreateWithFlags(&s.done, hipEventDisableTiming));
+    // only streams of this device wait on them: a device-scope release suffices
+    GPTQ_HIP_CHECK(hipEventCreateWithFlags(&s.ready, hipEventDisableTiming | hipEventReleaseToDevice));
+    GPTQ_HIP_CHECK(hipEventCreateWithFlags(&s.done, hipEventDisableTiming | hipEventReleaseToDevice));
+    for (hipEvent_t& e : s.aux)
+      GPTQ_HIP_CHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventReleaseToDevice));
   }
   out = s;
   return GPTQ_OK;

@@ -53,16 +53,18 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------- side stream
 // Lookahead: work the caller's stream does not need until later runs on
-// other streams of the same device, ordered by events.  Two side streams with
-// two events each per host thread and device, created on first use (default
-// priority) and kept until the process ends, so concurrent calls from
-// different host threads never share them.
+// other streams of the same device, ordered by events.  kSideStreams side
+// streams with four events each per host thread and device, created on first
+// use (default priority) and kept until the process ends, so concurrent calls
+// from different host threads never share them.
 struct SideStream {
   hipStream_t stream = nullptr;
   hipEvent_t ready = nullptr;   // recorded on the caller's stream, waited on by the side stream
   hipEvent_t done = nullptr;    // recorded on the side stream, waited on by the caller's stream
+  hipEvent_t aux[2] = {nullptr, nullptr};   // two more side-stream points, used alternately
 };
-gptq_status get_side_stream(SideStream& out, int which = 0);   // which: 0 or 1
+constexpr int kSideStreams = 3;
+gptq_status get_side_stream(SideStream& out, int which = 0);   // 0 <= which < kSideStreams
 
 // ---------------------------------------------------------------- Hessian (stage 1)
 constexpr int kSyrkTile = 256;      // output tile edge of the bf16 SYRK

@@ -197,11 +197,22 @@ __device__ __forceinline__ void diag_factor(float (&a)[LE], int r, bool& bad, fl
   }
 }
 
+// pre != 0: the block first takes the trailing update from the panel just
+// before it, A_kk -= P·Pᵀ with P = A[k0:k0+128, k0-128:k0] (that panel's
+// solved rows for this block), by v_mfma_f32_16x16x4f32: wave w computes the
+// 16 x 16 sub-blocks 4w .. 4w+3 and parks them in Ls, where their owners pick
+// them up.  P is staged in LDS 32 columns at a time (row pitch 36: the
+// operand reads of a wave hit 64 distinct banks), which keeps the kernel's LDS
+// small enough to share a CU with a trailing-update GEMM workgroup.
+constexpr int kPk = 32;          // columns of P per staged pass
+constexpr int kPp = kPk + 4;     // row pitch of the staged pass
+
 __global__ __launch_bounds__(kLeafThreads) void chol_leaf_kernel(float* A, float* Mm, int64_t lda,
-                                                                 int64_t k0, int* flag) {
+                                                                 int64_t k0, int pre, int* flag) {
   __shared__ __attribute__((aligned(16))) float Ls[LT * LSZ];   // L by lower sub-block
   __shared__ __attribute__((aligned(16))) float Ms[LN * LSZ];   // M row block of the step
   __shared__ float Ldi[NB];                                     // 1 / L[c][c]
+  __shared__ __attribute__((aligned(16))) float Ps[NB * kPp];   // one pass of P
   const int tid = threadIdx.x;
   const int t = tid >> 4, r = tid & (LE - 1);
   int bi, bj;
@@ -209,9 +220,71 @@ __global__ __launch_bounds__(kLeafThreads) void chol_leaf_kernel(float* A, float
   float* Ab = A + k0 * lda + k0;
   float* Mb = Mm + k0 * lda + k0;
 
+  // P for all passes is loaded up front with the block itself (one memory
+  // latency): thread tid holds float4 number tid and tid + 576 of each pass
+  // (a pass is 128 rows x 8 float4).
+  constexpr int kPq = NB * kPk / 4;   // float4 per pass
+  f32x4_t pv[NB / kPk][2];
+  if (pre) {
+    const float* P = Ab - NB;
+#pragma unroll
+    for (int ps = 0; ps < NB / kPk; ++ps)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int idx = tid + kLeafThreads * u;
+        if (idx < kPq)
+          pv[ps][u] = *reinterpret_cast<const f32x4_t*>(P + (int64_t)(idx >> 3) * lda + ps * kPk +
+                                                        4 * (idx & 7));
+      }
+  }
+
   float a[LE];
 #pragma unroll
   for (int c = 0; c < LE; ++c) a[c] = Ab[(int64_t)(LE * bi + r) * lda + LE * bj + c];
+
+  if (pre) {
+    const int lane = tid & 63, wave = tid >> 6;
+    f32x4_t d[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ps = 0; ps < NB / kPk; ++ps) {
+      if (ps > 0) __syncthreads();   // the previous pass is consumed
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int idx = tid + kLeafThreads * u;
+        if (idx < kPq) *reinterpret_cast<f32x4_t*>(Ps + (idx >> 3) * kPp + 4 * (idx & 7)) = pv[ps][u];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int ci, cj;
+        sub_decode(4 * wave + q, ci, cj);
+        // A = P rows of sub-block row ci, B = Pᵀ columns of sub-block column
+        // cj: lane l supplies P[16 ci + l % 16][4 kk + l / 16], same for cj
+        const float* pa = Ps + (LE * ci + (lane & 15)) * kPp + (lane >> 4);
+        const float* pb = Ps + (LE * cj + (lane & 15)) * kPp + (lane >> 4);
+#pragma unroll
+        for (int kk = 0; kk < kPk / 4; ++kk)
+          d[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[4 * kk], pb[4 * kk], d[q], 0, 0, 0);
+      }
+    }
+    // D[4 (l / 16) + v][l % 16]
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int ci, cj;
+      sub_decode(4 * wave + q, ci, cj);
+      float* dst = Ls + lblk(ci, cj) + (4 * (lane >> 4)) * LP + (lane & 15);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dst[v * LP] = d[q][v];
+    }
+    __syncthreads();
+    const float* src = Ls + lblk(bi, bj) + r * LP;
+#pragma unroll
+    for (int c = 0; c < LE; ++c) a[c] -= src[c];
+    // Ls(0, 0) is rewritten below only by the lanes that read it, in order;
+    // every other sub-block is rewritten after the step's first barrier
+  }
 
   // ---- Cholesky by 16-column block steps; thread = row r of (bi, bj)
   bool bad = false;
@@ -372,10 +445,12 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
   // outer block from its four panels (K = 512), so the trailing matrix is read
   // and written a quarter as often.
   constexpr int64_t OB = 4 * NB;
-  SideStream side, tri;
+  SideStream side, tri, inr;
   GPTQ_TRY(get_side_stream(side, 0));
   GPTQ_TRY(get_side_stream(tri, 1));
-  bool side_pending = false, tri_pending = false;
+  GPTQ_TRY(get_side_stream(inr, 2));
+  bool side_pending = false, tri_pending = false, inr_pending = false;
+  bool lower_pending[2] = {false, false};   // by panel parity
   // Triangular inverse, overlapped with the factorisation.  A node of the
   // bottom-up doubling joins blocks [l0, r0) and [r0, r1): its step 1
   // (T = L21·M11) needs L rows [r0, r1) of columns [l0, r0), final once panel
@@ -384,18 +459,18 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
   // that order on their own stream (smaller levels first, so children precede
   // parents).  Their writes (T parked in A's strict upper block triangle, M's
   // off-diagonal blocks) touch nothing the factorisation still uses.
-  auto issue_trtri = [&](int64_t kb) -> gptq_status {
-    bool recorded = false;
+  // `solved` is recorded on the caller's stream once panel kb is solved.
+  auto issue_trtri = [&](int64_t kb, hipEvent_t solved) -> gptq_status {
+    bool waited = false;
     for (int64_t half = 1; half < p.nblk; half *= 2) {
       for (int64_t q = 0; q * 2 * half + half < p.nblk; ++q) {
         const int64_t r0 = q * 2 * half + half;
         const int64_t r1 = std::min<int64_t>(r0 + half, p.nblk);
         for (int step = 1; step <= 2; ++step) {
           if ((step == 1 ? r0 : r1) != kb + 1) continue;
-          if (!recorded) {
-            GPTQ_HIP_CHECK(hipEventRecord(tri.ready, stream));
-            GPTQ_HIP_CHECK(hipStreamWaitEvent(tri.stream, tri.ready, 0));
-            recorded = true;
+          if (!waited) {
+            GPTQ_HIP_CHECK(hipStreamWaitEvent(tri.stream, solved, 0));
+            waited = true;
           }
           GPTQ_TRY(launch_trtri_nodes(A, Mm, lda, p.nblk, half, q, 1, step, tri.stream));
           tri_pending = true;
@@ -404,34 +479,69 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
     }
     return GPTQ_OK;
   };
+  // Inside an outer block, panel k's update of the block's later columns is
+  // split three ways: the next panel's 128 x 128 diagonal block is updated by
+  // the next leaf itself, which follows the panel solve at once; the rest of
+  // the next panel's columns ("rect") and the block's columns after it
+  // ("lower") run on the inner side stream beside that leaf.  The next panel
+  // solve waits only for rect (it rewrites those rows); lower covers the
+  // diagonal block of panel k + 2, whose leaf waits for it (events by panel
+  // parity).  Concurrent kernels always touch disjoint parts of A.
   for (int64_t K0 = 0; K0 < p.n_pad; K0 += OB) {
     const int64_t K1 = std::min<int64_t>(K0 + OB, p.n_pad);
     for (int64_t k0 = K0; k0 < K1; k0 += NB) {
-      hipLaunchKernelGGL(chol_leaf_kernel, dim3(1), dim3(kLeafThreads), 0, stream, A, Mm, lda, k0, flag);
+      // inside an outer block, the leaf applies the previous panel's update to
+      // its own diagonal block (the rows below get it on the inner stream)
+      const int par = (int)((k0 / NB) & 1);
+      if (lower_pending[par]) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, inr.aux[par], 0));
+      lower_pending[par] = false;
+      hipLaunchKernelGGL(chol_leaf_kernel, dim3(1), dim3(kLeafThreads), 0, stream, A, Mm, lda, k0,
+                         (int)(k0 > K0), flag);
       GPTQ_LAUNCH_CHECK();
       const int64_t rows = p.n_pad - k0 - NB;
       if (rows <= 0) {
-        GPTQ_TRY(issue_trtri(k0 / NB));
+        GPTQ_HIP_CHECK(hipEventRecord(inr.ready, stream));
+        GPTQ_TRY(issue_trtri(k0 / NB, inr.ready));
         break;
       }
-      GemmArgs g;
+      if (inr_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, inr.done, 0));
+      inr_pending = false;
       // panel solve: P = A_panel · D_kᵀ  (D_kᵀ read column-major from D_k)
+      GemmArgs g;
       g.A = A + (k0 + NB) * lda + k0; g.lda = lda;
       g.B = Mm + k0 * lda + k0; g.ldb = lda;
       g.C = A + (k0 + NB) * lda + k0; g.ldc = lda;
       g.M = rows; g.N = NB; g.k_begin = 0; g.k_end = NB; g.alpha = 1.f; g.beta = 0.f;
-      gptq_status st = launch_gemm_rect(g, /*b_colmajor=*/true, stream);
-      if (st != GPTQ_OK) return st;
-      GPTQ_TRY(issue_trtri(k0 / NB));
-      // inner update: A[k0+NB:, k0+NB:K1] -= P · P[k0+NB:K1]ᵀ (lower part)
+      GPTQ_TRY(launch_gemm_rect(g, /*b_colmajor=*/true, stream));
+      GPTQ_HIP_CHECK(hipEventRecord(inr.ready, stream));
+      GPTQ_TRY(issue_trtri(k0 / NB, inr.ready));
+      // inner update: A[k0+NB:, k0+NB:K1] -= P · P[k0+NB:K1]ᵀ (lower part); its
+      // first 128 x 128 diagonal block is left to the next leaf.  Here: the
+      // rows below that block, on the inner stream: the rest of the next
+      // panel's columns, then the lower part of the outer block's columns
+      // after it.
       const int64_t cols = K1 - k0 - NB;
-      if (cols > 0) {
-        g.A = A + (k0 + NB) * lda + k0; g.lda = lda;
-        g.B = A + (k0 + NB) * lda + k0; g.ldb = lda;
-        g.C = A + (k0 + NB) * lda + k0 + NB; g.ldc = lda;
-        g.M = rows; g.N = cols; g.k_begin = 0; g.k_end = NB; g.alpha = -1.f; g.beta = 1.f;
-        st = launch_gemm_lower(g, /*b_colmajor=*/true, stream);
-        if (st != GPTQ_OK) return st;
+      if (cols > 0 && rows > NB) {
+        const float* P = A + (k0 + 2 * NB) * lda + k0;   // solved rows k0+2NB .. n_pad
+        const float* Pc = A + (k0 + NB) * lda + k0;      // solved rows k0+NB .. K1
+        GPTQ_HIP_CHECK(hipStreamWaitEvent(inr.stream, inr.ready, 0));
+        GemmArgs r;
+        r.A = P; r.lda = lda;
+        r.B = Pc; r.ldb = lda;
+        r.C = A + (k0 + 2 * NB) * lda + k0 + NB; r.ldc = lda;
+        r.M = rows - NB; r.N = NB; r.k_begin = 0; r.k_end = NB; r.alpha = -1.f; r.beta = 1.f;
+        GPTQ_TRY(launch_gemm_rect(r, /*b_colmajor=*/true, inr.stream));
+        GPTQ_HIP_CHECK(hipEventRecord(inr.done, inr.stream));
+        inr_pending = true;
+        if (cols > NB) {
+          r.B = P;
+          r.C = A + (k0 + 2 * NB) * lda + k0 + 2 * NB;
+          r.N = cols - NB;
+          GPTQ_TRY(launch_gemm_lower(r, /*b_colmajor=*/true, inr.stream));
+          const int par = (int)((k0 / NB) & 1);   // = parity of panel k + 2
+          GPTQ_HIP_CHECK(hipEventRecord(inr.aux[par], inr.stream));
+          lower_pending[par] = true;
+        }
       }
     }
     // outer update: A[K1:, K1:] -= L[K1:, K0:K1] · L[K1:, K0:K1]ᵀ (lower part),
@@ -469,6 +579,9 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
     }
   }
   if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
+  if (inr_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, inr.done, 0));
+  for (int q = 0; q < 2; ++q)
+    if (lower_pending[q]) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, inr.aux[q], 0));
   if (tri_pending) {
     GPTQ_HIP_CHECK(hipEventRecord(tri.done, tri.stream));
     GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, tri.done, 0));
