@@ -17,8 +17,9 @@
 // no mask: columns already quantized see U[c][k] = 0 (k < c) or are never read
 // again (k = c).  The weight of column c is broadcast from its owner lane by
 // DPP row_newbcast, the group min/max is a 16-lane butterfly.  Codes, the
-// error block and ½Σe² are written out; the columns after the block are
-// updated by the trailing GEMM.
+// error block and ½Σe² are written out; the workgroup then applies the
+// block's errors to its own rows of the superblock's remaining columns, and
+// the columns after the superblock are updated by the trailing GEMM.
 #include <utility>
 
 #include "quant_common.hpp"
@@ -110,13 +111,66 @@ __device__ __forceinline__ void bq_cols(std::integer_sequence<int, Cs...>, BqCtx
   (bq_col<GW, Cs>(x), ...);
 }
 
+// The lazy update of the rest of the superblock from this block's errors,
+// W[rows, i2:i2+ncols] -= E[rows, 0:128] · U[i1:i1+128, i2:i2+ncols], done by
+// each workgroup for its own 16 rows (rows are independent, so no other
+// workgroup touches them) with v_mfma_f32_16x16x4f32.  Columns go in blocks
+// of 32, wave w taking blocks w, w+4, ...; in a block, lane l owns the two
+// adjacent columns 2 (l % 16) and 2 (l % 16) + 1, which feed MFMA 0 and MFMA 1
+// as their column l % 16, so U and W move as 8-byte loads (U row 4 kk + l/16
+// per k-step).  A = E from LDS, held in registers for all blocks.  Two blocks'
+// loads (U and the W values they update) are in flight at once, and the
+// first block's are issued before the column loop.
+constexpr int kPushK = QB / 4;    // MFMA k-steps per block
+constexpr int kEsPitch = QB + 4;  // row pitch of the error block in LDS
+constexpr int kPushCols = 32;     // columns per push block
+
+struct PushBlk {
+  float2 b[kPushK];   // U[4 kk + l/16][2 (l%16) + e], e = .x / .y
+  float2 w[4];        // W[4 (l/16) + v][2 (l%16) + e]
+};
+
+// pair: both columns in range and 8-byte aligned rows (even ld, even column)
+__device__ __forceinline__ float2 ld_pair(const float* __restrict__ p, bool ok0, bool ok1, bool vec) {
+  if (vec && ok1) return *reinterpret_cast<const float2*>(p);
+  return make_float2(ok0 ? p[0] : 0.f, ok1 ? p[1] : 0.f);
+}
+
+__device__ __forceinline__ void push_load(PushBlk& t, const float* __restrict__ up, int64_t ldu,
+                                          const float* __restrict__ wp, int64_t ldw, int64_t rows_left,
+                                          int blk, int ncols, bool vec, int lane) {
+  const int col = kPushCols * blk + 2 * (lane & 15);
+  const bool ok0 = col < ncols, ok1 = col + 1 < ncols;
+  const int c = ok0 ? col : 0;
+  const float* src = up + (int64_t)(lane >> 4) * ldu + c;
+#pragma unroll
+  for (int kk = 0; kk < kPushK; ++kk) t.b[kk] = ld_pair(src + (int64_t)(4 * kk) * ldu, ok0, ok1, vec);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int row = 4 * (lane >> 4) + v;
+    const bool rok = row < rows_left;
+    t.w[v] = ld_pair(wp + (int64_t)(rok ? row : 0) * ldw + c, ok0 && rok, ok1 && rok, vec);
+  }
+}
+
 // GW > 0: group width (a power of two dividing 128); GW == 0: one group per
 // row, its grid already in scales/zeros.
 template <int GW>
 __global__ __launch_bounds__(256) void block_quant_kernel(QArgs q, const float* __restrict__ ublk,
-                                                         int64_t ldu, int64_t i1, int bw) {
+                                                         int64_t ldu, int64_t i1, int bw,
+                                                         const float* __restrict__ upush, int ncols) {
   __shared__ __attribute__((aligned(16))) float us[QB * QB];
+  __shared__ __attribute__((aligned(16))) float es[kBqRows * kEsPitch];
   const int tid = threadIdx.x;
+  // the push's operands: its first block's loads go out now
+  const int64_t prow0 = (int64_t)blockIdx.x * kBqRows;
+  const int64_t rows_left = q.m - prow0;
+  float* wpush = q.Wp + prow0 * q.ldw + i1 + bw;   // processed column i2 = i1 + bw
+  const bool pvec = ((ldu | q.ldw | (i1 + bw)) & 1) == 0 &&
+                    ((reinterpret_cast<uintptr_t>(upush) | reinterpret_cast<uintptr_t>(q.Wp)) & 7) == 0;
+  PushBlk pb[2];
+  if ((tid >> 6) * kPushCols < ncols)
+    push_load(pb[0], upush, ldu, wpush, q.ldw, rows_left, tid >> 6, ncols, pvec, tid & 63);
   // U block: rows and columns < bw, upper triangle only (the rest zero)
   for (int idx = tid; idx < QB * QB; idx += 256) {
     const int r = idx >> 7, c = idx & (QB - 1);
@@ -170,15 +224,62 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs q, const float* 
     *reinterpret_cast<f32x4_t*>(erow + 4) = f32x4_t{x.e8[4], x.e8[5], x.e8[6], x.e8[7]};
     if (x.j == 0) q.loss_rows[r] += 0.5 * (double)lacc;
   }
+  if (ncols <= 0) return;   // uniform: last block of its superblock
+
+  // ---- push this block's errors into the rest of the superblock (own rows)
+  {
+    float* erow = es + (wave * 4 + (lane >> 4)) * kEsPitch + 8 * x.j;
+    *reinterpret_cast<f32x4_t*>(erow) = f32x4_t{x.e8[0], x.e8[1], x.e8[2], x.e8[3]};
+    *reinterpret_cast<f32x4_t*>(erow + 4) = f32x4_t{x.e8[4], x.e8[5], x.e8[6], x.e8[7]};
+  }
+  __syncthreads();
+  // A operand: lane l supplies E[l % 16][4 kk + l / 16]
+  float ea[kPushK];
+#pragma unroll
+  for (int kk = 0; kk < kPushK; ++kk) ea[kk] = es[(lane & 15) * kEsPitch + 4 * kk + (lane >> 4)];
+  const int nblk = (ncols + kPushCols - 1) / kPushCols;
+  auto apply = [&](const PushBlk& t, int blk) {
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < kPushK; ++kk) {
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[kk], t.b[kk].x, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[kk], t.b[kk].y, acc1, 0, 0, 0);
+    }
+    // D[4 (l / 16) + v][l % 16] of MFMA e: row 4 (l / 16) + v, column 2 (l % 16) + e
+    const int col = kPushCols * blk + 2 * (lane & 15);
+    const bool ok0 = col < ncols, ok1 = col + 1 < ncols;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = 4 * (lane >> 4) + v;
+      if (row >= rows_left || !ok0) continue;
+      float* dst = wpush + (int64_t)row * q.ldw + col;
+      const float2 nv = make_float2(t.w[v].x - acc0[v], t.w[v].y - acc1[v]);
+      if (pvec && ok1) {
+        *reinterpret_cast<float2*>(dst) = nv;
+      } else {
+        dst[0] = nv.x;
+        if (ok1) dst[1] = nv.y;
+      }
+    }
+  };
+  // blocks wave, wave + 4, ... alternate between pb[0] and pb[1]
+#pragma unroll 1
+  for (int blk = wave; blk < nblk; blk += 8) {
+    if (blk + 4 < nblk) push_load(pb[1], upush, ldu, wpush, q.ldw, rows_left, blk + 4, ncols, pvec, lane);
+    apply(pb[0], blk);
+    if (blk + 4 >= nblk) break;
+    if (blk + 8 < nblk) push_load(pb[0], upush, ldu, wpush, q.ldw, rows_left, blk + 8, ncols, pvec, lane);
+    apply(pb[1], blk + 4);
+  }
 }
 
 }  // namespace
 
 template <>
 void launch_block_quant<GPTQ_BQ_GW>(const QArgs& a, const float* ublk, int64_t ldu, int64_t i1,
-                                    int bw, hipStream_t stream) {
+                                    int bw, int ncols, hipStream_t stream) {
   hipLaunchKernelGGL(block_quant_kernel<GPTQ_BQ_GW>, dim3((unsigned)ceil_div(a.m, kBqRows)), dim3(256), 0,
-                     stream, a, ublk, ldu, i1, bw);
+                     stream, a, ublk, ldu, i1, bw, ublk + bw, ncols);
 }
 
 }  // namespace gptq

@@ -55,16 +55,19 @@ __device__ __forceinline__ float quant_code(float w, float s, float z, int bits,
 
 // One block of bw <= 128 columns starting at processed column i1, all rows;
 // GW = group width or 0 for one group per row.  ublk points at U[i1][i1] with
-// row stride ldu; only rows and columns < bw of the block are read.
+// row stride ldu; rows and columns < bw of the diagonal block are read, and,
+// with ncols > 0 (then bw = 128), the block's errors are pushed into the
+// ncols working-weight columns after it through U rows i1 .. i1+127, columns
+// i1+128 .. i1+128+ncols-1.
 // Instantiated in block_quant_g*.hip.
 template <int GW>
 void launch_block_quant(const QArgs& a, const float* ublk, int64_t ldu, int64_t i1, int bw,
-                        hipStream_t stream);
-template <> void launch_block_quant<0>(const QArgs&, const float*, int64_t, int64_t, int, hipStream_t);
-template <> void launch_block_quant<8>(const QArgs&, const float*, int64_t, int64_t, int, hipStream_t);
-template <> void launch_block_quant<16>(const QArgs&, const float*, int64_t, int64_t, int, hipStream_t);
-template <> void launch_block_quant<32>(const QArgs&, const float*, int64_t, int64_t, int, hipStream_t);
-template <> void launch_block_quant<64>(const QArgs&, const float*, int64_t, int64_t, int, hipStream_t);
-template <> void launch_block_quant<128>(const QArgs&, const float*, int64_t, int64_t, int, hipStream_t);
+                        int ncols, hipStream_t stream);
+template <> void launch_block_quant<0>(const QArgs&, const float*, int64_t, int64_t, int, int, hipStream_t);
+template <> void launch_block_quant<8>(const QArgs&, const float*, int64_t, int64_t, int, int, hipStream_t);
+template <> void launch_block_quant<16>(const QArgs&, const float*, int64_t, int64_t, int, int, hipStream_t);
+template <> void launch_block_quant<32>(const QArgs&, const float*, int64_t, int64_t, int, int, hipStream_t);
+template <> void launch_block_quant<64>(const QArgs&, const float*, int64_t, int64_t, int, int, hipStream_t);
+template <> void launch_block_quant<128>(const QArgs&, const float*, int64_t, int64_t, int, int, hipStream_t);
 
 }  // namespace gptq

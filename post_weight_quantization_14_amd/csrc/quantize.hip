@@ -10,8 +10,11 @@
 //   block_quant : one lane = one output row.  The row's 128-column slab lives
 //                 in VGPRs (fully unrolled, static indices); the rows of U's
 //                 128 x 128 diagonal block arrive by scalar loads.  Group
-//                 min/max at each group start, codes, Err block, ½Σe² per row.
-//   trailing    : W[:, i2:] -= Err · U[i1:i2, i2:] as an fp32 MFMA GEMM.
+//                 min/max at each group start, codes, Err block, ½Σe² per row;
+//                 then each workgroup pushes its rows' errors into the rest of
+//                 the 512-column superblock (fp32 MFMA, U streamed from HBM).
+//   trailing    : W[:, s2:] -= Err · U[s1:s2, s2:] per superblock, as an fp32
+//                 MFMA GEMM.
 //   finalize    : g_idx / inverse permutation, nibble packing in original
 //                 column order, ‖W − Ŵ‖² from the packed outputs, fixed-order
 //                 fp64 reductions.
@@ -240,9 +243,10 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
 
   // Two-level lazy update (exact: the same rank-1 corrections, grouped).  A
   // block's errors update the rest of its 512-column superblock at once
-  // (K = 128); the columns after the superblock are updated once per
-  // superblock from all of its errors (K = 512), so the working weights are
-  // read and written a quarter as often as with per-block updates.
+  // (K = 128, inside the block's own kernel); the columns after the
+  // superblock are updated once per superblock from all of its errors
+  // (K = 512), so the working weights are read and written a quarter as often
+  // as with per-block updates.
   // Lookahead: of that superblock update, the next superblock's columns run on
   // the caller's stream and the columns after them on the side stream, while
   // the next superblock's column loop (its own columns only) runs here.  The
@@ -260,28 +264,20 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
       const float* ublk = U + i1 * n + i1;
       const int64_t ldub = n;
       a.err = errs + (i1 - s1);
+      // W_p[rows, i1+bw : s2] -= Err_block · U[i1:i1+bw, i1+bw:s2], in the kernel
+      const int ncols = (int)(s2 - i1 - bw);
       switch (gw) {
-        case -1: launch_block_quant<0>(a, ublk, ldub, i1, bw, stream); break;
-        case 8: launch_block_quant<8>(a, ublk, ldub, i1, bw, stream); break;
-        case 16: launch_block_quant<16>(a, ublk, ldub, i1, bw, stream); break;
-        case 32: launch_block_quant<32>(a, ublk, ldub, i1, bw, stream); break;
-        case 64: launch_block_quant<64>(a, ublk, ldub, i1, bw, stream); break;
-        case 128: launch_block_quant<128>(a, ublk, ldub, i1, bw, stream); break;
+        case -1: launch_block_quant<0>(a, ublk, ldub, i1, bw, ncols, stream); break;
+        case 8: launch_block_quant<8>(a, ublk, ldub, i1, bw, ncols, stream); break;
+        case 16: launch_block_quant<16>(a, ublk, ldub, i1, bw, ncols, stream); break;
+        case 32: launch_block_quant<32>(a, ublk, ldub, i1, bw, ncols, stream); break;
+        case 64: launch_block_quant<64>(a, ublk, ldub, i1, bw, ncols, stream); break;
+        case 128: launch_block_quant<128>(a, ublk, ldub, i1, bw, ncols, stream); break;
         default:
           set_error("group_size %d not built", gw);
           return GPTQ_ERR_UNSUPPORTED;
       }
       GPTQ_LAUNCH_CHECK();
-      const int64_t i2 = i1 + bw;
-      if (i2 < s2) {   // W_p[:, i2:s2] -= Err_block · U[i1:i2, i2:s2]
-        GemmArgs g;
-        g.A = a.err; g.lda = kQSuper;
-        g.B = U + i1 * n + i2; g.ldb = n;
-        g.C = Wp + i2; g.ldc = p.ldw;
-        g.M = m; g.N = s2 - i2; g.k_begin = 0; g.k_end = bw; g.alpha = -1.f; g.beta = 1.f;
-        gptq_status st = launch_gemm_rect(g, /*b_colmajor=*/false, stream);
-        if (st != GPTQ_OK) return st;
-      }
     }
     if (s2 < n) {   // W_p[:, s2:] -= Err_super · U[s1:s2, s2:]
       const int64_t near = std::min<int64_t>(kQSuper, n - s2), far = n - s2 - near;
