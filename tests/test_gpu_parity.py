@@ -169,6 +169,10 @@ QUANT_CASES = [
     # several 512-column superblocks, ragged last block
     dict(m=48, n=1100, tokens=4400, bits=4, group_size=128, sym=False, desc_act=True),
     dict(m=40, n=1540, tokens=6000, bits=3, group_size=64, sym=True, desc_act=True),
+    # odd n: rows of U and of the working weights are not 8-byte aligned, and
+    # the in-superblock update of the first block covers an odd column count
+    dict(m=35, n=301, tokens=2400, bits=4, group_size=32, sym=False, desc_act=True),
+    dict(m=37, n=1037, tokens=4200, bits=3, group_size=128, sym=False, desc_act=False),
 ]
 
 
