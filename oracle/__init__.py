@@ -30,3 +30,9 @@ from .gptq_oracle import (  # noqa: F401
     unpack_codes,
     unpermute_codes,
 )
+from .linear_quantizer import (  # noqa: F401,E402
+    linear_codes,
+    linear_grid,
+    linear_quantize,
+    percentile_linear,
+)

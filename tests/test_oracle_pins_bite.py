@@ -114,3 +114,103 @@ def test_unplanted_oracle_passes_the_checks():
 def test_planted_mistake_is_caught(monkeypatch, name, fn):
     monkeypatch.setattr(go, name, fn)
     assert not (_hand_cases_pass() and _exact_route_passes())
+
+
+# ---------------------------------------------------------------------------
+# The linear (round-to-nearest) quantizer's pins bite too
+# ---------------------------------------------------------------------------
+from oracle import linear_quantizer as lq  # noqa: E402
+import test_oracle_linear_pins as lp  # noqa: E402
+
+
+def _linear_pins_pass():
+    checks = [
+        lp.test_worked_int8_example_through_linear_quantizer,
+        lambda: lp.test_percentile_is_numpy_linear_percentile(100, 0.99),
+        lambda: lp.test_percentile_is_numpy_linear_percentile(7, 0.3),
+        lp.test_percentile_hand_positions,
+        lp.test_asym_hand_case,
+        lp.test_sym_clip_hand_case,
+        lp.test_asym_clip_hand_case,
+        lambda: lp.test_clip_one_is_min_max(True),
+        lambda: lp.test_clip_one_is_min_max(False),
+        lambda: lp.test_codes_on_grid_and_dequant_identity(4, False),
+        lp.test_all_zero_row_uses_the_floor,
+        lp.test_mse_and_cos_against_fractions,
+    ]
+    for c in checks:
+        try:
+            c()
+        except AssertionError:
+            return False
+    return True
+
+
+def _pct_rank_n(values, frac):   # position f·N instead of f·(N-1)
+    a = np.sort(np.asarray(values, dtype=np.float64).ravel())
+    p = float(frac) * a.size
+    i = min(int(np.floor(p)), a.size - 1)
+    if i >= a.size - 1:
+        return float(a[-1])
+    return float(a[i] + (a[i + 1] - a[i]) * (p - i))
+
+
+def _codes_floor(v, scale, zp, qmin, qmax, sym):
+    v = np.asarray(v, dtype=np.float64)
+    q = np.floor(v / scale) if sym else np.floor(v / scale + zp)
+    return np.clip(q, qmin, qmax)
+
+
+def _grid_wrong_qmax(v, bits, sym, clip_ratio):
+    s, zp, qmin, qmax = _orig_grid(v, bits, sym, clip_ratio)
+    if sym:
+        s = s * (2 ** (bits - 1) - 1) / 2 ** (bits - 1)   # divides by 2^(b-1)
+    return s, zp, qmin, qmax
+
+
+def _grid_zp_sign(v, bits, sym, clip_ratio):
+    s, zp, qmin, qmax = _orig_grid(v, bits, sym, clip_ratio)
+    return s, -zp, qmin, qmax
+
+
+def _grid_widened(v, bits, sym, clip_ratio):   # the GPTQ path's range, not the page's
+    v = np.asarray(v, dtype=np.float64)
+    if sym:
+        return _orig_grid(v, bits, sym, clip_ratio)
+    lo, hi = min(float(np.min(v)), 0.0), max(float(np.max(v)), 0.0)
+    s = max((hi - lo) / (2 ** bits - 1), 1e-8)
+    return s, -float(np.rint(lo / s)), 0, 2 ** bits - 1
+
+
+_orig_grid = lq.linear_grid
+
+
+def _lq_mse_sum(W, bits, sym, group_size, clip_ratio):
+    out = _orig_lq(W, bits, sym, group_size, clip_ratio)
+    out["mse"] = out["mse"] * np.asarray(W).size
+    return out
+
+
+_orig_lq = lq.linear_quantize
+
+
+def test_linear_pins_pass_unpatched():
+    assert _linear_pins_pass()
+
+
+@pytest.mark.parametrize("target,wrong", [
+    ("percentile_linear", _pct_rank_n),
+    ("linear_codes", _codes_floor),
+    ("linear_grid", _grid_wrong_qmax),
+    ("linear_grid", _grid_zp_sign),
+    ("linear_grid", _grid_widened),
+    ("linear_quantize", _lq_mse_sum),
+], ids=["percentile_rank_N", "floor_rounding", "sym_qmax_2^(b-1)", "zero_point_sign", "asym_widened_to_0",
+        "mse_sum_not_mean"])
+def test_linear_pins_catch(monkeypatch, target, wrong):
+    monkeypatch.setattr(lq, target, wrong)
+    monkeypatch.setattr(oracle_pkg, target, wrong)
+    assert not _linear_pins_pass()
+
+
+import oracle as oracle_pkg  # noqa: E402
