@@ -164,6 +164,40 @@ def run_sweep(pq, torch, bits_groups, log_every=16):
     return res
 
 
+def measure_rtn(pq, torch, W, reps=5):
+    """The linear round-to-nearest quantizer (the pages' LinearQuantizer) on
+    this layer's weight, per setting: ms per call (HIP events on the stream
+    the kernels run on; the call ends with its own NaN check, a stream
+    synchronisation, which is included) and the HBM roofline of the call's
+    algorithmic bytes (W read once; codes, scales and zeros written once)."""
+    m, n = W.shape
+    res = {}
+    for name, cfg in (("int8_sym_per_row_clip0.99", pq.RtnConfig(8, -1, True, 0.99)),
+                      ("int4_asym_g128_clip1.0", pq.RtnConfig(4, 128, False, 1.0))):
+        outs = pq.rtn_quantize(W, cfg)   # allocates the outputs, warms the kernels
+        ws = torch.empty(max(pq.gptq_rtn_workspace_bytes(m, n, cfg), 1), dtype=torch.uint8, device=W.device)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            pq.gptq_rtn_quantize(W, cfg, outs["qweight"], outs["scales"], outs["zeros"], outs["err"], ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        words = pq.gptq_qweight_words(n, cfg.bits)
+        groups = pq.gptq_num_groups(n, cfg.group_size)
+        nbytes = m * n * W.element_size() + m * words * 4 + m * groups * 8
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        err = outs["err"].cpu().tolist()
+        res[name] = {"ms": ms, "mse": err[0], "cos": err[1],
+                     "roofline": {"bound": "hbm", "kernel": "rtn_row_kernel + rtn_reduce_kernel",
+                                  "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                                  "algorithmic_bytes_per_call": nbytes}}
+        log(f"bench: rtn {name}: {ms:.3f} ms, {gbs:.0f} GB/s, mse {err[0]:.4e}, cos {err[1]:.6f}")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,6 +294,8 @@ def main():
         },
         "loss": layer.out["loss"].cpu().tolist(),
     }
+    result["next_rows"] = {"rtn_quantize": {"workload": f"{spec.name} weight ({m} x {n})",
+                                            **measure_rtn(pq, torch, W)}}
     if not args.no_sweep and args.workload == "c3_down_proj_4096x11008":
         del layer
         torch.cuda.empty_cache()

@@ -155,6 +155,53 @@ gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t m, int64
                                 uint32_t* qweight, float* scales, int32_t* zeros, int32_t* g_idx,
                                 double* loss, void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The linear round-to-nearest quantizer (no Hessian, no error feedback).
+ * Defines: the LinearQuantizer of page "模型量化实战：从 INT8 PTQ 到 GPTQ…"
+ * §3.1 with the affine formula of its §2.1: per output row ("per channel")
+ * or per group of group_size consecutive columns of a row,
+ *   symmetric:  scale = percentile(|w|, clip) / (2^(b-1) - 1),
+ *               q = round(w / scale) clamped to [-2^(b-1), 2^(b-1) - 1];
+ *   asymmetric: lo, hi = percentile(w, (1-clip)/2), percentile(w, 1-(1-clip)/2),
+ *               scale = (hi - lo) / (2^b - 1), zero = -round(lo / scale),
+ *               q = round(w / scale + zero) clamped to [0, 2^b - 1];
+ * scale floored at 1e-8; round = half to even; percentile(v, f) interpolates
+ * linearly between the sorted values at position f·(N-1) (clip = 1: the
+ * maximum, or the minimum and maximum); the range is NOT widened to include
+ * 0, so an asymmetric zero may lie outside [0, 2^b - 1].  The grid and the
+ * codes are computed in fp64.
+ *
+ *   W        [m, n] of w_dtype (GPTQ_BF16 or GPTQ_FP32), row-major, read only.
+ *   cfg      bits 2, 3, 4 or 8; group_size -1 (one group per row) or >= 1;
+ *            sym 0/1; clip_ratio in (0, 1].
+ * Outputs (original column order; layouts as in gptq_quantize_layer):
+ *   qweight  [m, gptq_qweight_words(n, bits)] uint32.
+ *   scales   [m, G] fp32 (the fp64 scale rounded), G = gptq_num_groups(n, g).
+ *   zeros    [m, G] int32; dequantization is (q - zero)·scale, symmetric codes
+ *            stored offset by 2^(bits-1) with zero = 2^(bits-1).
+ *   err      [2] fp64 device: err[0] = mean over the m·n weights of
+ *            (w - ŵ)², err[1] = Σ w·ŵ / (‖w‖·‖ŵ‖ + 1e-8) (the page's
+ *            quantization_error), ŵ from the fp64 scale.
+ *   workspace at least gptq_rtn_workspace_bytes(m, n, cfg) bytes.
+ * Returns GPTQ_ERR_UNSUPPORTED when one row's groups do not fit the on-chip
+ * sort (n <= 32768 for one group per row; for groups of g columns,
+ * ceil(n/g)·(4·P + 16) <= 150 KiB with P = g rounded up to a power of two).
+ * Synchronises `stream` once at the end to return GPTQ_ERR_NONFINITE if W
+ * holds a NaN or Inf.  m == 0 or n == 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t bits;
+  int32_t group_size;
+  int32_t sym;
+  float clip_ratio;
+} gptq_rtn_config;
+
+size_t gptq_rtn_workspace_bytes(int64_t m, int64_t n, const gptq_rtn_config* cfg);
+gptq_status gptq_rtn_quantize(const void* W, int32_t w_dtype, int64_t m, int64_t n,
+                              const gptq_rtn_config* cfg, uint32_t* qweight, float* scales,
+                              int32_t* zeros, double* err, void* workspace, size_t ws_bytes,
+                              void* stream);
+
 /* Sizes of the outputs above (host-only helpers, no GPU work). */
 int64_t gptq_qweight_words(int64_t n, int32_t bits);
 int64_t gptq_num_groups(int64_t n, int32_t group_size);

@@ -6,6 +6,7 @@ from ._lib import GPTQ_BF16, GPTQ_FP32, LIB_PATH, lib  # noqa: F401
 from .gptq import (  # noqa: F401
     GptqError,
     QuantConfig,
+    RtnConfig,
     alloc_outputs,
     gptq_hessian_accumulate,
     gptq_hessian_workspace_bytes,
@@ -16,5 +17,8 @@ from .gptq import (  # noqa: F401
     gptq_quantize_layer,
     gptq_quantize_workspace_bytes,
     gptq_qweight_words,
+    gptq_rtn_quantize,
+    gptq_rtn_workspace_bytes,
     quantize_layer,
+    rtn_quantize,
 )

@@ -32,6 +32,11 @@ class GptqConfig(ctypes.Structure):
                 ("damp_percent", ctypes.c_double)]
 
 
+class GptqRtnConfig(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32), ("sym", ctypes.c_int32),
+                ("clip_ratio", ctypes.c_float)]
+
+
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
@@ -47,6 +52,9 @@ SIGNATURES = {
     "gptq_quantize_workspace_bytes": (_SZ, [_I64, _I64, ctypes.POINTER(GptqConfig)]),
     "gptq_quantize_layer": (_ST, [_P, _I32, _I64, _I64, _P, _P, ctypes.POINTER(GptqConfig), _P, _P,
                                   _P, _P, _P, _P, _SZ, _P]),
+    "gptq_rtn_workspace_bytes": (_SZ, [_I64, _I64, ctypes.POINTER(GptqRtnConfig)]),
+    "gptq_rtn_quantize": (_ST, [_P, _I32, _I64, _I64, ctypes.POINTER(GptqRtnConfig), _P, _P, _P, _P,
+                                _P, _SZ, _P]),
     "gptq_qweight_words": (_I64, [_I64, _I32]),
     "gptq_num_groups": (_I64, [_I64, _I32]),
     "gptq_last_error": (ctypes.c_char_p, []),

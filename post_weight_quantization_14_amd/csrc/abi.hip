@@ -196,4 +196,48 @@ gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t m, int64
                       workspace, plan, static_cast<hipStream_t>(stream));
 }
 
+static gptq_status check_rtn_config(const gptq_rtn_config* cfg) {
+  if (cfg == nullptr) return fail(GPTQ_ERR_INVALID_ARG, "cfg is NULL");
+  if (cfg->bits != 2 && cfg->bits != 3 && cfg->bits != 4 && cfg->bits != 8)
+    return fail(GPTQ_ERR_UNSUPPORTED, "bits=%d", cfg->bits);
+  if (cfg->group_size != -1 && cfg->group_size < 1)
+    return fail(GPTQ_ERR_INVALID_ARG, "group_size=%d", cfg->group_size);
+  if (cfg->sym != 0 && cfg->sym != 1) return fail(GPTQ_ERR_INVALID_ARG, "sym=%d", cfg->sym);
+  if (!(cfg->clip_ratio > 0.f && cfg->clip_ratio <= 1.f))
+    return fail(GPTQ_ERR_INVALID_ARG, "clip_ratio=%g outside (0, 1]", (double)cfg->clip_ratio);
+  return GPTQ_OK;
+}
+
+size_t gptq_rtn_workspace_bytes(int64_t m, int64_t n, const gptq_rtn_config* cfg) {
+  if (m < 0 || n < 0 || cfg == nullptr) return 0;
+  return plan_rtn(m, n, cfg->group_size).total;
+}
+
+gptq_status gptq_rtn_quantize(const void* W, int32_t w_dtype, int64_t m, int64_t n,
+                              const gptq_rtn_config* cfg, uint32_t* qweight, float* scales,
+                              int32_t* zeros, double* err, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  clear_error();
+  if (m < 0 || n < 0) return fail(GPTQ_ERR_INVALID_ARG, "m=%lld n=%lld", (long long)m, (long long)n);
+  gptq_status st = check_rtn_config(cfg);
+  if (st != GPTQ_OK) return st;
+  if (w_dtype != GPTQ_BF16 && w_dtype != GPTQ_FP32)
+    return fail(GPTQ_ERR_UNSUPPORTED, "w_dtype=%d", w_dtype);
+  if (m == 0 || n == 0) return GPTQ_OK;
+  if (m > ((int64_t)1 << 31) - 1) return fail(GPTQ_ERR_UNSUPPORTED, "m=%lld too large", (long long)m);
+  const RtnPlan plan = plan_rtn(m, n, cfg->group_size);
+  if (plan.lds_bytes > kRtnMaxLds)
+    return fail(GPTQ_ERR_UNSUPPORTED, "n=%lld with group_size %d needs %zu bytes of LDS per row (max %zu)",
+                (long long)n, cfg->group_size, plan.lds_bytes, kRtnMaxLds);
+  if (bad_ptr(W, w_dtype == GPTQ_BF16 ? 2 : 4)) return fail(GPTQ_ERR_INVALID_ARG, "W is NULL or misaligned");
+  if (bad_ptr(qweight, 4) || bad_ptr(scales, 4) || bad_ptr(zeros, 4))
+    return fail(GPTQ_ERR_INVALID_ARG, "an output pointer is NULL or misaligned");
+  if (bad_ptr(err, 8)) return fail(GPTQ_ERR_INVALID_ARG, "err is NULL or misaligned");
+  if (workspace == nullptr || ws_bytes < plan.total || bad_ptr(workspace, 256))
+    return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu (256-byte aligned)", ws_bytes,
+                plan.total);
+  return run_rtn(W, w_dtype, m, n, cfg->bits, cfg->sym, cfg->clip_ratio, qweight, scales, zeros, err,
+                 workspace, plan, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

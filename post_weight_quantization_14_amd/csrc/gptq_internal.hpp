@@ -114,6 +114,20 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
                          float* scales, int32_t* zeros, int32_t* g_idx, double* loss, void* ws,
                          const QuantPlan& plan, hipStream_t stream);
 
+// ---------------------------------------------------------------- linear (RTN) quantizer
+// One workgroup per output row sorts each group's keys in LDS: G·P floats plus
+// two doubles per group must fit in kRtnMaxLds.
+constexpr size_t kRtnMaxLds = 150 * 1024;
+struct RtnPlan {
+  int64_t g = 1, G = 1, P = 1;   // group width, groups per row, padded segment length
+  size_t lds_bytes = 0;
+  size_t part_off = 0, flag_off = 0, total = 0;
+};
+RtnPlan plan_rtn(int64_t m, int64_t n, int32_t group_size);
+gptq_status run_rtn(const void* W, int w_dtype, int64_t m, int64_t n, int bits, int sym, float clip,
+                    uint32_t* qweight, float* scales, int32_t* zeros, double* err, void* ws,
+                    const RtnPlan& plan, hipStream_t stream);
+
 // ---------------------------------------------------------------- fp32 MFMA GEMM (shared)
 // C[M,N] = alpha * A[M,K] * B[K,N] + beta * C, A row-major; B row-major or, with
 // b_colmajor, stored as B[k][j] = Bp[j * ldb + k].  Tiles of 128 x 128.

@@ -143,6 +143,57 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, cf
     _check(st, "gptq_quantize_layer")
 
 
+# ---------------------------------------------------------------- linear (RTN) quantizer
+@dataclass
+class RtnConfig:
+    """Settings of gptq_rtn_quantize: bits 2/3/4/8; group_size -1 (one group
+    per output row) or >= 1; sym; clip_ratio in (0, 1]."""
+    bits: int = 8
+    group_size: int = -1
+    sym: bool = True
+    clip_ratio: float = 0.99
+
+    def c(self) -> "_lib.GptqRtnConfig":
+        return _lib.GptqRtnConfig(self.bits, self.group_size, int(self.sym), self.clip_ratio)
+
+
+def gptq_rtn_workspace_bytes(m: int, n: int, cfg: RtnConfig) -> int:
+    c = cfg.c()
+    return int(lib().gptq_rtn_workspace_bytes(m, n, ctypes.byref(c)))
+
+
+def gptq_rtn_quantize(W: torch.Tensor, cfg: RtnConfig, qweight: torch.Tensor, scales: torch.Tensor,
+                      zeros: torch.Tensor, err: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    if not W.is_contiguous():
+        raise ValueError("W must be contiguous [m, n]")
+    m, n = W.shape
+    c = cfg.c()
+    ws = _workspace(gptq_rtn_workspace_bytes(m, n, cfg), W.device, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().gptq_rtn_quantize(_ptr(W), _dtype_code(W), m, n, ctypes.byref(c), _ptr(qweight),
+                                 _ptr(scales), _ptr(zeros), _ptr(err), _ptr(ws), nbytes, _stream(stream))
+    _check(st, "gptq_rtn_quantize")
+
+
+def rtn_quantize(W: torch.Tensor, cfg: RtnConfig) -> dict:
+    """Allocate the outputs and run gptq_rtn_quantize on W [m, n]."""
+    m, n = W.shape
+    dev = W.device
+    # sizes of an invalid config come back negative: allocate nothing and let
+    # the library report the config
+    words = max(gptq_qweight_words(n, cfg.bits), 0)
+    groups = max(gptq_num_groups(n, cfg.group_size), 0)
+    out = dict(
+        qweight=torch.empty(m, words, dtype=torch.int32, device=dev),
+        scales=torch.empty(m, groups, dtype=torch.float32, device=dev),
+        zeros=torch.empty(m, groups, dtype=torch.int32, device=dev),
+        err=torch.zeros(2, dtype=torch.float64, device=dev),
+    )
+    gptq_rtn_quantize(W, cfg, out["qweight"], out["scales"], out["zeros"], out["err"])
+    return out
+
+
 # ---------------------------------------------------------------- whole layer
 def alloc_outputs(m: int, n: int, cfg: QuantConfig, device) -> dict:
     words = gptq_qweight_words(n, cfg.bits)
