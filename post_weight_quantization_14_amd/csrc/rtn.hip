@@ -12,14 +12,16 @@
 // interpolate linearly between order statistics at position f·(N-1).
 //
 // One workgroup of 512 threads per output row:
-//   1. the row's sort keys (|w| or w) go to LDS, each group padded to a power
-//      of two P with +inf;
-//   2. every P-segment is bitonic-sorted in place (the network only pairs
-//      indices inside a segment, and the direction follows the index within
-//      the segment, so all segments end ascending);
-//   3. one thread per group reads its order statistics and forms the grid in
-//      fp64 (the same operations, in the same order, as the float64
-//      definition: no contraction into fused multiply-adds);
+//   1. the row's keys (|w| or w, as order-preserving uint32) go to LDS, each
+//      group padded to a power of two P with the largest key;
+//   2. the order statistics each percentile needs: for one group per row, the
+//      extremes by a block reduction, or ranks floor(p) and floor(p)+1 by
+//      four 8-bit radix-select passes; for groups, a bitonic sort of every
+//      P-segment in place when clipping (the network only pairs indices
+//      inside a segment and takes its direction from the index within the
+//      segment, so all segments end ascending), else a scan per group;
+//   3. the grid in fp64 from those values, with the same operations in the
+//      same order as the float64 definition (no fused multiply-adds);
 //   4. the row is read again, coded in fp64, packed (the GPTQ path's layout)
 //      and its squared error, dot product and norms are summed in fp64.
 // A second kernel reduces the per-row sums in a fixed order.
@@ -54,113 +56,366 @@ struct RtnArgs {
   int* flag;
 };
 
+// Order-preserving map of a float to uint32 (and back): unsigned order of the
+// codes is the numeric order (-0 just below +0).
+__device__ __forceinline__ uint32_t f2u(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return b ^ ((b & 0x80000000u) ? 0xffffffffu : 0x80000000u);
+}
+__device__ __forceinline__ float u2f(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u ^ 0x80000000u) : ~u);
+}
+
 #pragma clang fp contract(off)
-// a[0..L-1] ascending; linear interpolation at position f·(L-1)
-__device__ double rtn_percentile(const float* a, int64_t L, double f) {
-  const double p = f * (double)(L - 1);
-  const double fl = floor(p);
-  const int64_t i = (int64_t)fl;
-  if (i >= L - 1) return (double)a[L - 1];
-  const double t = p - fl;
-  const double lo = (double)a[i], hi = (double)a[i + 1];
+// Linear interpolation between the order statistics v_i <= v_i1 (ranks i and
+// i+1 of L values) at position p = f·(L-1), i = floor(p).
+__device__ double rtn_lerp(float vi, float vi1, double p) {
+  const double t = p - floor(p);
+  const double lo = (double)vi, hi = (double)vi1;
   return lo + (hi - lo) * t;
 }
 
-__device__ void rtn_grid(const float* a, int64_t L, int bits, int sym, float clip, double& scale,
-                         double& zp) {
-  const double c = (double)clip;
-  if (sym) {
-    const double qmax = (double)((1 << (bits - 1)) - 1);
-    const double amax = rtn_percentile(a, L, c < 1.0 ? c : 1.0);   // a = sorted |w|
-    scale = fmax(amax / qmax, 1e-8);
+__device__ void rtn_grid(double lo, double hi, int bits, int sym, double& scale, double& zp) {
+  if (sym) {   // hi = the clipped max|w|
+    scale = fmax(hi / (double)((1 << (bits - 1)) - 1), 1e-8);
     zp = 0.0;
   } else {
-    const double qmax = (double)((1 << bits) - 1);
-    double lo, hi;
-    if (c < 1.0) {
-      const double f = (1.0 - c) / 2.0;
-      lo = rtn_percentile(a, L, f);
-      hi = rtn_percentile(a, L, 1.0 - f);
-    } else {
-      lo = (double)a[0];
-      hi = (double)a[L - 1];
-    }
-    scale = fmax((hi - lo) / qmax, 1e-8);
+    scale = fmax((hi - lo) / (double)((1 << bits) - 1), 1e-8);
     zp = 0.0 - rint(lo / scale);
   }
 }
 #pragma clang fp contract(on)
 
+// Positions of the percentiles of one group of L values: sym uses f = c on
+// |w|; asym f = (1-c)/2 and 1-(1-c)/2 on w (c = 1: the extremes).
+struct RtnRanks {
+  double p[2];   // positions (lo, hi); sym: only p[1]
+  int r[2];      // floor of each position
+};
+__device__ __forceinline__ RtnRanks rtn_ranks(int L, int sym, float clip) {
+  RtnRanks k;
+  const double c = (double)clip;
+  const double f = (1.0 - c) / 2.0;
+  const double flo = sym ? 0.0 : (c < 1.0 ? f : 0.0);
+  const double fhi = sym ? (c < 1.0 ? c : 1.0) : (c < 1.0 ? 1.0 - f : 1.0);
+  k.p[0] = flo * (double)(L - 1);
+  k.p[1] = fhi * (double)(L - 1);
+  k.r[0] = (int)floor(k.p[0]);
+  k.r[1] = (int)floor(k.p[1]);
+  return k;
+}
+
+constexpr int kWaves = kRtnThreads / 64;
+
+// The k-th smallest (0-based) of L uint32 keys in LDS, by four 8-bit radix
+// passes; each wave counts into its own 256-bin histogram (hist[8][256]) and
+// wave 0 adds them while it scans.  The whole workgroup calls it.
+__device__ uint32_t block_select(const uint32_t* keys, int L, int k, uint32_t* hist, int* bc) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t prefix = 0u, mask = 0u;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int b = tid; b < kWaves * 256; b += kRtnThreads) hist[b] = 0u;
+    __syncthreads();
+    uint32_t* hw = hist + wave * 256;
+    for (int i = tid; i < L; i += kRtnThreads) {
+      const uint32_t u = keys[i];
+      if ((u & mask) == prefix) atomicAdd(&hw[(u >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int wv = 0; wv < kWaves; ++wv)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c[q] += hist[wv * 256 + 4 * lane + q];
+      const uint32_t s = c[0] + c[1] + c[2] + c[3];
+      uint32_t inc = s;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += o;
+      }
+      const uint32_t before = inc - s, kk = (uint32_t)k;
+      if (before <= kk && kk < inc) {
+        uint32_t rem = kk - before, bin = 4 * lane;
+        if (rem >= c[0]) { rem -= c[0]; ++bin;
+          if (rem >= c[1]) { rem -= c[1]; ++bin;
+            if (rem >= c[2]) { rem -= c[2]; ++bin; } } }
+        bc[0] = (int)bin;
+        bc[1] = (int)rem;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)bc[0] << shift;
+    mask |= 0xffu << shift;
+    k = bc[1];
+    __syncthreads();   // bc and hist are rewritten by the next pass
+  }
+  return prefix;
+}
+
+// Given v = the key of rank r, the key of rank r+1 (r+1 < L): v itself when
+// more than r+1 keys are <= v, else the smallest key above v.
+__device__ uint32_t block_next(const uint32_t* keys, int L, int r, uint32_t v, uint32_t* red) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t cnt = 0u, mn = 0xffffffffu;
+  for (int i = tid; i < L; i += kRtnThreads) {
+    const uint32_t u = keys[i];
+    if (u <= v) ++cnt;
+    else mn = min(mn, u);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    cnt += (uint32_t)__shfl_xor(cnt, d, 64);
+    mn = min(mn, (uint32_t)__shfl_xor(mn, d, 64));
+  }
+  if (lane == 0) { red[wave] = cnt; red[kWaves + wave] = mn; }
+  __syncthreads();
+  uint32_t c = 0u, m = 0xffffffffu;
+  for (int wv = 0; wv < kWaves; ++wv) { c += red[wv]; m = min(m, red[kWaves + wv]); }
+  __syncthreads();   // red is reused
+  return c >= (uint32_t)(r + 2) ? v : m;
+}
+
+// Keys of ranks r and r+1 (0-based, r+1 clamped to L-1) of one group of L
+// keys, by one wave: distinct values are peeled from the nearer end (the
+// next minimum above, or maximum below, the last one, with its count) until
+// both ranks are covered.
+__device__ void wave_select2(const uint32_t* seg, int L, int r, uint32_t& va, uint32_t& vb);
+
+// Wave-wide reductions of uint32
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x = min(x, (uint32_t)__shfl_xor(x, d, 64));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x = max(x, (uint32_t)__shfl_xor(x, d, 64));
+  return x;
+}
+
+__device__ void wave_select2(const uint32_t* seg, int L, int r, uint32_t& va, uint32_t& vb) {
+  const int lane = threadIdx.x & 63;
+  const int r1 = min(r + 1, L - 1);
+  const bool top = r >= L / 2;
+  bool ga = false, gb = false;
+  uint32_t prev = 0u;
+  int done = 0;   // keys already peeled (from the chosen end)
+  for (int it = 0; it < L && !(ga && gb); ++it) {
+    uint32_t m = top ? 0u : 0xffffffffu;
+    for (int i = lane; i < L; i += 64) {
+      const uint32_t u = seg[i];
+      if (top) { if (it == 0 || u < prev) m = max(m, u); }
+      else     { if (it == 0 || u > prev) m = min(m, u); }
+    }
+    m = top ? wave_max(m) : wave_min(m);
+    int c = 0;
+    for (int i = lane; i < L; i += 64) c += seg[i] == m;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
+    // ranks held by m: [done, done + c) from the bottom, or from the top
+    const int lo = top ? L - done - c : done, hi = top ? L - done : done + c;
+    if (!ga && r >= lo && r < hi) { va = m; ga = true; }
+    if (!gb && r1 >= lo && r1 < hi) { vb = m; gb = true; }
+    done += c;
+    prev = m;
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kRtnThreads) void rtn_row_kernel(RtnArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float keys[];   // [G*P], then the grids
+  extern __shared__ __attribute__((aligned(16))) uint32_t keys[];   // [G*P], the grids, then hist
+  __shared__ int bc[2];
+  __shared__ uint32_t red_u[2][kRtnThreads / 64];
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
+  const int n = (int)a.n, g = (int)a.g, G = (int)a.G, P = (int)a.P;
+  const int lgP = 31 - __builtin_clz(P);
   const T* w = static_cast<const T*>(a.W) + r * a.n;
-  const int64_t total = a.G * a.P;
-  double* gsc = reinterpret_cast<double*>(keys + ((total + 3) & ~int64_t(3)));   // [G] scale
-  double* gzp = gsc + a.G;                                  // [G] zero point
+  const int total = G * P;
+  double* gsc = reinterpret_cast<double*>(keys + ((total + 3) & ~3));   // [G] scale
+  double* gzp = gsc + G;                                                 // [G] zero point
+  uint32_t* hist = reinterpret_cast<uint32_t*>(gzp + G);                 // [8][256], one group per row
+  const bool clipped = a.clip < 1.f;
   bool bad = false;
 
-  for (int64_t i = tid; i < total; i += kRtnThreads) {
-    const int64_t j = i / a.P, pos = i - j * a.P, c = j * a.g + pos;
-    float key = __builtin_huge_valf();
-    if (pos < a.g && c < a.n) {
+  // 1. order-preserving keys of |w| (sym) or w (asym); padding sorts last
+  uint32_t tmin = 0xffffffffu, tmax = 0u;
+  for (int i = tid; i < total; i += kRtnThreads) {
+    const int j = i >> lgP, pos = i & (P - 1), c = j * g + pos;
+    uint32_t key = 0xffffffffu;
+    if (pos < g && c < n) {
       const float x = rtn_f32<T>(w[c]);
       bad |= !isfinite(x);
-      key = a.sym ? fabsf(x) : x;
+      key = f2u(a.sym ? fabsf(x) : x);
+      tmin = min(tmin, key);
+      tmax = max(tmax, key);
     }
     keys[i] = key;
   }
   __syncthreads();
-  for (int64_t k = 2; k <= a.P; k <<= 1) {
-    for (int64_t j = k >> 1; j > 0; j >>= 1) {
-      for (int64_t i = tid; i < total; i += kRtnThreads) {
-        const int64_t ixj = i ^ j;
-        if (ixj > i) {
-          const bool up = ((i & (a.P - 1)) & k) == 0;
-          const float x = keys[i], y = keys[ixj];
-          if ((x > y) == up) {
-            keys[i] = y;
-            keys[ixj] = x;
+
+  if (G == 1) {
+    // 2a. one group per row: the extremes by a block reduction, or each
+    // needed order statistic by radix selection
+    const RtnRanks rk = rtn_ranks(n, a.sym, a.clip);
+    float lo0 = 0.f, lo1 = 0.f, hi0, hi1;   // values at ranks floor(p), floor(p)+1
+    if (!clipped) {
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) {
+        tmin = min(tmin, (uint32_t)__shfl_xor(tmin, d, 64));
+        tmax = max(tmax, (uint32_t)__shfl_xor(tmax, d, 64));
+      }
+      if ((tid & 63) == 0) { red_u[0][tid >> 6] = tmin; red_u[1][tid >> 6] = tmax; }
+      __syncthreads();
+      uint32_t mn = red_u[0][0], mx = red_u[1][0];
+      for (int wv = 1; wv < kRtnThreads / 64; ++wv) { mn = min(mn, red_u[0][wv]); mx = max(mx, red_u[1][wv]); }
+      lo0 = lo1 = u2f(mn);
+      hi0 = hi1 = u2f(mx);
+    } else {
+      if (!a.sym) {
+        const uint32_t u = block_select(keys, n, rk.r[0], hist, bc);
+        lo0 = u2f(u);
+        lo1 = rk.r[0] + 1 < n ? u2f(block_next(keys, n, rk.r[0], u, &red_u[0][0])) : lo0;
+      }
+      const uint32_t u = block_select(keys, n, rk.r[1], hist, bc);
+      hi0 = u2f(u);
+      hi1 = rk.r[1] + 1 < n ? u2f(block_next(keys, n, rk.r[1], u, &red_u[0][0])) : hi0;
+    }
+    if (tid == 0) {
+      // unclipped: the extremes themselves; clipped: interpolate unless the
+      // position is the last rank
+      const double lo = (!clipped || rk.r[0] >= n - 1) ? (double)lo0 : rtn_lerp(lo0, lo1, rk.p[0]);
+      const double hi = (!clipped || rk.r[1] >= n - 1) ? (double)hi0 : rtn_lerp(hi0, hi1, rk.p[1]);
+      double s_, z_;
+      rtn_grid(lo, hi, a.bits, a.sym, s_, z_);
+      gsc[0] = s_;
+      gzp[0] = z_;
+    }
+  } else {
+    // 2b. groups.  Up to 256 columns: one wave per group -- the extremes by
+    // a wave reduction, or the needed ranks by counting (rank of an element =
+    // keys below it, ties broken by position; every rank is held by exactly
+    // one element) and a wave max over the element holding each rank.
+    // Wider groups: bitonic sort of every P-segment, then one thread each.
+    const int lane = tid & 63, wave = tid >> 6;
+    if (P <= 256) {
+      for (int j = wave; j < G; j += kWaves) {
+        const int L = (n - j * g < g) ? n - j * g : g;
+        const uint32_t* seg = keys + j * P;
+        double lo, hi;
+        if (!clipped) {
+          uint32_t mn = 0xffffffffu, mx = 0u;
+          for (int i = lane; i < L; i += 64) { mn = min(mn, seg[i]); mx = max(mx, seg[i]); }
+          lo = (double)u2f(wave_min(mn));
+          hi = (double)u2f(wave_max(mx));
+        } else {
+          const RtnRanks rk = rtn_ranks(L, a.sym, a.clip);
+          uint32_t v0 = 0u, v1 = 0u, v2 = 0u, v3 = 0u;
+          if (!a.sym) wave_select2(seg, L, rk.r[0], v0, v1);
+          wave_select2(seg, L, rk.r[1], v2, v3);
+          lo = (rk.r[0] >= L - 1) ? (double)u2f(v0) : rtn_lerp(u2f(v0), u2f(v1), rk.p[0]);
+          hi = (rk.r[1] >= L - 1) ? (double)u2f(v2) : rtn_lerp(u2f(v2), u2f(v3), rk.p[1]);
+        }
+        if (lane == 0) {
+          double s_, z_;
+          rtn_grid(lo, hi, a.bits, a.sym, s_, z_);
+          gsc[j] = s_;
+          gzp[j] = z_;
+        }
+      }
+    } else {
+      if (clipped) {
+        for (int k = 2; k <= P; k <<= 1) {
+          for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < total; i += kRtnThreads) {
+              const int ixj = i ^ j;
+              if (ixj > i) {
+                const bool up = ((i & (P - 1)) & k) == 0;
+                const uint32_t x = keys[i], y = keys[ixj];
+                if ((x > y) == up) {
+                  keys[i] = y;
+                  keys[ixj] = x;
+                }
+              }
+            }
+            __syncthreads();
           }
         }
       }
-      __syncthreads();
+      for (int j = wave; j < G; j += kWaves) {
+        const int L = (n - j * g < g) ? n - j * g : g;
+        const uint32_t* seg = keys + j * P;
+        double lo, hi;
+        if (clipped) {
+          const RtnRanks rk = rtn_ranks(L, a.sym, a.clip);
+          lo = (rk.r[0] >= L - 1) ? (double)u2f(seg[L - 1]) : rtn_lerp(u2f(seg[rk.r[0]]), u2f(seg[rk.r[0] + 1]), rk.p[0]);
+          hi = (rk.r[1] >= L - 1) ? (double)u2f(seg[L - 1]) : rtn_lerp(u2f(seg[rk.r[1]]), u2f(seg[rk.r[1] + 1]), rk.p[1]);
+        } else {
+          uint32_t mn = 0xffffffffu, mx = 0u;
+          for (int i = lane; i < L; i += 64) { mn = min(mn, seg[i]); mx = max(mx, seg[i]); }
+          lo = (double)u2f(wave_min(mn));
+          hi = (double)u2f(wave_max(mx));
+        }
+        if (lane == 0) {
+          double s_, z_;
+          rtn_grid(lo, hi, a.bits, a.sym, s_, z_);
+          gsc[j] = s_;
+          gzp[j] = z_;
+        }
+      }
     }
-  }
-  for (int64_t j = tid; j < a.G; j += kRtnThreads) {
-    const int64_t L = (a.n - j * a.g < a.g) ? a.n - j * a.g : a.g;
-    double s, z;
-    rtn_grid(keys + j * a.P, L, a.bits, a.sym, a.clip, s, z);
-    gsc[j] = s;
-    gzp[j] = z;
   }
   __syncthreads();
 
+  // 3. codes, packing and the row's error sums.  The code is rint(x/s) or
+  // rint(x/s + z) of the fp64 quotient.  An fp32 quotient y (correctly
+  // rounded division by the fp32-rounded scale, then + z) is within
+  // 2e-7·(|x/s| + |y|) of it, so wherever y is farther than that from a
+  // half-integer both round the same way; only the rest is recomputed in fp64.
+  // The error sums keep Σd², Σx·d and Σx² (d = x - ŵ) in fp64; Σx·ŵ and Σŵ²
+  // follow from them.
   const int off = a.sym ? (1 << (a.bits - 1)) : 0;
-  const double qmin = a.sym ? -(double)(1 << (a.bits - 1)) : 0.0;
-  const double qmax = a.sym ? (double)((1 << (a.bits - 1)) - 1) : (double)((1 << a.bits) - 1);
-  double se = 0.0, dot = 0.0, ww = 0.0, dd = 0.0;
+  const float qminf = a.sym ? -(float)(1 << (a.bits - 1)) : 0.f;
+  const float qmaxf = a.sym ? (float)((1 << (a.bits - 1)) - 1) : (float)((1 << a.bits) - 1);
+  double se = 0.0, xd = 0.0, ww = 0.0;
   uint32_t* qrow = a.qweight + r * a.words;
-  for (int64_t c8 = tid; c8 * 8 < a.n; c8 += kRtnThreads) {
+  for (int c8 = tid; c8 * 8 < n; c8 += kRtnThreads) {
     uint32_t word0 = 0u, word1 = 0u;
+    int j = (c8 * 8) / g, jend = (j + 1) * g;
+    double s = gsc[j], z = gzp[j];
+    float sf = (float)s, zf = (float)z;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int64_t c = c8 * 8 + e;
-      if (c >= a.n) break;
-      const double x = (double)rtn_f32<T>(w[c]);
-      const int64_t j = c / a.g;
-      const double s = gsc[j], z = gzp[j];
-      double q = a.sym ? rint(x / s) : rint(x / s + z);
-      q = fmin(fmax(q, qmin), qmax);
+      const int c = c8 * 8 + e;
+      if (c >= n) break;
+      if (c >= jend) {
+        while (c >= jend) { ++j; jend += g; }
+        s = gsc[j];
+        z = gzp[j];
+        sf = (float)s;
+        zf = (float)z;
+      }
+      const float xf = rtn_f32<T>(w[c]);
+      const float qf = xf / sf;
+      const float y = a.sym ? qf : qf + zf;
+      const float half = floorf(y) + 0.5f;
+      const float tol = 2e-7f * (fabsf(qf) + fabsf(y)) + 1e-30f;
+      float q;
+      if (fabsf(y - half) > tol) {
+        q = rintf(y);
+      } else {
+        const double xq = (double)xf / s;
+        q = (float)(a.sym ? rint(xq) : rint(xq + z));
+      }
+      q = fminf(fmaxf(q, qminf), qmaxf);
       const uint32_t code = (uint32_t)((int)q + off);
-      const double dq = (q - z) * s;
-      const double d = x - dq;
+      const double x = (double)xf;
+      const double d = x - ((double)q - z) * s;
       se += d * d;
-      dot += x * dq;
+      xd += x * d;
       ww += x * x;
-      dd += dq * dq;
       if (a.bits <= 4) {
         word0 |= code << (4 * e);
       } else if (e < 4) {
@@ -176,7 +431,7 @@ __global__ __launch_bounds__(kRtnThreads) void rtn_row_kernel(RtnArgs a) {
       if (2 * c8 + 1 < a.words) qrow[2 * c8 + 1] = word1;
     }
   }
-  for (int64_t j = tid; j < a.G; j += kRtnThreads) {
+  for (int j = tid; j < G; j += kRtnThreads) {
     a.scales[r * a.G + j] = (float)gsc[j];
     a.zeros[r * a.G + j] = (int32_t)gzp[j] + off;
   }
@@ -184,19 +439,20 @@ __global__ __launch_bounds__(kRtnThreads) void rtn_row_kernel(RtnArgs a) {
 
   // row sums: wave butterflies, then the 8 waves in order
   __shared__ double red[4][kRtnThreads / 64];
-  double v[4] = {se, dot, ww, dd};
+  // Σx·ŵ = Σx² - Σx·d, Σŵ² = Σx² - 2Σx·d + Σd²
+  double v4[4] = {se, ww - xd, ww, ww - 2.0 * xd + se};
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v[q] += __shfl_xor(v[q], d, 64);
+    for (int d = 32; d >= 1; d >>= 1) v4[q] += __shfl_xor(v4[q], d, 64);
   if ((tid & 63) == 0)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) red[q][tid >> 6] = v[q];
+    for (int q = 0; q < 4; ++q) red[q][tid >> 6] = v4[q];
   __syncthreads();
   if (tid < 4) {
-    double s = 0.0;
-    for (int wv = 0; wv < kRtnThreads / 64; ++wv) s += red[tid][wv];
-    a.part[r * 4 + tid] = s;
+    double sum = 0.0;
+    for (int wv = 0; wv < kRtnThreads / 64; ++wv) sum += red[tid][wv];
+    a.part[r * 4 + tid] = sum;
   }
 }
 
@@ -234,6 +490,7 @@ RtnPlan plan_rtn(int64_t m, int64_t n, int32_t group_size) {
   p.P = 1;
   while (p.P < p.g) p.P <<= 1;
   p.lds_bytes = (size_t)((p.G * p.P + 3) & ~int64_t(3)) * sizeof(float) + (size_t)p.G * 2 * sizeof(double);
+  if (p.G == 1) p.lds_bytes += 8 * 256 * sizeof(uint32_t);   // radix-select histograms
   p.part_off = 0;
   p.flag_off = align256((size_t)std::max<int64_t>(m, 1) * 4 * sizeof(double));
   p.total = p.flag_off + 256;
