@@ -23,7 +23,7 @@ It is written step by step from these web pages (cited by title and section):
   [P1] "Qwen2.5模型GPTQ量化精度损失实测" (m.cn486.com): act-order reorders
        weights.
 
-Everything is float64.  Inputs arrive as the exact bytes the GPU consumed
+Everything else is float64.  Inputs arrive as the exact bytes the GPU consumed
 (bf16 / fp32, converted exactly to float64).
 
 Readings taken where the pages are silent, garbled or contradict each other
@@ -44,6 +44,11 @@ Readings taken where the pages are silent, garbled or contradict each other
   * rounding is round-half-to-even (numpy / torch round).  asym codes are
     rne(w/s + z) as [P4] §2.1 and §3.1 write it; sym codes are rne(w/s).
   * scale floor 1e-8 ([P4] §3.1).
+  * integers that floating point decides (each zero point, each code) are
+    decided on float32 operands with float32 operations, the precision the
+    pages' quantizers run in ([P4] §3.2 works on a .float() copy of W, [P5]
+    on an astype(np.float32) copy); the scales, compensated weights, errors,
+    factor and losses stay float64.
   * desc_act: stable sort of the diagonal of H, descending, ties to the lower
     original column index.
 """
@@ -156,6 +161,11 @@ def prepare(H, key, damp_percent, desc_act):
 # ---------------------------------------------------------------------------
 # The quantization grid  ([P4] §2.1, §3.1; [P5] quantization basics)
 # ---------------------------------------------------------------------------
+def _f32(x):
+    """x rounded to the nearest float32."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
 def group_params(v, bits, sym):
     """Per-row (scale, zero) of one group of current weights v [m, w].
 
@@ -163,6 +173,12 @@ def group_params(v, bits, sym):
           is the rounded position of 0 on that grid.
     sym:  scale = max|v| / (2^(b-1)-1); the zero is the storage offset 2^(b-1).
     Both scales are floored at 1e-8.
+
+    The scale is float64.  The zero point is an integer that floating point
+    decides, and it is decided in float32, the precision the pages'
+    quantizers run in ([P4] §3.2 quantizes a .float() copy of the weights,
+    [P5]'s GPTQ sketch an astype(np.float32) copy): rne of the float32
+    quotient of the float32 range end and the float32 scale.
     """
     v = np.asarray(v, dtype=np.float64)
     if sym:
@@ -173,17 +189,20 @@ def group_params(v, bits, sym):
         lo = np.minimum(np.min(v, axis=1), 0.0)
         hi = np.maximum(np.max(v, axis=1), 0.0)
         s = np.maximum((hi - lo) / (2 ** bits - 1), SCALE_FLOOR)
-        z = np.round(-lo / s)
+        z = np.rint(-_f32(lo) / _f32(s)).astype(np.float64)
     return s, z
 
 
 def quantize_values(w, s, z, bits, sym):
-    """Stored integer code of w on the grid (s, z); all arrays broadcast."""
-    w = np.asarray(w, dtype=np.float64)
+    """Stored integer code of w on the grid (s, z); all arrays broadcast.
+
+    The rounding is decided in float32 as in group_params: rne(fl(w/s))
+    (sym) or rne(fl(fl(w/s) + z)) (asym) on w and s rounded to float32."""
+    q = _f32(w) / _f32(s)
     if sym:
         qmax = 2 ** (bits - 1) - 1
-        return np.clip(np.round(w / s), -qmax, qmax) + z
-    return np.clip(np.round(w / s + z), 0, 2 ** bits - 1)
+        return np.clip(np.rint(q), -qmax, qmax).astype(np.float64) + z
+    return np.clip(np.rint(q + _f32(z)), 0, 2 ** bits - 1).astype(np.float64)
 
 
 def dequantize_values(q, s, z):

@@ -210,6 +210,40 @@ def test_quantize_stage_matches_oracle(pq, case):
     assert Q.min() >= (1 if sp.sym else 0) and Q.max() <= 2 ** sp.bits - 1
 
 
+@pytest.mark.parametrize("bits,group", [(2, -1), (3, -1), (4, -1), (8, -1), (4, 128), (8, 64)])
+def test_symmetric_range_zero_point_ties(pq, bits, group):
+    """Rows whose first group has max = -min put the zero point at exactly
+    (2^b - 1)/2 in exact arithmetic; the float32 quotient that decides it then
+    falls on either side of the tie.  Both sides decide in float32, so zeros
+    (and, given them, codes) must agree on every row."""
+    m, n = 96, 384
+    sp = spec(m=m, n=n, tokens=3000, bits=bits, group_size=group, desc_act=False, w_seed=4242)
+    cfg = _cfg(pq, sp)
+    W = workloads.gen_weight(sp, "cuda").float()
+    g0 = n if group == -1 else group
+    rows = torch.arange(m, device="cuda")
+    a = W[:, :g0].abs().amax(dim=1) * torch.linspace(1.05, 1.6, m, device="cuda")
+    j1 = (rows * 7) % g0
+    j2 = (rows * 7 + 1 + rows % (g0 - 1)) % g0
+    W[rows, j1] = a
+    W[rows, j2] = -a
+    W = W.to(torch.bfloat16)
+    Wb = W.float()
+    assert torch.equal(Wb[rows, j1], -Wb[rows, j2])
+    tiles = list(workloads.x_tiles(sp, "cuda"))
+    out = pq.quantize_layer(W, tiles, cfg, keep_hessian=True)
+    torch.cuda.synchronize()
+    perm = out["perm"].cpu().numpy().astype(np.int64)
+    ref = oracle.gptq_quantize(f64(W)[:, perm], f64(out["U"]), bits, group, False)
+    zr = out["zeros"].cpu().numpy()
+    assert np.array_equal(zr[:, 0], ref["zeros"][:, 0])
+    Q = unpack_u32(out["qweight"], n, bits)
+    agree, mx = assert_codes(Q, oracle.unpermute_codes(ref["codes"], perm))
+    half = (2 ** bits - 1) / 2
+    print(f"{bits}-bit g{group}: zero points {sorted(set(zr[:, 0].tolist()))} around {half}; codes agree {agree:.6f}")
+    assert set(zr[:, 0].tolist()) <= {int(np.floor(half)), int(np.ceil(half))}
+
+
 def test_end_to_end_tiny_layer_config(pq):
     """The 256 x 256 fp32 layer, 512 tokens, 4-bit asym g128, no act-order:
     both sides free-running from W and X."""
