@@ -9,7 +9,10 @@ tokens x 11008 bf16, 4-bit asym, group 128, desc_act.
 
 With the default workload it also times the 7B-shaped sweep (32 decoder
 layers x {q, k, v, o, gate, up, down}, at 4-bit g128 and at 3-bit g64; X and W
-regenerated per linear outside the timed calls) and reports its total seconds.
+regenerated per linear outside the timed calls) and reports its total seconds;
+then the same sweep as a model is quantized: one calibration input per
+(decoder layer, input) shared by the linears that read it (q/k/v, gate/up), its
+H and inverse factor computed once and reused for both settings.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-sweep]
@@ -94,6 +97,75 @@ class Layer:
     def stage_ms(self):
         self.ev[3].synchronize()
         return [self.ev[i].elapsed_time(self.ev[i + 1]) for i in range(3)]
+
+
+def run_sweep_shared(pq, torch, bits_groups, log_every=32):
+    """The 7B-shaped sweep with one calibration input per (decoder layer, input)
+    and both settings in one pass: per input, H = 2·XᵀX and U once, then every
+    linear reading that input quantized at every setting.  X and W are
+    generated outside the timed calls; returns total and per-stage seconds."""
+    import workloads
+    cfgs = [pq.QuantConfig(bits=b, group_size=g, sym=False, desc_act=True, damp_percent=0.01)
+            for b, g in bits_groups]
+    groups = workloads.sweep_shared_groups(*bits_groups[0])
+    bufs = {}
+
+    def buf(key, make):
+        if key not in bufs:
+            bufs[key] = make()
+        return bufs[key]
+
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    stage = [0.0, 0.0, 0.0]
+    total = gen_total = 0.0
+    linears = 0
+    for i, (xs, wspecs) in enumerate(groups):
+        tg = time.perf_counter()
+        n, T = xs.n, xs.tokens
+        for k in [k for k in bufs if k[0] == "X" and k[1] != n]:
+            del bufs[k]
+        X = workloads.gen_x(xs, "cuda", out=buf(("X", n), lambda: torch.empty(T, n, dtype=torch.bfloat16,
+                                                                              device="cuda")))
+        Ws = [workloads.gen_weight(w, "cuda") for w in wspecs]
+        H = buf(("H", n), lambda: torch.empty(n, n, dtype=torch.float32, device="cuda"))
+        key = buf(("key", n), lambda: torch.empty(n, dtype=torch.float64, device="cuda"))
+        perm = buf(("perm", n), lambda: torch.empty(n, dtype=torch.int32, device="cuda"))
+        ws_h = buf(("wsh", n), lambda: torch.empty(max(pq.gptq_hessian_workspace_bytes(n, T, pq.GPTQ_BF16), 1), **u8))
+        ws_p = buf(("wsp", n), lambda: torch.empty(pq.gptq_prepare_workspace_bytes(n), **u8))
+        jobs = []
+        for W in Ws:
+            m = W.shape[0]
+            for j, cfg in enumerate(cfgs):
+                o = buf(("out", m, n, j), lambda: pq.alloc_outputs(m, n, cfg, "cuda"))
+                wq = buf(("wsq", m, n, j), lambda: torch.empty(pq.gptq_quantize_workspace_bytes(m, n, cfg), **u8))
+                jobs.append((W, cfg, o, wq))
+        torch.cuda.synchronize()
+        gen_total += time.perf_counter() - tg
+        t0 = time.perf_counter()
+        H.zero_()
+        key.zero_()
+        ev[0].record()
+        pq.gptq_hessian_accumulate(H, key, X, 2.0, ws_h)
+        ev[1].record()
+        pq.gptq_prepare_hinv(H, key, 0.01, True, perm, ws_p)
+        ev[2].record()
+        for W, cfg, o, wq in jobs:
+            pq.gptq_quantize_layer(W, H, perm, cfg, o["qweight"], o["scales"], o["zeros"], o["g_idx"],
+                                   o["loss"], wq)
+        ev[3].record()
+        torch.cuda.synchronize()
+        total += time.perf_counter() - t0
+        for s_ in range(3):
+            stage[s_] += ev[s_].elapsed_time(ev[s_ + 1]) / 1e3
+        linears += len(Ws)
+        del Ws
+        if (i + 1) % log_every == 0:
+            log(f"sweep (shared inputs): {i + 1}/{len(groups)} inputs, {total:.2f}s so far")
+    names = "+".join(f"{b}bit_g{g}" for b, g in bits_groups)
+    return {"settings": names, "total_s": total, "inputs": len(groups), "linears": linears,
+            "quantizations": linears * len(cfgs), "data_gen_s": gen_total,
+            "stage_s": {"hessian": stage[0], "prepare": stage[1], "quantize": stage[2]}}
 
 
 def cpu_baseline(spec, W, X, log_prefix="cpu_baseline"):
@@ -301,6 +373,8 @@ def main():
         torch.cuda.empty_cache()
         log("bench: 7B-shaped sweep")
         result["sweep"] = run_sweep(pq, torch, workloads.SWEEP_SETTINGS)
+        log("bench: 7B-shaped sweep, one input per (decoder layer, input), both settings")
+        result["next_rows"]["sweep_shared_inputs"] = run_sweep_shared(pq, torch, workloads.SWEEP_SETTINGS)
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle on a bounded sample)")
         result["cpu_baseline"] = cpu_baseline(spec, W, X)

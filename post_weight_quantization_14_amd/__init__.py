@@ -20,5 +20,6 @@ from .gptq import (  # noqa: F401
     gptq_rtn_quantize,
     gptq_rtn_workspace_bytes,
     quantize_layer,
+    quantize_shared_input,
     rtn_quantize,
 )

@@ -228,3 +228,43 @@ def quantize_layer(W: torch.Tensor, x_tiles, cfg: QuantConfig, alpha: float = 2.
     gptq_quantize_layer(W, H, out["perm"], cfg, out["qweight"], out["scales"], out["zeros"],
                         out["g_idx"], out["loss"])
     return out
+
+
+def quantize_shared_input(Ws, x_tiles, cfgs, alpha: float = 2.0) -> list:
+    """Linears that read the same input (q/k/v of one attention block, gate/up
+    of one MLP) have one Hessian H = 2·XᵀX, and the inverse factor U and the
+    column order depend only on H, the damping and act-order: accumulate H and
+    prepare U once, then quantize every W under every config (for instance
+    two bit widths).  All configs must share damp_percent and desc_act.
+
+    Returns out[i][j] for W i under config j (the alloc_outputs dict), each
+    identical to what quantize_layer gives for that W, X and config."""
+    cfgs = list(cfgs)
+    Ws = list(Ws)
+    if not Ws or not cfgs:
+        raise ValueError("need at least one weight and one config")
+    n = Ws[0].shape[1]
+    if any(W.dim() != 2 or W.shape[1] != n for W in Ws):
+        raise ValueError("every W must be [m_i, n] with the same n")
+    if any(c.damp_percent != cfgs[0].damp_percent or bool(c.desc_act) != bool(cfgs[0].desc_act)
+           for c in cfgs):
+        raise ValueError("configs sharing one U must agree on damp_percent and desc_act")
+    dev = Ws[0].device
+    H = torch.zeros(n, n, dtype=torch.float32, device=dev)
+    key = torch.zeros(n, dtype=torch.float64, device=dev)
+    for X in x_tiles:
+        gptq_hessian_accumulate(H, key, X, alpha)
+    perm = torch.empty(n, dtype=torch.int32, device=dev)
+    lam = gptq_prepare_hinv(H, key, cfgs[0].damp_percent, cfgs[0].desc_act, perm)
+    res = []
+    for W in Ws:
+        row = []
+        for cfg in cfgs:
+            o = alloc_outputs(W.shape[0], n, cfg, dev)
+            o["perm"].copy_(perm)
+            gptq_quantize_layer(W, H, perm, cfg, o["qweight"], o["scales"], o["zeros"], o["g_idx"],
+                                o["loss"])
+            o["lam"] = lam
+            row.append(o)
+        res.append(row)
+    return res

@@ -1,0 +1,125 @@
+"""Linears that read one calibration input share one H, one inverse factor U
+and one column order: quantize_shared_input accumulates H and prepares U once
+and quantizes every weight at every setting.
+
+Small sizes: every (weight, setting) bit for bit against the per-linear path
+(quantize_layer on the same W and X); its column order and damping against the
+oracle's, computed from its own float64 H of the same X bytes; its codes,
+scales, zeros, g_idx and losses against the oracle's quantizer run on the
+GPU's factor and that order.  Full size
+(q/k/v of a 7B attention block, 4096 x 4096 over 262144 tokens): bit for bit
+against the per-linear path, which the full-size parity tests pin to the
+oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import LOSS_REL, SCALE_REL, assert_codes, f64, spec, unpack_u32
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("qweight", "scales", "zeros", "g_idx", "loss", "perm")
+
+
+@pytest.fixture(scope="module")
+def pq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import post_weight_quantization_14_amd as pq
+    pq.lib()
+    return pq
+
+
+def _cfgs(pq, settings, sym=False, desc_act=True):
+    return [pq.QuantConfig(bits=b, group_size=g, sym=sym, desc_act=desc_act, damp_percent=0.01)
+            for b, g in settings]
+
+
+def _assert_same(a, b, what):
+    for k in KEYS:
+        assert torch.equal(a[k], b[k]), f"{what}: {k} differs from the per-linear path"
+
+
+SMALL = [
+    # (rows of each weight, n, tokens, settings, sym, desc_act)
+    ((40, 96, 33), 384, 3000, ((4, 128), (3, 64), (8, -1)), False, True),
+    ((64, 17), 1100, 4400, ((4, 128), (2, 32)), False, True),
+    ((24, 50), 301, 2400, ((4, 32), (3, 16)), True, False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"m{'-'.join(map(str, c[0]))}_n{c[1]}")
+def test_shared_input_matches_oracle_and_per_linear_path(pq, case):
+    ms, n, tokens, settings, sym, desc_act = case
+    xs = spec(m=ms[0], n=n, tokens=tokens, sym=sym, desc_act=desc_act)
+    X = workloads.gen_x(xs, "cuda")
+    Ws = [workloads.gen_weight(xs.with_(m=m, w_seed=xs.w_seed + 31 * i), "cuda")
+          for i, m in enumerate(ms)]
+    cfgs = _cfgs(pq, settings, sym, desc_act)
+    res = pq.quantize_shared_input(Ws, [X], cfgs)
+    torch.cuda.synchronize()
+    H_ref, key_ref = oracle.hessian([f64(X)], n)
+    _, perm_ref, lam_ref = oracle.prepare(H_ref, key_ref, 0.01, desc_act)
+    U = None
+    for i, W in enumerate(Ws):
+        for j, cfg in enumerate(cfgs):
+            out = res[i][j]
+            single = pq.quantize_layer(W, [X], cfg)
+            _assert_same(out, single, f"W{i} setting {j}")
+            assert out["perm"].cpu().numpy().tolist() == perm_ref.tolist()
+            assert out["lam"] == pytest.approx(lam_ref, rel=1e-9)
+            if U is None:
+                U = f64(single["U"])
+            # the oracle's quantizer on the GPU's factor and order
+            ref = oracle.gptq_layer(f64(W), None, None, cfg.bits, cfg.group_size, sym, desc_act, 0.01,
+                                    U=U, perm=perm_ref)
+            Q = unpack_u32(out["qweight"], n, cfg.bits)
+            agree, mx = assert_codes(Q, ref["codes"], f"W{i} setting {j}")
+            clean = np.all(Q == ref["codes"], axis=1)
+            np.testing.assert_allclose(out["scales"].cpu().numpy()[clean], ref["scales"][clean],
+                                       rtol=SCALE_REL)
+            assert np.array_equal(out["zeros"].cpu().numpy()[clean], ref["zeros"][clean])
+            assert out["g_idx"].cpu().numpy().tolist() == ref["g_idx"].tolist()
+            loss = out["loss"].cpu().numpy()
+            print(f"W{i} ({W.shape[0]}x{n}) {cfg.bits}-bit g{cfg.group_size}: codes agree {agree:.6f}; "
+                  f"loss0 {loss[0]:.6e} vs {ref['loss0']:.6e}")
+            assert loss[0] == pytest.approx(ref["loss0"], rel=LOSS_REL)
+            assert loss[1] == pytest.approx(ref["loss1"], rel=LOSS_REL)
+
+
+def test_shared_input_full_size_qkv_matches_per_linear_path(pq):
+    """q, k, v of one 7B-shaped decoder layer on its attention input (262144
+    tokens), at 4-bit g128 and 3-bit g64: every output identical to the
+    per-linear path on the same bytes."""
+    layer = 5
+    groups = workloads.sweep_shared_groups(4, 128, layers=layer + 1)
+    xs, wspecs = groups[4 * layer]
+    assert [w.name[-1] for w in wspecs] == ["q", "k", "v"]
+    X = workloads.gen_x(xs, "cuda")
+    Ws = [workloads.gen_weight(w, "cuda") for w in wspecs]
+    cfgs = _cfgs(pq, workloads.SWEEP_SETTINGS)
+    res = pq.quantize_shared_input(Ws, [X], cfgs)
+    torch.cuda.synchronize()
+    for i in (0, 2):            # q (its own X in the per-linear sweep too) and v
+        for j, cfg in enumerate(cfgs):
+            single = pq.quantize_layer(Ws[i], [X], cfg)
+            _assert_same(res[i][j], single, f"{wspecs[i].name} setting {j}")
+            del single
+    codes = unpack_u32(res[1][1]["qweight"], xs.n, 3)
+    assert codes.min() >= 0 and codes.max() <= 7
+
+
+def test_shared_input_rejects_configs_that_need_different_factors(pq):
+    W = torch.zeros(8, 64, dtype=torch.bfloat16, device="cuda")
+    X = torch.zeros(16, 64, dtype=torch.bfloat16, device="cuda")
+    bad = [pq.QuantConfig(damp_percent=0.01), pq.QuantConfig(damp_percent=0.02)]
+    with pytest.raises(ValueError):
+        pq.quantize_shared_input([W], [X], bad)
+    bad = [pq.QuantConfig(desc_act=True), pq.QuantConfig(desc_act=False)]
+    with pytest.raises(ValueError):
+        pq.quantize_shared_input([W], [X], bad)
+    with pytest.raises(ValueError):
+        pq.quantize_shared_input([W, torch.zeros(8, 32, dtype=torch.bfloat16, device="cuda")], [X],
+                                 [pq.QuantConfig()])
