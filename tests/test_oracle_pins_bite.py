@@ -214,3 +214,71 @@ def test_linear_pins_catch(monkeypatch, target, wrong):
 
 
 import oracle as oracle_pkg  # noqa: E402
+
+
+# ---------------------------------------------------------------------------
+# The quantized-weight product's pins bite too
+# ---------------------------------------------------------------------------
+from oracle import dequant_matmul as dm  # noqa: E402
+import test_oracle_dequant_pins as dp  # noqa: E402
+
+
+def _dequant_pins_pass():
+    checks = [dp.test_hand_case, dp.test_codes_at_the_zero_point_give_zero]
+    checks += [lambda b=b: dp.test_brute_force_from_packed_words(b) for b in (2, 3, 4, 8)]
+    checks += [lambda a=a: dp.test_product_error_is_the_quantizers_loss(*a)
+               for a in ((4, 4, False), (3, 8, False), (2, 4, True), (8, -1, False))]
+    for check in checks:
+        try:
+            check()
+        except (AssertionError, ValueError, IndexError):
+            return False
+    return True
+
+
+_dm_orig = {"dequantized_weight": dm.dequantized_weight, "unpack_codes": dm.unpack_codes}
+
+
+def _contiguous_groups(qweight, scales, zeros, g_idx, n, bits):
+    g = max(1, -(-n // np.asarray(scales).shape[1]))
+    return _dm_orig["dequantized_weight"](qweight, scales, zeros, np.arange(n) // g, n, bits)
+
+
+def _zero_sign(qweight, scales, zeros, g_idx, n, bits):
+    Q = dm.unpack_codes(np.asarray(qweight).view(np.uint32), n, bits).astype(np.float64)
+    gi = np.asarray(g_idx, dtype=np.int64)
+    return (np.asarray(zeros, dtype=np.float64)[:, gi] - Q) * np.asarray(scales, dtype=np.float64)[:, gi]
+
+
+def _reversed_nibbles(qweight, n, bits):
+    Q = _dm_orig["unpack_codes"](qweight, n, bits)
+    per = 8 if bits <= 4 else 4
+    out = Q.copy()
+    for w0 in range(0, n - n % per, per):
+        out[:, w0:w0 + per] = Q[:, w0:w0 + per][:, ::-1]
+    return out
+
+
+def _scale_by_row_group(qweight, scales, zeros, g_idx, n, bits):
+    Q = dm.unpack_codes(np.asarray(qweight).view(np.uint32), n, bits).astype(np.float64)
+    gi = np.asarray(g_idx, dtype=np.int64)
+    s = np.asarray(scales, dtype=np.float64)
+    return (Q - np.asarray(zeros, dtype=np.float64)[:, gi]) * s[:, :1]   # first group's scale
+
+
+DM_PLANTS = [
+    ("dequantized_weight", _contiguous_groups),
+    ("dequantized_weight", _zero_sign),
+    ("unpack_codes", _reversed_nibbles),
+    ("dequantized_weight", _scale_by_row_group),
+]
+
+
+def test_unplanted_dequant_oracle_passes():
+    assert _dequant_pins_pass()
+
+
+@pytest.mark.parametrize("name,fn", DM_PLANTS, ids=[f"{n}:{f.__name__}" for n, f in DM_PLANTS])
+def test_planted_dequant_mistake_is_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(dm, name, fn)
+    assert not _dequant_pins_pass()
