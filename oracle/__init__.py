@@ -36,7 +36,7 @@ from .linear_quantizer import (  # noqa: F401,E402
     linear_quantize,
     percentile_linear,
 )
-from .dequant_matmul import (  # noqa: F401,E402
+from .quantized_matmul import (  # noqa: F401,E402
     dequant_matmul,
     dequantized_weight,
 )

@@ -1,4 +1,4 @@
-"""Pins of the quantized-weight matrix product oracle (oracle/dequant_matmul.py),
+"""Pins of the quantized-weight matrix product oracle (oracle/quantized_matmul.py),
 CPU only: a hand-worked case, the exact link to the quantizer's own loss, a
 brute-force product that reads the packed words bit by bit, and zero codes."""
 import json
@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import dequant_matmul as dm
+from oracle import quantized_matmul as dm
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 

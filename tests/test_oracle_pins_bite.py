@@ -219,7 +219,7 @@ import oracle as oracle_pkg  # noqa: E402
 # ---------------------------------------------------------------------------
 # The quantized-weight product's pins bite too
 # ---------------------------------------------------------------------------
-from oracle import dequant_matmul as dm  # noqa: E402
+from oracle import quantized_matmul as dm  # noqa: E402
 import test_oracle_dequant_pins as dp  # noqa: E402
 
 
