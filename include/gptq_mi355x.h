@@ -202,6 +202,43 @@ gptq_status gptq_rtn_quantize(const void* W, int32_t w_dtype, int64_t m, int64_t
                               int32_t* zeros, double* err, void* workspace, size_t ws_bytes,
                               void* stream);
 
+/* ------------------------------------------------------------------------
+ * Product of bf16 activations with the quantized weights (W4A16)
+ *
+ * Page "模型量化实战：从 INT8 PTQ 到 GPTQ 的精度保持与推理加速全解析" §4.3:
+ * 4-bit weights have no native matrix product; they are dequantized to a
+ * 16-bit type (§2.1: x̂ = (q - z)·s) and multiplied, and the gain is the 4x
+ * smaller weight stream.  Y[t][r] = Σ_k X[t][k]·(q[r][k] - z[r][g_idx[k]])·
+ * s[r][g_idx[k]] with bf16 X, fp32 Y.  The codes enter the bf16 products
+ * exactly (as 128 + q) and each group's scale is applied to its fp32 partial
+ * sum, so the only roundings are those of the fp32 sums.
+ *
+ * gptq_w4a16_pack converts gptq_quantize_layer's output (qweight, scales,
+ * zeros, g_idx of an m x n weight, bits 2, 3 or 4, group_size 32, 64, 128 or
+ * -1) once into the product's layout, `packed` (device memory of at least
+ * gptq_w4a16_packed_bytes(m, n, group_size) bytes, 256-byte aligned, owned by
+ * the caller, read-only afterwards): the column order is derived from g_idx
+ * (group p's columns in ascending order), so act-order weights need no
+ * separate permutation.  Synchronises `stream` once and returns
+ * GPTQ_ERR_INVALID_ARG if g_idx does not assign exactly min(g, n - p·g)
+ * columns to every group p (exactly n to group 0 when group_size = -1).
+ *
+ * gptq_w4a16_matmul computes Y = X·Ŵᵀ for X bf16 [tokens][ldx] (unit column
+ * stride, ldx >= n), Y fp32 [tokens][ldy] (ldy >= m), with workspace of at
+ * least gptq_w4a16_workspace_bytes(tokens, m, n) bytes (256-byte aligned).
+ * Stream-ordered, no synchronisation; tokens are processed 64 per launch
+ * sequence (gather, product, reduce); the summation order is fixed, so the
+ * result is reproducible bit for bit.  tokens == 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+size_t gptq_w4a16_packed_bytes(int64_t m, int64_t n, int32_t group_size);
+gptq_status gptq_w4a16_pack(const uint32_t* qweight, const float* scales, const int32_t* zeros,
+                            const int32_t* g_idx, int64_t m, int64_t n, int32_t bits,
+                            int32_t group_size, void* packed, size_t packed_bytes, void* stream);
+size_t gptq_w4a16_workspace_bytes(int64_t tokens, int64_t m, int64_t n);
+gptq_status gptq_w4a16_matmul(const void* X, int64_t tokens, int64_t ldx, const void* packed,
+                              int64_t m, int64_t n, int32_t group_size, float* Y, int64_t ldy,
+                              void* workspace, size_t ws_bytes, void* stream);
+
 /* Sizes of the outputs above (host-only helpers, no GPU work). */
 int64_t gptq_qweight_words(int64_t n, int32_t bits);
 int64_t gptq_num_groups(int64_t n, int32_t group_size);

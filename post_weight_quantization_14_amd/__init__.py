@@ -19,6 +19,10 @@ from .gptq import (  # noqa: F401
     gptq_qweight_words,
     gptq_rtn_quantize,
     gptq_rtn_workspace_bytes,
+    gptq_w4a16_matmul,
+    gptq_w4a16_pack,
+    gptq_w4a16_packed_bytes,
+    gptq_w4a16_workspace_bytes,
     quantize_layer,
     quantize_shared_input,
     rtn_quantize,

@@ -55,6 +55,10 @@ SIGNATURES = {
     "gptq_rtn_workspace_bytes": (_SZ, [_I64, _I64, ctypes.POINTER(GptqRtnConfig)]),
     "gptq_rtn_quantize": (_ST, [_P, _I32, _I64, _I64, ctypes.POINTER(GptqRtnConfig), _P, _P, _P, _P,
                                 _P, _SZ, _P]),
+    "gptq_w4a16_packed_bytes": (_SZ, [_I64, _I64, _I32]),
+    "gptq_w4a16_pack": (_ST, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _SZ, _P]),
+    "gptq_w4a16_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "gptq_w4a16_matmul": (_ST, [_P, _I64, _I64, _P, _I64, _I64, _I32, _P, _I64, _P, _SZ, _P]),
     "gptq_qweight_words": (_I64, [_I64, _I32]),
     "gptq_num_groups": (_I64, [_I64, _I32]),
     "gptq_last_error": (ctypes.c_char_p, []),

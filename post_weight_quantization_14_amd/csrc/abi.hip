@@ -240,4 +240,62 @@ gptq_status gptq_rtn_quantize(const void* W, int32_t w_dtype, int64_t m, int64_t
                  workspace, plan, static_cast<hipStream_t>(stream));
 }
 
+static bool w4_group_ok(int32_t g) { return g == -1 || g == 32 || g == 64 || g == 128; }
+
+size_t gptq_w4a16_packed_bytes(int64_t m, int64_t n, int32_t group_size) {
+  if (m < 0 || n < 0 || !w4_group_ok(group_size)) return 0;
+  return plan_w4a16(m, n, group_size).total;
+}
+
+gptq_status gptq_w4a16_pack(const uint32_t* qweight, const float* scales, const int32_t* zeros,
+                            const int32_t* g_idx, int64_t m, int64_t n, int32_t bits,
+                            int32_t group_size, void* packed, size_t packed_bytes, void* stream) {
+  clear_error();
+  if (m < 0 || n < 0) return fail(GPTQ_ERR_INVALID_ARG, "m=%lld n=%lld", (long long)m, (long long)n);
+  if (bits != 2 && bits != 3 && bits != 4)
+    return fail(GPTQ_ERR_UNSUPPORTED, "bits=%d (the W4A16 product takes 2-, 3- and 4-bit codes)", bits);
+  if (!w4_group_ok(group_size))
+    return fail(GPTQ_ERR_UNSUPPORTED, "group_size=%d (32, 64, 128 or -1)", group_size);
+  if (m == 0 || n == 0) return GPTQ_OK;
+  if (m > ((int64_t)1 << 30) || n > ((int64_t)1 << 30))
+    return fail(GPTQ_ERR_UNSUPPORTED, "m=%lld n=%lld too large", (long long)m, (long long)n);
+  if (bad_ptr(qweight, 4) || bad_ptr(scales, 4) || bad_ptr(zeros, 4) || bad_ptr(g_idx, 4))
+    return fail(GPTQ_ERR_INVALID_ARG, "an input pointer is NULL or misaligned");
+  const W4Layout L = plan_w4a16(m, n, group_size);
+  if (packed == nullptr || packed_bytes < L.total || bad_ptr(packed, 256))
+    return fail(GPTQ_ERR_WORKSPACE, "packed buffer %zu bytes, need %zu (256-byte aligned)",
+                packed_bytes, L.total);
+  return run_w4a16_pack(qweight, scales, zeros, g_idx, bits, L, packed,
+                        static_cast<hipStream_t>(stream));
+}
+
+size_t gptq_w4a16_workspace_bytes(int64_t tokens, int64_t m, int64_t n) {
+  if (tokens < 0 || m < 0 || n < 0) return 0;
+  return plan_w4a16_gemm(tokens, m, n).total;
+}
+
+gptq_status gptq_w4a16_matmul(const void* X, int64_t tokens, int64_t ldx, const void* packed,
+                              int64_t m, int64_t n, int32_t group_size, float* Y, int64_t ldy,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (tokens < 0 || m < 0 || n < 0)
+    return fail(GPTQ_ERR_INVALID_ARG, "tokens=%lld m=%lld n=%lld", (long long)tokens, (long long)m,
+                (long long)n);
+  if (!w4_group_ok(group_size))
+    return fail(GPTQ_ERR_UNSUPPORTED, "group_size=%d (32, 64, 128 or -1)", group_size);
+  if (tokens == 0 || m == 0 || n == 0) return GPTQ_OK;
+  if (m > ((int64_t)1 << 30) || n > ((int64_t)1 << 30))
+    return fail(GPTQ_ERR_UNSUPPORTED, "m=%lld n=%lld too large", (long long)m, (long long)n);
+  if (ldx < n || ldy < m)
+    return fail(GPTQ_ERR_INVALID_ARG, "ldx=%lld < n or ldy=%lld < m", (long long)ldx, (long long)ldy);
+  if (bad_ptr(X, 2) || bad_ptr(Y, 4)) return fail(GPTQ_ERR_INVALID_ARG, "X or Y is NULL or misaligned");
+  if (bad_ptr(packed, 256)) return fail(GPTQ_ERR_INVALID_ARG, "packed is NULL or not 256-byte aligned");
+  const W4GemmPlan p = plan_w4a16_gemm(tokens, m, n);
+  if (workspace == nullptr || ws_bytes < p.total || bad_ptr(workspace, 256))
+    return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu (256-byte aligned)", ws_bytes, p.total);
+  return run_w4a16_matmul(static_cast<const uint16_t*>(X), tokens, ldx, packed,
+                          plan_w4a16(m, n, group_size), Y, ldy, workspace, p,
+                          static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

@@ -128,6 +128,24 @@ gptq_status run_rtn(const void* W, int w_dtype, int64_t m, int64_t n, int bits, 
                     uint32_t* qweight, float* scales, int32_t* zeros, double* err, void* ws,
                     const RtnPlan& plan, hipStream_t stream);
 
+// ---------------------------------------------------------------- W4A16 product
+struct W4Layout {
+  int64_t m = 0, n = 0, mt = 0, kc = 0, n128 = 0, g = 0, G = 0, Gp = 0;
+  size_t flag_off = 0, order_off = 0, param_off = 0, code_off = 0, total = 0;
+};
+W4Layout plan_w4a16(int64_t m, int64_t n, int32_t group_size);
+struct W4GemmPlan {
+  int64_t chunk_tokens = 0, mp = 0, chunks = 0, splits = 0;
+  size_t xp_off = 0, xs_off = 0, part_off = 0, total = 0;
+};
+W4GemmPlan plan_w4a16_gemm(int64_t tokens, int64_t m, int64_t n);
+gptq_status run_w4a16_pack(const uint32_t* qweight, const float* scales, const int32_t* zeros,
+                           const int32_t* g_idx, int bits, const W4Layout& L, void* packed,
+                           hipStream_t stream);
+gptq_status run_w4a16_matmul(const uint16_t* X, int64_t tokens, int64_t ldx, const void* packed,
+                             const W4Layout& L, float* Y, int64_t ldy, void* ws,
+                             const W4GemmPlan& p, hipStream_t stream);
+
 // ---------------------------------------------------------------- fp32 MFMA GEMM (shared)
 // C[M,N] = alpha * A[M,K] * B[K,N] + beta * C, A row-major; B row-major or, with
 // b_colmajor, stored as B[k][j] = Bp[j * ldb + k].  Tiles of 128 x 128.

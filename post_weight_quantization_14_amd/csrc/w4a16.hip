@@ -1,0 +1,415 @@
+// Product of bf16 activations with the quantizer's low-bit weights (W4A16).
+//
+// The page "模型量化实战：从 INT8 PTQ 到 GPTQ…" §4.3 notes that 4-bit weights
+// have no native matrix product: they are dequantized to a 16-bit type and
+// multiplied, and the gain is the 4x smaller weight stream.  §2.1 gives the
+// dequantization x̂ = (q - z)·s.  Here the 16-bit type is bf16 and the scale
+// is applied per group after the product, which keeps every weight exact:
+//   Y[t][r] = Σ_g s_g · ( Σ_{k∈g} x_k·(128 + q_k) - (128 + z_g)·Σ_{k∈g} x_k ).
+// 128 + q (q < 16) is exactly the bf16 with bits 0x4300 | q, so a 4-bit code
+// becomes an MFMA operand with one AND-OR: bf16 × bf16 products are exact in
+// the fp32 accumulator, and only the group sums round.
+//
+// Packed weight (gptq_w4a16_pack, once per weight):
+//   order  int32 [n128]            processing position -> input column (-1: pad);
+//                                  groups contiguous, derived from g_idx
+//   params float2 [mt][Gp][16]     (s, 128 + z) per row and group
+//   codes  u32x4 [mt][kc][64]      the B operand of v_mfma_f32_16x16x32_bf16 in
+//                                  lane order: lane l, word j of 128-chunk C of
+//                                  row tile T holds the 8 codes of row 16T + l%16,
+//                                  positions 128C + 32j + 8(l/16) + e, e = 0..7,
+//                                  e in nibble (e%2)·4 + e/2, so that
+//                                  ((w >> 4v) & 0x000F000F) | 0x43004300 is the
+//                                  bf16 pair (e = 2v, 2v + 1)
+// with mt = ceil(m/16), kc = ceil(n/128), n128 = 128·kc, Gp = ceil(n128/g).
+//
+// Product (gptq_w4a16_matmul), per call of up to 64 tokens:
+//   gather : X' [Mp][n128] bf16 in processing order and its 32-position sums
+//   gemm   : split-K over 128-chunks; a workgroup of 4 waves holds 8 row tiles
+//            (128 rows) x one slice; each wave streams its codes straight from
+//            HBM into registers (16 B per lane per chunk), the slice of X' and
+//            the slice's scales sit in LDS; per group the accumulator is
+//            scaled and folded into the result
+//   reduce : Y = Σ over slices in slice order (deterministic)
+#include <algorithm>
+
+#include "gptq_internal.hpp"
+
+namespace gptq {
+namespace {
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kW4Rows = 16;          // rows per tile (MFMA N)
+constexpr int kW4Chunk = 128;        // positions per chunk (4 MFMA k-steps of 32)
+constexpr int kW4TilesPerWave = 2;
+constexpr int kW4Waves = 4;
+constexpr int kW4TilesPerWg = kW4TilesPerWave * kW4Waves;
+constexpr int kW4MaxChunks = 4;      // chunks per slice
+constexpr int kW4MaxGroups = kW4MaxChunks * 4 + 1;   // groups one slice can touch (g >= 32)
+constexpr int kW4TokTile = 16;
+constexpr int kW4MaxTokTiles = 4;    // tokens per launch <= 64
+constexpr int kW4Pad = 8;            // bf16 padding per LDS row of X'
+
+// ---------------------------------------------------------------- pack
+// One workgroup per group slot: the columns with g_idx == grp, ascending, go
+// to positions grp·g ...; a count other than the group's size flags the call.
+__global__ __launch_bounds__(256) void w4_order_kernel(const int32_t* __restrict__ g_idx, int64_t n,
+                                                       int64_t g, int64_t G, int64_t n128,
+                                                       int32_t* __restrict__ order, int* flag) {
+  __shared__ int wcnt[4];
+  const int64_t grp = blockIdx.x;
+  const int64_t base = grp * g;
+  const int64_t want = grp < G ? std::min<int64_t>(g, n - base) : 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t cnt = 0;
+  for (int64_t c0 = 0; c0 < n; c0 += 256) {
+    const int64_t j = c0 + threadIdx.x;
+    const bool hit = j < n && (int64_t)g_idx[j] == grp;
+    const uint64_t b = __ballot(hit);
+    const int before = __popcll(b & ((1ull << lane) - 1ull));
+    if (lane == 0) wcnt[wave] = __popcll(b);
+    __syncthreads();
+    int off = 0, tot = 0;
+    for (int w = 0; w < 4; ++w) {
+      off += w < wave ? wcnt[w] : 0;
+      tot += wcnt[w];
+    }
+    if (hit) {
+      const int64_t pos = cnt + off + before;
+      if (pos < want) order[base + pos] = (int32_t)j;
+    }
+    cnt += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0 && cnt != want) atomicOr(flag, 1);
+  const int64_t end = std::min<int64_t>(base + g, n128);
+  for (int64_t p = base + std::min<int64_t>(cnt, want) + threadIdx.x; p < end; p += 256)
+    order[p] = -1;
+}
+
+__global__ __launch_bounds__(256) void w4_params_kernel(const float* __restrict__ scales,
+                                                        const int32_t* __restrict__ zeros, int64_t m,
+                                                        int64_t G, int64_t mt, int64_t Gp,
+                                                        float2* __restrict__ params) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= mt * Gp * kW4Rows) return;
+  const int64_t r = (i / (Gp * kW4Rows)) * kW4Rows + (i % kW4Rows);
+  const int64_t grp = (i / kW4Rows) % Gp;
+  float2 v = make_float2(0.f, 0.f);
+  if (r < m && grp < G) v = make_float2(scales[r * G + grp], 128.f + (float)zeros[r * G + grp]);
+  params[i] = v;
+}
+
+__global__ __launch_bounds__(256) void w4_codes_kernel(const uint32_t* __restrict__ qweight,
+                                                       int64_t words, int64_t m, int64_t n,
+                                                       int64_t kc, int64_t total,
+                                                       const int32_t* __restrict__ order,
+                                                       uint32_t* __restrict__ codes) {
+  const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (w >= total) return;
+  const int j = (int)(w & 3), l = (int)((w >> 2) & 63);
+  const int64_t tc = w >> 8;              // T·kc + C
+  const int64_t T = tc / kc, C = tc % kc;
+  const int64_t r = T * kW4Rows + (l & 15);
+  const int64_t kb = C * kW4Chunk + 32 * j + 8 * (l >> 4);
+  uint32_t word = 0;
+  if (r < m) {
+    for (int e = 0; e < 8; ++e) {
+      const int64_t p = kb + e;
+      if (p >= n) break;
+      const int32_t col = order[p];
+      if (col < 0) continue;
+      const uint32_t q = (qweight[r * words + (col >> 3)] >> (4 * (col & 7))) & 15u;
+      word |= q << (4 * ((e & 1) * 4 + (e >> 1)));
+    }
+  }
+  codes[w] = word;
+}
+
+// ---------------------------------------------------------------- product
+// X' = X[:, order] (rows >= tokens zero) and the sum of every 32 positions.
+// Thread: 4 consecutive positions; 8 threads make one 32-position sum.
+__global__ __launch_bounds__(256) void w4_gather_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                        int64_t tokens, const int32_t* __restrict__ order,
+                                                        int64_t n128, uint16_t* __restrict__ Xp,
+                                                        float* __restrict__ xs) {
+  const int64_t t = blockIdx.y;
+  const int64_t p0 = (int64_t)blockIdx.x * 1024 + 4 * threadIdx.x;
+  if (p0 >= n128) return;   // n128 is a multiple of 128: whole 8-thread groups leave together
+  uint16_t v[4] = {0, 0, 0, 0};
+  float s = 0.f;
+  if (t < tokens) {
+    const int4 o = *reinterpret_cast<const int4*>(order + p0);
+    const int oi[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (oi[e] >= 0) v[e] = X[t * ldx + oi[e]];
+      s += __builtin_bit_cast(float, (uint32_t)v[e] << 16);
+    }
+  }
+  uint2 pk;
+  pk.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
+  pk.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
+  *reinterpret_cast<uint2*>(Xp + t * n128 + p0) = pk;
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 4);
+  if ((threadIdx.x & 7) == 0) xs[t * (n128 / 32) + (p0 >> 5)] = s;
+}
+
+struct W4GemmArgs {
+  const uint16_t* Xp;      // [Mp][n128]
+  const float* xs;         // [Mp][n128 / 32]
+  const float2* params;    // [mt][Gp][16]
+  const u32x4_t* codes;    // [mt][kc][64]
+  float* part;             // [splits][tokens][m16]
+  int64_t tokens, m16, mt, kc, n128, Gp;
+  int gsteps;              // 32-position steps per group; 0 = one group
+  int chunks;              // 128-chunks per slice (<= kW4MaxChunks)
+};
+
+__device__ __forceinline__ bf16x8_t w4_unpack(uint32_t w) {
+  u32x4_t r;
+  r[0] = (w & 0x000F000Fu) | 0x43004300u;
+  r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+  r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+  r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+template <int TT>
+__global__ __launch_bounds__(256) void w4_gemm_kernel(W4GemmArgs a) {
+  constexpr int RS = kW4MaxChunks * kW4Chunk + kW4Pad;   // LDS row of X' (bf16)
+  constexpr int SS = kW4MaxChunks * 4;                   // 32-sums per LDS row
+  __shared__ __attribute__((aligned(16))) uint16_t xsh[TT * kW4TokTile * RS];
+  __shared__ float ssh[TT * kW4TokTile * SS];
+  __shared__ float2 psh[kW4TilesPerWg * kW4MaxGroups * kW4Rows];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t s = blockIdx.y;
+  const int64_t C0 = s * a.chunks;
+  const int nch = (int)std::min<int64_t>(a.chunks, a.kc - C0);
+  const int64_t T0 = (int64_t)blockIdx.x * kW4TilesPerWg;
+
+  // codes first: the HBM stream starts before anything else waits
+  u32x4_t cw[kW4TilesPerWave][kW4MaxChunks];
+#pragma unroll
+  for (int r = 0; r < kW4TilesPerWave; ++r) {
+    const int64_t T = T0 + wave * kW4TilesPerWave + r;
+#pragma unroll
+    for (int c = 0; c < kW4MaxChunks; ++c) {
+      cw[r][c] = u32x4_t{0u, 0u, 0u, 0u};
+      if (T < a.mt && c < nch) cw[r][c] = a.codes[(T * a.kc + C0 + c) * 64 + lane];
+    }
+  }
+
+  // slice of X' (16-byte pieces) and its 32-sums
+  const int pos = nch * kW4Chunk;                 // positions in this slice
+  const int vec_per_row = pos / 8;
+  for (int i = tid; i < TT * kW4TokTile * vec_per_row; i += 256) {
+    const int t = i / vec_per_row, v = i % vec_per_row;
+    const uint4 x = *reinterpret_cast<const uint4*>(a.Xp + (int64_t)t * a.n128 + C0 * kW4Chunk + 8 * v);
+    *reinterpret_cast<uint4*>(xsh + t * RS + 8 * v) = x;
+  }
+  const int steps = nch * 4;
+  for (int i = tid; i < TT * kW4TokTile * steps; i += 256) {
+    const int t = i / steps, j = i % steps;
+    ssh[t * SS + j] = a.xs[(int64_t)t * (a.n128 / 32) + C0 * 4 + j];
+  }
+  // the slice's (s, 128 + z) of the workgroup's tiles
+  const int64_t st0 = C0 * 4, st1 = st0 + steps;   // global 32-steps [st0, st1)
+  const int64_t g0 = a.gsteps > 0 ? st0 / a.gsteps : 0;
+  const int ng = a.gsteps > 0 ? (int)((st1 - 1) / a.gsteps - g0 + 1) : 1;
+  for (int i = tid; i < kW4TilesPerWg * ng * kW4Rows; i += 256) {
+    const int tl = i / (ng * kW4Rows), gi = (i / kW4Rows) % ng, rr = i % kW4Rows;
+    const int64_t T = T0 + tl;
+    psh[(tl * kW4MaxGroups + gi) * kW4Rows + rr] =
+        T < a.mt ? a.params[(T * a.Gp + g0 + gi) * kW4Rows + rr] : make_float2(0.f, 0.f);
+  }
+  __syncthreads();
+
+  const int row = lane & 15, quad = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < kW4TilesPerWave; ++r) {
+    const int tl = wave * kW4TilesPerWave + r;
+    const int64_t T = T0 + tl;
+    if (T >= a.mt) break;
+    f32x4_t acc[TT], y[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      y[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    int fs = 0;   // first local step of the open group
+#pragma unroll
+    for (int c = 0; c < kW4MaxChunks; ++c) {
+      if (c >= nch) break;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8_t b = w4_unpack(cw[r][c][j]);
+        const int ls = 4 * c + j;
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          const uint4 av = *reinterpret_cast<const uint4*>(
+              xsh + (tt * kW4TokTile + row) * RS + c * kW4Chunk + 32 * j + 8 * quad);
+          acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), b,
+                                                            acc[tt], 0, 0, 0);
+        }
+        const int64_t gs = st0 + ls;
+        const bool close = ls == steps - 1 || (a.gsteps > 0 && (gs + 1) % a.gsteps == 0);
+        if (close) {
+          const int gi = a.gsteps > 0 ? (int)(gs / a.gsteps - g0) : 0;
+          const float2 p = psh[(tl * kW4MaxGroups + gi) * kW4Rows + row];
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float* sp = ssh + (tt * kW4TokTile + 4 * quad + v) * SS;
+              float sx = 0.f;
+              for (int q = fs; q <= ls; ++q) sx += sp[q];
+              y[tt][v] = fmaf(p.x, fmaf(-p.y, sx, acc[tt][v]), y[tt][v]);
+            }
+            acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+          fs = ls + 1;
+        }
+      }
+    }
+    // D[4·quad + v][row]: token 16tt + 4·quad + v, weight row 16T + row
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t t = tt * kW4TokTile + 4 * quad + v;
+        if (t < a.tokens) a.part[(s * a.tokens + t) * a.m16 + T * kW4Rows + row] = y[tt][v];
+      }
+  }
+}
+
+__global__ __launch_bounds__(256) void w4_reduce_kernel(const float* __restrict__ part, int64_t splits,
+                                                        int64_t tokens, int64_t m16, int64_t m,
+                                                        float* __restrict__ Y, int64_t ldy) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t t = blockIdx.y;
+  if (r >= m) return;
+  float acc = 0.f;
+  for (int64_t s = 0; s < splits; ++s) acc += part[(s * tokens + t) * m16 + r];
+  Y[t * ldy + r] = acc;
+}
+
+}  // namespace
+
+W4Layout plan_w4a16(int64_t m, int64_t n, int32_t group_size) {
+  W4Layout L;
+  L.m = m;
+  L.n = n;
+  L.mt = ceil_div(m, kW4Rows);
+  L.kc = ceil_div(n, kW4Chunk);
+  L.n128 = L.kc * kW4Chunk;
+  L.g = group_size == -1 ? L.n128 : group_size;
+  L.G = group_size == -1 ? 1 : ceil_div(n, group_size);
+  L.Gp = ceil_div(L.n128, L.g);
+  L.flag_off = 0;
+  L.order_off = 256;
+  L.param_off = L.order_off + align256((size_t)L.n128 * sizeof(int32_t));
+  L.code_off = L.param_off + align256((size_t)(L.mt * L.Gp * kW4Rows) * sizeof(float2));
+  L.total = L.code_off + (size_t)(L.mt * L.kc) * 64 * sizeof(u32x4_t);
+  return L;
+}
+
+W4GemmPlan plan_w4a16_gemm(int64_t tokens, int64_t m, int64_t n) {
+  W4GemmPlan p;
+  p.chunk_tokens = std::min<int64_t>(std::max<int64_t>(tokens, 1), (int64_t)kW4TokTile * kW4MaxTokTiles);
+  p.mp = round_up(p.chunk_tokens, kW4TokTile);
+  const int64_t mt = ceil_div(m, kW4Rows), kc = ceil_div(n, kW4Chunk);
+  const int64_t wgs_rows = ceil_div(mt, kW4TilesPerWg);
+  // chunks per slice: the largest (<= 4) that still gives >= 512 workgroups
+  p.chunks = kW4MaxChunks;
+  while (p.chunks > 1 && wgs_rows * ceil_div(kc, p.chunks) < 512) p.chunks /= 2;
+  p.splits = ceil_div(kc, p.chunks);
+  const int64_t n128 = kc * kW4Chunk, m16 = mt * kW4Rows;
+  p.xp_off = 0;
+  p.xs_off = align256((size_t)(p.mp * n128) * sizeof(uint16_t));
+  p.part_off = p.xs_off + align256((size_t)(p.mp * (n128 / 32)) * sizeof(float));
+  p.total = p.part_off + (size_t)(p.splits * p.chunk_tokens * m16) * sizeof(float);
+  return p;
+}
+
+gptq_status run_w4a16_pack(const uint32_t* qweight, const float* scales, const int32_t* zeros,
+                           const int32_t* g_idx, int bits, const W4Layout& L, void* packed,
+                           hipStream_t stream) {
+  (void)bits;
+  char* base = static_cast<char*>(packed);
+  int* flag = reinterpret_cast<int*>(base + L.flag_off);
+  int32_t* order = reinterpret_cast<int32_t*>(base + L.order_off);
+  GPTQ_HIP_CHECK(hipMemsetAsync(flag, 0, sizeof(int), stream));
+  hipLaunchKernelGGL(w4_order_kernel, dim3((unsigned)L.Gp), dim3(256), 0, stream, g_idx, L.n, L.g,
+                     L.G, L.n128, order, flag);
+  GPTQ_LAUNCH_CHECK();
+  const int64_t np = L.mt * L.Gp * kW4Rows;
+  hipLaunchKernelGGL(w4_params_kernel, dim3((unsigned)ceil_div(np, 256)), dim3(256), 0, stream,
+                     scales, zeros, L.m, L.G, L.mt, L.Gp,
+                     reinterpret_cast<float2*>(base + L.param_off));
+  GPTQ_LAUNCH_CHECK();
+  const int64_t nw = L.mt * L.kc * 256;
+  hipLaunchKernelGGL(w4_codes_kernel, dim3((unsigned)ceil_div(nw, 256)), dim3(256), 0, stream,
+                     qweight, ceil_div(L.n, 8), L.m, L.n, L.kc, nw, (const int32_t*)order,
+                     reinterpret_cast<uint32_t*>(base + L.code_off));
+  GPTQ_LAUNCH_CHECK();
+  int hflag = 0;
+  GPTQ_HIP_CHECK(hipMemcpyAsync(&hflag, flag, sizeof(int), hipMemcpyDeviceToHost, stream));
+  GPTQ_HIP_CHECK(hipStreamSynchronize(stream));
+  if (hflag) {
+    set_error("gptq_w4a16_pack: g_idx does not split the columns into groups of the group size "
+              "(group p must hold min(g, n - p·g) columns)");
+    return GPTQ_ERR_INVALID_ARG;
+  }
+  return GPTQ_OK;
+}
+
+gptq_status run_w4a16_matmul(const uint16_t* X, int64_t tokens, int64_t ldx, const void* packed,
+                             const W4Layout& L, float* Y, int64_t ldy, void* ws,
+                             const W4GemmPlan& p, hipStream_t stream) {
+  const char* base = static_cast<const char*>(packed);
+  char* w = static_cast<char*>(ws);
+  uint16_t* Xp = reinterpret_cast<uint16_t*>(w + p.xp_off);
+  float* xs = reinterpret_cast<float*>(w + p.xs_off);
+  float* part = reinterpret_cast<float*>(w + p.part_off);
+  W4GemmArgs a;
+  a.Xp = Xp;
+  a.xs = xs;
+  a.params = reinterpret_cast<const float2*>(base + L.param_off);
+  a.codes = reinterpret_cast<const u32x4_t*>(base + L.code_off);
+  a.part = part;
+  a.m16 = L.mt * kW4Rows;
+  a.mt = L.mt;
+  a.kc = L.kc;
+  a.n128 = L.n128;
+  a.Gp = L.Gp;
+  a.gsteps = L.g >= L.n128 ? 0 : (int)(L.g / 32);
+  a.chunks = (int)p.chunks;
+  const int32_t* order = reinterpret_cast<const int32_t*>(base + L.order_off);
+  for (int64_t t0 = 0; t0 < tokens; t0 += p.chunk_tokens) {
+    const int64_t tk = std::min<int64_t>(p.chunk_tokens, tokens - t0);
+    const int64_t mp = round_up(tk, kW4TokTile);
+    hipLaunchKernelGGL(w4_gather_kernel, dim3((unsigned)ceil_div(L.n128, 1024), (unsigned)mp),
+                       dim3(256), 0, stream, X + t0 * ldx, ldx, tk, order, L.n128, Xp, xs);
+    GPTQ_LAUNCH_CHECK();
+    a.tokens = tk;
+    const dim3 grid((unsigned)ceil_div(L.mt, kW4TilesPerWg), (unsigned)p.splits);
+    switch (mp / kW4TokTile) {
+      case 1: hipLaunchKernelGGL(w4_gemm_kernel<1>, grid, dim3(256), 0, stream, a); break;
+      case 2: hipLaunchKernelGGL(w4_gemm_kernel<2>, grid, dim3(256), 0, stream, a); break;
+      case 3: hipLaunchKernelGGL(w4_gemm_kernel<3>, grid, dim3(256), 0, stream, a); break;
+      default: hipLaunchKernelGGL(w4_gemm_kernel<4>, grid, dim3(256), 0, stream, a); break;
+    }
+    GPTQ_LAUNCH_CHECK();
+    hipLaunchKernelGGL(w4_reduce_kernel, dim3((unsigned)ceil_div(L.m, 256), (unsigned)tk), dim3(256),
+                       0, stream, (const float*)part, p.splits, tk, a.m16, L.m, Y + t0 * ldy, ldy);
+    GPTQ_LAUNCH_CHECK();
+  }
+  return GPTQ_OK;
+}
+
+}  // namespace gptq

@@ -194,6 +194,48 @@ def rtn_quantize(W: torch.Tensor, cfg: RtnConfig) -> dict:
     return out
 
 
+# ---------------------------------------------------------------- W4A16 product
+def gptq_w4a16_packed_bytes(m: int, n: int, group_size: int) -> int:
+    return int(lib().gptq_w4a16_packed_bytes(m, n, group_size))
+
+
+def gptq_w4a16_pack(qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                    g_idx: torch.Tensor, n: int, bits: int, group_size: int,
+                    packed: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The quantizer's output of an m x n weight -> the product's layout (uint8 tensor)."""
+    m = qweight.shape[0]
+    nbytes = gptq_w4a16_packed_bytes(m, n, group_size)
+    if packed is None:
+        packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=qweight.device)
+    st = lib().gptq_w4a16_pack(_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(g_idx), m, n, bits,
+                               group_size, _ptr(packed), packed.numel() * packed.element_size(),
+                               _stream(stream))
+    _check(st, "gptq_w4a16_pack")
+    return packed
+
+
+def gptq_w4a16_workspace_bytes(tokens: int, m: int, n: int) -> int:
+    return int(lib().gptq_w4a16_workspace_bytes(tokens, m, n))
+
+
+def gptq_w4a16_matmul(X: torch.Tensor, packed: torch.Tensor, m: int, n: int, group_size: int,
+                      Y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """Y [tokens, m] fp32 = X [tokens, n] bf16 · Ŵᵀ from a packed weight."""
+    if X.dim() != 2 or X.shape[1] != n or (X.shape[0] > 0 and X.stride(1) != 1):
+        raise ValueError("X must be [tokens, n] with contiguous rows")
+    tokens = X.shape[0]
+    if Y is None:
+        Y = torch.empty(tokens, m, dtype=torch.float32, device=X.device)
+    ws = _workspace(gptq_w4a16_workspace_bytes(tokens, m, n), X.device, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().gptq_w4a16_matmul(_ptr(X), tokens, X.stride(0) if tokens > 0 else n, _ptr(packed), m, n,
+                                 group_size, _ptr(Y), Y.stride(0) if tokens > 0 else m, _ptr(ws), nbytes,
+                                 _stream(stream))
+    _check(st, "gptq_w4a16_matmul")
+    return Y
+
+
 # ---------------------------------------------------------------- whole layer
 def alloc_outputs(m: int, n: int, cfg: QuantConfig, device) -> dict:
     words = gptq_qweight_words(n, cfg.bits)
