@@ -270,6 +270,53 @@ def measure_rtn(pq, torch, W, reps=5):
     return res
 
 
+def measure_w4a16(pq, torch, out, m, n, bits, group_size, reps=200):
+    """The product of bf16 activations with this layer's quantized weight
+    (W4A16: gptq_w4a16_pack once, then gptq_w4a16_matmul per call) at 1, 16
+    and 64 tokens: µs per call (HIP events on the stream the kernels run on,
+    `reps` calls back to back), the HBM roofline of its algorithmic bytes
+    (codes m·n/2, per-group scale and zero 8 bytes, column order 4·n, X read
+    once, Y written once), and the same product through torch.matmul on the
+    dequantized bf16 weight (hipBLASLt) for comparison."""
+    groups = pq.gptq_num_groups(n, group_size)
+    packed = pq.gptq_w4a16_pack(out["qweight"], out["scales"], out["zeros"], out["g_idx"], n, bits,
+                                group_size)
+    Wd = torch.randn(m, n, device="cuda").to(torch.bfloat16)   # dense weight of the same shape
+    gen = torch.Generator(device="cuda").manual_seed(99)
+    res = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for tokens in (1, 16, 64):
+        X = torch.randn(tokens, n, device="cuda", generator=gen).to(torch.bfloat16)
+        Y = torch.empty(tokens, m, device="cuda")
+        ws = torch.empty(pq.gptq_w4a16_workspace_bytes(tokens, m, n), dtype=torch.uint8, device="cuda")
+        for _ in range(10):
+            pq.gptq_w4a16_matmul(X, packed, m, n, group_size, Y=Y, workspace=ws)
+            torch.matmul(X, Wd.t())
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            pq.gptq_w4a16_matmul(X, packed, m, n, group_size, Y=Y, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(X, Wd.t())
+        e1.record()
+        torch.cuda.synchronize()
+        us_bf16 = e0.elapsed_time(e1) / reps * 1e3
+        nbytes = m * n // 2 + m * groups * 8 + 4 * n + tokens * n * 2 + tokens * m * 4
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[f"tokens_{tokens}"] = {
+            "us": us, "bf16_matmul_us": us_bf16, "speedup_vs_bf16": us_bf16 / us,
+            "roofline": {"bound": "hbm", "kernel": "w4_gather_kernel + w4_gemm_kernel + w4_reduce_kernel",
+                         "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                         "traffic": None, "algorithmic_bytes_per_call": nbytes}}
+        log(f"bench: w4a16 {m}x{n} tokens {tokens}: {us:.2f} us ({gbs:.0f} GB/s), "
+            f"bf16 matmul {us_bf16:.2f} us, speedup {us_bf16 / us:.2f}x")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -368,6 +415,10 @@ def main():
     }
     result["next_rows"] = {"rtn_quantize": {"workload": f"{spec.name} weight ({m} x {n})",
                                             **measure_rtn(pq, torch, W)}}
+    if spec.bits <= 4 and spec.group_size in (32, 64, 128, -1):
+        result["next_rows"]["w4a16_matmul"] = {
+            "workload": f"bf16 activations x this layer's {spec.bits}-bit g{spec.group_size} act-order weight",
+            **measure_w4a16(pq, torch, layer.out, m, n, spec.bits, spec.group_size)}
     if not args.no_sweep and args.workload == "c3_down_proj_4096x11008":
         del layer
         torch.cuda.empty_cache()
