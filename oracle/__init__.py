@@ -40,3 +40,9 @@ from .quantized_matmul import (  # noqa: F401,E402
     dequant_matmul,
     dequantized_weight,
 )
+from .awq import (  # noqa: F401,E402
+    awq_quantize,
+    channel_abs_sum,
+    channel_scale,
+    lower_median,
+)

@@ -282,3 +282,66 @@ def test_unplanted_dequant_oracle_passes():
 def test_planted_dequant_mistake_is_caught(monkeypatch, name, fn):
     monkeypatch.setattr(dm, name, fn)
     assert not _dequant_pins_pass()
+
+
+# ---------------------------------------------------------------------------
+# The AWQ channel-scaling pins bite too
+# ---------------------------------------------------------------------------
+from oracle import awq  # noqa: E402
+import test_oracle_awq_pins as ap  # noqa: E402
+
+
+def _awq_pins_pass():
+    checks = [ap.test_hand_case, ap.test_scale_one_is_the_plain_linear_quantizer,
+              ap.test_equal_importance_scales_nothing]
+    checks += [lambda n=n: ap.test_lower_median_is_torch_convention(n) for n in (2, 8, 101)]
+    checks += [lambda s=s: ap.test_scaled_channels_and_round_trip(s) for s in (False, True)]
+    for check in checks:
+        try:
+            check()
+        except (AssertionError, ValueError, IndexError):
+            return False
+    return True
+
+
+_awq_orig = {k: getattr(awq, k) for k in ("lower_median", "channel_scale", "channel_abs_sum", "awq_quantize")}
+
+
+def _mean_median(v):
+    return float(np.median(np.asarray(v, dtype=np.float64)))
+
+
+def _scale_at_or_above(abs_sum, tokens, s=2.0):
+    imp = np.asarray(abs_sum, dtype=np.float64) / float(tokens)
+    med = awq.lower_median(imp)
+    sc = np.ones(imp.shape, dtype=np.float32)
+    sc[imp >= med] = np.float32(s)
+    return sc, imp, med
+
+
+def _signed_sum(X):
+    return np.sum(np.asarray(X, dtype=np.float64), axis=0)
+
+
+def _dequant_times_scale(W, abs_sum, tokens, s=2.0, bits=4, sym=False, group_size=128, clip_ratio=1.0):
+    out = _awq_orig["awq_quantize"](W, abs_sum, tokens, s, bits, sym, group_size, clip_ratio)
+    out["deq"] = out["deq"] * out["channel_scale"].astype(np.float64) ** 2
+    return out
+
+
+AWQ_PLANTS = [
+    ("lower_median", _mean_median),
+    ("channel_scale", _scale_at_or_above),
+    ("channel_abs_sum", _signed_sum),
+    ("awq_quantize", _dequant_times_scale),
+]
+
+
+def test_unplanted_awq_oracle_passes():
+    assert _awq_pins_pass()
+
+
+@pytest.mark.parametrize("name,fn", AWQ_PLANTS, ids=[f"{n}:{f.__name__}" for n, f in AWQ_PLANTS])
+def test_planted_awq_mistake_is_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(awq, name, fn)
+    assert not _awq_pins_pass()
