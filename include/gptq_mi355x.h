@@ -203,6 +203,44 @@ gptq_status gptq_rtn_quantize(const void* W, int32_t w_dtype, int64_t m, int64_t
                               void* stream);
 
 /* ------------------------------------------------------------------------
+ * Activation-aware channel scaling (AWQ) in front of the linear quantizer
+ *
+ * Page "大模型量化：GPTQ/AWQ/GGUF 原理对比，4-bit 量化对推理精度的影响", AWQ
+ * section: the importance of input channel j is mean_t |x_t[j]| over the
+ * calibration tokens; channels whose importance is strictly above its median
+ * (torch.median: the lower middle value for an even count) are multiplied by
+ * a protection factor s (2.0 in the page), the others by 1; the scaled weight
+ * is quantized, and dequantization divides by the channel factor again (at
+ * inference the activations are divided by it).
+ *
+ * gptq_awq_channel_stats ACCUMULATES abs_sum[j] += Σ_t |X[t][j]| (fp64) over
+ * X [tokens][ldx] (bf16 or fp32, unit column stride): the caller zeroes
+ * abs_sum once and may call once per token tile.  Stream-ordered; the
+ * summation order is fixed (reproducible).  workspace: at least
+ * gptq_awq_stats_workspace_bytes(n, tokens) bytes, 256-byte aligned.
+ *
+ * gptq_awq_quantize computes the channel factors from abs_sum and the token
+ * count (tokens > 0), writes them to channel_scale (fp32 [n], s or 1), and
+ * quantizes fl32(W·channel_scale) with the linear quantizer of
+ * gptq_rtn_quantize (same cfg, same qweight / scales / zeros layout).  err[0],
+ * err[1] are the MSE and cosine between W and the dequantized weight divided
+ * by the channel factor.  protect > 0 and finite.  workspace: at least
+ * gptq_awq_workspace_bytes(m, n, cfg) bytes.  Synchronises `stream` once and
+ * returns GPTQ_ERR_NONFINITE if W or abs_sum holds a NaN or Inf.  The same
+ * limits as gptq_rtn_quantize apply (GPTQ_ERR_UNSUPPORTED).
+ * ---------------------------------------------------------------------- */
+size_t gptq_awq_stats_workspace_bytes(int64_t n, int64_t tokens);
+gptq_status gptq_awq_channel_stats(const void* X, int32_t x_dtype, int64_t tokens, int64_t ldx,
+                                   int64_t n, double* abs_sum, void* workspace, size_t ws_bytes,
+                                   void* stream);
+size_t gptq_awq_workspace_bytes(int64_t m, int64_t n, const gptq_rtn_config* cfg);
+gptq_status gptq_awq_quantize(const void* W, int32_t w_dtype, int64_t m, int64_t n,
+                              const double* abs_sum, int64_t tokens, float protect,
+                              const gptq_rtn_config* cfg, uint32_t* qweight, float* scales,
+                              int32_t* zeros, float* channel_scale, double* err, void* workspace,
+                              size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Product of bf16 activations with the quantized weights (W4A16)
  *
  * Page "模型量化实战：从 INT8 PTQ 到 GPTQ 的精度保持与推理加速全解析" §4.3:

@@ -8,6 +8,11 @@ from .gptq import (  # noqa: F401
     QuantConfig,
     RtnConfig,
     alloc_outputs,
+    awq_quantize,
+    gptq_awq_channel_stats,
+    gptq_awq_quantize,
+    gptq_awq_stats_workspace_bytes,
+    gptq_awq_workspace_bytes,
     gptq_hessian_accumulate,
     gptq_hessian_workspace_bytes,
     gptq_last_error,

@@ -55,6 +55,11 @@ SIGNATURES = {
     "gptq_rtn_workspace_bytes": (_SZ, [_I64, _I64, ctypes.POINTER(GptqRtnConfig)]),
     "gptq_rtn_quantize": (_ST, [_P, _I32, _I64, _I64, ctypes.POINTER(GptqRtnConfig), _P, _P, _P, _P,
                                 _P, _SZ, _P]),
+    "gptq_awq_stats_workspace_bytes": (_SZ, [_I64, _I64]),
+    "gptq_awq_channel_stats": (_ST, [_P, _I32, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    "gptq_awq_workspace_bytes": (_SZ, [_I64, _I64, ctypes.POINTER(GptqRtnConfig)]),
+    "gptq_awq_quantize": (_ST, [_P, _I32, _I64, _I64, _P, _I64, ctypes.c_float, ctypes.POINTER(GptqRtnConfig),
+                                _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "gptq_w4a16_packed_bytes": (_SZ, [_I64, _I64, _I32]),
     "gptq_w4a16_pack": (_ST, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _SZ, _P]),
     "gptq_w4a16_workspace_bytes": (_SZ, [_I64, _I64, _I64]),

@@ -240,6 +240,64 @@ gptq_status gptq_rtn_quantize(const void* W, int32_t w_dtype, int64_t m, int64_t
                  workspace, plan, static_cast<hipStream_t>(stream));
 }
 
+size_t gptq_awq_stats_workspace_bytes(int64_t n, int64_t tokens) {
+  if (n < 0 || tokens < 0) return 0;
+  return plan_awq_stats(n, tokens).total;
+}
+
+gptq_status gptq_awq_channel_stats(const void* X, int32_t x_dtype, int64_t tokens, int64_t ldx,
+                                   int64_t n, double* abs_sum, void* workspace, size_t ws_bytes,
+                                   void* stream) {
+  clear_error();
+  if (tokens < 0 || n < 0) return fail(GPTQ_ERR_INVALID_ARG, "tokens=%lld n=%lld", (long long)tokens, (long long)n);
+  if (x_dtype != GPTQ_BF16 && x_dtype != GPTQ_FP32) return fail(GPTQ_ERR_UNSUPPORTED, "x_dtype=%d", x_dtype);
+  if (tokens == 0 || n == 0) return GPTQ_OK;
+  if (ldx < n) return fail(GPTQ_ERR_INVALID_ARG, "ldx=%lld < n=%lld", (long long)ldx, (long long)n);
+  if (bad_ptr(X, x_dtype == GPTQ_BF16 ? 2 : 4)) return fail(GPTQ_ERR_INVALID_ARG, "X is NULL or misaligned");
+  if (bad_ptr(abs_sum, 8)) return fail(GPTQ_ERR_INVALID_ARG, "abs_sum is NULL or misaligned");
+  const AwqStatsPlan p = plan_awq_stats(n, tokens);
+  if (workspace == nullptr || ws_bytes < p.total || bad_ptr(workspace, 256))
+    return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu (256-byte aligned)", ws_bytes, p.total);
+  return run_awq_stats(X, x_dtype, tokens, ldx, n, abs_sum, workspace, p, static_cast<hipStream_t>(stream));
+}
+
+size_t gptq_awq_workspace_bytes(int64_t m, int64_t n, const gptq_rtn_config* cfg) {
+  if (m < 0 || n < 0 || cfg == nullptr) return 0;
+  return awq_extra_bytes() + plan_rtn(m, n, cfg->group_size).total;
+}
+
+gptq_status gptq_awq_quantize(const void* W, int32_t w_dtype, int64_t m, int64_t n,
+                              const double* abs_sum, int64_t tokens, float protect,
+                              const gptq_rtn_config* cfg, uint32_t* qweight, float* scales,
+                              int32_t* zeros, float* channel_scale, double* err, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  clear_error();
+  if (m < 0 || n < 0) return fail(GPTQ_ERR_INVALID_ARG, "m=%lld n=%lld", (long long)m, (long long)n);
+  gptq_status st = check_rtn_config(cfg);
+  if (st != GPTQ_OK) return st;
+  if (w_dtype != GPTQ_BF16 && w_dtype != GPTQ_FP32) return fail(GPTQ_ERR_UNSUPPORTED, "w_dtype=%d", w_dtype);
+  if (tokens <= 0) return fail(GPTQ_ERR_INVALID_ARG, "tokens=%lld: importance is a mean over tokens", (long long)tokens);
+  if (!(protect > 0.f) || !std::isfinite(protect))
+    return fail(GPTQ_ERR_INVALID_ARG, "protect=%g must be positive and finite", (double)protect);
+  if (m == 0 || n == 0) return GPTQ_OK;
+  if (m > ((int64_t)1 << 31) - 1) return fail(GPTQ_ERR_UNSUPPORTED, "m=%lld too large", (long long)m);
+  const RtnPlan plan = plan_rtn(m, n, cfg->group_size);
+  if (plan.lds_bytes > kRtnMaxLds)
+    return fail(GPTQ_ERR_UNSUPPORTED, "n=%lld with group_size %d needs %zu bytes of LDS per row (max %zu)",
+                (long long)n, cfg->group_size, plan.lds_bytes, kRtnMaxLds);
+  if (bad_ptr(W, w_dtype == GPTQ_BF16 ? 2 : 4)) return fail(GPTQ_ERR_INVALID_ARG, "W is NULL or misaligned");
+  if (bad_ptr(abs_sum, 8)) return fail(GPTQ_ERR_INVALID_ARG, "abs_sum is NULL or misaligned");
+  if (bad_ptr(qweight, 4) || bad_ptr(scales, 4) || bad_ptr(zeros, 4) || bad_ptr(channel_scale, 4))
+    return fail(GPTQ_ERR_INVALID_ARG, "an output pointer is NULL or misaligned");
+  if (bad_ptr(err, 8)) return fail(GPTQ_ERR_INVALID_ARG, "err is NULL or misaligned");
+  const size_t need = awq_extra_bytes() + plan.total;
+  if (workspace == nullptr || ws_bytes < need || bad_ptr(workspace, 256))
+    return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu (256-byte aligned)", ws_bytes, need);
+  return run_awq_quantize(W, w_dtype, m, n, abs_sum, tokens, protect, cfg->bits, cfg->sym, cfg->clip_ratio,
+                          qweight, scales, zeros, channel_scale, err, workspace, plan,
+                          static_cast<hipStream_t>(stream));
+}
+
 static bool w4_group_ok(int32_t g) { return g == -1 || g == 32 || g == 64 || g == 128; }
 
 size_t gptq_w4a16_packed_bytes(int64_t m, int64_t n, int32_t group_size) {

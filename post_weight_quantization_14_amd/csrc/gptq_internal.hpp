@@ -124,9 +124,27 @@ struct RtnPlan {
   size_t part_off = 0, flag_off = 0, total = 0;
 };
 RtnPlan plan_rtn(int64_t m, int64_t n, int32_t group_size);
+// colscale (optional, per input column): quantize fl(w·colscale) and take the
+// errors against w with ŵ = (q - z)·s / colscale.  extra_flag (optional):
+// a device flag set by an earlier kernel of the same call, read at the end.
 gptq_status run_rtn(const void* W, int w_dtype, int64_t m, int64_t n, int bits, int sym, float clip,
                     uint32_t* qweight, float* scales, int32_t* zeros, double* err, void* ws,
-                    const RtnPlan& plan, hipStream_t stream);
+                    const RtnPlan& plan, hipStream_t stream, const float* colscale = nullptr,
+                    const int* extra_flag = nullptr);
+
+// ---------------------------------------------------------------- AWQ channel scaling
+struct AwqStatsPlan {
+  int64_t slices = 1, rows_per_slice = 0;
+  size_t total = 0;   // partial sums [slices][n] fp64
+};
+AwqStatsPlan plan_awq_stats(int64_t n, int64_t tokens);
+gptq_status run_awq_stats(const void* X, int x_dtype, int64_t tokens, int64_t ldx, int64_t n,
+                          double* abs_sum, void* ws, const AwqStatsPlan& plan, hipStream_t stream);
+size_t awq_extra_bytes();   // workspace of the scale step, before the quantizer's
+gptq_status run_awq_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const double* abs_sum,
+                             int64_t tokens, float protect, int bits, int sym, float clip,
+                             uint32_t* qweight, float* scales, int32_t* zeros, float* channel_scale,
+                             double* err, void* ws, const RtnPlan& plan, hipStream_t stream);
 
 // ---------------------------------------------------------------- W4A16 product
 struct W4Layout {

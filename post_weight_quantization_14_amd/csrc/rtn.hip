@@ -54,6 +54,7 @@ struct RtnArgs {
   int32_t* zeros;
   double* part;      // [m][4]: Σ(w-ŵ)², Σwŵ, Σw², Σŵ²
   int* flag;
+  const float* colscale;   // per input column, or null: quantize fl(w·colscale), errors against w
 };
 
 // Order-preserving map of a float to uint32 (and back): unsigned order of the
@@ -246,7 +247,8 @@ __global__ __launch_bounds__(kRtnThreads) void rtn_row_kernel(RtnArgs a) {
     const int j = i >> lgP, pos = i & (P - 1), c = j * g + pos;
     uint32_t key = 0xffffffffu;
     if (pos < g && c < n) {
-      const float x = rtn_f32<T>(w[c]);
+      float x = rtn_f32<T>(w[c]);
+      if (a.colscale) x *= a.colscale[c];
       bad |= !isfinite(x);
       key = f2u(a.sym ? fabsf(x) : x);
       tmin = min(tmin, key);
@@ -397,7 +399,9 @@ __global__ __launch_bounds__(kRtnThreads) void rtn_row_kernel(RtnArgs a) {
         sf = (float)s;
         zf = (float)z;
       }
-      const float xf = rtn_f32<T>(w[c]);
+      const float x0 = rtn_f32<T>(w[c]);
+      const float cs = a.colscale ? a.colscale[c] : 1.f;
+      const float xf = a.colscale ? x0 * cs : x0;
       const float qf = xf / sf;
       const float y = a.sym ? qf : qf + zf;
       const float half = floorf(y) + 0.5f;
@@ -411,8 +415,10 @@ __global__ __launch_bounds__(kRtnThreads) void rtn_row_kernel(RtnArgs a) {
       }
       q = fminf(fmaxf(q, qminf), qmaxf);
       const uint32_t code = (uint32_t)((int)q + off);
-      const double x = (double)xf;
-      const double d = x - ((double)q - z) * s;
+      // with a column scale the error is taken in the original domain:
+      // ŵ = (q - z)·s / colscale
+      const double x = (double)x0;
+      const double d = a.colscale ? x - ((double)q - z) * s / (double)cs : x - ((double)q - z) * s;
       se += d * d;
       xd += x * d;
       ww += x * x;
@@ -499,7 +505,7 @@ RtnPlan plan_rtn(int64_t m, int64_t n, int32_t group_size) {
 
 gptq_status run_rtn(const void* W, int w_dtype, int64_t m, int64_t n, int bits, int sym, float clip,
                     uint32_t* qweight, float* scales, int32_t* zeros, double* err, void* ws,
-                    const RtnPlan& p, hipStream_t stream) {
+                    const RtnPlan& p, hipStream_t stream, const float* colscale, const int* extra_flag) {
   char* w = static_cast<char*>(ws);
   RtnArgs a;
   a.W = W; a.m = m; a.n = n; a.bits = bits; a.sym = sym;
@@ -508,6 +514,7 @@ gptq_status run_rtn(const void* W, int w_dtype, int64_t m, int64_t n, int bits, 
   a.scales = scales; a.zeros = zeros;
   a.part = reinterpret_cast<double*>(w + p.part_off);
   a.flag = reinterpret_cast<int*>(w + p.flag_off);
+  a.colscale = colscale;
   GPTQ_HIP_CHECK(hipMemsetAsync(a.flag, 0, sizeof(int), stream));
   const int lds = (int)p.lds_bytes;
   if (w_dtype == GPTQ_BF16) {
@@ -525,11 +532,17 @@ gptq_status run_rtn(const void* W, int w_dtype, int64_t m, int64_t n, int bits, 
   hipLaunchKernelGGL(rtn_reduce_kernel, dim3(1), dim3(1024), 0, stream, (const double*)a.part, m, m * n,
                      err);
   GPTQ_LAUNCH_CHECK();
-  int hflag = 0;
+  int hflag = 0, xflag = 0;
   GPTQ_HIP_CHECK(hipMemcpyAsync(&hflag, a.flag, sizeof(int), hipMemcpyDeviceToHost, stream));
+  if (extra_flag)
+    GPTQ_HIP_CHECK(hipMemcpyAsync(&xflag, extra_flag, sizeof(int), hipMemcpyDeviceToHost, stream));
   GPTQ_HIP_CHECK(hipStreamSynchronize(stream));
+  if (xflag) {
+    set_error("channel statistics hold a NaN or Inf");
+    return GPTQ_ERR_NONFINITE;
+  }
   if (hflag & kFlagNonFinite) {
-    set_error("gptq_rtn_quantize: W holds a NaN or Inf");
+    set_error("%s: W holds a NaN or Inf", colscale ? "gptq_awq_quantize" : "gptq_rtn_quantize");
     return GPTQ_ERR_NONFINITE;
   }
   return GPTQ_OK;

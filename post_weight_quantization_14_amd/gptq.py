@@ -194,6 +194,70 @@ def rtn_quantize(W: torch.Tensor, cfg: RtnConfig) -> dict:
     return out
 
 
+# ---------------------------------------------------------------- AWQ channel scaling
+def gptq_awq_stats_workspace_bytes(n: int, tokens: int) -> int:
+    return int(lib().gptq_awq_stats_workspace_bytes(n, tokens))
+
+
+def gptq_awq_channel_stats(X: torch.Tensor, abs_sum: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> None:
+    """abs_sum [n] fp64 += Σ_t |X[t]| for X [tokens, n] (bf16 or fp32) with contiguous rows."""
+    if X.dim() != 2 or (X.shape[0] > 0 and X.stride(1) != 1):
+        raise ValueError("X must be [tokens, n] with contiguous rows")
+    tokens, n = X.shape
+    ws = _workspace(gptq_awq_stats_workspace_bytes(n, tokens), X.device, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().gptq_awq_channel_stats(_ptr(X), _dtype_code(X), tokens, X.stride(0) if tokens > 0 else n, n,
+                                      _ptr(abs_sum), _ptr(ws), nbytes, _stream(stream))
+    _check(st, "gptq_awq_channel_stats")
+
+
+def gptq_awq_workspace_bytes(m: int, n: int, cfg: RtnConfig) -> int:
+    c = cfg.c()
+    return int(lib().gptq_awq_workspace_bytes(m, n, ctypes.byref(c)))
+
+
+def gptq_awq_quantize(W: torch.Tensor, abs_sum: torch.Tensor, tokens: int, protect: float, cfg: RtnConfig,
+                      qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                      channel_scale: torch.Tensor, err: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    if not W.is_contiguous():
+        raise ValueError("W must be contiguous [m, n]")
+    m, n = W.shape
+    c = cfg.c()
+    ws = _workspace(gptq_awq_workspace_bytes(m, n, cfg), W.device, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().gptq_awq_quantize(_ptr(W), _dtype_code(W), m, n, _ptr(abs_sum), tokens, float(protect),
+                                 ctypes.byref(c), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(channel_scale),
+                                 _ptr(err), _ptr(ws), nbytes, _stream(stream))
+    _check(st, "gptq_awq_quantize")
+
+
+def awq_quantize(W: torch.Tensor, x_tiles, cfg: RtnConfig, protect: float = 2.0) -> dict:
+    """Channel statistics over every X tile, then gptq_awq_quantize on W [m, n]."""
+    m, n = W.shape
+    dev = W.device
+    abs_sum = torch.zeros(n, dtype=torch.float64, device=dev)
+    tokens = 0
+    for X in x_tiles:
+        gptq_awq_channel_stats(X, abs_sum)
+        tokens += X.shape[0]
+    words = max(gptq_qweight_words(n, cfg.bits), 0)
+    groups = max(gptq_num_groups(n, cfg.group_size), 0)
+    out = dict(
+        qweight=torch.empty(m, words, dtype=torch.int32, device=dev),
+        scales=torch.empty(m, groups, dtype=torch.float32, device=dev),
+        zeros=torch.empty(m, groups, dtype=torch.int32, device=dev),
+        channel_scale=torch.empty(n, dtype=torch.float32, device=dev),
+        err=torch.zeros(2, dtype=torch.float64, device=dev),
+        abs_sum=abs_sum,
+        tokens=tokens,
+    )
+    gptq_awq_quantize(W, abs_sum, tokens, protect, cfg, out["qweight"], out["scales"], out["zeros"],
+                      out["channel_scale"], out["err"])
+    return out
+
+
 # ---------------------------------------------------------------- W4A16 product
 def gptq_w4a16_packed_bytes(m: int, n: int, group_size: int) -> int:
     return int(lib().gptq_w4a16_packed_bytes(m, n, group_size))
