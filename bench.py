@@ -317,6 +317,84 @@ def measure_w4a16(pq, torch, out, m, n, bits, group_size, reps=200):
     return res
 
 
+def _dequant(torch, qweight, scales, zeros, gidx, n):
+    """Ŵ [m, n] fp32 from the packed 4-bit output (evaluation only)."""
+    shifts = torch.arange(0, 32, 4, device=qweight.device, dtype=torch.int32)
+    codes = ((qweight.unsqueeze(-1) >> shifts) & 15).reshape(qweight.shape[0], -1)[:, :n].float()
+    g = gidx.long()
+    return (codes - zeros[:, g].float()) * scales[:, g]
+
+
+def measure_awq(pq, torch, W, X, gptq_out, reps=3, eval_tokens=4096):
+    """The pages' AWQ channel scaling on this layer (4-bit asym g128, s = 2):
+    the channel statistics pass over the whole calibration X (HBM roofline of
+    reading X once) and the scaled linear quantizer, each in ms per call (HIP
+    events on the stream the kernels run on; the quantizer's call ends with its
+    NaN check, a stream synchronisation, which is included).  For context, the
+    relative output error ‖X(W - Ŵ)ᵀ‖ / ‖X Wᵀ‖ on the first `eval_tokens`
+    calibration tokens for AWQ, plain round-to-nearest and GPTQ."""
+    m, n = W.shape
+    T = X.shape[0]
+    cfg = pq.RtnConfig(bits=4, group_size=128, sym=False, clip_ratio=1.0)
+    abs_sum = torch.zeros(n, dtype=torch.float64, device="cuda")
+    ws = torch.empty(pq.gptq_awq_stats_workspace_bytes(n, T), dtype=torch.uint8, device="cuda")
+    pq.gptq_awq_channel_stats(X, abs_sum, ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        abs_sum.zero_()
+        pq.gptq_awq_channel_stats(X, abs_sum, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    stats_ms = e0.elapsed_time(e1) / reps
+    xbytes = T * n * X.element_size()
+    G = pq.gptq_num_groups(n, 128)
+    out = dict(qweight=torch.empty(m, pq.gptq_qweight_words(n, 4), dtype=torch.int32, device="cuda"),
+               scales=torch.empty(m, G, device="cuda"), zeros=torch.empty(m, G, dtype=torch.int32, device="cuda"),
+               channel_scale=torch.empty(n, device="cuda"), err=torch.zeros(2, dtype=torch.float64, device="cuda"))
+    qws = torch.empty(pq.gptq_awq_workspace_bytes(m, n, cfg), dtype=torch.uint8, device="cuda")
+    args = (W, abs_sum, T, 2.0, cfg, out["qweight"], out["scales"], out["zeros"], out["channel_scale"],
+            out["err"], qws)
+    pq.gptq_awq_quantize(*args)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        pq.gptq_awq_quantize(*args)
+    e1.record()
+    torch.cuda.synchronize()
+    quant_ms = e0.elapsed_time(e1) / reps
+    qbytes = m * n * W.element_size() + m * (n // 8) * 4 + m * ((n + 127) // 128) * 8 + 4 * n
+    # output error on a token sample
+    Xs = X[:eval_tokens].float()
+    Wf = W.float()
+    Y = Xs @ Wf.t()
+    col_g = torch.arange(n, device="cuda") // 128
+    W_awq = _dequant(torch, out["qweight"], out["scales"], out["zeros"], col_g, n) / out["channel_scale"]
+    rtn = pq.rtn_quantize(W, cfg)
+    W_rtn = _dequant(torch, rtn["qweight"], rtn["scales"], rtn["zeros"], col_g, n)
+    W_gptq = _dequant(torch, gptq_out["qweight"], gptq_out["scales"], gptq_out["zeros"], gptq_out["g_idx"], n)
+    rel = {k: float(torch.linalg.norm(Xs @ (Wf - Wq).t()) / torch.linalg.norm(Y))
+           for k, Wq in (("awq", W_awq), ("rtn", W_rtn), ("gptq", W_gptq))}
+    err = out["err"].cpu().tolist()
+    res = {
+        "channel_stats": {"ms": stats_ms, "roofline": {
+            "bound": "hbm", "kernel": "awq_stats_kernel + awq_stats_reduce_kernel",
+            "achieved": xbytes / (stats_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": xbytes / (stats_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
+            "algorithmic_bytes_per_call": xbytes}},
+        "quantize": {"ms": quant_ms, "weight_mse": err[0], "weight_cos": err[1], "roofline": {
+            "bound": "hbm", "kernel": "awq_scale_kernel + rtn_row_kernel + rtn_reduce_kernel",
+            "achieved": qbytes / (quant_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": qbytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
+            "algorithmic_bytes_per_call": qbytes}},
+        "output_rel_error_first_%d_tokens" % eval_tokens: rel,
+    }
+    log(f"bench: awq stats {stats_ms:.3f} ms ({xbytes / (stats_ms * 1e-3) / 1e9:.0f} GB/s), quantize "
+        f"{quant_ms:.3f} ms; output rel error awq {rel['awq']:.4f} rtn {rel['rtn']:.4f} gptq {rel['gptq']:.4f}")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -419,6 +497,10 @@ def main():
         result["next_rows"]["w4a16_matmul"] = {
             "workload": f"bf16 activations x this layer's {spec.bits}-bit g{spec.group_size} act-order weight",
             **measure_w4a16(pq, torch, layer.out, m, n, spec.bits, spec.group_size)}
+    if spec.x_dtype == "bf16" and spec.bits == 4:
+        result["next_rows"]["awq"] = {
+            "workload": f"{spec.name}: channel statistics over the {T}-token X, 4-bit asym g128, s = 2",
+            **measure_awq(pq, torch, W, X, layer.out)}
     if not args.no_sweep and args.workload == "c3_down_proj_4096x11008":
         del layer
         torch.cuda.empty_cache()
