@@ -65,41 +65,46 @@ __global__ __launch_bounds__(1024) void stats_kernel(const double* key, const fl
 }
 
 // perm[rank(j)] = j, rank = #{i: k_i > k_j} + #{i < j: k_i == k_j}.  NaN keys
-// sort as -inf, so the result is always a permutation.
-__global__ __launch_bounds__(256) void rank_kernel(const double* key, const float* H, int64_t n,
-                                                   int desc_act, int32_t* perm) {
-  __shared__ double ks[2048];
+// sort as -inf, so the result is always a permutation.  Two kernels: block
+// (jb, ic) counts, for the 256 columns j of block jb, the columns i of chunk
+// ic that precede j (part[ic][j]); then rank(j) = Σ_ic part[ic][j], summed in
+// chunk order, and perm[rank(j)] = j.  Counts are integers: the order of the
+// sums cannot change them.
+__device__ __forceinline__ double rank_key(const double* key, const float* H, int64_t n, int64_t j) {
+  const double k = key_of(key, H, n, j);
+  return isnan(k) ? -INFINITY : k;
+}
+
+__global__ __launch_bounds__(256) void rank_part_kernel(const double* key, const float* H, int64_t n,
+                                                        int32_t* __restrict__ part) {
+  __shared__ double ks[256];
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i0 = (int64_t)blockIdx.y * 256;
+  const int64_t li = i0 + threadIdx.x;
+  ks[threadIdx.x] = li < n ? rank_key(key, H, n, li) : -INFINITY;
+  __syncthreads();
+  if (j >= n) return;
+  const double kj = rank_key(key, H, n, j);
+  const int lim = (int)std::min<int64_t>(256, n - i0);
+  int cnt = 0;
+  for (int t = 0; t < lim; ++t) {
+    const double ki = ks[t];
+    cnt += (ki > kj) || (ki == kj && i0 + t < j);
+  }
+  part[blockIdx.y * n + j] = cnt;
+}
+
+__global__ __launch_bounds__(256) void rank_perm_kernel(const int32_t* __restrict__ part, int64_t chunks,
+                                                        int64_t n, int desc_act, int32_t* perm) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= n) return;
   if (!desc_act) {
-    if (j < n) perm[j] = (int32_t)j;
+    perm[j] = (int32_t)j;
     return;
   }
-  double kj = -INFINITY;
-  if (j < n) {
-    kj = key_of(key, H, n, j);
-    if (isnan(kj)) kj = -INFINITY;
-  }
   int64_t rank = 0;
-  for (int64_t c0 = 0; c0 < n; c0 += 2048) {
-    __syncthreads();
-    for (int t = threadIdx.x; t < 2048; t += 256) {
-      const int64_t i = c0 + t;
-      double k = -INFINITY;
-      if (i < n) {
-        k = key_of(key, H, n, i);
-        if (isnan(k)) k = -INFINITY;
-      }
-      ks[t] = k;
-    }
-    __syncthreads();
-    const int64_t lim = std::min<int64_t>(2048, n - c0);
-    for (int64_t t = 0; t < lim; ++t) {
-      const double ki = ks[t];
-      const int64_t i = c0 + t;
-      rank += (ki > kj) || (ki == kj && i < j);
-    }
-  }
-  if (j < n) perm[rank] = (int32_t)j;
+  for (int64_t c = 0; c < chunks; ++c) rank += part[c * n + j];
+  perm[rank] = (int32_t)j;
 }
 
 // One output row a of A = J P (H + λI) Pᵀ J, padded with the identity.
@@ -427,8 +432,15 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
   hipLaunchKernelGGL(stats_kernel, dim3(1), dim3(1024), 0, stream, key, (const float*)H, n, damp,
                      lam, flag);
   GPTQ_LAUNCH_CHECK();
-  hipLaunchKernelGGL(rank_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, key,
-                     (const float*)H, n, desc_act, perm);
+  // the ranks' partial counts borrow M, which the factorisation writes later
+  const int64_t chunks = ceil_div(n, 256);
+  if (desc_act) {
+    hipLaunchKernelGGL(rank_part_kernel, dim3((unsigned)chunks, (unsigned)chunks), dim3(256), 0, stream, key,
+                       (const float*)H, n, reinterpret_cast<int32_t*>(Mm));
+    GPTQ_LAUNCH_CHECK();
+  }
+  hipLaunchKernelGGL(rank_perm_kernel, dim3((unsigned)chunks), dim3(256), 0, stream,
+                     (const int32_t*)reinterpret_cast<int32_t*>(Mm), chunks, n, desc_act, perm);
   GPTQ_LAUNCH_CHECK();
   const size_t row_bytes = (size_t)n * sizeof(float);
   if (row_bytes > 65536)
