@@ -128,10 +128,10 @@ __global__ __launch_bounds__(256) void w4_codes_kernel(const uint32_t* __restric
 }
 
 // ---------------------------------------------------------------- product
-// X' = X[:, order] (rows >= tokens zero) and the sum of every 32 positions.
+// X' = X[:, order] and the sum of every 32 positions, for the real tokens.
 // Thread: 4 consecutive positions; 8 threads make one 32-position sum.
 __global__ __launch_bounds__(256) void w4_gather_kernel(const uint16_t* __restrict__ X, int64_t ldx,
-                                                        int64_t tokens, const int32_t* __restrict__ order,
+                                                        const int32_t* __restrict__ order,
                                                         int64_t n128, uint16_t* __restrict__ Xp,
                                                         float* __restrict__ xs) {
   const int64_t t = blockIdx.y;
@@ -139,15 +139,13 @@ __global__ __launch_bounds__(256) void w4_gather_kernel(const uint16_t* __restri
   if (p0 >= n128) return;   // n128 is a multiple of 128: whole 8-thread groups leave together
   uint16_t v[4] = {0, 0, 0, 0};
   float s = 0.f;
-  if (t < tokens) {
-    const int4 o = *reinterpret_cast<const int4*>(order + p0);
-    const int oi[4] = {o.x, o.y, o.z, o.w};
+  const int4 o = *reinterpret_cast<const int4*>(order + p0);
+  const int oi[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (oi[e] >= 0) v[e] = X[t * ldx + oi[e]];
-      s += __builtin_bit_cast(float, (uint32_t)v[e] << 16);
-    }
-  }
+  for (int e = 0; e < 4; ++e)
+    if (oi[e] >= 0) v[e] = X[t * ldx + oi[e]];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s += __builtin_bit_cast(float, (uint32_t)v[e] << 16);
   uint2 pk;
   pk.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
   pk.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
@@ -159,17 +157,19 @@ __global__ __launch_bounds__(256) void w4_gather_kernel(const uint16_t* __restri
 }
 
 struct W4GemmArgs {
-  const uint16_t* Xp;      // [Mp][n128]
-  const float* xs;         // [Mp][n128 / 32]
+  const uint16_t* Xp;      // [tokens][n128], processing order
+  const float* xs;         // [tokens][n128 / 32]
   const float2* params;    // [mt][Gp][16]
   const u32x4_t* codes;    // [mt][kc][64]
   float* part;             // [splits][tokens][m16]
   int64_t tokens, m16, mt, kc, n128, Gp;
-  int gsteps;              // 32-position steps per group; 0 = one group
   int chunks;              // 128-chunks per slice (<= kW4MaxChunks)
 };
 
+// The empty asm keeps the unpacking at its use: hoisted out of the token-tile
+// loop, the unpacked operands of every chunk would stay live (4x the VGPRs).
 __device__ __forceinline__ bf16x8_t w4_unpack(uint32_t w) {
+  asm volatile("" : "+v"(w));
   u32x4_t r;
   r[0] = (w & 0x000F000Fu) | 0x43004300u;
   r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
@@ -178,21 +178,29 @@ __device__ __forceinline__ bf16x8_t w4_unpack(uint32_t w) {
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
-template <int TT>
+// GS = 32-position steps per group (1, 2, 4 for groups of 32, 64, 128), or 0
+// for one group per row.  Slices are whole 128-chunks, so with GS > 0 every
+// slice starts on a group boundary and holds steps / GS whole groups.
+template <int GS>
 __global__ __launch_bounds__(256) void w4_gemm_kernel(W4GemmArgs a) {
   constexpr int RS = kW4MaxChunks * kW4Chunk + kW4Pad;   // LDS row of X' (bf16)
   constexpr int SS = kW4MaxChunks * 4;                   // 32-sums per LDS row
-  __shared__ __attribute__((aligned(16))) uint16_t xsh[TT * kW4TokTile * RS];
-  __shared__ float ssh[TT * kW4TokTile * SS];
-  __shared__ float2 psh[kW4TilesPerWg * kW4MaxGroups * kW4Rows];
+  constexpr int NG = GS > 0 ? SS / GS : 1;               // groups per slice (max)
+  constexpr int PI = (kW4TilesPerWg * NG * kW4Rows + 255) / 256;   // param items per thread
+  __shared__ __attribute__((aligned(16))) uint16_t xsh[kW4TokTile * RS];
+  __shared__ float ssh[kW4TokTile * SS];
+  __shared__ float2 psh[kW4TilesPerWg * NG * kW4Rows];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t s = blockIdx.y;
   const int64_t C0 = s * a.chunks;
   const int nch = (int)std::min<int64_t>(a.chunks, a.kc - C0);
+  const int steps = 4 * nch;
+  const int ng = GS > 0 ? steps / GS : 1;
   const int64_t T0 = (int64_t)blockIdx.x * kW4TilesPerWg;
+  const int64_t g0 = GS > 0 ? C0 * 4 / GS : 0;
 
-  // codes first: the HBM stream starts before anything else waits
+  // every global load of the prologue is issued before the first store
   u32x4_t cw[kW4TilesPerWave][kW4MaxChunks];
 #pragma unroll
   for (int r = 0; r < kW4TilesPerWave; ++r) {
@@ -203,98 +211,118 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(W4GemmArgs a) {
       if (T < a.mt && c < nch) cw[r][c] = a.codes[(T * a.kc + C0 + c) * 64 + lane];
     }
   }
-
-  // slice of X' (16-byte pieces) and its 32-sums
-  const int pos = nch * kW4Chunk;                 // positions in this slice
-  const int vec_per_row = pos / 8;
-  for (int i = tid; i < TT * kW4TokTile * vec_per_row; i += 256) {
-    const int t = i / vec_per_row, v = i % vec_per_row;
-    const uint4 x = *reinterpret_cast<const uint4*>(a.Xp + (int64_t)t * a.n128 + C0 * kW4Chunk + 8 * v);
-    *reinterpret_cast<uint4*>(xsh + t * RS + 8 * v) = x;
-  }
-  const int steps = nch * 4;
-  for (int i = tid; i < TT * kW4TokTile * steps; i += 256) {
-    const int t = i / steps, j = i % steps;
-    ssh[t * SS + j] = a.xs[(int64_t)t * (a.n128 / 32) + C0 * 4 + j];
-  }
-  // the slice's (s, 128 + z) of the workgroup's tiles
-  const int64_t st0 = C0 * 4, st1 = st0 + steps;   // global 32-steps [st0, st1)
-  const int64_t g0 = a.gsteps > 0 ? st0 / a.gsteps : 0;
-  const int ng = a.gsteps > 0 ? (int)((st1 - 1) / a.gsteps - g0 + 1) : 1;
-  for (int i = tid; i < kW4TilesPerWg * ng * kW4Rows; i += 256) {
+  float2 pv[PI];
+#pragma unroll
+  for (int u = 0; u < PI; ++u) {
+    const int i = tid + 256 * u;
     const int tl = i / (ng * kW4Rows), gi = (i / kW4Rows) % ng, rr = i % kW4Rows;
     const int64_t T = T0 + tl;
-    psh[(tl * kW4MaxGroups + gi) * kW4Rows + rr] =
-        T < a.mt ? a.params[(T * a.Gp + g0 + gi) * kW4Rows + rr] : make_float2(0.f, 0.f);
+    pv[u] = make_float2(0.f, 0.f);
+    if (tl < kW4TilesPerWg && T < a.mt) pv[u] = a.params[(T * a.Gp + g0 + gi) * kW4Rows + rr];
   }
-  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < PI; ++u) {
+    const int i = tid + 256 * u;
+    if (i < kW4TilesPerWg * ng * kW4Rows) psh[i] = pv[u];
+  }
 
   const int row = lane & 15, quad = lane >> 4;
+  const int vec_per_row = nch * (kW4Chunk / 8);   // 16-byte pieces of a row of the slice
+  const int ntt = (int)((a.tokens + kW4TokTile - 1) / kW4TokTile);
+  for (int tt = 0; tt < ntt; ++tt) {
+    const int64_t t0 = (int64_t)tt * kW4TokTile;
+    // X' tile: 16 rows x the slice, rows past the last token are zero
+    uint4 xv[4];
+    float sv;
 #pragma unroll
-  for (int r = 0; r < kW4TilesPerWave; ++r) {
-    const int tl = wave * kW4TilesPerWave + r;
-    const int64_t T = T0 + tl;
-    if (T >= a.mt) break;
-    f32x4_t acc[TT], y[TT];
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      y[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 256 * u;
+      const int t = i / vec_per_row, v = i % vec_per_row;
+      xv[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (i < kW4TokTile * vec_per_row && t0 + t < a.tokens)
+        xv[u] = *reinterpret_cast<const uint4*>(a.Xp + (t0 + t) * a.n128 + C0 * kW4Chunk + 8 * v);
     }
-    int fs = 0;   // first local step of the open group
+    {
+      const int t = tid / steps, j = tid % steps;
+      sv = 0.f;
+      if (tid < kW4TokTile * steps && t0 + t < a.tokens) sv = a.xs[(t0 + t) * (a.n128 / 32) + C0 * 4 + j];
+    }
+    if (tt > 0) __syncthreads();   // the previous tile is consumed
 #pragma unroll
-    for (int c = 0; c < kW4MaxChunks; ++c) {
-      if (c >= nch) break;
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 256 * u;
+      if (i < kW4TokTile * vec_per_row)
+        *reinterpret_cast<uint4*>(xsh + (i / vec_per_row) * RS + 8 * (i % vec_per_row)) = xv[u];
+    }
+    if (tid < kW4TokTile * steps) ssh[(tid / steps) * SS + tid % steps] = sv;
+    __syncthreads();
+
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8_t b = w4_unpack(cw[r][c][j]);
-        const int ls = 4 * c + j;
+    for (int r = 0; r < kW4TilesPerWave; ++r) {
+      const int tl = wave * kW4TilesPerWave + r;
+      const int64_t T = T0 + tl;
+      if (T >= a.mt) break;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
+      for (int c = 0; c < kW4MaxChunks; ++c) {
+        if (c >= nch) break;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int ls = 4 * c + j;
           const uint4 av = *reinterpret_cast<const uint4*>(
-              xsh + (tt * kW4TokTile + row) * RS + c * kW4Chunk + 32 * j + 8 * quad);
-          acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), b,
-                                                            acc[tt], 0, 0, 0);
-        }
-        const int64_t gs = st0 + ls;
-        const bool close = ls == steps - 1 || (a.gsteps > 0 && (gs + 1) % a.gsteps == 0);
-        if (close) {
-          const int gi = a.gsteps > 0 ? (int)(gs / a.gsteps - g0) : 0;
-          const float2 p = psh[(tl * kW4MaxGroups + gi) * kW4Rows + row];
-#pragma unroll
-          for (int tt = 0; tt < TT; ++tt) {
+              xsh + row * RS + c * kW4Chunk + 32 * j + 8 * quad);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                        w4_unpack(cw[r][c][j]), acc, 0, 0, 0);
+          const bool close = GS > 0 ? (ls + 1) % GS == 0 : (c == nch - 1 && j == 3);
+          if (close) {
+            const int gi = GS > 0 ? ls / GS : 0;
+            const int fs = GS > 0 ? ls + 1 - GS : 0;
+            const float2 p = psh[(tl * ng + gi) * kW4Rows + row];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              const float* sp = ssh + (tt * kW4TokTile + 4 * quad + v) * SS;
+              const float* sp = ssh + (4 * quad + v) * SS;
               float sx = 0.f;
-              for (int q = fs; q <= ls; ++q) sx += sp[q];
-              y[tt][v] = fmaf(p.x, fmaf(-p.y, sx, acc[tt][v]), y[tt][v]);
+              if (GS > 0) {
+#pragma unroll
+                for (int q = 0; q < (GS > 0 ? GS : 1); ++q) sx += sp[fs + q];
+              } else {
+                for (int q = 0; q < steps; ++q) sx += sp[q];
+              }
+              y[v] = fmaf(p.x, fmaf(-p.y, sx, acc[v]), y[v]);
             }
-            acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
           }
-          fs = ls + 1;
         }
       }
-    }
-    // D[4·quad + v][row]: token 16tt + 4·quad + v, weight row 16T + row
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
+      // D[4·quad + v][row]: token t0 + 4·quad + v, weight row 16T + row
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int64_t t = tt * kW4TokTile + 4 * quad + v;
-        if (t < a.tokens) a.part[(s * a.tokens + t) * a.m16 + T * kW4Rows + row] = y[tt][v];
+        const int64_t t = t0 + 4 * quad + v;
+        if (t < a.tokens) a.part[(s * a.tokens + t) * a.m16 + T * kW4Rows + row] = y[v];
       }
+    }
   }
 }
 
+// Y = Σ over slices in slice order; eight loads in flight per thread.
 __global__ __launch_bounds__(256) void w4_reduce_kernel(const float* __restrict__ part, int64_t splits,
                                                         int64_t tokens, int64_t m16, int64_t m,
                                                         float* __restrict__ Y, int64_t ldy) {
   const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t t = blockIdx.y;
   if (r >= m) return;
+  const int64_t stride = tokens * m16;
+  const float* p = part + t * m16 + r;
   float acc = 0.f;
-  for (int64_t s = 0; s < splits; ++s) acc += part[(s * tokens + t) * m16 + r];
+  int64_t s = 0;
+  for (; s + 8 <= splits; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(s + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
+  }
+  for (; s < splits; ++s) acc += p[s * stride];
   Y[t * ldy + r] = acc;
 }
 
@@ -321,7 +349,7 @@ W4Layout plan_w4a16(int64_t m, int64_t n, int32_t group_size) {
 W4GemmPlan plan_w4a16_gemm(int64_t tokens, int64_t m, int64_t n) {
   W4GemmPlan p;
   p.chunk_tokens = std::min<int64_t>(std::max<int64_t>(tokens, 1), (int64_t)kW4TokTile * kW4MaxTokTiles);
-  p.mp = round_up(p.chunk_tokens, kW4TokTile);
+  p.mp = p.chunk_tokens;
   const int64_t mt = ceil_div(m, kW4Rows), kc = ceil_div(n, kW4Chunk);
   const int64_t wgs_rows = ceil_div(mt, kW4TilesPerWg);
   // chunks per slice: the largest (<= 4) that still gives >= 512 workgroups
@@ -387,22 +415,24 @@ gptq_status run_w4a16_matmul(const uint16_t* X, int64_t tokens, int64_t ldx, con
   a.kc = L.kc;
   a.n128 = L.n128;
   a.Gp = L.Gp;
-  a.gsteps = L.g >= L.n128 ? 0 : (int)(L.g / 32);
   a.chunks = (int)p.chunks;
   const int32_t* order = reinterpret_cast<const int32_t*>(base + L.order_off);
+  const int gsteps = L.g >= L.n128 ? 0 : (int)(L.g / 32);
   for (int64_t t0 = 0; t0 < tokens; t0 += p.chunk_tokens) {
     const int64_t tk = std::min<int64_t>(p.chunk_tokens, tokens - t0);
-    const int64_t mp = round_up(tk, kW4TokTile);
-    hipLaunchKernelGGL(w4_gather_kernel, dim3((unsigned)ceil_div(L.n128, 1024), (unsigned)mp),
-                       dim3(256), 0, stream, X + t0 * ldx, ldx, tk, order, L.n128, Xp, xs);
+    hipLaunchKernelGGL(w4_gather_kernel, dim3((unsigned)ceil_div(L.n128, 1024), (unsigned)tk),
+                       dim3(256), 0, stream, X + t0 * ldx, ldx, order, L.n128, Xp, xs);
     GPTQ_LAUNCH_CHECK();
     a.tokens = tk;
     const dim3 grid((unsigned)ceil_div(L.mt, kW4TilesPerWg), (unsigned)p.splits);
-    switch (mp / kW4TokTile) {
+    switch (gsteps) {
       case 1: hipLaunchKernelGGL(w4_gemm_kernel<1>, grid, dim3(256), 0, stream, a); break;
       case 2: hipLaunchKernelGGL(w4_gemm_kernel<2>, grid, dim3(256), 0, stream, a); break;
-      case 3: hipLaunchKernelGGL(w4_gemm_kernel<3>, grid, dim3(256), 0, stream, a); break;
-      default: hipLaunchKernelGGL(w4_gemm_kernel<4>, grid, dim3(256), 0, stream, a); break;
+      case 4: hipLaunchKernelGGL(w4_gemm_kernel<4>, grid, dim3(256), 0, stream, a); break;
+      case 0: hipLaunchKernelGGL(w4_gemm_kernel<0>, grid, dim3(256), 0, stream, a); break;
+      default:
+        set_error("group width %lld not built", (long long)L.g);
+        return GPTQ_ERR_UNSUPPORTED;
     }
     GPTQ_LAUNCH_CHECK();
     hipLaunchKernelGGL(w4_reduce_kernel, dim3((unsigned)ceil_div(L.m, 256), (unsigned)tk), dim3(256),
