@@ -50,6 +50,7 @@ constexpr int kW4MaxGroups = kW4MaxChunks * 4 + 1;   // groups one slice can tou
 constexpr int kW4TokTile = 16;
 constexpr int kW4MaxTokTiles = 4;    // tokens per launch <= 64
 constexpr int kW4Pad = 8;            // bf16 padding per LDS row of X'
+constexpr int kW4GemvMaxTokens = 4;  // the whole-K path: X' of every position in LDS
 
 // ---------------------------------------------------------------- pack
 // One workgroup per group slot: the columns with g_idx == grp, ascending, go
@@ -304,6 +305,167 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(W4GemmArgs a) {
   }
 }
 
+// Few tokens (decode): one workgroup of 8 waves per 16-row tile covers the
+// whole K range, wave w a contiguous eighth of the chunks, so no partial sums
+// leave the workgroup.  X' (every position, the real tokens only), its
+// 32-sums and the tile's (s, 128 + z) of every group sit in LDS; each wave
+// streams its codes in batches of 8 chunks, the next batch in flight while
+// one computes; the 8 waves' results are added in wave order in LDS.
+struct W4GemvArgs {
+  const uint16_t* Xp;      // [tokens][n128]
+  const float* xs;         // [tokens][n128 / 32]
+  const float2* params;    // [mt][Gp][16]
+  const u32x4_t* codes;    // [mt][kc][64]
+  float* Y;                // [tokens][ldy]
+  int64_t ldy, m, mt, kc, n128, Gp;
+  int tokens;              // 1 .. kW4GemvMaxTokens
+};
+
+template <int GS>
+__global__ __launch_bounds__(512) void w4_gemv_kernel(W4GemvArgs a) {
+  constexpr int B = 8;                       // chunks per batch
+  extern __shared__ __attribute__((aligned(16))) uint8_t w4_lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t T = blockIdx.x;
+  const int xrow = (int)a.n128 + kW4Pad;     // bf16 per LDS row of X'
+  const int srow = (int)(a.n128 / 32);
+  uint16_t* xsh = reinterpret_cast<uint16_t*>(w4_lds);
+  float* ssh = reinterpret_cast<float*>(w4_lds + (size_t)a.tokens * xrow * 2);
+  float2* psh = reinterpret_cast<float2*>(ssh + a.tokens * srow + ((a.tokens * srow) & 1));
+  float* red = reinterpret_cast<float*>(psh + a.Gp * kW4Rows);   // [8][64][4]
+
+  const int cpw = (int)((a.kc + 7) / 8);
+  const int c0 = wave * cpw, c1 = (int)std::min<int64_t>(a.kc, (int64_t)c0 + cpw);
+  const u32x4_t* cbase = a.codes + T * a.kc * 64 + lane;
+  u32x4_t cw[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    cw[b] = u32x4_t{0u, 0u, 0u, 0u};
+    if (c0 + b < c1) cw[b] = cbase[(int64_t)(c0 + b) * 64];
+  }
+
+  // LDS fills, four loads in flight per thread before their stores
+  {
+    const int vrow = (int)(a.n128 / 8);
+    const int nv = a.tokens * vrow;
+    for (int i0 = 0; i0 < nv; i0 += 4 * 512) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * 512 + tid;
+        v[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (i < nv) v[u] = *reinterpret_cast<const uint4*>(a.Xp + (int64_t)(i / vrow) * a.n128 + 8 * (i % vrow));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * 512 + tid;
+        if (i < nv) *reinterpret_cast<uint4*>(xsh + (i / vrow) * xrow + 8 * (i % vrow)) = v[u];
+      }
+    }
+    const int ns = a.tokens * srow;
+    for (int i0 = 0; i0 < ns; i0 += 4 * 512) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * 512 + tid;
+        v[u] = 0.f;
+        if (i < ns) v[u] = a.xs[i];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * 512 + tid;
+        if (i < ns) ssh[i] = v[u];
+      }
+    }
+    const int np = (int)(a.Gp * kW4Rows);
+    const float2* pb = a.params + T * a.Gp * kW4Rows;
+    for (int i0 = 0; i0 < np; i0 += 4 * 512) {
+      float2 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * 512 + tid;
+        v[u] = make_float2(0.f, 0.f);
+        if (i < np) v[u] = pb[i];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * 512 + tid;
+        if (i < np) psh[i] = v[u];
+      }
+    }
+  }
+  __syncthreads();
+
+  const int row = lane & 15, quad = lane >> 4;
+  const bool arow = row < a.tokens;           // A-operand rows past the last token are zero
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+  int fs = 4 * c0;                            // first global 32-step of the open group
+  for (int cb = c0; cb < c1; cb += B) {
+    u32x4_t nx[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      nx[b] = u32x4_t{0u, 0u, 0u, 0u};
+      if (cb + B + b < c1) nx[b] = cbase[(int64_t)(cb + B + b) * 64];
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int c = cb + b;
+      if (c < c1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int st = 4 * c + j;
+        uint4 av = make_uint4(0u, 0u, 0u, 0u);
+        if (arow) av = *reinterpret_cast<const uint4*>(xsh + row * xrow + 32 * st + 8 * quad);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                      w4_unpack(cw[b][j]), acc, 0, 0, 0);
+        const bool close = GS > 0 ? (st + 1) % GS == 0 : (c == c1 - 1 && j == 3);
+        if (close) {
+          const int grp = GS > 0 ? st / GS : 0;
+          const float2 p = psh[grp * kW4Rows + row];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int t = 4 * quad + v;
+            float sx = 0.f;
+            if (t < a.tokens) {
+              const float* sp = ssh + t * srow;
+              if (GS > 0) {
+#pragma unroll
+                for (int q = 0; q < (GS > 0 ? GS : 1); ++q) sx += sp[st + 1 - GS + q];
+              } else {
+                for (int q = fs; q <= st; ++q) sx += sp[q];
+              }
+            }
+            y[v] = fmaf(p.x, fmaf(-p.y, sx, acc[v]), y[v]);
+          }
+          acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          fs = st + 1;
+        }
+      }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) cw[b] = nx[b];
+  }
+
+  // D[4·quad + v][row]: token 4·quad + v; the waves' sums in wave order
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[(wave * 64 + lane) * 4 + v] = y[v];
+  __syncthreads();
+  if (tid < 64) {
+    const int t0 = 4 * (tid >> 4);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = t0 + v;
+      const int64_t r = T * kW4Rows + (tid & 15);
+      if (t < a.tokens && r < a.m) {
+        float sum = 0.f;
+        for (int w = 0; w < 8; ++w) sum += red[(w * 64 + tid) * 4 + v];
+        a.Y[t * a.ldy + r] = sum;
+      }
+    }
+  }
+}
+
 // Y = Σ over slices in slice order; eight loads in flight per thread.
 __global__ __launch_bounds__(256) void w4_reduce_kernel(const float* __restrict__ part, int64_t splits,
                                                         int64_t tokens, int64_t m16, int64_t m,
@@ -327,6 +489,14 @@ __global__ __launch_bounds__(256) void w4_reduce_kernel(const float* __restrict_
 }
 
 }  // namespace
+
+constexpr size_t kW4GemvMaxLds = 150 * 1024;
+
+size_t w4_gemv_lds(int64_t tokens, const W4Layout& L) {
+  const size_t x = (size_t)tokens * (size_t)(L.n128 + kW4Pad) * 2;
+  const size_t sc = (size_t)tokens * (size_t)(L.n128 / 32);
+  return x + (sc + (sc & 1)) * 4 + (size_t)L.Gp * kW4Rows * sizeof(float2) + 8 * 64 * 4 * sizeof(float);
+}
 
 W4Layout plan_w4a16(int64_t m, int64_t n, int32_t group_size) {
   W4Layout L;
@@ -418,6 +588,36 @@ gptq_status run_w4a16_matmul(const uint16_t* X, int64_t tokens, int64_t ldx, con
   a.chunks = (int)p.chunks;
   const int32_t* order = reinterpret_cast<const int32_t*>(base + L.order_off);
   const int gsteps = L.g >= L.n128 ? 0 : (int)(L.g / 32);
+  // few tokens: gather, then one product kernel over the whole K range
+  const size_t gemv_lds = w4_gemv_lds(tokens, L);
+  if (tokens <= kW4GemvMaxTokens && gemv_lds <= kW4GemvMaxLds) {
+    hipLaunchKernelGGL(w4_gather_kernel, dim3((unsigned)ceil_div(L.n128, 1024), (unsigned)tokens),
+                       dim3(256), 0, stream, X, ldx, order, L.n128, Xp, xs);
+    GPTQ_LAUNCH_CHECK();
+    W4GemvArgs g;
+    g.Xp = Xp; g.xs = xs; g.params = a.params; g.codes = a.codes; g.Y = Y; g.ldy = ldy;
+    g.m = L.m; g.mt = L.mt; g.kc = L.kc; g.n128 = L.n128; g.Gp = L.Gp; g.tokens = (int)tokens;
+    const void* fn = nullptr;
+    switch (gsteps) {
+      case 1: fn = (const void*)w4_gemv_kernel<1>; break;
+      case 2: fn = (const void*)w4_gemv_kernel<2>; break;
+      case 4: fn = (const void*)w4_gemv_kernel<4>; break;
+      case 0: fn = (const void*)w4_gemv_kernel<0>; break;
+      default:
+        set_error("group width %lld not built", (long long)L.g);
+        return GPTQ_ERR_UNSUPPORTED;
+    }
+    if (gemv_lds > 65536)
+      GPTQ_HIP_CHECK(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemv_lds));
+    switch (gsteps) {
+      case 1: hipLaunchKernelGGL(w4_gemv_kernel<1>, dim3((unsigned)L.mt), dim3(512), gemv_lds, stream, g); break;
+      case 2: hipLaunchKernelGGL(w4_gemv_kernel<2>, dim3((unsigned)L.mt), dim3(512), gemv_lds, stream, g); break;
+      case 4: hipLaunchKernelGGL(w4_gemv_kernel<4>, dim3((unsigned)L.mt), dim3(512), gemv_lds, stream, g); break;
+      default: hipLaunchKernelGGL(w4_gemv_kernel<0>, dim3((unsigned)L.mt), dim3(512), gemv_lds, stream, g); break;
+    }
+    GPTQ_LAUNCH_CHECK();
+    return GPTQ_OK;
+  }
   for (int64_t t0 = 0; t0 < tokens; t0 += p.chunk_tokens) {
     const int64_t tk = std::min<int64_t>(p.chunk_tokens, tokens - t0);
     hipLaunchKernelGGL(w4_gather_kernel, dim3((unsigned)ceil_div(L.n128, 1024), (unsigned)tk),

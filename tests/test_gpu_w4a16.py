@@ -109,6 +109,13 @@ CASES = [
     (1, 256, 4, 64, 130, True),
     (300, 4096, 4, 128, 8, True),
     (17, 640, 3, 128, 33, False),
+    # up to 4 tokens take the whole-K kernel
+    (200, 1100, 4, 128, 1, True),
+    (64, 512, 2, 32, 4, True),
+    (300, 4096, 3, 64, 2, True),
+    (1, 256, 4, 64, 1, True),
+    (17, 640, 3, -1, 3, False),
+    (40, 100, 4, 32, 4, True),
 ]
 
 
@@ -120,11 +127,12 @@ def test_w4a16_matches_oracle(pq, case):
     _check(pq, X, Q, scales, zeros, gidx, bits, g, f"m={m} n={n} {bits}-bit g{g} tokens={tokens}")
 
 
+@pytest.mark.parametrize("tokens", [1, 4, 20])
 @pytest.mark.parametrize("g", [32, 64, 128, -1])
-def test_w4a16_exact_inputs_match_bit_for_bit(pq, g):
+def test_w4a16_exact_inputs_match_bit_for_bit(pq, g, tokens):
     """Small-integer activations and power-of-two scales: every sum is exact,
-    so the product equals the float64 oracle exactly."""
-    m, n, bits, tokens = 96, 1000, 4, 20
+    so the product equals the float64 oracle exactly (both kernels)."""
+    m, n, bits = 96, 1000, 4
     Q, scales, zeros, gidx = _case(m, n, bits, g, seed=11 + g, act_order=True, exact=True)
     rng = np.random.default_rng(3)
     X = torch.from_numpy(rng.integers(-8, 9, size=(tokens, n)).astype(np.float32)).to(torch.bfloat16)
@@ -179,6 +187,7 @@ def test_w4a16_full_size_down_proj(pq):
     Xa = workloads.gen_x(sp.with_(tokens=16, x_seed=sp.x_seed + 5), "cuda")
     Y1 = pq.gptq_w4a16_matmul(Xa, packed, sp.m, sp.n, 128)
     Y2 = pq.gptq_w4a16_matmul(Xa, packed, sp.m, sp.n, 128)
+    Yd = pq.gptq_w4a16_matmul(Xa[:1], packed, sp.m, sp.n, 128)   # one token: the whole-K kernel
     torch.cuda.synchronize()
     assert torch.equal(Y1, Y2)
     rows = np.random.default_rng(0).choice(sp.m, 64, replace=False)
@@ -193,6 +202,9 @@ def test_w4a16_full_size_down_proj(pq):
     rel = float(np.linalg.norm(Yg - ref) / np.linalg.norm(ref))
     print(f"down_proj 4096x11008, 16 tokens, 64 sampled rows: rel frob {rel:.3e}")
     assert rel <= 1e-4
+    Yd = Yd.cpu().numpy()[:, rows].astype(np.float64)
+    assert np.all(np.abs(Yd - ref[:1]) <= _bound(Xf[:1], sc, gi, sp.n, 128, 64))
+    assert float(np.linalg.norm(Yd - ref[:1]) / np.linalg.norm(ref[:1])) <= 1e-4
 
 
 def test_w4a16_rejects_bad_g_idx_and_settings(pq):
