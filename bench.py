@@ -46,6 +46,23 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+NEXT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "next_rows_traffic.json")
+
+
+def next_rows_traffic(row: str, key: str):
+    """HBM bytes per call of a next-row kernel from the committed counter runs,
+    if they were taken on the current source of that row; else None."""
+    try:
+        with open(NEXT_TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        src = rec["sources"][row]
+        if src["sha"] != source_hash(os.path.join(ROOT, src["file"])):
+            return None
+        return rec["hbm_bytes_per_call"].get(key)
+    except (OSError, ValueError, KeyError):
+        return None
+
+
 def measured_traffic(workload: str):
     """HBM bytes per SYRK launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel source; else None."""
@@ -309,9 +326,12 @@ def measure_w4a16(pq, torch, out, m, n, bits, group_size, reps=200):
         gbs = nbytes / (us * 1e-6) / 1e9
         res[f"tokens_{tokens}"] = {
             "us": us, "bf16_matmul_us": us_bf16, "speedup_vs_bf16": us_bf16 / us,
-            "roofline": {"bound": "hbm", "kernel": "w4_gather_kernel + w4_gemm_kernel + w4_reduce_kernel",
+            "roofline": {"bound": "hbm",
+                         "kernel": ("w4_gather_kernel + w4_gemv_kernel" if tokens <= 4 else
+                                    "w4_gather_kernel + w4_gemm_kernel + w4_reduce_kernel"),
                          "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                         "traffic": None, "algorithmic_bytes_per_call": nbytes}}
+                         "traffic": next_rows_traffic("w4a16", f"tokens_{tokens}") if (m, n) == (4096, 11008) else None,
+                         "algorithmic_bytes_per_call": nbytes}}
         log(f"bench: w4a16 {m}x{n} tokens {tokens}: {us:.2f} us ({gbs:.0f} GB/s), "
             f"bf16 matmul {us_bf16:.2f} us, speedup {us_bf16 / us:.2f}x")
     return res
@@ -381,7 +401,8 @@ def measure_awq(pq, torch, W, X, gptq_out, reps=3, eval_tokens=4096):
         "channel_stats": {"ms": stats_ms, "roofline": {
             "bound": "hbm", "kernel": "awq_stats_kernel + awq_stats_reduce_kernel",
             "achieved": xbytes / (stats_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": xbytes / (stats_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
+            "frac": xbytes / (stats_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "traffic": next_rows_traffic("awq", "awq_channel_stats") if (m, n, T) == (4096, 11008, 262144) else None,
             "algorithmic_bytes_per_call": xbytes}},
         "quantize": {"ms": quant_ms, "weight_mse": err[0], "weight_cos": err[1], "roofline": {
             "bound": "hbm", "kernel": "awq_scale_kernel + rtn_row_kernel + rtn_reduce_kernel",
