@@ -50,7 +50,7 @@ constexpr int kW4MaxGroups = kW4MaxChunks * 4 + 1;   // groups one slice can tou
 constexpr int kW4TokTile = 16;
 constexpr int kW4MaxTokTiles = 4;    // tokens per launch <= 64
 constexpr int kW4Pad = 8;            // bf16 padding per LDS row of X'
-constexpr int kW4GemvMaxTokens = 4;  // the whole-K path: X' of every position in LDS
+constexpr int kW4GemvMaxTokens = 16; // the whole-K path: X' of every position in LDS
 
 // ---------------------------------------------------------------- pack
 // One workgroup per group slot: the columns with g_idx == grp, ascending, go
@@ -305,7 +305,8 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(W4GemmArgs a) {
   }
 }
 
-// Few tokens (decode): one workgroup of 8 waves per 16-row tile covers the
+// Few tokens (up to 16, while X' fits in LDS and all workgroups are resident
+// at once): one workgroup of 8 waves per 16-row tile covers the
 // whole K range, wave w a contiguous eighth of the chunks, so no partial sums
 // leave the workgroup.  X' (every position, the real tokens only), its
 // 32-sums and the tile's (s, 128 + z) of every group sit in LDS; each wave
@@ -590,7 +591,9 @@ gptq_status run_w4a16_matmul(const uint16_t* X, int64_t tokens, int64_t ldx, con
   const int gsteps = L.g >= L.n128 ? 0 : (int)(L.g / 32);
   // few tokens: gather, then one product kernel over the whole K range
   const size_t gemv_lds = w4_gemv_lds(tokens, L);
-  if (tokens <= kW4GemvMaxTokens && gemv_lds <= kW4GemvMaxLds) {
+  // while its X' fits in LDS and every workgroup is resident at once
+  const int64_t resident = 256 * std::max<int64_t>(1, (int64_t)(160 * 1024 / std::max<size_t>(gemv_lds, 1)));
+  if (tokens <= kW4GemvMaxTokens && gemv_lds <= kW4GemvMaxLds && L.mt <= resident) {
     hipLaunchKernelGGL(w4_gather_kernel, dim3((unsigned)ceil_div(L.n128, 1024), (unsigned)tokens),
                        dim3(256), 0, stream, X, ldx, order, L.n128, Xp, xs);
     GPTQ_LAUNCH_CHECK();
