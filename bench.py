@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 METRIC = "GPTQ s/layer (4096x11008, g128); XᵀX TFLOP/s; total s for 7B-shaped sweep"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA
 SYRK_KERNEL_SOURCE = os.path.join(ROOT, "post_weight_quantization_14_amd", "csrc", "hessian.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "syrk_bf16_traffic.json")
 
@@ -416,6 +417,40 @@ def measure_awq(pq, torch, W, X, gptq_out, reps=3, eval_tokens=4096):
     return res
 
 
+def stage_rates(spec, stages_ms):
+    """Per-stage rates against their bounds, counted on the algorithmic work
+    (triangle only): X bytes = 2·T·n through the Hessian, Cholesky + triangular
+    inverse 2n³/3 flop in the prepare stage, the trailing update m·n·(n - 128)
+    flop in the quantize stage; the end-to-end fraction is the sum of the
+    stages' ideal times (SYRK at the bf16 peak, the other two at the fp32
+    peak) over the measured layer time."""
+    n, m, T = spec.n, spec.m, spec.tokens
+    h, p, q = (x * 1e-3 for x in stages_ms)
+    xb = 2.0 * T * n if spec.x_dtype == "bf16" else 4.0 * T * n
+    syrk = float(T) * n * (n + 1)
+    chol = 2.0 * n ** 3 / 3.0
+    trail = float(m) * n * max(n - 128, 0)
+    ideal = syrk / (PEAK_BF16_TFLOPS * 1e12) + chol / (PEAK_FP32_TFLOPS * 1e12) + trail / (PEAK_FP32_TFLOPS * 1e12)
+    return {
+        "x_gbs": xb / h / 1e9, "x_frac_of_hbm": xb / h / 1e9 / PEAK_HBM_GBS,
+        "prepare_tflops": chol / p / 1e12, "prepare_frac_of_fp32": chol / p / 1e12 / PEAK_FP32_TFLOPS,
+        "trailing_tflops": trail / q / 1e12, "trailing_frac_of_fp32": trail / q / 1e12 / PEAK_FP32_TFLOPS,
+        "end_to_end_ideal_ms": ideal * 1e3, "end_to_end_frac": ideal / (h + p + q),
+    }
+
+
+def gpu_clocks():
+    """Current clocks as rocm-smi reports them (best effort, a child process)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        rec = json.loads(r.stdout)
+        card = next(iter(rec.values()))
+        return {k: v for k, v in card.items() if "clock" in k.lower() or "sclk" in k.lower() or "mclk" in k.lower()}
+    except Exception as e:   # the tool may be missing or print no JSON
+        return {"error": repr(e)[:120]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -500,6 +535,7 @@ def main():
                    "damp_percent": spec.damp_percent, "parallelism": "single-gpu"},
         "stages_ms": {"hessian": stages[0], "prepare": stages[1], "quantize": stages[2]},
         "xtx_tflops": syrk_tflops,
+        "stage_rates": stage_rates(spec, stages),
         "roofline": {
             "bound": "mfma",
             "kernel": "gptq_hessian_accumulate = syrk_bf16_ring_kernel + syrk_reduce_kernel (H += 2·XᵀX)",
@@ -529,6 +565,7 @@ def main():
         result["sweep"] = run_sweep(pq, torch, workloads.SWEEP_SETTINGS)
         log("bench: 7B-shaped sweep, one input per (decoder layer, input), both settings")
         result["next_rows"]["sweep_shared_inputs"] = run_sweep_shared(pq, torch, workloads.SWEEP_SETTINGS)
+    result["clocks"] = gpu_clocks()
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle on a bounded sample)")
         result["cpu_baseline"] = cpu_baseline(spec, W, X)
