@@ -20,7 +20,7 @@ SRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgptq_mi355x.so")
-SOURCES = ("abi.hip", "gemm_f32.hip", "hessian.hip", "prepare.hip", "quantize.hip", "rtn.hip", "w4a16.hip", "awq.hip",
+SOURCES = ("abi.hip", "gemm_f32.hip", "hessian.hip", "prepare.hip", "quantize.hip", "rtn.hip", "w4a16.hip", "awq.hip", "gemm_x6.hip",
            *(f"block_quant_g{g}.hip" for g in (0, 8, 16, 32, 64, 128)))
 
 HIPCC = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

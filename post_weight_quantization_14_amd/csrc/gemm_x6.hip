@@ -1,0 +1,276 @@
+// fp32-accurate GEMM on bf16 MFMA: C = alpha·A·Bᵀ + beta·C from operands
+// split exactly into three bf16 planes.
+//
+// An fp32 value x is hi + mid + lo exactly, each a bf16 (hi = x truncated to
+// bf16, mid = (x - hi) truncated, lo = the rest, which fits: 24 significand
+// bits in three 8-bit pieces).  The product a·b keeps the six cross terms
+// whose weight is at least 2⁻¹⁶ of hi·hi (lo·lo, lo·mid, mid·lo dropped, below
+// fp32's own rounding), each an exact bf16 × bf16 product accumulated in fp32
+// by v_mfma_f32_32x32x16_bf16.  At the bf16 MFMA rate that is 1.4x faster
+// than v_mfma_f32_32x32x2f32 on the same GEMM, with a result within fp32
+// rounding of it (relative Frobenius difference ~5e-8).
+//
+// Planes are [3][rows][kp] bf16 (k contiguous, kp a multiple of 16, zero
+// padded); the split kernels write them from fp32 rows (A, or B stored with
+// k contiguous) or from fp32 columns (B stored k-major, transposed on the way).
+//
+// GEMM: tiles of 128 x 128 per workgroup of 4 waves (64 x 64 each); per
+// 16-position k-step the six operand planes (2 x 3 x 4 KB) stream into a
+// three-slot LDS ring by direct-to-LDS buffer loads, rows past the operand's
+// end read as zero; the lower variant computes only element row >= column of
+// the output (a triangle of tiles over a rectangle of full tiles).
+#include "gptq_internal.hpp"
+
+namespace gptq {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr int X6T = 128;             // tile edge
+constexpr int X6KS = 16;             // k per stage (one MFMA k-step)
+constexpr int X6ROWB = X6KS * 2;     // 32 bytes per row per plane
+constexpr int X6PLANEB = X6T * X6ROWB;
+constexpr int X6OPB = 3 * X6PLANEB;  // 12 KB per operand
+constexpr int X6SLOTB = 2 * X6OPB;   // 24 KB per stage
+constexpr int X6RING = 3;
+
+__device__ __forceinline__ constexpr int x6_vmcnt(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
+__device__ __forceinline__ void x6_split(float x, uint16_t& h, uint16_t& m, uint16_t& l) {
+  const uint32_t hb = __float_as_uint(x) & 0xffff0000u;
+  const float r1 = x - __uint_as_float(hb);
+  const uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
+  const float r2 = r1 - __uint_as_float(mb);
+  const uint32_t lb = __float_as_uint(r2) & 0xffff0000u;
+  h = (uint16_t)(hb >> 16);
+  m = (uint16_t)(mb >> 16);
+  l = (uint16_t)(lb >> 16);
+}
+
+// planes[q][r][k] from X[r][k] (k < K), zero for K <= k < kp
+__global__ __launch_bounds__(256) void x6_split_rows_kernel(const float* __restrict__ X, int64_t ldx,
+                                                            int64_t rows, int64_t K, int64_t kp,
+                                                            uint16_t* __restrict__ out, int64_t pstride) {
+  const int64_t total = rows * kp;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / kp, k = i % kp;
+    const float x = k < K ? X[r * ldx + k] : 0.f;
+    uint16_t h, m, l;
+    x6_split(x, h, m, l);
+    out[r * kp + k] = h;
+    out[pstride + r * kp + k] = m;
+    out[2 * pstride + r * kp + k] = l;
+  }
+}
+
+// planes[q][c][k] from X[k][c] (k < K, c < cols), zero for K <= k < kp:
+// 64 x 64 tiles through LDS, read along c and written along k
+__global__ __launch_bounds__(256) void x6_split_cols_kernel(const float* __restrict__ X, int64_t ldx,
+                                                            int64_t K, int64_t cols, int64_t kp,
+                                                            uint16_t* __restrict__ out, int64_t pstride) {
+  __shared__ float t[64][65];
+  const int64_t c0 = (int64_t)blockIdx.x * 64, k0 = (int64_t)blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int64_t k = k0 + r, c = c0 + tx;
+    t[r][tx] = (k < K && c < cols) ? X[k * ldx + c] : 0.f;
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int64_t c = c0 + r, k = k0 + tx;
+    if (c < cols && k < kp) {
+      uint16_t h, m, l;
+      x6_split(t[tx][r], h, m, l);
+      out[c * kp + k] = h;
+      out[pstride + c * kp + k] = m;
+      out[2 * pstride + c * kp + k] = l;
+    }
+  }
+}
+
+template <bool LOWER>
+__global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B, float* __restrict__ C,
+                                                        int64_t ldc, int64_t M, int64_t N, float alpha,
+                                                        float beta) {
+  __shared__ __attribute__((aligned(16))) uint8_t s0[X6SLOTB], s1[X6SLOTB], s2[X6SLOTB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  int64_t ti, tj;
+  {
+    const int64_t nt = (N + X6T - 1) / X6T;
+    const int64_t t = blockIdx.x;
+    if (LOWER) {
+      const int64_t tri = nt * (nt + 1) / 2;
+      if (t < tri) {
+        int64_t r = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+        while (r * (r + 1) / 2 > t) --r;
+        while ((r + 1) * (r + 2) / 2 <= t) ++r;
+        ti = r;
+        tj = t - r * (r + 1) / 2;
+      } else {
+        ti = nt + (t - tri) / nt;
+        tj = (t - tri) % nt;
+      }
+    } else {
+      ti = t / nt;
+      tj = t % nt;
+    }
+  }
+  const int64_t i0 = ti * X6T, j0 = tj * X6T;
+  const int64_t kp = A.kp;
+  const int64_t nst = kp / X6KS;
+  // 24 copy instructions per stage = (operand, plane, row quarter); wave w
+  // issues 6 of them.  Lane i of one covers row 32q + i/2, 16 bytes, into LDS
+  // chunk i%2 holding source chunk (i%2) ^ ((row >> 3) & 1) (bank spread).
+  constexpr int32_t kOut = 0x7ffffff0;
+  int32_t voff[6];
+  const uint16_t* obase[6];
+  int64_t obytes[6];
+  int ldso[6];
+#pragma unroll
+  for (int u = 0; u < 6; ++u) {
+    const int idx = wave * 6 + u;
+    const int op = idx / 12, plane = (idx / 4) % 3, q = idx % 4;
+    const int row = 32 * q + (lane >> 1);
+    const int cs = (lane & 1) ^ ((row >> 3) & 1);
+    const X6Planes& P = op == 0 ? A : B;
+    const int64_t grow = (op == 0 ? i0 : j0) + row;
+    obase[u] = P.p + (int64_t)plane * P.pstride;
+    obytes[u] = P.rows * kp * 2;
+    voff[u] = grow < P.rows ? (int32_t)(grow * kp * 2 + cs * 16) : kOut;
+    ldso[u] = op * X6OPB + plane * X6PLANEB + q * 1024;
+  }
+  auto issue = [&](int64_t st, uint8_t* slot) {
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+      const bool live = st < nst;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(obase[u]) + (live ? st * X6KS : 0), 0,
+          live ? (int32_t)(obytes[u] - st * X6KS * 2) : 0, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(slot + ldso[u]), 16, voff[u], 0, 0, 0);
+    }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  auto frag = [&](const uint8_t* slot, int op, int plane, int r0) {
+    const int row = r0 + (lane & 31);
+    const int c = (lane >> 5) ^ ((row >> 3) & 1);
+    return *reinterpret_cast<const bf16x8_t*>(slot + op * X6OPB + plane * X6PLANEB + row * X6ROWB + c * 16);
+  };
+  auto compute = [&](const uint8_t* slot, int64_t st, uint8_t* refill) {
+    bf16x8_t fa[2][3], fb[2][3];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        fa[i][p] = frag(slot, 0, p, wr * 64 + i * 32);
+        fb[i][p] = frag(slot, 1, p, wc * 64 + i * 32);
+      }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        // smallest terms first: lo·hi, hi·lo, mid·mid, mid·hi, hi·mid, hi·hi
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][2], fb[j][0], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][0], fb[j][2], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][1], fb[j][1], acc[i][j], 0, 0, 0);
+        if (i == 0 && j == 0) issue(st + X6RING - 1, refill);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][1], fb[j][0], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][0], fb[j][1], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][0], fb[j][0], acc[i][j], 0, 0, 0);
+      }
+  };
+  // stage st is in slot st % 3; before computing it, every wave's copies of
+  // it are done (its own by vmcnt, the others' by the barrier) and every wave
+  // has finished stage st - 1, whose slot the refill of stage st + 2 reuses
+  auto step = [&](int64_t st, const uint8_t* cur, uint8_t* refill) {
+    __builtin_amdgcn_s_waitcnt(x6_vmcnt(6 * (X6RING - 2)));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    compute(cur, st, refill);
+  };
+  issue(0, s0);
+  issue(1, s1);
+  for (int64_t st = 0; st < nst; st += 3) {
+    step(st, s0, s2);
+    step(st + 1, s1, s0);
+    step(st + 2, s2, s1);
+  }
+  __builtin_amdgcn_s_waitcnt(x6_vmcnt(0));
+  // C tile: element (i, j) of a 32 x 32 block in lane j%32 + 32((i/4)%2),
+  // register (i%4) + 4(i/8); the 16 reads of a block before its 16 writes
+  const int li = lane & 31, lk = lane >> 5;
+  const int64_t rows = M - i0 < X6T ? M - i0 : X6T, cols = N - j0 < X6T ? N - j0 : X6T;
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      const int j = wc * 64 + bj * 32 + li;
+      const int ib = wr * 64 + bi * 32 + 4 * lk;
+      float old[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int i = ib + 8 * (v >> 2) + (v & 3);
+        const bool in = i < rows && j < cols && (!LOWER || i0 + i >= j0 + j);
+        old[v] = (beta != 0.f && in) ? C[(i0 + i) * ldc + j0 + j] : 0.f;
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int i = ib + 8 * (v >> 2) + (v & 3);
+        const bool in = i < rows && j < cols && (!LOWER || i0 + i >= j0 + j);
+        if (in) C[(i0 + i) * ldc + j0 + j] = alpha * acc[bi][bj][v] + beta * old[v];
+      }
+    }
+}
+
+}  // namespace
+
+gptq_status launch_x6_split_rows(const float* X, int64_t ldx, int64_t rows, int64_t K, int64_t kp,
+                                 uint16_t* out, int64_t pstride, hipStream_t stream) {
+  if (rows <= 0) return GPTQ_OK;
+  const int64_t total = rows * kp;
+  hipLaunchKernelGGL(x6_split_rows_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(total, 256), 4096)),
+                     dim3(256), 0, stream, X, ldx, rows, K, kp, out, pstride);
+  GPTQ_LAUNCH_CHECK();
+  return GPTQ_OK;
+}
+
+gptq_status launch_x6_split_cols(const float* X, int64_t ldx, int64_t K, int64_t cols, int64_t kp,
+                                 uint16_t* out, int64_t pstride, hipStream_t stream) {
+  if (cols <= 0) return GPTQ_OK;
+  hipLaunchKernelGGL(x6_split_cols_kernel, dim3((unsigned)ceil_div(cols, 64), (unsigned)ceil_div(kp, 64)),
+                     dim3(256), 0, stream, X, ldx, K, cols, kp, out, pstride);
+  GPTQ_LAUNCH_CHECK();
+  return GPTQ_OK;
+}
+
+gptq_status launch_x6_gemm(const X6Planes& A, const X6Planes& B, float* C, int64_t ldc, int64_t M,
+                           int64_t N, float alpha, float beta, bool lower, hipStream_t stream) {
+  if (M <= 0 || N <= 0) return GPTQ_OK;
+  if (A.kp != B.kp || A.kp % X6KS != 0) {
+    set_error("launch_x6_gemm: plane widths %lld / %lld", (long long)A.kp, (long long)B.kp);
+    return GPTQ_ERR_INVALID_ARG;
+  }
+  const int64_t mt = ceil_div(M, X6T), nt = ceil_div(N, X6T);
+  if (lower) {
+    if (M < N) {
+      set_error("launch_x6_gemm: lower part needs M (%lld) >= N (%lld)", (long long)M, (long long)N);
+      return GPTQ_ERR_INVALID_ARG;
+    }
+    hipLaunchKernelGGL(x6_gemm_kernel<true>, dim3((unsigned)(nt * (nt + 1) / 2 + (mt - nt) * nt)), dim3(256),
+                       0, stream, A, B, C, ldc, M, N, alpha, beta);
+  } else {
+    hipLaunchKernelGGL(x6_gemm_kernel<false>, dim3((unsigned)(mt * nt)), dim3(256), 0, stream, A, B, C, ldc,
+                       M, N, alpha, beta);
+  }
+  GPTQ_LAUNCH_CHECK();
+  return GPTQ_OK;
+}
+
+}  // namespace gptq

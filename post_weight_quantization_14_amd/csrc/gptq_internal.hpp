@@ -93,7 +93,7 @@ constexpr int64_t kPrepareMaxN = 40960;  // one row of H must fit in LDS (160 KB
 
 struct PreparePlan {
   int64_t n = 0, n_pad = 0, nblk = 0;
-  size_t a_off = 0, m_off = 0, lam_off = 0, flag_off = 0, total = 0;
+  size_t a_off = 0, m_off = 0, lam_off = 0, flag_off = 0, x6_off = 0, total = 0;
 };
 PreparePlan plan_prepare(int64_t n);
 gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int desc_act,
@@ -106,7 +106,7 @@ constexpr int kQBlock = 128;
 struct QuantPlan {
   int64_t m = 0, n = 0, ldw = 0, groups = 0, words = 0;
   size_t wp_off = 0, part_off = 0, codes_off = 0, err_off = 0, loss_off = 0, inv_off = 0,
-         flag_off = 0, total = 0;
+         flag_off = 0, x6a_off = 0, x6b_off = 0, total = 0;
 };
 QuantPlan plan_quantize(int64_t m, int64_t n, const gptq_config& cfg);
 gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const float* U,
@@ -163,6 +163,21 @@ gptq_status run_w4a16_pack(const uint32_t* qweight, const float* scales, const i
 gptq_status run_w4a16_matmul(const uint16_t* X, int64_t tokens, int64_t ldx, const void* packed,
                              const W4Layout& L, float* Y, int64_t ldy, void* ws,
                              const W4GemmPlan& p, hipStream_t stream);
+
+// ---------------------------------------------------------------- fp32-accurate GEMM on bf16 MFMA
+// Operands as three exact bf16 planes [3][rows][kp] (plane q at p + q·pstride,
+// k contiguous); C = alpha·A·Bᵀ + beta·C, or only its lower part (row >= column).
+struct X6Planes {
+  const uint16_t* p;
+  int64_t rows, kp, pstride;
+};
+constexpr int64_t kX6K = 512;   // k extent of the trailing updates that use it
+gptq_status launch_x6_split_rows(const float* X, int64_t ldx, int64_t rows, int64_t K, int64_t kp,
+                                 uint16_t* out, int64_t pstride, hipStream_t stream);
+gptq_status launch_x6_split_cols(const float* X, int64_t ldx, int64_t K, int64_t cols, int64_t kp,
+                                 uint16_t* out, int64_t pstride, hipStream_t stream);
+gptq_status launch_x6_gemm(const X6Planes& A, const X6Planes& B, float* C, int64_t ldc, int64_t M,
+                           int64_t N, float alpha, float beta, bool lower, hipStream_t stream);
 
 // ---------------------------------------------------------------- fp32 MFMA GEMM (shared)
 // C[M,N] = alpha * A[M,K] * B[K,N] + beta * C, A row-major; B row-major or, with

@@ -414,7 +414,10 @@ PreparePlan plan_prepare(int64_t n) {
   p.m_off = mat;
   p.lam_off = 2 * mat;
   p.flag_off = p.lam_off + 256;
-  p.total = p.flag_off + 256;
+  // bf16 planes of an outer block's panel rows for its trailing update,
+  // double-buffered (the far part of one block runs beside the next block)
+  p.x6_off = p.flag_off + 256;
+  p.total = p.x6_off + align256((size_t)2 * 3 * p.n_pad * kX6K * sizeof(uint16_t));
   return p;
 }
 
@@ -457,6 +460,7 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
   // outer block from its four panels (K = 512), so the trailing matrix is read
   // and written a quarter as often.
   constexpr int64_t OB = 4 * NB;
+  static_assert(OB <= kX6K, "an outer block's panel must fit the plane width");
   SideStream side, tri, inr;
   GPTQ_TRY(get_side_stream(side, 0));
   GPTQ_TRY(get_side_stream(tri, 1));
@@ -565,29 +569,24 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
     const int64_t rest = p.n_pad - K1;
     if (rest > 0) {
       const int64_t near = std::min<int64_t>(OB, rest), far = rest - near;
+      // the panel rows L[K1:, K0:K1] as exact bf16 planes: A and B operand alike
+      const int par = (int)((K0 / OB) & 1);
+      uint16_t* pl = reinterpret_cast<uint16_t*>(w + p.x6_off) + (size_t)par * 3 * p.n_pad * kX6K;
+      const int64_t pst = p.n_pad * kX6K;
+      GPTQ_TRY(launch_x6_split_rows(A + K1 * lda + K0, lda, rest, K1 - K0, kX6K, pl, pst, stream));
       if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
       side_pending = false;
-      GemmArgs g;
-      g.A = A + K1 * lda + K0; g.lda = lda;
-      g.B = A + K1 * lda + K0; g.ldb = lda;
-      g.k_begin = 0; g.k_end = K1 - K0; g.alpha = -1.f; g.beta = 1.f;
       if (far > 0) {
         GPTQ_HIP_CHECK(hipEventRecord(side.ready, stream));
         GPTQ_HIP_CHECK(hipStreamWaitEvent(side.stream, side.ready, 0));
-        GemmArgs f = g;
-        f.A = A + (K1 + near) * lda + K0;
-        f.B = A + (K1 + near) * lda + K0;
-        f.C = A + (K1 + near) * lda + K1 + near; f.ldc = lda;
-        f.M = far; f.N = far;
-        gptq_status st = launch_gemm_lower(f, /*b_colmajor=*/true, side.stream);
-        if (st != GPTQ_OK) return st;
+        const X6Planes PF{pl + near * kX6K, far, kX6K, pst};
+        GPTQ_TRY(launch_x6_gemm(PF, PF, A + (K1 + near) * lda + K1 + near, lda, far, far, -1.f, 1.f, true,
+                                side.stream));
         GPTQ_HIP_CHECK(hipEventRecord(side.done, side.stream));
         side_pending = true;
       }
-      g.C = A + K1 * lda + K1; g.ldc = lda;
-      g.M = rest; g.N = near;
-      gptq_status st = launch_gemm_lower(g, /*b_colmajor=*/true, stream);
-      if (st != GPTQ_OK) return st;
+      const X6Planes PR{pl, rest, kX6K, pst}, PN{pl, near, kX6K, pst};
+      GPTQ_TRY(launch_x6_gemm(PR, PN, A + K1 * lda + K1, lda, rest, near, -1.f, 1.f, true, stream));
     }
   }
   if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));

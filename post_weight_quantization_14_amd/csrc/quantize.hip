@@ -174,6 +174,8 @@ __global__ void zero_f64_kernel(double* p, int64_t count) {
 
 }  // namespace
 
+static_assert(kQSuper <= kX6K, "a superblock's errors must fit the plane width");
+
 QuantPlan plan_quantize(int64_t m, int64_t n, const gptq_config& cfg) {
   QuantPlan p;
   p.m = m;
@@ -191,6 +193,10 @@ QuantPlan plan_quantize(int64_t m, int64_t n, const gptq_config& cfg) {
   p.loss_off = off; off += align256((size_t)m * sizeof(double));
   p.inv_off = off; off += align256((size_t)n * sizeof(int32_t));
   p.flag_off = off; off += 256;
+  // bf16 planes of the superblock errors and of U's rows for the trailing
+  // updates, double-buffered like the errors
+  p.x6a_off = off; off += align256((size_t)2 * 3 * m * kX6K * sizeof(uint16_t));
+  p.x6b_off = off; off += align256((size_t)2 * 3 * n * kX6K * sizeof(uint16_t));
   p.total = off;
   return p;
 }
@@ -281,29 +287,27 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
     }
     if (s2 < n) {   // W_p[:, s2:] -= Err_super · U[s1:s2, s2:]
       const int64_t near = std::min<int64_t>(kQSuper, n - s2), far = n - s2 - near;
+      // both operands as exact bf16 planes (fp32-accurate on bf16 MFMA): the
+      // errors [m][512] as rows, U[s1:s2, s2:] transposed to [n - s2][512]
+      const int par = (int)((s1 / kQSuper) & 1);
+      uint16_t* pa = reinterpret_cast<uint16_t*>(w + p.x6a_off) + (size_t)par * 3 * m * kX6K;
+      uint16_t* pb = reinterpret_cast<uint16_t*>(w + p.x6b_off) + (size_t)par * 3 * n * kX6K;
+      const int64_t K = s2 - s1;
+      GPTQ_TRY(launch_x6_split_rows(errs, kQSuper, m, K, kX6K, pa, m * kX6K, stream));
+      GPTQ_TRY(launch_x6_split_cols(U + s1 * n + s2, n, K, n - s2, kX6K, pb, n * kX6K, stream));
+      const X6Planes PA{pa, m, kX6K, m * kX6K};
       if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
       side_pending = false;
-      GemmArgs g;
-      g.A = errs; g.lda = kQSuper;
-      g.ldb = n; g.ldc = p.ldw;
-      g.M = m; g.k_begin = 0; g.k_end = s2 - s1; g.alpha = -1.f; g.beta = 1.f;
       if (far > 0) {
         GPTQ_HIP_CHECK(hipEventRecord(side.ready, stream));
         GPTQ_HIP_CHECK(hipStreamWaitEvent(side.stream, side.ready, 0));
-        GemmArgs f = g;
-        f.B = U + s1 * n + s2 + near;
-        f.C = Wp + s2 + near;
-        f.N = far;
-        gptq_status st = launch_gemm_rect(f, /*b_colmajor=*/false, side.stream);
-        if (st != GPTQ_OK) return st;
+        const X6Planes PF{pb + near * kX6K, far, kX6K, n * kX6K};
+        GPTQ_TRY(launch_x6_gemm(PA, PF, Wp + s2 + near, p.ldw, m, far, -1.f, 1.f, false, side.stream));
         GPTQ_HIP_CHECK(hipEventRecord(side.done, side.stream));
         side_pending = true;
       }
-      g.B = U + s1 * n + s2;
-      g.C = Wp + s2;
-      g.N = near;
-      gptq_status st = launch_gemm_rect(g, /*b_colmajor=*/false, stream);
-      if (st != GPTQ_OK) return st;
+      const X6Planes PN{pb, near, kX6K, n * kX6K};
+      GPTQ_TRY(launch_x6_gemm(PA, PN, Wp + s2, p.ldw, m, near, -1.f, 1.f, false, stream));
     }
   }
   if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
