@@ -33,6 +33,7 @@ constexpr int X6PLANEB = X6T * X6ROWB;
 constexpr int X6OPB = 3 * X6PLANEB;  // 12 KB per operand
 constexpr int X6SLOTB = 2 * X6OPB;   // 24 KB per stage
 constexpr int X6RING = 3;
+constexpr int kX6Band = 16;         // tile rows per band of the tile order
 
 __device__ __forceinline__ constexpr int x6_vmcnt(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
@@ -90,7 +91,53 @@ __global__ __launch_bounds__(256) void x6_split_cols_kernel(const float* __restr
   }
 }
 
-template <bool LOWER>
+// Tile order.  Workgroup b runs on XCD b mod 8 (each XCD has its own L2), so
+// XCD x is given a contiguous chunk of the order below and its resident
+// workgroups work on neighbouring tiles.  The order sweeps bands of GM tile
+// rows column by column (the band's A panels stay in L2 while B panels are
+// read by GM tiles each); for the lower part the bands cover the triangle of
+// tiles (band rows f..f+GM-1, columns up to each row's diagonal) and then the
+// full rows below it.
+template <bool LOWER, int GM>
+__host__ __device__ inline void x6_tile(int64_t b, int64_t T, int64_t M, int64_t N, int64_t& ti, int64_t& tj) {
+  const int64_t x = b % 8, q = T / 8, rr = T % 8;
+  int64_t t = x * q + (x < rr ? x : rr) + b / 8;
+  const int64_t mt = (M + X6T - 1) / X6T, nt = (N + X6T - 1) / X6T;
+  int64_t f = 0;   // first row of the current band
+  if (LOWER) {
+    // bands of the triangle: rows f..f+g-1 hold g·f + g(g+1)/2 tiles
+    for (;;) {
+      const int64_t g = nt - f < GM ? nt - f : GM;
+      if (g <= 0) break;
+      const int64_t cnt = g * f + g * (g + 1) / 2;
+      if (t < cnt) {
+        if (t < (f + 1) * g) {   // columns 0..f: all g rows
+          ti = f + t % g;
+          tj = t / g;
+          return;
+        }
+        int64_t r = t - (f + 1) * g;   // column f + c holds rows f + c..f + g - 1
+        for (int64_t c = 1;; ++c) {
+          if (r < g - c) {
+            ti = f + c + r;
+            tj = f + c;
+            return;
+          }
+          r -= g - c;
+        }
+      }
+      t -= cnt;
+      f += g;
+    }
+    // rows below the triangle: a rectangle of mt - nt full rows
+  }
+  const int64_t rows = mt - f, per = GM * nt, g0 = t / per, f1 = g0 * GM;
+  const int64_t g = rows - f1 < GM ? rows - f1 : GM, r = t % per;
+  ti = f + f1 + r % g;
+  tj = r / g;
+}
+
+template <bool LOWER, int GM>
 __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B, float* __restrict__ C,
                                                         int64_t ldc, int64_t M, int64_t N, float alpha,
                                                         float beta) {
@@ -98,26 +145,7 @@ __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   int64_t ti, tj;
-  {
-    const int64_t nt = (N + X6T - 1) / X6T;
-    const int64_t t = blockIdx.x;
-    if (LOWER) {
-      const int64_t tri = nt * (nt + 1) / 2;
-      if (t < tri) {
-        int64_t r = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
-        while (r * (r + 1) / 2 > t) --r;
-        while ((r + 1) * (r + 2) / 2 <= t) ++r;
-        ti = r;
-        tj = t - r * (r + 1) / 2;
-      } else {
-        ti = nt + (t - tri) / nt;
-        tj = (t - tri) % nt;
-      }
-    } else {
-      ti = t / nt;
-      tj = t % nt;
-    }
-  }
+  x6_tile<LOWER, GM>(blockIdx.x, gridDim.x, M, N, ti, tj);
   const int64_t i0 = ti * X6T, j0 = tj * X6T;
   const int64_t kp = A.kp;
   const int64_t nst = kp / X6KS;
@@ -263,10 +291,10 @@ gptq_status launch_x6_gemm(const X6Planes& A, const X6Planes& B, float* C, int64
       set_error("launch_x6_gemm: lower part needs M (%lld) >= N (%lld)", (long long)M, (long long)N);
       return GPTQ_ERR_INVALID_ARG;
     }
-    hipLaunchKernelGGL(x6_gemm_kernel<true>, dim3((unsigned)(nt * (nt + 1) / 2 + (mt - nt) * nt)), dim3(256),
+    hipLaunchKernelGGL((x6_gemm_kernel<true, kX6Band>), dim3((unsigned)(nt * (nt + 1) / 2 + (mt - nt) * nt)), dim3(256),
                        0, stream, A, B, C, ldc, M, N, alpha, beta);
   } else {
-    hipLaunchKernelGGL(x6_gemm_kernel<false>, dim3((unsigned)(mt * nt)), dim3(256), 0, stream, A, B, C, ldc,
+    hipLaunchKernelGGL((x6_gemm_kernel<false, kX6Band>), dim3((unsigned)(mt * nt)), dim3(256), 0, stream, A, B, C, ldc,
                        M, N, alpha, beta);
   }
   GPTQ_LAUNCH_CHECK();
