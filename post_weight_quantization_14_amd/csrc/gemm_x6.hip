@@ -34,6 +34,10 @@ constexpr int X6OPB = 3 * X6PLANEB;  // 12 KB per operand
 constexpr int X6SLOTB = 2 * X6OPB;   // 24 KB per stage
 constexpr int X6RING = 3;
 constexpr int kX6Band = 16;         // tile rows per band of the tile order
+// 73728 B static + this > 80 KB (one workgroup per CU), and <= 160 KB - 75264 B
+constexpr size_t kX6PolitePad = 12288;
+static_assert(3 * X6SLOTB + kX6PolitePad > 81920 && 3 * X6SLOTB + kX6PolitePad + 75264 <= 163840,
+              "polite footprint: one per CU, a 74 KB workgroup beside it");
 
 __device__ __forceinline__ constexpr int x6_vmcnt(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
@@ -279,22 +283,25 @@ gptq_status launch_x6_split_cols(const float* X, int64_t ldx, int64_t K, int64_t
 }
 
 gptq_status launch_x6_gemm(const X6Planes& A, const X6Planes& B, float* C, int64_t ldc, int64_t M,
-                           int64_t N, float alpha, float beta, bool lower, hipStream_t stream) {
+                           int64_t N, float alpha, float beta, bool lower, hipStream_t stream, bool polite) {
   if (M <= 0 || N <= 0) return GPTQ_OK;
   if (A.kp != B.kp || A.kp % X6KS != 0) {
     set_error("launch_x6_gemm: plane widths %lld / %lld", (long long)A.kp, (long long)B.kp);
     return GPTQ_ERR_INVALID_ARG;
   }
   const int64_t mt = ceil_div(M, X6T), nt = ceil_div(N, X6T);
+  // polite: dynamic LDS padding to more than half a CU's LDS, so one workgroup
+  // per CU and room beside it for a 74 KB workgroup of another kernel
+  const size_t pad = polite ? kX6PolitePad : 0;
   if (lower) {
     if (M < N) {
       set_error("launch_x6_gemm: lower part needs M (%lld) >= N (%lld)", (long long)M, (long long)N);
       return GPTQ_ERR_INVALID_ARG;
     }
     hipLaunchKernelGGL((x6_gemm_kernel<true, kX6Band>), dim3((unsigned)(nt * (nt + 1) / 2 + (mt - nt) * nt)), dim3(256),
-                       0, stream, A, B, C, ldc, M, N, alpha, beta);
+                       pad, stream, A, B, C, ldc, M, N, alpha, beta);
   } else {
-    hipLaunchKernelGGL((x6_gemm_kernel<false, kX6Band>), dim3((unsigned)(mt * nt)), dim3(256), 0, stream, A, B, C, ldc,
+    hipLaunchKernelGGL((x6_gemm_kernel<false, kX6Band>), dim3((unsigned)(mt * nt)), dim3(256), pad, stream, A, B, C, ldc,
                        M, N, alpha, beta);
   }
   GPTQ_LAUNCH_CHECK();

@@ -176,8 +176,11 @@ gptq_status launch_x6_split_rows(const float* X, int64_t ldx, int64_t rows, int6
                                  uint16_t* out, int64_t pstride, hipStream_t stream);
 gptq_status launch_x6_split_cols(const float* X, int64_t ldx, int64_t K, int64_t cols, int64_t kp,
                                  uint16_t* out, int64_t pstride, hipStream_t stream);
+// polite: at most one workgroup per CU, leaving LDS for a latency-bound
+// kernel of another stream (the leaf or the block quantizer) beside it.
 gptq_status launch_x6_gemm(const X6Planes& A, const X6Planes& B, float* C, int64_t ldc, int64_t M,
-                           int64_t N, float alpha, float beta, bool lower, hipStream_t stream);
+                           int64_t N, float alpha, float beta, bool lower, hipStream_t stream,
+                           bool polite = false);
 
 // ---------------------------------------------------------------- fp32 MFMA GEMM (shared)
 // C[M,N] = alpha * A[M,K] * B[K,N] + beta * C, A row-major; B row-major or, with

@@ -461,6 +461,9 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
   // and written a quarter as often.
   constexpr int64_t OB = 4 * NB;
   static_assert(OB <= kX6K, "an outer block's panel must fit the plane width");
+  // far outer updates of fewer columns run one workgroup per CU (measured
+  // crossover between the leaf chain and the far GEMM as the bottleneck)
+  constexpr int64_t kPolitePrepFar = 11000;
   SideStream side, tri, inr;
   GPTQ_TRY(get_side_stream(side, 0));
   GPTQ_TRY(get_side_stream(tri, 1));
@@ -580,8 +583,11 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
         GPTQ_HIP_CHECK(hipEventRecord(side.ready, stream));
         GPTQ_HIP_CHECK(hipStreamWaitEvent(side.stream, side.ready, 0));
         const X6Planes PF{pl + near * kX6K, far, kX6K, pst};
+        // a small far update leaves CU room for the next outer block's
+        // leaves; a large one is the bottleneck and takes the whole chip
+        const bool polite = far < kPolitePrepFar;
         GPTQ_TRY(launch_x6_gemm(PF, PF, A + (K1 + near) * lda + K1 + near, lda, far, far, -1.f, 1.f, true,
-                                side.stream));
+                                side.stream, polite));
         GPTQ_HIP_CHECK(hipEventRecord(side.done, side.stream));
         side_pending = true;
       }

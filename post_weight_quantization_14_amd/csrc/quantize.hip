@@ -175,6 +175,9 @@ __global__ void zero_f64_kernel(double* p, int64_t count) {
 }  // namespace
 
 static_assert(kQSuper <= kX6K, "a superblock's errors must fit the plane width");
+// far updates narrower than this run one workgroup per CU (measured crossover
+// between the block quantizer's chain and the far GEMM as the bottleneck)
+constexpr int64_t kQPoliteFar = 6500;
 
 QuantPlan plan_quantize(int64_t m, int64_t n, const gptq_config& cfg) {
   QuantPlan p;
@@ -302,7 +305,10 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
         GPTQ_HIP_CHECK(hipEventRecord(side.ready, stream));
         GPTQ_HIP_CHECK(hipStreamWaitEvent(side.stream, side.ready, 0));
         const X6Planes PF{pb + near * kX6K, far, kX6K, n * kX6K};
-        GPTQ_TRY(launch_x6_gemm(PA, PF, Wp + s2 + near, p.ldw, m, far, -1.f, 1.f, false, side.stream));
+        // a small far update leaves CU room for the next superblock's blocks;
+        // a large one is the stage's bottleneck and takes the whole chip
+        const bool polite = far < kQPoliteFar;
+        GPTQ_TRY(launch_x6_gemm(PA, PF, Wp + s2 + near, p.ldw, m, far, -1.f, 1.f, false, side.stream, polite));
         GPTQ_HIP_CHECK(hipEventRecord(side.done, side.stream));
         side_pending = true;
       }
