@@ -440,8 +440,12 @@ def stage_rates(spec, stages_ms):
 
 
 def gpu_clocks():
-    """Current clocks as rocm-smi reports them (best effort, a child process)."""
+    """Current clocks as rocm-smi reports them (best effort, a child process).
+    Skipped under a profiler: its preloaded library would follow the child
+    into rocm-smi's interpreter start-up."""
     import subprocess
+    if "rocprof" in os.environ.get("LD_PRELOAD", "").lower() or any(k.startswith("ROCPROF") for k in os.environ):
+        return {"skipped": "under a profiler"}
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
         rec = json.loads(r.stdout)
