@@ -131,9 +131,10 @@ __device__ __forceinline__ void gemm_tile_acc(const float* __restrict__ A, int64
 
 // C tile update.  Element (i, j) of the tile sits in lane j % 32 + 32 * ((i / 4) % 2),
 // register (i % 4) + 4 * (i / 8) of the 32 x 32 block (the MFMA output layout).
-// Per 32 x 32 block, the 16 reads of C are issued before its 16 writes:
-// interleaved, each read would wait for the store before it (same base
-// pointer), serialising one memory latency per element.
+// All 64 reads of C are issued before the first write, as unconditional loads
+// from an address inside the tile (an element outside the result reads the
+// tile's first element, C[0], and drops it): a conditional load compiles to a
+// branch with a wait of its own, one memory latency per element.
 template <bool LOWER>
 __device__ __forceinline__ void gemm_tile_store(float* __restrict__ C, int64_t ldc, int64_t c_rows,
                                                 int64_t c_cols, int64_t diag_off, float alpha,
@@ -143,24 +144,41 @@ __device__ __forceinline__ void gemm_tile_store(float* __restrict__ C, int64_t l
   const int wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int li = lane & 31, lk = lane >> 5;
+  float old[2][2][16];
+  if (beta != 0.f) {
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj) {
+        const int j = wc * 64 + bj * 32 + li;
+        const int ib = wr * 64 + bi * 32 + 4 * lk;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int i = ib + 8 * (v >> 2) + (v & 3);
+          const bool in = i < c_rows && j < c_cols && (!LOWER || i + diag_off >= j);
+          const float x = C[in ? (int64_t)i * ldc + j : 0];
+          old[bi][bj][v] = in ? x : 0.f;
+        }
+      }
+  } else {
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) old[bi][bj][v] = 0.f;
+  }
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
     for (int bj = 0; bj < 2; ++bj) {
       const int j = wc * 64 + bj * 32 + li;
       const int ib = wr * 64 + bi * 32 + 4 * lk;
-      float old[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int i = ib + 8 * (v >> 2) + (v & 3);
         const bool in = i < c_rows && j < c_cols && (!LOWER || i + diag_off >= j);
-        old[v] = (beta != 0.f && in) ? C[(int64_t)i * ldc + j] : 0.f;
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int i = ib + 8 * (v >> 2) + (v & 3);
-        const bool in = i < c_rows && j < c_cols && (!LOWER || i + diag_off >= j);
-        if (in) C[(int64_t)i * ldc + j] = alpha * acc[bi][bj][v] + beta * old[v];
+        if (in) C[(int64_t)i * ldc + j] = alpha * acc[bi][bj][v] + beta * old[bi][bj][v];
       }
     }
 }

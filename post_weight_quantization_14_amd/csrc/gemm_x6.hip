@@ -236,27 +236,49 @@ __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B,
   }
   __builtin_amdgcn_s_waitcnt(x6_vmcnt(0));
   // C tile: element (i, j) of a 32 x 32 block in lane j%32 + 32((i/4)%2),
-  // register (i%4) + 4(i/8); the 16 reads of a block before its 16 writes
+  // register (i%4) + 4(i/8).  Reads of C are unconditional loads from an
+  // address inside the tile (elements outside the result read the tile's
+  // first element and drop it), so all of them are in flight together; a
+  // conditional load would be compiled as a branch with a wait of its own.
   const int li = lane & 31, lk = lane >> 5;
   const int64_t rows = M - i0 < X6T ? M - i0 : X6T, cols = N - j0 < X6T ? N - j0 : X6T;
+  float* const ct = C + i0 * ldc + j0;
+  const bool diag = LOWER && ti == tj;   // a diagonal tile of the lower part: row >= column only
+  float old[2][2][16];
+  if (beta != 0.f) {
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj) {
+        const int j = wc * 64 + bj * 32 + li;
+        const int ib = wr * 64 + bi * 32 + 4 * lk;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int i = ib + 8 * (v >> 2) + (v & 3);
+          const bool in = i < rows && j < cols && (!diag || i >= j);
+          const float x = ct[in ? (int64_t)i * ldc + j : 0];
+          old[bi][bj][v] = in ? x : 0.f;
+        }
+      }
+  } else {
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) old[bi][bj][v] = 0.f;
+  }
 #pragma unroll
   for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
     for (int bj = 0; bj < 2; ++bj) {
       const int j = wc * 64 + bj * 32 + li;
       const int ib = wr * 64 + bi * 32 + 4 * lk;
-      float old[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int i = ib + 8 * (v >> 2) + (v & 3);
-        const bool in = i < rows && j < cols && (!LOWER || i0 + i >= j0 + j);
-        old[v] = (beta != 0.f && in) ? C[(i0 + i) * ldc + j0 + j] : 0.f;
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int i = ib + 8 * (v >> 2) + (v & 3);
-        const bool in = i < rows && j < cols && (!LOWER || i0 + i >= j0 + j);
-        if (in) C[(i0 + i) * ldc + j0 + j] = alpha * acc[bi][bj][v] + beta * old[v];
+        const bool in = i < rows && j < cols && (!diag || i >= j);
+        if (in) ct[(int64_t)i * ldc + j] = alpha * acc[bi][bj][v] + beta * old[bi][bj][v];
       }
     }
 }
