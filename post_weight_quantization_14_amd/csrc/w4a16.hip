@@ -338,60 +338,43 @@ __global__ __launch_bounds__(512) void w4_gemv_kernel(W4GemvArgs a) {
   const int cpw = (int)((a.kc + 7) / 8);
   const int c0 = wave * cpw, c1 = (int)std::min<int64_t>(a.kc, (int64_t)c0 + cpw);
   const u32x4_t* cbase = a.codes + T * a.kc * 64 + lane;
+
+  // the first batch of codes (HBM) goes out first, so that its latency and
+  // the LDS fills' below overlap; chunk indices are clamped into this wave's
+  // range (an empty range loads some other chunk and never uses it)
   u32x4_t cw[B];
 #pragma unroll
-  for (int b = 0; b < B; ++b) {
-    cw[b] = u32x4_t{0u, 0u, 0u, 0u};
-    if (c0 + b < c1) cw[b] = cbase[(int64_t)(c0 + b) * 64];
-  }
-
-  // LDS fills, four loads in flight per thread before their stores
+  for (int b = 0; b < B; ++b) cw[b] = cbase[(int64_t)std::max(0, std::min(c0 + b, c1 - 1)) * 64];
+  // LDS fills: per round, twelve loads in flight per thread (X', sums,
+  // params) before their stores.  Loads and stores are unconditional, at an
+  // index clamped into range (past the end a thread rewrites the last element
+  // with its own value): under a condition each load compiles to a branch and
+  // a wait of its own.
   {
     const int vrow = (int)(a.n128 / 8);
-    const int nv = a.tokens * vrow;
-    for (int i0 = 0; i0 < nv; i0 += 4 * 512) {
-      uint4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * 512 + tid;
-        v[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (i < nv) v[u] = *reinterpret_cast<const uint4*>(a.Xp + (int64_t)(i / vrow) * a.n128 + 8 * (i % vrow));
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * 512 + tid;
-        if (i < nv) *reinterpret_cast<uint4*>(xsh + (i / vrow) * xrow + 8 * (i % vrow)) = v[u];
-      }
-    }
-    const int ns = a.tokens * srow;
-    for (int i0 = 0; i0 < ns; i0 += 4 * 512) {
-      float v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * 512 + tid;
-        v[u] = 0.f;
-        if (i < ns) v[u] = a.xs[i];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * 512 + tid;
-        if (i < ns) ssh[i] = v[u];
-      }
-    }
-    const int np = (int)(a.Gp * kW4Rows);
+    const int nv = a.tokens * vrow;            // 16-byte pieces of X'
+    const int ns = a.tokens * srow;            // 32-sums
+    const int np = (int)(a.Gp * kW4Rows);      // (s, 128 + z) pairs of the tile
     const float2* pb = a.params + T * a.Gp * kW4Rows;
-    for (int i0 = 0; i0 < np; i0 += 4 * 512) {
-      float2 v[4];
+    const int rounds = (std::max(nv, std::max(ns, np)) + 4 * 512 - 1) / (4 * 512);
+    for (int rd = 0; rd < rounds; ++rd) {
+      const int i0 = rd * 4 * 512;
+      uint4 xv[4];
+      float sv[4];
+      float2 pv[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * 512 + tid;
-        v[u] = make_float2(0.f, 0.f);
-        if (i < np) v[u] = pb[i];
+        const int ix = std::min(i0 + u * 512 + tid, nv - 1);
+        xv[u] = *reinterpret_cast<const uint4*>(a.Xp + (int64_t)(ix / vrow) * a.n128 + 8 * (ix % vrow));
+        sv[u] = a.xs[std::min(i0 + u * 512 + tid, ns - 1)];
+        pv[u] = pb[std::min(i0 + u * 512 + tid, np - 1)];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * 512 + tid;
-        if (i < np) psh[i] = v[u];
+        const int ix = std::min(i0 + u * 512 + tid, nv - 1);
+        *reinterpret_cast<uint4*>(xsh + (ix / vrow) * xrow + 8 * (ix % vrow)) = xv[u];
+        ssh[std::min(i0 + u * 512 + tid, ns - 1)] = sv[u];
+        psh[std::min(i0 + u * 512 + tid, np - 1)] = pv[u];
       }
     }
   }
@@ -402,12 +385,9 @@ __global__ __launch_bounds__(512) void w4_gemv_kernel(W4GemvArgs a) {
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
   int fs = 4 * c0;                            // first global 32-step of the open group
   for (int cb = c0; cb < c1; cb += B) {
-    u32x4_t nx[B];
+    u32x4_t nx[B];   // the next batch (clamped: chunks past the range are loaded, not used)
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      nx[b] = u32x4_t{0u, 0u, 0u, 0u};
-      if (cb + B + b < c1) nx[b] = cbase[(int64_t)(cb + B + b) * 64];
-    }
+    for (int b = 0; b < B; ++b) nx[b] = cbase[(int64_t)std::min(cb + B + b, c1 - 1) * 64];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       const int c = cb + b;
