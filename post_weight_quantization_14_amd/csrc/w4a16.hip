@@ -138,13 +138,17 @@ __global__ __launch_bounds__(256) void w4_gather_kernel(const uint16_t* __restri
   const int64_t t = blockIdx.y;
   const int64_t p0 = (int64_t)blockIdx.x * 1024 + 4 * threadIdx.x;
   if (p0 >= n128) return;   // n128 is a multiple of 128: whole 8-thread groups leave together
-  uint16_t v[4] = {0, 0, 0, 0};
+  uint16_t v[4];
   float s = 0.f;
   const int4 o = *reinterpret_cast<const int4*>(order + p0);
   const int oi[4] = {o.x, o.y, o.z, o.w};
+  // unconditional loads (padding positions, order < 0, read column 0 and
+  // drop it): all four in flight at once instead of a branch and wait each
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (oi[e] >= 0) v[e] = X[t * ldx + oi[e]];
+  for (int e = 0; e < 4; ++e) {
+    const uint16_t x = X[t * ldx + (oi[e] >= 0 ? oi[e] : 0)];
+    v[e] = oi[e] >= 0 ? x : (uint16_t)0;
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) s += __builtin_bit_cast(float, (uint32_t)v[e] << 16);
   uint2 pk;
@@ -201,61 +205,64 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(W4GemmArgs a) {
   const int64_t T0 = (int64_t)blockIdx.x * kW4TilesPerWg;
   const int64_t g0 = GS > 0 ? C0 * 4 / GS : 0;
 
-  // every global load of the prologue is issued before the first store
+  // Every global load of the prologue is issued before the first store.  All
+  // loads and LDS stores are unconditional, at indices clamped into range (a
+  // load under a condition compiles to a branch and a wait of its own):
+  // clamped items reload and rewrite an in-range item with its own value, and
+  // tiles past the last row tile (never computed) hold the last tile's data.
   u32x4_t cw[kW4TilesPerWave][kW4MaxChunks];
 #pragma unroll
   for (int r = 0; r < kW4TilesPerWave; ++r) {
-    const int64_t T = T0 + wave * kW4TilesPerWave + r;
+    const int64_t T = std::min<int64_t>(T0 + wave * kW4TilesPerWave + r, a.mt - 1);
 #pragma unroll
-    for (int c = 0; c < kW4MaxChunks; ++c) {
-      cw[r][c] = u32x4_t{0u, 0u, 0u, 0u};
-      if (T < a.mt && c < nch) cw[r][c] = a.codes[(T * a.kc + C0 + c) * 64 + lane];
-    }
+    for (int c = 0; c < kW4MaxChunks; ++c)
+      cw[r][c] = a.codes[(T * a.kc + C0 + std::min(c, nch - 1)) * 64 + lane];
   }
+  const int npar = kW4TilesPerWg * ng * kW4Rows;
   float2 pv[PI];
 #pragma unroll
   for (int u = 0; u < PI; ++u) {
-    const int i = tid + 256 * u;
+    const int i = std::min(tid + 256 * u, npar - 1);
     const int tl = i / (ng * kW4Rows), gi = (i / kW4Rows) % ng, rr = i % kW4Rows;
-    const int64_t T = T0 + tl;
-    pv[u] = make_float2(0.f, 0.f);
-    if (tl < kW4TilesPerWg && T < a.mt) pv[u] = a.params[(T * a.Gp + g0 + gi) * kW4Rows + rr];
+    const int64_t T = std::min<int64_t>(T0 + tl, a.mt - 1);
+    pv[u] = a.params[(T * a.Gp + g0 + gi) * kW4Rows + rr];
   }
-#pragma unroll
-  for (int u = 0; u < PI; ++u) {
-    const int i = tid + 256 * u;
-    if (i < kW4TilesPerWg * ng * kW4Rows) psh[i] = pv[u];
-  }
+  // (their LDS stores go with the first X' tile's, so the code loads are not
+  // held back behind a wait for these)
 
   const int row = lane & 15, quad = lane >> 4;
   const int vec_per_row = nch * (kW4Chunk / 8);   // 16-byte pieces of a row of the slice
   const int ntt = (int)((a.tokens + kW4TokTile - 1) / kW4TokTile);
   for (int tt = 0; tt < ntt; ++tt) {
     const int64_t t0 = (int64_t)tt * kW4TokTile;
-    // X' tile: 16 rows x the slice, rows past the last token are zero
-    uint4 xv[4];
-    float sv;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = tid + 256 * u;
-      const int t = i / vec_per_row, v = i % vec_per_row;
-      xv[u] = make_uint4(0u, 0u, 0u, 0u);
-      if (i < kW4TokTile * vec_per_row && t0 + t < a.tokens)
-        xv[u] = *reinterpret_cast<const uint4*>(a.Xp + (t0 + t) * a.n128 + C0 * kW4Chunk + 8 * v);
-    }
-    {
-      const int t = tid / steps, j = tid % steps;
-      sv = 0.f;
-      if (tid < kW4TokTile * steps && t0 + t < a.tokens) sv = a.xs[(t0 + t) * (a.n128 / 32) + C0 * 4 + j];
-    }
+    // X' tile: 16 rows x the slice.  Rows past the last token repeat the last
+    // token (their outputs are never written); loads and stores at clamped
+    // indices, unconditional, as above.
+    const int nxv = kW4TokTile * vec_per_row, nsv = kW4TokTile * steps;
+    // four named loads (an array here stays in scratch memory)
+    auto xidx = [&](int u) { return std::min(tid + 256 * u, nxv - 1); };
+    auto xload = [&](int u) {
+      const int i = xidx(u);
+      const int64_t t = std::min<int64_t>(t0 + i / vec_per_row, a.tokens - 1);
+      return *reinterpret_cast<const uint4*>(a.Xp + t * a.n128 + C0 * kW4Chunk + 8 * (i % vec_per_row));
+    };
+    auto xstore = [&](int u, const uint4& v) {
+      const int i = xidx(u);
+      *reinterpret_cast<uint4*>(xsh + (i / vec_per_row) * RS + 8 * (i % vec_per_row)) = v;
+    };
+    const uint4 x0 = xload(0), x1 = xload(1), x2 = xload(2), x3 = xload(3);
+    const int si = std::min(tid, nsv - 1);
+    const float sv = a.xs[std::min<int64_t>(t0 + si / steps, a.tokens - 1) * (a.n128 / 32) + C0 * 4 + si % steps];
     if (tt > 0) __syncthreads();   // the previous tile is consumed
+    if (tt == 0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = tid + 256 * u;
-      if (i < kW4TokTile * vec_per_row)
-        *reinterpret_cast<uint4*>(xsh + (i / vec_per_row) * RS + 8 * (i % vec_per_row)) = xv[u];
+      for (int u = 0; u < PI; ++u) psh[std::min(tid + 256 * u, npar - 1)] = pv[u];
     }
-    if (tid < kW4TokTile * steps) ssh[(tid / steps) * SS + tid % steps] = sv;
+    xstore(0, x0);
+    xstore(1, x1);
+    xstore(2, x2);
+    xstore(3, x3);
+    ssh[(si / steps) * SS + si % steps] = sv;
     __syncthreads();
 
 #pragma unroll
