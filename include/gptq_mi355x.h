@@ -10,11 +10,18 @@
  *
  * Conventions shared by every call:
  *   - All tensor pointers are DEVICE memory owned by the caller (allocated
- *     through PyTorch or hipMalloc).  The library keeps no allocation and no
- *     global state besides a thread-local error message.
+ *     through PyTorch or hipMalloc).  The library allocates no device memory;
+ *     its only state is a thread-local error message and, for
+ *     gptq_prepare_hinv and gptq_quantize_layer, up to three extra HIP
+ *     streams (default priority) with their events per host thread and
+ *     device, created on first use and kept until the process ends.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
  *     on it in order; calls return after enqueueing, except where a call says
- *     it synchronises.
+ *     it synchronises.  Work a call puts on its extra streams is ordered
+ *     after what `stream` held at the call and before anything enqueued on
+ *     `stream` after it (events), so to the caller it is one stream-ordered
+ *     operation.  Concurrent calls from one host thread on different
+ *     streams share those extra streams and are serialised by them.
  *   - Argument errors are detected on the host and returned before anything
  *     is launched.  A failed HIP launch or copy returns GPTQ_ERR_HIP.
  *   - Matrices are row-major.  n = in_features (columns of W, size of H),
