@@ -46,6 +46,10 @@ struct BqCtx {
   f32x4_t u0, u1;  // U[c][8j .. 8j+7] of the current column c (prefetched one step ahead)
   float ud;        // U[c][c]
   float s, z, lacc;
+  // branch-free code: clamp(rint(fl(w/s) + zpre), qlo, qhi) + post, with
+  // zpre = z, post = 0 (asym) or zpre = 0, post = z (sym): the same roundings
+  // as quant_code, no branch on sym in the column chain
+  float zpre, post, qlo, qhi;
   int bits, sym, bw, j;
   bool act;
   float* srow;
@@ -77,6 +81,8 @@ __device__ __forceinline__ void bq_col(BqCtx& x) {
       am = fmaxf(am, __shfl_xor(am, d, 16));
     }
     grid_params(lo, hi, am, x.bits, x.sym, x.s, x.z);
+    x.zpre = x.sym ? 0.f : x.z;
+    x.post = x.sym ? x.z : 0.f;
     if (x.act && x.j == 0) {
       const int64_t g = (x.g_base + C) / GW;
       x.srow[g] = x.s;
@@ -89,7 +95,7 @@ __device__ __forceinline__ void bq_col(BqCtx& x) {
   const f32x4_t n1 = *reinterpret_cast<const f32x4_t*>(x.us + CN * QB + 8 * x.j + 4);
   const float nd = x.us[CN * QB + CN];
   const float v = row_bcast<J>(x.w[P]);
-  const float code = quant_code(v, x.s, x.z, x.bits, x.sym);
+  const float code = fminf(fmaxf(rintf(v / x.s + x.zpre), x.qlo), x.qhi) + x.post;
   const float e = (v - (code - x.z) * x.s) / x.ud;
   if (x.j == J) {
     x.e8[P] = e;
@@ -202,6 +208,10 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs q, const float* 
     x.s = q.scales[rr * q.G];
     x.z = (float)q.zeros[rr * q.G];
   }
+  x.qlo = q.sym ? -(float)((1 << (q.bits - 1)) - 1) : 0.f;
+  x.qhi = q.sym ? (float)((1 << (q.bits - 1)) - 1) : (float)((1 << q.bits) - 1);
+  x.zpre = q.sym ? 0.f : x.z;
+  x.post = q.sym ? x.z : 0.f;
   x.lacc = 0.f;
   x.srow = q.scales + rr * q.G;
   x.zrow = q.zeros + rr * q.G;
