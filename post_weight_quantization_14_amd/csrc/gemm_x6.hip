@@ -102,11 +102,11 @@ __global__ __launch_bounds__(256) void x6_split_cols_kernel(const float* __restr
 // read by GM tiles each); for the lower part the bands cover the triangle of
 // tiles (band rows f..f+GM-1, columns up to each row's diagonal) and then the
 // full rows below it.
-template <bool LOWER, int GM>
+template <bool LOWER, int GM, int TM = X6T>
 __host__ __device__ inline void x6_tile(int64_t b, int64_t T, int64_t M, int64_t N, int64_t& ti, int64_t& tj) {
   const int64_t x = b % 8, q = T / 8, rr = T % 8;
   int64_t t = x * q + (x < rr ? x : rr) + b / 8;
-  const int64_t mt = (M + X6T - 1) / X6T, nt = (N + X6T - 1) / X6T;
+  const int64_t mt = (M + TM - 1) / TM, nt = (N + X6T - 1) / X6T;
   int64_t f = 0;   // first row of the current band
   if (LOWER) {
     // bands of the triangle: rows f..f+g-1 hold g·f + g(g+1)/2 tiles
@@ -141,7 +141,9 @@ __host__ __device__ inline void x6_tile(int64_t b, int64_t T, int64_t M, int64_t
   tj = r / g;
 }
 
-template <bool LOWER, int GM>
+// TM: rows of C per tile, 128 or (full product only) 64 for products of few
+// tiles; the waves then hold one 32-row block each instead of two.
+template <bool LOWER, int GM, int TM>
 __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B, float* __restrict__ C,
                                                         int64_t ldc, int64_t M, int64_t N, float alpha,
                                                         float beta) {
@@ -149,8 +151,10 @@ __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   int64_t ti, tj;
-  x6_tile<LOWER, GM>(blockIdx.x, gridDim.x, M, N, ti, tj);
-  const int64_t i0 = ti * X6T, j0 = tj * X6T;
+  static_assert(TM == X6T || (TM == 64 && !LOWER), "64-row tiles for the full product only");
+  constexpr int BI = TM / 64;   // 32-row blocks per wave
+  x6_tile<LOWER, GM, TM>(blockIdx.x, gridDim.x, M, N, ti, tj);
+  const int64_t i0 = ti * TM, j0 = tj * X6T;
   const int64_t kp = A.kp;
   const int64_t nst = kp / X6KS;
   // 24 copy instructions per stage = (operand, plane, row quarter); wave w
@@ -171,7 +175,8 @@ __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B,
     const int64_t grow = (op == 0 ? i0 : j0) + row;
     obase[u] = P.p + (int64_t)plane * P.pstride;
     obytes[u] = P.rows * kp * 2;
-    voff[u] = grow < P.rows ? (int32_t)(grow * kp * 2 + cs * 16) : kOut;
+    // A rows past the tile (TM = 64) read as zero like rows past the operand
+    voff[u] = (grow < P.rows && (op != 0 || row < TM)) ? (int32_t)(grow * kp * 2 + cs * 16) : kOut;
     ldso[u] = op * X6OPB + plane * X6PLANEB + q * 1024;
   }
   auto issue = [&](int64_t st, uint8_t* slot) {
@@ -184,9 +189,9 @@ __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B,
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(slot + ldso[u]), 16, voff[u], 0, 0, 0);
     }
   };
-  f32x16 acc[2][2];
+  f32x16 acc[BI][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < BI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -197,16 +202,16 @@ __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B,
     return *reinterpret_cast<const bf16x8_t*>(slot + op * X6OPB + plane * X6PLANEB + row * X6ROWB + c * 16);
   };
   auto compute = [&](const uint8_t* slot, int64_t st, uint8_t* refill) {
-    bf16x8_t fa[2][3], fb[2][3];
+    bf16x8_t fa[BI][3], fb[2][3];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int p = 0; p < 3; ++p) {
 #pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        fa[i][p] = frag(slot, 0, p, wr * 64 + i * 32);
-        fb[i][p] = frag(slot, 1, p, wc * 64 + i * 32);
-      }
+      for (int i = 0; i < BI; ++i) fa[i][p] = frag(slot, 0, p, wr * (TM / 2) + i * 32);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i) fb[i][p] = frag(slot, 1, p, wc * 64 + i * 32);
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         // smallest terms first: lo·hi, hi·lo, mid·mid, mid·hi, hi·mid, hi·hi
@@ -241,17 +246,17 @@ __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B,
   // first element and drop it), so all of them are in flight together; a
   // conditional load would be compiled as a branch with a wait of its own.
   const int li = lane & 31, lk = lane >> 5;
-  const int64_t rows = M - i0 < X6T ? M - i0 : X6T, cols = N - j0 < X6T ? N - j0 : X6T;
+  const int64_t rows = M - i0 < TM ? M - i0 : TM, cols = N - j0 < X6T ? N - j0 : X6T;
   float* const ct = C + i0 * ldc + j0;
   const bool diag = LOWER && ti == tj;   // a diagonal tile of the lower part: row >= column only
-  float old[2][2][16];
+  float old[BI][2][16];
   if (beta != 0.f) {
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+    for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
       for (int bj = 0; bj < 2; ++bj) {
         const int j = wc * 64 + bj * 32 + li;
-        const int ib = wr * 64 + bi * 32 + 4 * lk;
+        const int ib = wr * (TM / 2) + bi * 32 + 4 * lk;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int i = ib + 8 * (v >> 2) + (v & 3);
@@ -262,18 +267,18 @@ __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B,
       }
   } else {
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+    for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
       for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
         for (int v = 0; v < 16; ++v) old[bi][bj][v] = 0.f;
   }
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
+  for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
     for (int bj = 0; bj < 2; ++bj) {
       const int j = wc * 64 + bj * 32 + li;
-      const int ib = wr * 64 + bi * 32 + 4 * lk;
+      const int ib = wr * (TM / 2) + bi * 32 + 4 * lk;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int i = ib + 8 * (v >> 2) + (v & 3);
@@ -305,7 +310,8 @@ gptq_status launch_x6_split_cols(const float* X, int64_t ldx, int64_t K, int64_t
 }
 
 gptq_status launch_x6_gemm(const X6Planes& A, const X6Planes& B, float* C, int64_t ldc, int64_t M,
-                           int64_t N, float alpha, float beta, bool lower, hipStream_t stream, bool polite) {
+                           int64_t N, float alpha, float beta, bool lower, hipStream_t stream, bool polite,
+                           int tile_rows) {
   if (M <= 0 || N <= 0) return GPTQ_OK;
   if (A.kp != B.kp || A.kp % X6KS != 0) {
     set_error("launch_x6_gemm: plane widths %lld / %lld", (long long)A.kp, (long long)B.kp);
@@ -315,16 +321,23 @@ gptq_status launch_x6_gemm(const X6Planes& A, const X6Planes& B, float* C, int64
   // polite: dynamic LDS padding to more than half a CU's LDS, so one workgroup
   // per CU and room beside it for a 74 KB workgroup of another kernel
   const size_t pad = polite ? kX6PolitePad : 0;
+  if (tile_rows != X6T && (tile_rows != 64 || lower)) {
+    set_error("launch_x6_gemm: tile_rows %d (128, or 64 for a full product)", tile_rows);
+    return GPTQ_ERR_INVALID_ARG;
+  }
   if (lower) {
     if (M < N) {
       set_error("launch_x6_gemm: lower part needs M (%lld) >= N (%lld)", (long long)M, (long long)N);
       return GPTQ_ERR_INVALID_ARG;
     }
-    hipLaunchKernelGGL((x6_gemm_kernel<true, kX6Band>), dim3((unsigned)(nt * (nt + 1) / 2 + (mt - nt) * nt)), dim3(256),
-                       pad, stream, A, B, C, ldc, M, N, alpha, beta);
+    hipLaunchKernelGGL((x6_gemm_kernel<true, kX6Band, X6T>), dim3((unsigned)(nt * (nt + 1) / 2 + (mt - nt) * nt)),
+                       dim3(256), pad, stream, A, B, C, ldc, M, N, alpha, beta);
+  } else if (tile_rows == 64) {
+    hipLaunchKernelGGL((x6_gemm_kernel<false, kX6Band, 64>), dim3((unsigned)(ceil_div(M, 64) * nt)), dim3(256), pad,
+                       stream, A, B, C, ldc, M, N, alpha, beta);
   } else {
-    hipLaunchKernelGGL((x6_gemm_kernel<false, kX6Band>), dim3((unsigned)(mt * nt)), dim3(256), pad, stream, A, B, C, ldc,
-                       M, N, alpha, beta);
+    hipLaunchKernelGGL((x6_gemm_kernel<false, kX6Band, X6T>), dim3((unsigned)(mt * nt)), dim3(256), pad, stream, A,
+                       B, C, ldc, M, N, alpha, beta);
   }
   GPTQ_LAUNCH_CHECK();
   return GPTQ_OK;

@@ -178,9 +178,10 @@ gptq_status launch_x6_split_cols(const float* X, int64_t ldx, int64_t K, int64_t
                                  uint16_t* out, int64_t pstride, hipStream_t stream);
 // polite: at most one workgroup per CU, leaving LDS for a latency-bound
 // kernel of another stream (the leaf or the block quantizer) beside it.
+// tile_rows: 128, or 64 (full product only) for products of few tiles.
 gptq_status launch_x6_gemm(const X6Planes& A, const X6Planes& B, float* C, int64_t ldc, int64_t M,
                            int64_t N, float alpha, float beta, bool lower, hipStream_t stream,
-                           bool polite = false);
+                           bool polite = false, int tile_rows = 128);
 
 // ---------------------------------------------------------------- fp32 MFMA GEMM (shared)
 // C[M,N] = alpha * A[M,K] * B[K,N] + beta * C, A row-major; B row-major or, with

@@ -313,7 +313,9 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
         side_pending = true;
       }
       const X6Planes PN{pb, near, kX6K, n * kX6K};
-      GPTQ_TRY(launch_x6_gemm(PA, PN, Wp + s2, p.ldw, m, near, -1.f, 1.f, false, stream));
+      // on the chain: with fewer 128-row tiles than CUs, 64-row tiles
+      const int near_rows = ceil_div(m, 128) * ceil_div(near, 128) < 256 ? 64 : 128;
+      GPTQ_TRY(launch_x6_gemm(PA, PN, Wp + s2, p.ldw, m, near, -1.f, 1.f, false, stream, false, near_rows));
     }
   }
   if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
