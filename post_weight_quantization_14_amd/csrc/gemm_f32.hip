@@ -53,11 +53,14 @@ __device__ __forceinline__ f32x4_t load4(const float* __restrict__ base, int64_t
 //   A: tile row 0, k = 0 of a row-major [rows x K] operand (lda); rows < a_rows valid.
 //   B: row-major -> points at k = 0, tile column 0 (ldb); column-major -> points at
 //      tile column 0, k = 0 with B[k][j] = B[j * ldb + k].  Columns < b_cols valid.
-template <bool BCOL, bool VEC>
+// TM = rows of the tile: 128, or 64 (each wave then holds one 32-row block;
+// A rows 64..127 load as zero and are never multiplied).
+template <bool BCOL, bool VEC, int TM = GT>
 __device__ __forceinline__ void gemm_tile_acc(const float* __restrict__ A, int64_t lda,
                                               int64_t a_rows, const float* __restrict__ B,
                                               int64_t ldb, int64_t b_cols, int64_t k_begin,
-                                              int64_t k_end, GemmSmem& sm, f32x16_t (&acc)[2][2]) {
+                                              int64_t k_end, GemmSmem& sm, f32x16_t (&acc)[TM / 64][2]) {
+  constexpr int BI = TM / 64;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -65,7 +68,7 @@ __device__ __forceinline__ void gemm_tile_acc(const float* __restrict__ A, int64
   const int li = lane & 31, lk = lane >> 5;
 
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
+  for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
     for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
@@ -112,14 +115,14 @@ __device__ __forceinline__ void gemm_tile_acc(const float* __restrict__ A, int64
 #pragma unroll
     for (int kk = 0; kk < GK / 2; ++kk) {
       const int k = 2 * kk + lk;
-      float af[2], bf[2];
+      float af[BI], bf[2];
 #pragma unroll
-      for (int bi = 0; bi < 2; ++bi) af[bi] = sa[(wr * 64 + bi * 32 + li) * PA + k];
+      for (int bi = 0; bi < BI; ++bi) af[bi] = sa[(wr * (TM / 2) + bi * 32 + li) * PA + k];
 #pragma unroll
       for (int bj = 0; bj < 2; ++bj)
         bf[bj] = BCOL ? sb[(wc * 64 + bj * 32 + li) * PA + k] : sb[k * PB + wc * 64 + bj * 32 + li];
 #pragma unroll
-      for (int bi = 0; bi < 2; ++bi)
+      for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
         for (int bj = 0; bj < 2; ++bj)
           acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[bi], bf[bj], acc[bi][bj], 0, 0, 0);
@@ -135,23 +138,24 @@ __device__ __forceinline__ void gemm_tile_acc(const float* __restrict__ A, int64
 // from an address inside the tile (an element outside the result reads the
 // tile's first element, C[0], and drops it): a conditional load compiles to a
 // branch with a wait of its own, one memory latency per element.
-template <bool LOWER>
+template <bool LOWER, int TM = GT>
 __device__ __forceinline__ void gemm_tile_store(float* __restrict__ C, int64_t ldc, int64_t c_rows,
                                                 int64_t c_cols, int64_t diag_off, float alpha,
-                                                float beta, const f32x16_t (&acc)[2][2]) {
+                                                float beta, const f32x16_t (&acc)[TM / 64][2]) {
+  constexpr int BI = TM / 64;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int li = lane & 31, lk = lane >> 5;
-  float old[2][2][16];
+  float old[BI][2][16];
   if (beta != 0.f) {
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+    for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
       for (int bj = 0; bj < 2; ++bj) {
         const int j = wc * 64 + bj * 32 + li;
-        const int ib = wr * 64 + bi * 32 + 4 * lk;
+        const int ib = wr * (TM / 2) + bi * 32 + 4 * lk;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int i = ib + 8 * (v >> 2) + (v & 3);
@@ -162,18 +166,18 @@ __device__ __forceinline__ void gemm_tile_store(float* __restrict__ C, int64_t l
       }
   } else {
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+    for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
       for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
         for (int v = 0; v < 16; ++v) old[bi][bj][v] = 0.f;
   }
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
+  for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
     for (int bj = 0; bj < 2; ++bj) {
       const int j = wc * 64 + bj * 32 + li;
-      const int ib = wr * 64 + bi * 32 + 4 * lk;
+      const int ib = wr * (TM / 2) + bi * 32 + 4 * lk;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int i = ib + 8 * (v >> 2) + (v & 3);
@@ -183,17 +187,17 @@ __device__ __forceinline__ void gemm_tile_store(float* __restrict__ C, int64_t l
     }
 }
 
-template <bool BCOL, bool VEC>
+template <bool BCOL, bool VEC, int TM = GT>
 __global__ __launch_bounds__(256) void gemm_rect_kernel(GemmArgs g) {
   __shared__ GemmSmem sm;
-  const int64_t i0 = (int64_t)blockIdx.y * GT, j0 = (int64_t)blockIdx.x * GT;
+  const int64_t i0 = (int64_t)blockIdx.y * TM, j0 = (int64_t)blockIdx.x * GT;
   const float* A = g.A + i0 * g.lda;
   const float* B = BCOL ? g.B + j0 * g.ldb : g.B + j0;
-  f32x16_t acc[2][2];
-  const int64_t rows = g.M - i0 < GT ? g.M - i0 : GT;
+  f32x16_t acc[TM / 64][2];
+  const int64_t rows = g.M - i0 < TM ? g.M - i0 : TM;
   const int64_t cols = g.N - j0 < GT ? g.N - j0 : GT;
-  gemm_tile_acc<BCOL, VEC>(A, g.lda, rows, B, g.ldb, cols, g.k_begin, g.k_end, sm, acc);
-  gemm_tile_store<false>(g.C + i0 * g.ldc + j0, g.ldc, rows, cols, 0, g.alpha, g.beta, acc);
+  gemm_tile_acc<BCOL, VEC, TM>(A, g.lda, rows, B, g.ldb, cols, g.k_begin, g.k_end, sm, acc);
+  gemm_tile_store<false, TM>(g.C + i0 * g.ldc + j0, g.ldc, rows, cols, 0, g.alpha, g.beta, acc);
 }
 
 __device__ __forceinline__ void tri_decode(int64_t t, int64_t& ti, int64_t& tj) {
@@ -296,10 +300,21 @@ bool vec_ok(const GemmArgs& g, bool bcol) {
 
 }  // namespace
 
-gptq_status launch_gemm_rect(const GemmArgs& g, bool b_colmajor, hipStream_t stream) {
+gptq_status launch_gemm_rect(const GemmArgs& g, bool b_colmajor, hipStream_t stream, int tile_rows) {
   if (g.M <= 0 || g.N <= 0) return GPTQ_OK;
-  dim3 grid((unsigned)ceil_div(g.N, GT), (unsigned)ceil_div(g.M, GT));
+  if (tile_rows != GT && (tile_rows != 64 || !b_colmajor)) {
+    set_error("launch_gemm_rect: tile_rows %d (128, or 64 with a column-major B)", tile_rows);
+    return GPTQ_ERR_INVALID_ARG;
+  }
   const bool v = vec_ok(g, b_colmajor);
+  if (tile_rows == 64) {
+    dim3 grid64((unsigned)ceil_div(g.N, GT), (unsigned)ceil_div(g.M, 64));
+    if (v) hipLaunchKernelGGL((gemm_rect_kernel<true, true, 64>), grid64, dim3(256), 0, stream, g);
+    else hipLaunchKernelGGL((gemm_rect_kernel<true, false, 64>), grid64, dim3(256), 0, stream, g);
+    GPTQ_LAUNCH_CHECK();
+    return GPTQ_OK;
+  }
+  dim3 grid((unsigned)ceil_div(g.N, GT), (unsigned)ceil_div(g.M, GT));
   if (b_colmajor) {
     if (v) hipLaunchKernelGGL((gemm_rect_kernel<true, true>), grid, dim3(256), 0, stream, g);
     else hipLaunchKernelGGL((gemm_rect_kernel<true, false>), grid, dim3(256), 0, stream, g);

@@ -194,7 +194,8 @@ struct GemmArgs {
   int64_t k_begin, k_end;
   float alpha, beta;
 };
-gptq_status launch_gemm_rect(const GemmArgs& g, bool b_colmajor, hipStream_t stream);
+// tile_rows: 128, or 64 (column-major B only) for products of few row tiles.
+gptq_status launch_gemm_rect(const GemmArgs& g, bool b_colmajor, hipStream_t stream, int tile_rows = 128);
 // Lower part only (element row >= column) of an M x N result, M >= N: the
 // trailing updates of the blocked Cholesky (a triangle, or a triangle over a
 // rectangle of full tiles).

@@ -531,7 +531,8 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
       g.B = Mm + k0 * lda + k0; g.ldb = lda;
       g.C = A + (k0 + NB) * lda + k0; g.ldc = lda;
       g.M = rows; g.N = NB; g.k_begin = 0; g.k_end = NB; g.alpha = 1.f; g.beta = 0.f;
-      GPTQ_TRY(launch_gemm_rect(g, /*b_colmajor=*/true, stream));
+      // on the chain: with fewer than 128 row tiles of 128, tiles of 64 rows
+      GPTQ_TRY(launch_gemm_rect(g, /*b_colmajor=*/true, stream, ceil_div(rows, NB) < 128 ? 64 : NB));
       GPTQ_HIP_CHECK(hipEventRecord(inr.ready, stream));
       GPTQ_TRY(issue_trtri(k0 / NB, inr.ready));
       // inner update: A[k0+NB:, k0+NB:K1] -= P · P[k0+NB:K1]ᵀ (lower part); its
