@@ -469,7 +469,6 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
   GPTQ_TRY(get_side_stream(tri, 1));
   GPTQ_TRY(get_side_stream(inr, 2));
   bool side_pending = false, tri_pending = false, inr_pending = false;
-  bool lower_pending[2] = {false, false};   // by panel parity
   // Triangular inverse, overlapped with the factorisation.  A node of the
   // bottom-up doubling joins blocks [l0, r0) and [r0, r1): its step 1
   // (T = L21·M11) needs L rows [r0, r1) of columns [l0, r0), final once panel
@@ -503,17 +502,14 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
   // the next leaf itself, which follows the panel solve at once; the rest of
   // the next panel's columns ("rect") and the block's columns after it
   // ("lower") run on the inner side stream beside that leaf.  The next panel
-  // solve waits only for rect (it rewrites those rows); lower covers the
-  // diagonal block of panel k + 2, whose leaf waits for it (events by panel
-  // parity).  Concurrent kernels always touch disjoint parts of A.
+  // solve waits for both (rect rewrites its rows; lower covers the diagonal
+  // block of panel k + 2, whose leaf comes after that solve on this stream),
+  // one event for the two.  Concurrent kernels always touch disjoint parts of A.
   for (int64_t K0 = 0; K0 < p.n_pad; K0 += OB) {
     const int64_t K1 = std::min<int64_t>(K0 + OB, p.n_pad);
     for (int64_t k0 = K0; k0 < K1; k0 += NB) {
       // inside an outer block, the leaf applies the previous panel's update to
       // its own diagonal block (the rows below get it on the inner stream)
-      const int par = (int)((k0 / NB) & 1);
-      if (lower_pending[par]) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, inr.aux[par], 0));
-      lower_pending[par] = false;
       hipLaunchKernelGGL(chol_leaf_kernel, dim3(1), dim3(kLeafThreads), 0, stream, A, Mm, lda, k0,
                          (int)(k0 > K0), flag);
       GPTQ_LAUNCH_CHECK();
@@ -551,17 +547,16 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
         r.C = A + (k0 + 2 * NB) * lda + k0 + NB; r.ldc = lda;
         r.M = rows - NB; r.N = NB; r.k_begin = 0; r.k_end = NB; r.alpha = -1.f; r.beta = 1.f;
         GPTQ_TRY(launch_gemm_rect(r, /*b_colmajor=*/true, inr.stream));
-        GPTQ_HIP_CHECK(hipEventRecord(inr.done, inr.stream));
-        inr_pending = true;
         if (cols > NB) {
           r.B = P;
           r.C = A + (k0 + 2 * NB) * lda + k0 + 2 * NB;
           r.N = cols - NB;
           GPTQ_TRY(launch_gemm_lower(r, /*b_colmajor=*/true, inr.stream));
-          const int par = (int)((k0 / NB) & 1);   // = parity of panel k + 2
-          GPTQ_HIP_CHECK(hipEventRecord(inr.aux[par], inr.stream));
-          lower_pending[par] = true;
         }
+        // one event for both: the next panel solve waits for it, and the leaf
+        // of panel k + 2 (which needs lower) follows that solve here
+        GPTQ_HIP_CHECK(hipEventRecord(inr.done, inr.stream));
+        inr_pending = true;
       }
     }
     // outer update: A[K1:, K1:] -= L[K1:, K0:K1] · L[K1:, K0:K1]ᵀ (lower part),
@@ -598,8 +593,6 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
   }
   if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
   if (inr_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, inr.done, 0));
-  for (int q = 0; q < 2; ++q)
-    if (lower_pending[q]) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, inr.aux[q], 0));
   if (tri_pending) {
     GPTQ_HIP_CHECK(hipEventRecord(tri.done, tri.stream));
     GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, tri.done, 0));
