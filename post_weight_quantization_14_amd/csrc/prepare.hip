@@ -121,16 +121,32 @@ __global__ __launch_bounds__(256) void permute_kernel(const float* __restrict__ 
   }
   const int64_t src = perm[n - 1 - a];
   const float* h = H + src * n;
-  for (int64_t b = threadIdx.x; b < n; b += 256) row[b] = h[b];
+  // four loads per thread in flight (unconditional, at clamped indices; a
+  // conditional load compiles to a branch and a wait of its own)
+  for (int64_t b0 = threadIdx.x; b0 < n; b0 += 4 * 256) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = h[std::min<int64_t>(b0 + 256 * u, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) row[std::min<int64_t>(b0 + 256 * u, n - 1)] = v[u];
+  }
   __syncthreads();
   const float l = (float)*lam;
-  for (int64_t b = threadIdx.x; b < lda; b += 256) {
-    float v = 0.f;
-    if (b < n) {
-      v = row[perm[n - 1 - b]];
-      if (b == a) v += l;
+  for (int64_t b0 = threadIdx.x; b0 < lda; b0 += 4 * 256) {
+    int32_t pi[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pi[u] = perm[n - 1 - std::min<int64_t>(b0 + 256 * u, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t b = b0 + 256 * u;
+      if (b >= lda) break;
+      float v = 0.f;
+      if (b < n) {
+        v = row[pi[u]];
+        if (b == a) v += l;
+      }
+      out[b] = v;
     }
-    out[b] = v;
   }
 }
 
