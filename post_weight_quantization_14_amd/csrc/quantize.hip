@@ -45,16 +45,32 @@ __global__ __launch_bounds__(256) void qprep_kernel(const T* __restrict__ W, int
   const int64_t r = blockIdx.x;
   if (threadIdx.x == 0) bad = 0;
   __syncthreads();
+  // four loads per thread in flight (unconditional, at clamped indices; a
+  // conditional load compiles to a branch and a wait of its own)
   int b = 0;
-  for (int64_t j = threadIdx.x; j < n; j += 256) {
-    const float x = to_f32<T>(W[r * n + j]);
-    if (!isfinite(x)) b = 1;
-    row[j] = x;
+  for (int64_t j0 = threadIdx.x; j0 < n; j0 += 4 * 256) {
+    float x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = to_f32<T>(W[r * n + std::min<int64_t>(j0 + 256 * u, n - 1)]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (!isfinite(x[u])) b = 1;
+      row[std::min<int64_t>(j0 + 256 * u, n - 1)] = x[u];
+    }
   }
   if (b) atomicOr(&bad, 1);
   __syncthreads();
   if (threadIdx.x == 0 && bad) atomicOr(flag, kFlagNonFinite);
-  for (int64_t p = threadIdx.x; p < ldw; p += 256) Wp[r * ldw + p] = (p < n) ? row[perm[p]] : 0.f;
+  for (int64_t p0 = threadIdx.x; p0 < ldw; p0 += 4 * 256) {
+    int32_t pi[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pi[u] = perm[std::min<int64_t>(p0 + 256 * u, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t p = p0 + 256 * u;
+      if (p < ldw) Wp[r * ldw + p] = (p < n) ? row[pi[u]] : 0.f;
+    }
+  }
 }
 
 // One group per row (group_size = -1): grid from the whole original row.
