@@ -78,9 +78,18 @@ __global__ __launch_bounds__(256) void x6_split_cols_kernel(const float* __restr
   __shared__ float t[64][65];
   const int64_t c0 = (int64_t)blockIdx.x * 64, k0 = (int64_t)blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) {
-    const int64_t k = k0 + r, c = c0 + tx;
-    t[r][tx] = (k < K && c < cols) ? X[k * ldx + c] : 0.f;
+  // all sixteen loads in flight: unconditional at clamped indices (a
+  // conditional load compiles to a branch and a wait of its own)
+  float v[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int64_t k = k0 + ty + 4 * u, c = c0 + tx;
+    v[u] = X[std::min<int64_t>(k, K - 1) * ldx + std::min<int64_t>(c, cols - 1)];
+  }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int r = ty + 4 * u;
+    t[r][tx] = (k0 + r < K && c0 + tx < cols) ? v[u] : 0.f;
   }
   __syncthreads();
   for (int r = ty; r < 64; r += 4) {
@@ -303,6 +312,10 @@ gptq_status launch_x6_split_rows(const float* X, int64_t ldx, int64_t rows, int6
 gptq_status launch_x6_split_cols(const float* X, int64_t ldx, int64_t K, int64_t cols, int64_t kp,
                                  uint16_t* out, int64_t pstride, hipStream_t stream) {
   if (cols <= 0) return GPTQ_OK;
+  if (K <= 0 || K > kp) {   // the kernel reads rows up to min(k, K - 1)
+    set_error("launch_x6_split_cols: K = %lld (1 .. %lld)", (long long)K, (long long)kp);
+    return GPTQ_ERR_INVALID_ARG;
+  }
   hipLaunchKernelGGL(x6_split_cols_kernel, dim3((unsigned)ceil_div(cols, 64), (unsigned)ceil_div(kp, 64)),
                      dim3(256), 0, stream, X, ldx, K, cols, kp, out, pstride);
   GPTQ_LAUNCH_CHECK();
