@@ -21,6 +21,7 @@ from .gptq_oracle import (  # noqa: F401
     group_params,
     hessian,
     hessian_accumulate,
+    hessian_diagonal_accumulate,
     inverse_upper_factor,
     loss_terms,
     pack_codes,

@@ -23,7 +23,7 @@ It is written step by step from these web pages (cited by title and section):
   [P1] "Qwen2.5模型GPTQ量化精度损失实测" (m.cn486.com): act-order reorders
        weights.
 
-Everything else is float64.  Inputs arrive as the exact bytes the GPU consumed
+Everything is float64.  Inputs arrive as the exact bytes the GPU consumed
 (bf16 / fp32, converted exactly to float64).
 
 Readings taken where the pages are silent, garbled or contradict each other
@@ -44,15 +44,20 @@ Readings taken where the pages are silent, garbled or contradict each other
   * rounding is round-half-to-even (numpy / torch round).  asym codes are
     rne(w/s + z) as [P4] §2.1 and §3.1 write it; sym codes are rne(w/s).
   * scale floor 1e-8 ([P4] §3.1).
-  * integers that floating point decides (each zero point, each code) are
-    decided on float32 operands with float32 operations, the precision the
-    pages' quantizers run in ([P4] §3.2 works on a .float() copy of W, [P5]
-    on an astype(np.float32) copy); the scales, compensated weights, errors,
-    factor and losses stay float64.
+  * the two integers the grid decides, each zero point and each code, are
+    the exact round-half-to-even of their real-valued definition on the
+    exact grid step (hi - lo)/(2^b - 1) (sym: max|w|/(2^(b-1) - 1)), not of
+    a rounded copy of it: a float64 estimate decides, and wherever it lies
+    too close to a half-integer for its rounding error to be ruled out, the
+    quotient is evaluated in exact rational arithmetic.  The stored scale is
+    that step rounded to float64.  So a range with max = -min puts the zero
+    point exactly at (2^b - 1)/2 and it goes to the even neighbour.
   * desc_act: stable sort of the diagonal of H, descending, ties to the lower
     original column index.
 """
 from __future__ import annotations
+
+from fractions import Fraction
 
 import numpy as np
 import scipy.linalg
@@ -80,6 +85,13 @@ def hessian_accumulate(H, key, X, alpha=2.0):
     H = np.asarray(H, dtype=np.float64) + alpha * S
     key = np.asarray(key, dtype=np.float64) + alpha * np.einsum("ti,ti->i", X, X)
     return H, key
+
+
+def hessian_diagonal_accumulate(key, X, alpha=2.0):
+    """key + alpha·Σ_t x_t² (the diagonal of alpha·XᵀX) in float64, without
+    forming H: the act-order key of a layer too wide for the full product."""
+    X = np.asarray(X, dtype=np.float64)
+    return np.asarray(key, dtype=np.float64) + alpha * np.einsum("ti,ti->i", X, X)
 
 
 def hessian(x_tiles, n, alpha=2.0):
@@ -161,48 +173,89 @@ def prepare(H, key, damp_percent, desc_act):
 # ---------------------------------------------------------------------------
 # The quantization grid  ([P4] §2.1, §3.1; [P5] quantization basics)
 # ---------------------------------------------------------------------------
-def _f32(x):
-    """x rounded to the nearest float32."""
-    return np.asarray(x, dtype=np.float64).astype(np.float32)
+# A float64 estimate x of a grid position carries four roundings (the range
+# width, the step, the quotient, adding the zero point), so it is within
+# 4·2^-53·(|w/step| + |x|) of the exact value: below 2.3e-13 wherever the
+# rounding is not clamped away on a grid of at most 255 steps.  Positions
+# estimated closer than the filter bound 1e-12·(1 + |x|) to a half-integer
+# are re-evaluated exactly, so every rounding below is the exact
+# round-half-to-even of the real number the definition names.
+_TIE_FILTER = 1e-12
+
+
+def _exact_step(lo, hi, qmax):
+    """The exact grid step (hi - lo)/qmax of float64 range ends, floored at
+    1e-8 (the floor as the float64 constant), as a Fraction."""
+    step = (Fraction(float(hi)) - Fraction(float(lo))) / qmax
+    return max(step, Fraction(SCALE_FLOOR))
+
+
+def _rne(x, exact_at):
+    """Round half to even of real numbers whose float64 estimates are x.
+
+    Where an estimate lies within the filter bound of a half-integer, the
+    value exact_at(index) (a Fraction) is rounded instead; Python's round of
+    a Fraction is round-half-to-even."""
+    x = np.asarray(x, dtype=np.float64)
+    q = np.rint(x)
+    near = np.abs((x - np.floor(x)) - 0.5) <= _TIE_FILTER * (1.0 + np.abs(x))
+    for idx in zip(*np.nonzero(near)):
+        q[idx] = float(round(exact_at(idx)))
+    return q
+
+
+def _qmax(bits, sym):
+    return 2 ** (bits - 1) - 1 if sym else 2 ** bits - 1
 
 
 def group_params(v, bits, sym):
-    """Per-row (scale, zero) of one group of current weights v [m, w].
+    """Per-row grid of one group of current weights v [m, w]: (s, z, lo, hi).
 
-    asym: range [min(v,0), max(v,0)] split into 2^b-1 steps; the zero point
-          is the rounded position of 0 on that grid.
-    sym:  scale = max|v| / (2^(b-1)-1); the zero is the storage offset 2^(b-1).
-    Both scales are floored at 1e-8.
-
-    The scale is float64.  The zero point is an integer that floating point
-    decides, and it is decided in float32, the precision the pages'
-    quantizers run in ([P4] §3.2 quantizes a .float() copy of the weights,
-    [P5]'s GPTQ sketch an astype(np.float32) copy): rne of the float32
-    quotient of the float32 range end and the float32 scale.
+    asym: range [lo, hi] = [min(v,0), max(v,0)] split into 2^b-1 steps; the
+          zero point is the rounded position of 0 on that grid, rne(-lo/step).
+    sym:  step = max|v| / (2^(b-1)-1) (lo = 0, hi = max|v|); the zero is the
+          storage offset 2^(b-1).
+    The step is floored at 1e-8.  s is the step rounded to float64 (the
+    stored scale); lo and hi define the exact step for the decisions.
     """
     v = np.asarray(v, dtype=np.float64)
+    qmax = _qmax(bits, sym)
     if sym:
-        qmax = 2 ** (bits - 1) - 1
-        s = np.maximum(np.max(np.abs(v), axis=1) / qmax, SCALE_FLOOR)
-        z = np.full(v.shape[0], float(2 ** (bits - 1)))
+        lo = np.zeros(v.shape[0])
+        hi = np.max(np.abs(v), axis=1)
     else:
         lo = np.minimum(np.min(v, axis=1), 0.0)
         hi = np.maximum(np.max(v, axis=1), 0.0)
-        s = np.maximum((hi - lo) / (2 ** bits - 1), SCALE_FLOOR)
-        z = np.rint(-_f32(lo) / _f32(s)).astype(np.float64)
-    return s, z
+    s = np.maximum((hi - lo) / qmax, SCALE_FLOOR)
+    if sym:
+        z = np.full(v.shape[0], float(2 ** (bits - 1)))
+    else:
+        z = _rne(-lo / s, lambda i: -Fraction(float(lo[i])) / _exact_step(lo[i], hi[i], qmax))
+    return s, z, lo, hi
 
 
-def quantize_values(w, s, z, bits, sym):
+def quantize_values(w, s, z, bits, sym, lo=None, hi=None):
     """Stored integer code of w on the grid (s, z); all arrays broadcast.
 
-    The rounding is decided in float32 as in group_params: rne(fl(w/s))
-    (sym) or rne(fl(fl(w/s) + z)) (asym) on w and s rounded to float32."""
-    q = _f32(w) / _f32(s)
+    asym: rne(w/step + z) clamped to [0, 2^b-1]; sym: rne(w/step) clamped to
+    ±(2^(b-1)-1), plus the offset z.  step is the exact (hi - lo)/qmax when
+    the range ends are given, else s itself."""
+    w, s, z = np.broadcast_arrays(*(np.asarray(a, dtype=np.float64) for a in (w, s, z)))
+    qmax = _qmax(bits, sym)
+    if lo is None:
+        def step(i):
+            return Fraction(float(s[i]))
+    else:
+        lo_b, hi_b = np.broadcast_arrays(np.asarray(lo, dtype=np.float64), np.asarray(hi, dtype=np.float64))
+        lo_b, hi_b = np.broadcast_to(lo_b, w.shape), np.broadcast_to(hi_b, w.shape)
+
+        def step(i):
+            return _exact_step(lo_b[i], hi_b[i], qmax)
     if sym:
-        qmax = 2 ** (bits - 1) - 1
-        return np.clip(np.rint(q), -qmax, qmax).astype(np.float64) + z
-    return np.clip(np.rint(q + _f32(z)), 0, 2 ** bits - 1).astype(np.float64)
+        q = _rne(w / s, lambda i: Fraction(float(w[i])) / step(i))
+        return np.clip(q, -qmax, qmax) + z
+    q = _rne(w / s + z, lambda i: Fraction(float(w[i])) / step(i) + Fraction(float(z[i])))
+    return np.clip(q, 0, qmax)
 
 
 def dequantize_values(q, s, z):
@@ -218,7 +271,8 @@ def _group_width(g, n):
     return n if g == -1 else g
 
 
-def gptq_quantize(Wp, U, bits, group_size, sym, block=None, forced=None, tie_tol=1e-3):
+def gptq_quantize(Wp, U, bits, group_size, sym, block=None, forced=None, forced_zeros=None,
+                  tie_tol=1e-4):
     """GPTQ on permuted weights Wp [m, n] with the inverse factor U [n, n].
 
     For each processed column c in order:
@@ -231,12 +285,15 @@ def gptq_quantize(Wp, U, bits, group_size, sym, block=None, forced=None, tie_tol
     with one matrix product when the block ends; it computes the same thing
     (only the order of the additions to each w_k changes).
 
-    forced (codes [m,n], processed order) replays another implementation's
-    decisions: at every column where its code differs from this one, the
-    difference must be one step at a rounding boundary (the unrounded grid
-    position within tie_tol steps of the half-way point), and the forced code is
-    used from there on, so both sides stay on the same trajectory.  The result
-    then also holds replay = dict(flips, bad, max_tie_dist).
+    Replay of another implementation's decisions (a diagnostic for results
+    that part ways only at rounding ties): forced (codes [m, n], processed
+    order) and forced_zeros (zero points [m, G], group order) are adopted
+    wherever they differ from this oracle's own decision, so both sides stay
+    on one trajectory.  Each such difference must be one step across a
+    rounding boundary: the unrounded grid position (w/step + z for a code,
+    -lo/step for a zero point) within tie_tol steps of the half-integer
+    between the two choices; any other difference counts as bad.  The result
+    then also holds replay = dict(flips, zero_flips, bad, max_tie_dist).
 
     Returns dict(codes [m,n] processed order, scales [m,G], zeros [m,G],
     err [m,n], loss0 = ½Σe²).
@@ -254,28 +311,46 @@ def gptq_quantize(Wp, U, bits, group_size, sym, block=None, forced=None, tie_tol
     B = n if block is None else block
     if block is not None and group_size != -1 and block % group_size != 0:
         raise ValueError("block must be a multiple of group_size")
-    s = z = None
-    replay = dict(flips=0, bad=0, max_tie_dist=0.0)
+    s = z = lo = hi = None
+    replay = dict(flips=0, zero_flips=0, bad=0, max_tie_dist=0.0)
+
+    def judge(own, other, x, key):
+        # other differs from own on the masked rows; x = unrounded position
+        d = np.abs(other - own)
+        dist = np.abs(x - (np.minimum(own, other) + 0.5))
+        ok = (d == 1) & (dist <= tie_tol)
+        replay[key] += int(own.size)
+        replay["bad"] += int((~ok).sum())
+        if own.size:
+            replay["max_tie_dist"] = max(replay["max_tie_dist"], float(dist.max()))
+
     for i1 in range(0, n, max(B, 1)):
         i2 = min(i1 + B, n)
         for c in range(i1, i2):
             if c % gw == 0:
-                s, z = group_params(W[:, c:min(c + gw, n)], bits, sym)
+                s, z, lo, hi = group_params(W[:, c:min(c + gw, n)], bits, sym)
+                if forced_zeros is not None:
+                    zf = np.asarray(forced_zeros[:, c // gw], dtype=np.float64)
+                    d = zf != z
+                    if d.any():
+                        if sym:   # the offset is fixed: any difference is wrong
+                            replay["zero_flips"] += int(d.sum())
+                            replay["bad"] += int(d.sum())
+                        else:
+                            judge(z[d], zf[d], -lo[d] / s[d], "zero_flips")
+                        z = zf
                 scales[:, c // gw] = s
                 zeros[:, c // gw] = z
-            q = quantize_values(W[:, c], s, z, bits, sym)
+            q = quantize_values(W[:, c], s, z, bits, sym, lo, hi)
             if forced is not None:
                 qf = np.asarray(forced[:, c], dtype=np.float64)
                 d = qf != q
                 if d.any():
                     # position on the grid before rounding, in code units
-                    x = W[d, c] / s[d] + (0.0 if sym else z[d])
-                    lo = np.minimum(q[d], qf[d]) - (z[d] if sym else 0.0)
-                    dist = np.abs(x - (lo + 0.5))
-                    ok = (np.abs(qf[d] - q[d]) == 1) & (dist <= tie_tol)
-                    replay["flips"] += int(d.sum())
-                    replay["bad"] += int((~ok).sum())
-                    replay["max_tie_dist"] = max(replay["max_tie_dist"], float(dist.max()))
+                    x = W[d, c] / s[d] + (z[d] if not sym else 0.0)
+                    own = q[d] - (z[d] if sym else 0.0)
+                    other = qf[d] - (z[d] if sym else 0.0)
+                    judge(own, other, x, "flips")
                 q = qf
             e = (W[:, c] - dequantize_values(q, s, z)) / U[c, c]
             codes[:, c] = q
@@ -286,7 +361,7 @@ def gptq_quantize(Wp, U, bits, group_size, sym, block=None, forced=None, tie_tol
             W[:, i2:] -= err[:, i1:i2] @ U[i1:i2, i2:]
     out = dict(codes=codes.astype(np.int64), scales=scales,
                zeros=zeros.astype(np.int64), err=err, loss0=loss0)
-    if forced is not None:
+    if forced is not None or forced_zeros is not None:
         out["replay"] = replay
     return out
 
@@ -302,10 +377,11 @@ def rtn_quantize(Wp, bits, group_size, sym):
     zeros = np.zeros((m, G))
     for gi in range(G):
         c0, c1 = gi * gw, min((gi + 1) * gw, n)
-        s, z = group_params(Wp[:, c0:c1], bits, sym)
+        s, z, lo, hi = group_params(Wp[:, c0:c1], bits, sym)
         scales[:, gi] = s
         zeros[:, gi] = z
-        codes[:, c0:c1] = quantize_values(Wp[:, c0:c1], s[:, None], z[:, None], bits, sym)
+        codes[:, c0:c1] = quantize_values(Wp[:, c0:c1], s[:, None], z[:, None], bits, sym,
+                                          lo[:, None], hi[:, None])
     return dict(codes=codes.astype(np.int64), scales=scales, zeros=zeros.astype(np.int64))
 
 

@@ -9,18 +9,15 @@ remaining columns in proportion to the inverse Hessian).  All arithmetic is
 in ``fractions.Fraction``, so no rounding error enters the weights, scales
 and errors, and the loss is the exact ½·d²/[H_F⁻¹]_cc sum.
 
-The two integers that floating point decides, the zero point and each code,
-are decided on float32 operands with float32 operations, the precision the
-pages' quantizers run in (a .float() / astype(np.float32) copy of the
-weights); the rounding is half to even.  Exact decisions would break the ties
-a symmetric range makes (max = -min puts the zero point at (2^b - 1)/2) in
-another way than every float32 implementation does.
+Python's ``round`` of a Fraction rounds half to even, like numpy's, so the
+zero point and each code are the exact round-half-to-even of their
+definition on the exact grid step.
 """
 from __future__ import annotations
 
 from fractions import Fraction
 
-import numpy as np
+SCALE_FLOOR = Fraction(1e-8)
 
 
 def as_frac(x):
@@ -48,25 +45,19 @@ def grid(vals, bits, sym):
     """(scale, zero) of one group, exactly."""
     if sym:
         qmax = 2 ** (bits - 1) - 1
-        s = max(abs(v) for v in vals) / qmax
+        s = max(max(abs(v) for v in vals) / qmax, SCALE_FLOOR)
         return s, Fraction(2 ** (bits - 1))
     lo = min(min(vals), Fraction(0))
     hi = max(max(vals), Fraction(0))
-    s = (hi - lo) / (2 ** bits - 1)
-    return s, Fraction(int(np.rint(_f32(-lo) / _f32(s))))
-
-
-def _f32(x):
-    """Nearest float32 of a Fraction (through its nearest float64)."""
-    return np.float32(float(x))
+    s = max((hi - lo) / (2 ** bits - 1), SCALE_FLOOR)
+    return s, Fraction(round(-lo / s))
 
 
 def code(w, s, z, bits, sym):
-    q = _f32(w) / _f32(s)
     if sym:
         qmax = 2 ** (bits - 1) - 1
-        return min(max(int(np.rint(q)), -qmax), qmax) + int(z)
-    return min(max(int(np.rint(q + _f32(z))), 0), 2 ** bits - 1)
+        return min(max(round(w / s), -qmax), qmax) + int(z)
+    return min(max(round(w / s + z), 0), 2 ** bits - 1)
 
 
 def gptq_exact(W, H, bits, group, sym):

@@ -39,7 +39,7 @@ def _rand_spd(rng, n, cond_boost=1.0):
 def test_worked_int8_example_codes_and_scale():
     g = _load("int8_worked_example.json")
     w = np.array(g["input_float32"], dtype=np.float32).astype(np.float64)
-    s, z = oracle.group_params(w[None, :], 8, sym=True)
+    s, z, _, _ = oracle.group_params(w[None, :], 8, sym=True)
     assert s[0] == pytest.approx(float(np.float32(3.7)) / 127, rel=1e-15)
     q = oracle.quantize_values(w, s[0], z[0], 8, sym=True)
     assert list((q - z[0]).astype(int)) == g["codes_signed"]
@@ -312,6 +312,11 @@ def test_hessian_brute_force_and_tiling():
     H1, key1 = oracle.hessian([X], n, alpha=0.5)
     np.testing.assert_allclose(H1 * 4, H, rtol=1e-13)
     np.testing.assert_allclose(key1 * 4, key, rtol=1e-13)
+    # the key alone, tile by tile, without forming H
+    k2 = oracle.hessian_diagonal_accumulate(np.zeros(n), X[:4])
+    k2 = oracle.hessian_diagonal_accumulate(k2, X[4:])
+    for i in range(n):
+        assert k2[i] == pytest.approx(2 * sum(X[t, i] ** 2 for t in range(T)), rel=1e-13)
 
 
 def test_damping_value_and_permuted_matrix():
@@ -382,7 +387,7 @@ def test_replay_hand_tie():
     assert own["codes"].tolist() == [[6, 0, 15]]
     rep = go.gptq_quantize(_TIE_W, _TIE_U, 4, -1, False, forced=np.array([[5, 0, 15]]))
     assert rep["codes"].tolist() == [[5, 0, 15]]
-    assert rep["replay"] == dict(flips=1, bad=0, max_tie_dist=0.0)
+    assert rep["replay"] == dict(flips=1, zero_flips=0, bad=0, max_tie_dist=0.0)
     assert rep["err"][0].tolist() == [0.25, -0.125, 0.0]
     for wrong in ([[7, 0, 15]], [[4, 0, 15]], [[6, 1, 15]]):
         r = go.gptq_quantize(_TIE_W, _TIE_U, 4, -1, False, forced=np.array(wrong))
@@ -397,5 +402,89 @@ def test_replay_of_own_codes_changes_nothing():
     Wp = 0.02 * rng.standard_normal((m, n))
     own = go.gptq_quantize(Wp, U, 3, 8, True)
     rep = go.gptq_quantize(Wp, U, 3, 8, True, forced=own["codes"])
-    assert rep["replay"] == dict(flips=0, bad=0, max_tie_dist=0.0)
+    assert rep["replay"] == dict(flips=0, zero_flips=0, bad=0, max_tie_dist=0.0)
     assert np.array_equal(rep["codes"], own["codes"]) and rep["loss0"] == own["loss0"]
+
+
+# ---------------------------------------------------------------------------
+# Exact rounding ties on the grid (round half to even of the real quotient,
+# "模型量化实战：从 INT8 PTQ 到 GPTQ…" §2.1/§3.1 round; the exact route's
+# Fraction arithmetic decides them independently)
+# ---------------------------------------------------------------------------
+def _bf16_grid(lo, hi, count):
+    """count values of the bf16 grid in [lo, hi) (8 significant bits)."""
+    out = []
+    for e in range(-12, 2):
+        for mant in range(128, 256):
+            v = mant * 2.0 ** (e - 7)
+            if lo <= v < hi:
+                out.append(v)
+    return out[::max(1, len(out) // count)][:count]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_symmetric_range_zero_point_tie_goes_to_even(bits):
+    """max = -min puts the grid position of 0 exactly at (2^b - 1)/2; round
+    half to even gives 2^(b-1) on every such range, as the exact route does,
+    also where the float64 estimate -lo/s falls below the half-way point."""
+    qmax = 2 ** bits - 1
+    vals = _bf16_grid(0.001, 2.0, 400)
+    v = np.array([[a, -a, 0.375 * a] for a in vals])
+    s, z, lo, hi = go.group_params(v, bits, False)
+    assert z.tolist() == [2 ** (bits - 1)] * len(vals)
+    for row, zz in zip(v[:40], z[:40]):
+        assert exact_obs.grid([Fraction(float(x)) for x in row], bits, False)[1] == zz
+    below = [a for a in vals if a / ((2 * a) / qmax) < qmax / 2]
+    print(f"{bits}-bit: {len(below)} of {len(vals)} float64 estimates below the tie")
+    if bits > 2:
+        assert below, "no case where the float64 estimate alone would round down"
+
+
+def test_code_ties_match_exact_route():
+    """Every dyadic (lo, hi, w) on a 1/32 grid whose exact grid position is a
+    half-integer (2476 cases at 3 and 4 bits): codes equal the exact route's,
+    although the plain float64 quotient rounds the other way on some."""
+    cases, wrong64 = 0, 0
+    g = [i / 32 for i in range(-32, 33)]
+    for bits in (3, 4):
+        qmax = 2 ** bits - 1
+        los, his, ws = [], [], []
+        for lo_ in (x for x in g if x < 0):
+            for hi_ in (x for x in g if x > 0):
+                step = (Fraction(hi_) - Fraction(lo_)) / qmax
+                z = round(-Fraction(lo_) / step)
+                for w in g:
+                    x = Fraction(w) / step + z
+                    if x.denominator == 2 and 0 < x < qmax:
+                        los.append(lo_), his.append(hi_), ws.append(w)
+        lo_a, hi_a, w_a = map(np.array, (los, his, ws))
+        s = (hi_a - lo_a) / qmax
+        _, z, _, _ = go.group_params(np.stack([lo_a, hi_a], axis=1), bits, False)
+        q = go.quantize_values(w_a, s, z, bits, False, lo_a, hi_a)
+        for i in range(len(ws)):
+            sf, zf = exact_obs.grid([Fraction(los[i]), Fraction(his[i])], bits, False)
+            assert q[i] == exact_obs.code(Fraction(ws[i]), sf, zf, bits, False), (los[i], his[i], ws[i])
+        wrong64 += int(np.sum(np.rint(w_a / s + z) != q))
+        cases += len(ws)
+    print(f"{cases} exact code ties; plain float64 rounding differs on {wrong64}")
+    assert cases == 2476 and wrong64 > 0
+
+
+def test_replay_accepts_zero_point_flips_only_at_ties():
+    """Row [-0.75, 0.75, 0.3], 4-bit asym, one group: step 0.1, the position
+    of 0 is 7.5 exactly, so the oracle takes z = 8 and a replayed z = 7 is a
+    tie flip; z = 6 is not.  A symmetric grid's fixed offset never flips."""
+    W = np.array([[-0.75, 0.75, 0.3]])
+    U = np.eye(3)
+    own = go.gptq_quantize(W, U, 4, -1, False)
+    assert own["zeros"].tolist() == [[8]]
+    rep = go.gptq_quantize(W, U, 4, -1, False, forced_zeros=np.array([[7]]))
+    assert rep["zeros"].tolist() == [[7]]
+    assert rep["replay"]["zero_flips"] == 1 and rep["replay"]["bad"] == 0
+    assert rep["replay"]["max_tie_dist"] <= 1e-12
+    # codes follow the adopted zero: -0.75/0.1 + 7 = -0.5 -> 0, 0.75/0.1 + 7 = 14.5 -> 14
+    assert rep["codes"][0, :2].tolist() == [0, 14]
+    bad = go.gptq_quantize(W, U, 4, -1, False, forced_zeros=np.array([[6]]))
+    assert bad["replay"]["bad"] == 1
+    sym = go.gptq_quantize(W, U, 4, -1, True, forced_zeros=np.array([[7]]))
+    assert sym["replay"]["bad"] == 1

@@ -52,6 +52,32 @@ def _exact_route_passes():
     return True
 
 
+def _ties_pass():
+    import test_oracle_pins as tp
+    try:
+        for bits in (3, 4, 8):
+            tp.test_symmetric_range_zero_point_tie_goes_to_even(bits)
+        tp.test_code_ties_match_exact_route()
+    except AssertionError:
+        return False
+    return True
+
+
+def _plain_rint_zero(v, bits, sym):
+    s, z, lo, hi = _orig["group_params"](v, bits, sym)
+    if not sym:
+        z = np.rint(-lo / s)    # the rounded step decides the tie
+    return s, z, lo, hi
+
+
+def _plain_rint_codes(w, s, z, bits, sym, lo=None, hi=None):
+    w = np.asarray(w, dtype=np.float64)
+    if sym:
+        q = 2 ** (bits - 1) - 1
+        return np.clip(np.rint(w / s), -q, q) + z
+    return np.clip(np.rint(w / s + z), 0, 2 ** bits - 1)
+
+
 def _wrong_factor_lower(Hp):
     U = _orig["inverse_upper_factor"](Hp)
     return U.T.copy()            # lower factor handed out as if it were U
@@ -67,10 +93,10 @@ def _no_widening(v, bits, sym):
         return _orig["group_params"](v, bits, sym)
     lo, hi = np.min(v, axis=1), np.max(v, axis=1)
     s = np.maximum((hi - lo) / (2 ** bits - 1), go.SCALE_FLOOR)
-    return s, np.round(-lo / s)
+    return s, np.round(-lo / s), lo, hi
 
 
-def _floor_codes(w, s, z, bits, sym):
+def _floor_codes(w, s, z, bits, sym, lo=None, hi=None):
     if sym:
         q = 2 ** (bits - 1) - 1
         return np.clip(np.floor(w / s), -q, q) + z
@@ -103,17 +129,19 @@ PLANTS = [
     ("damping", _damping_sum),
     ("act_order", _ascending),
     ("dequantize_values", _wrong_sign_dequant),
+    ("group_params", _plain_rint_zero),
+    ("quantize_values", _plain_rint_codes),
 ]
 
 
 def test_unplanted_oracle_passes_the_checks():
-    assert _hand_cases_pass() and _exact_route_passes()
+    assert _hand_cases_pass() and _exact_route_passes() and _ties_pass()
 
 
 @pytest.mark.parametrize("name,fn", PLANTS, ids=[f"{n}:{f.__name__}" for n, f in PLANTS])
 def test_planted_mistake_is_caught(monkeypatch, name, fn):
     monkeypatch.setattr(go, name, fn)
-    assert not (_hand_cases_pass() and _exact_route_passes())
+    assert not (_hand_cases_pass() and _exact_route_passes() and _ties_pass())
 
 
 # ---------------------------------------------------------------------------
