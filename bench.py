@@ -109,7 +109,7 @@ class Layer:
                                         o["perm"], self.ws_p)
         self.ev[2].record()
         pq.gptq_quantize_layer(self.W, self.H, o["perm"], self.cfg, o["qweight"], o["scales"],
-                               o["zeros"], o["g_idx"], o["loss"], self.ws_q)
+                               o["zeros"], o["g_idx"], o["loss"], o["status"], self.ws_q)
         self.ev[3].record()
 
     def stage_ms(self):
@@ -136,8 +136,9 @@ def run_sweep_shared(pq, torch, bits_groups, log_every=32):
     u8 = dict(dtype=torch.uint8, device="cuda")
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     stage = [0.0, 0.0, 0.0]
-    total = gen_total = 0.0
+    total = gen_total = ideal = 0.0
     linears = 0
+    outs = []
     for i, (xs, wspecs) in enumerate(groups):
         tg = time.perf_counter()
         n, T = xs.n, xs.tokens
@@ -170,24 +171,32 @@ def run_sweep_shared(pq, torch, bits_groups, log_every=32):
         ev[2].record()
         for W, cfg, o, wq in jobs:
             pq.gptq_quantize_layer(W, H, perm, cfg, o["qweight"], o["scales"], o["zeros"], o["g_idx"],
-                                   o["loss"], wq)
+                                   o["loss"], o["status"], wq)
         ev[3].record()
         torch.cuda.synchronize()
         total += time.perf_counter() - t0
+        ideal += ideal_seconds(0, n, T, trail=False)
+        for W, cfg, o, wq in jobs:
+            ideal += ideal_seconds(W.shape[0], n, T, syrk=False, chol=False)
+            outs.append({"status": o["status"].clone()})
         for s_ in range(3):
             stage[s_] += ev[s_].elapsed_time(ev[s_ + 1]) / 1e3
         linears += len(Ws)
         del Ws
         if (i + 1) % log_every == 0:
             log(f"sweep (shared inputs): {i + 1}/{len(groups)} inputs, {total:.2f}s so far")
+    pq.check_status(outs)
     names = "+".join(f"{b}bit_g{g}" for b, g in bits_groups)
-    return {"settings": names, "total_s": total, "inputs": len(groups), "linears": linears,
+    log(f"sweep (shared inputs): {total:.3f}s, ideal {ideal:.3f}s, fraction {ideal / total:.3f}")
+    return {"settings": names, "total_s": total, "ideal_s": ideal, "roofline_frac": ideal / total,
+            "inputs": len(groups), "linears": linears,
             "quantizations": linears * len(cfgs), "data_gen_s": gen_total,
             "stage_s": {"hessian": stage[0], "prepare": stage[1], "quantize": stage[2]}}
 
 
-def cpu_baseline(spec, W, X, log_prefix="cpu_baseline"):
-    """The float64 oracle on a bounded sample of the same layer, scaled to s/layer."""
+def cpu_baseline(spec, W, X, log_prefix="cpu_baseline", full=False):
+    """The float64 oracle on a bounded sample of the same layer, scaled to
+    s/layer (full=True: the whole layer, every token and row, unscaled)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -195,8 +204,27 @@ def cpu_baseline(spec, W, X, log_prefix="cpu_baseline"):
     import workloads
 
     cores = len(os.sched_getaffinity(0))
-    t_tok = min(2048, spec.tokens)
-    r_rows = min(32, spec.m)
+    t_tok = spec.tokens if full else min(2048, spec.tokens)
+    r_rows = spec.m if full else min(32, spec.m)
+    if full:
+        with threadpool_limits(limits=cores):
+            t0 = time.perf_counter()
+            H = np.zeros((spec.n, spec.n))
+            key = np.zeros(spec.n)
+            for r0 in range(0, spec.tokens, workloads.TILE_TOKENS):
+                H, key = oracle.hessian_accumulate(H, key, workloads.to_numpy_f64(X[r0:r0 + workloads.TILE_TOKENS]))
+            t1 = time.perf_counter()
+            log(f"{log_prefix}: full hessian {t1 - t0:.1f}s")
+            U, perm, lam = oracle.prepare(H, key, spec.damp_percent, spec.desc_act)
+            t2 = time.perf_counter()
+            Wf = workloads.to_numpy_f64(W)
+            oracle.gptq_quantize(Wf[:, perm], U, spec.bits, spec.group_size, spec.sym, block=128)
+            t3 = time.perf_counter()
+        th, tp, tq = t1 - t0, t2 - t1, t3 - t2
+        log(f"{log_prefix}: full layer: hessian {th:.1f}s, prepare {tp:.1f}s, quantize {tq:.1f}s")
+        return {"value": th + tp + tq, "unit": "s/layer", "cores": cores, "kind": "oracle",
+                "sample": "float64 NumPy oracle on the whole layer (every token and row), not scaled",
+                "stage_s": {"hessian": th, "prepare": tp, "quantize": tq}}
     Xs = workloads.to_numpy_f64(X[:t_tok])
     Ws = workloads.to_numpy_f64(W[:r_rows])
     with threadpool_limits(limits=cores):
@@ -230,6 +258,8 @@ def run_sweep(pq, torch, bits_groups, log_every=16):
         specs = workloads.sweep_specs(bits, g)
         total = 0.0
         gen_total = 0.0
+        ideal = 0.0
+        statuses = []
         xbuf = {}
         for i, sp in enumerate(specs):
             tg = time.perf_counter()
@@ -247,32 +277,41 @@ def run_sweep(pq, torch, bits_groups, log_every=16):
             layer.step()
             torch.cuda.synchronize()
             total += time.perf_counter() - t0
+            statuses.append(layer.out)
+            ideal += ideal_seconds(sp.m, sp.n, sp.tokens)
             del layer
             if (i + 1) % log_every == 0:
                 log(f"sweep {bits}-bit g{g}: {i + 1}/{len(specs)} linears, {total:.2f}s so far")
-        res[f"{bits}bit_g{g}"] = {"total_s": total, "linears": len(specs), "data_gen_s": gen_total}
+        pq.check_status(statuses)
+        res[f"{bits}bit_g{g}"] = {"total_s": total, "linears": len(specs), "data_gen_s": gen_total,
+                                  "ideal_s": ideal, "roofline_frac": ideal / total}
+        log(f"sweep {bits}-bit g{g}: {total:.3f}s, ideal {ideal:.3f}s, fraction {ideal / total:.3f}")
     return res
 
 
-def measure_rtn(pq, torch, W, reps=5):
+def measure_rtn(pq, torch, W, reps=20):
     """The linear round-to-nearest quantizer (the pages' LinearQuantizer) on
     this layer's weight, per setting: ms per call (HIP events on the stream
-    the kernels run on; the call ends with its own NaN check, a stream
-    synchronisation, which is included) and the HBM roofline of the call's
-    algorithmic bytes (W read once; codes, scales and zeros written once)."""
+    the kernels run on, `reps` stream-ordered calls back to back; the NaN
+    check is a device status word, read once after them) and the HBM
+    roofline of the call's algorithmic bytes (W read once; codes, scales and
+    zeros written once)."""
     m, n = W.shape
     res = {}
     for name, cfg in (("int8_sym_per_row_clip0.99", pq.RtnConfig(8, -1, True, 0.99)),
                       ("int4_asym_g128_clip1.0", pq.RtnConfig(4, 128, False, 1.0))):
         outs = pq.rtn_quantize(W, cfg)   # allocates the outputs, warms the kernels
         ws = torch.empty(max(pq.gptq_rtn_workspace_bytes(m, n, cfg), 1), dtype=torch.uint8, device=W.device)
+        status = torch.zeros(1, dtype=torch.int32, device=W.device)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
         for _ in range(reps):
-            pq.gptq_rtn_quantize(W, cfg, outs["qweight"], outs["scales"], outs["zeros"], outs["err"], ws)
+            pq.gptq_rtn_quantize(W, cfg, outs["qweight"], outs["scales"], outs["zeros"], outs["err"], ws,
+                                 status=status, check=False)
         e1.record()
         torch.cuda.synchronize()
+        assert int(status.item()) == 0
         ms = e0.elapsed_time(e1) / reps
         words = pq.gptq_qweight_words(n, cfg.bits)
         groups = pq.gptq_num_groups(n, cfg.group_size)
@@ -346,12 +385,12 @@ def _dequant(torch, qweight, scales, zeros, gidx, n):
     return (codes - zeros[:, g].float()) * scales[:, g]
 
 
-def measure_awq(pq, torch, W, X, gptq_out, reps=3, eval_tokens=4096):
+def measure_awq(pq, torch, W, X, gptq_out, reps=10, eval_tokens=4096):
     """The pages' AWQ channel scaling on this layer (4-bit asym g128, s = 2):
     the channel statistics pass over the whole calibration X (HBM roofline of
     reading X once) and the scaled linear quantizer, each in ms per call (HIP
-    events on the stream the kernels run on; the quantizer's call ends with its
-    NaN check, a stream synchronisation, which is included).  For context, the
+    events on the stream the kernels run on; the quantizer's NaN check is a
+    device status word read once after the timed calls).  For context, the
     relative output error ‖X(W - Ŵ)ᵀ‖ / ‖X Wᵀ‖ on the first `eval_tokens`
     calibration tokens for AWQ, plain round-to-nearest and GPTQ."""
     m, n = W.shape
@@ -378,12 +417,14 @@ def measure_awq(pq, torch, W, X, gptq_out, reps=3, eval_tokens=4096):
     args = (W, abs_sum, T, 2.0, cfg, out["qweight"], out["scales"], out["zeros"], out["channel_scale"],
             out["err"], qws)
     pq.gptq_awq_quantize(*args)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
     e0.record()
     for _ in range(reps):
-        pq.gptq_awq_quantize(*args)
+        pq.gptq_awq_quantize(*args, status=status, check=False)
     e1.record()
     torch.cuda.synchronize()
+    assert int(status.item()) == 0
     quant_ms = e0.elapsed_time(e1) / reps
     qbytes = m * n * W.element_size() + m * (n // 8) * 4 + m * ((n + 127) // 128) * 8 + 4 * n
     # output error on a token sample
@@ -439,6 +480,51 @@ def stage_rates(spec, stages_ms):
     }
 
 
+def ideal_seconds(m, n, T, syrk=True, chol=True, trail=True):
+    """Ideal time of one layer's stages on the algorithmic work (triangle
+    only): the SYRK T·n(n+1) flop at the bf16 MFMA peak, the Cholesky +
+    triangular inverse 2n³/3 and the trailing update m·n·(n - 128) flop at
+    the fp32 MFMA peak."""
+    t = 0.0
+    if syrk:
+        t += float(T) * n * (n + 1) / (PEAK_BF16_TFLOPS * 1e12)
+    if chol:
+        t += 2.0 * n ** 3 / 3.0 / (PEAK_FP32_TFLOPS * 1e12)
+    if trail:
+        t += float(m) * n * max(n - 128, 0) / (PEAK_FP32_TFLOPS * 1e12)
+    return t
+
+
+def measure_layer(pq, torch, spec, steps, warmup):
+    """Seconds per layer and per stage of another workload (same protocol as
+    the headline: inputs resident, H cleared inside the step)."""
+    import workloads
+    W = workloads.gen_weight(spec, "cuda")
+    X = workloads.gen_x(spec, "cuda")
+    layer = Layer(pq, spec, W, X)
+    for _ in range(warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    tot = [0.0, 0.0, 0.0]
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.step()
+        for k, v in enumerate(layer.stage_ms()):
+            tot[k] += v
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    st = [x / steps for x in tot]
+    pq.check_status(layer.out)
+    syrk = float(spec.tokens) * spec.n * (spec.n + 1)
+    tf = syrk / (st[0] * 1e-3) / 1e12
+    res = {"s_per_layer": ms / 1e3, "steps": steps, "stages_ms": dict(zip(("hessian", "prepare", "quantize"), st)),
+           "xtx_tflops": tf, "xtx_frac_of_bf16": tf / PEAK_BF16_TFLOPS, "stage_rates": stage_rates(spec, st)}
+    log(f"bench: {spec.name}: {ms:.2f} ms/layer, stages {['%.2f' % x for x in st]}, XᵀX {tf:.0f} TFLOP/s")
+    del layer, W, X
+    torch.cuda.empty_cache()
+    return res
+
+
 def gpu_clocks():
     """Current clocks as rocm-smi reports them (best effort, a child process).
     Skipped under a profiler: its preloaded library would follow the child
@@ -464,6 +550,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the 7B-shaped sweep (224 linears at 4-bit g128 and at 3-bit g64)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the per-layer lines of the 4096x4096 and 8192x29568 workloads")
+    ap.add_argument("--cpu-baseline-full", action="store_true",
+                    help="run the oracle on the whole layer instead of a bounded sample (minutes)")
+    ap.add_argument("--only-layer", action="store_true",
+                    help="time the headline layer only (no next rows, sweeps, extras or CPU baseline)")
     ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; "
                          "the reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE counters")
@@ -552,6 +644,10 @@ def main():
         },
         "loss": layer.out["loss"].cpu().tolist(),
     }
+    pq.check_status(layer.out)
+    if args.only_layer:
+        print(json.dumps(result), flush=True)
+        return
     result["next_rows"] = {"rtn_quantize": {"workload": f"{spec.name} weight ({m} x {n})",
                                             **measure_rtn(pq, torch, W)}}
     if spec.bits <= 4 and spec.group_size in (32, 64, 128, -1):
@@ -569,10 +665,15 @@ def main():
         result["sweep"] = run_sweep(pq, torch, workloads.SWEEP_SETTINGS)
         log("bench: 7B-shaped sweep, one input per (decoder layer, input), both settings")
         result["next_rows"]["sweep_shared_inputs"] = run_sweep_shared(pq, torch, workloads.SWEEP_SETTINGS)
+    if not args.no_extra and args.workload == "c3_down_proj_4096x11008":
+        log("bench: per-layer lines of the other full-size workloads")
+        result["other_workloads"] = {
+            name: measure_layer(pq, torch, workloads.CONFIGS[name], steps, 1)
+            for name, steps in (("c2_q_proj_4096", 5), ("c4_down_proj_8192x29568", 3))}
     result["clocks"] = gpu_clocks()
     if not args.no_cpu_baseline:
-        log("bench: cpu baseline (oracle on a bounded sample)")
-        result["cpu_baseline"] = cpu_baseline(spec, W, X)
+        log("bench: cpu baseline (oracle on " + ("the whole layer)" if args.cpu_baseline_full else "a bounded sample)"))
+        result["cpu_baseline"] = cpu_baseline(spec, W, X, full=args.cpu_baseline_full)
     print(json.dumps(result), flush=True)
 
 

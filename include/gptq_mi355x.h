@@ -14,14 +14,18 @@
  *     its only state is a thread-local error message and, for
  *     gptq_prepare_hinv and gptq_quantize_layer, up to three extra HIP
  *     streams (default priority) with their events per host thread and
- *     device, created on first use and kept until the process ends.
+ *     device, created on first use and kept until the process ends.  They
+ *     carry no data between calls: they are execution resources, like a BLAS
+ *     handle's internal streams, that let the latency-bound chain of a call
+ *     run beside its bulk updates.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
  *     on it in order; calls return after enqueueing, except where a call says
  *     it synchronises.  Work a call puts on its extra streams is ordered
  *     after what `stream` held at the call and before anything enqueued on
  *     `stream` after it (events), so to the caller it is one stream-ordered
- *     operation.  Concurrent calls from one host thread on different
- *     streams share those extra streams and are serialised by them.
+ *     operation; this holds for a call that fails after launching, too.
+ *     Concurrent calls from one host thread on different streams share those
+ *     extra streams and are serialised by them.
  *   - Argument errors are detected on the host and returned before anything
  *     is launched.  A failed HIP launch or copy returns GPTQ_ERR_HIP.
  *   - Matrices are row-major.  n = in_features (columns of W, size of H),
@@ -152,15 +156,22 @@ gptq_status gptq_prepare_hinv(float* H_inout, const double* diag_key, int64_t n,
  *   loss     [2] fp64 device: loss[0] = ½·Σ e² over all columns, which
  *            equals ½·tr(ΔW (H+λI) ΔWᵀ); loss[1] = ‖W − Ŵ‖²_F.  The
  *            reconstruction loss ‖ΔW Xᵀ‖²_F = loss[0] − (λ/2)·loss[1].
+ *   status_out  [1] int32 DEVICE word, may be NULL: receives GPTQ_OK, or
+ *            GPTQ_ERR_NONFINITE if W holds a NaN or Inf (the other outputs
+ *            are then meaningless).  Written in stream order as the call's
+ *            last step; the caller reads it when it chooses to synchronise.
  *   workspace at least gptq_quantize_workspace_bytes(m, n, cfg) bytes.
- * Synchronises `stream` once at the end to return GPTQ_ERR_NONFINITE if W
- * holds a NaN or Inf.  m == 0 or n == 0 is a no-op.
+ * Stream-ordered: the call returns after enqueueing and never synchronises
+ * the host (a layer sweep issues no host sync per quantization).  The return
+ * value covers argument checks and launch failures only.  m == 0 or n == 0
+ * is a no-op (status_out is left unchanged).
  * ---------------------------------------------------------------------- */
 size_t gptq_quantize_workspace_bytes(int64_t m, int64_t n, const gptq_config* cfg);
 gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t m, int64_t n,
                                 const float* U, const int32_t* perm, const gptq_config* cfg,
                                 uint32_t* qweight, float* scales, int32_t* zeros, int32_t* g_idx,
-                                double* loss, void* workspace, size_t ws_bytes, void* stream);
+                                double* loss, int32_t* status_out, void* workspace, size_t ws_bytes,
+                                void* stream);
 
 /* ------------------------------------------------------------------------
  * The linear round-to-nearest quantizer (no Hessian, no error feedback).
@@ -189,12 +200,16 @@ gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t m, int64
  *   err      [2] fp64 device: err[0] = mean over the m·n weights of
  *            (w - ŵ)², err[1] = Σ w·ŵ / (‖w‖·‖ŵ‖ + 1e-8) (the page's
  *            quantization_error), ŵ from the fp64 scale.
+ *   status_out  [1] int32 DEVICE word, may be NULL: receives GPTQ_OK, or
+ *            GPTQ_ERR_NONFINITE if W holds a NaN or Inf, in stream order.
  *   workspace at least gptq_rtn_workspace_bytes(m, n, cfg) bytes.
  * Returns GPTQ_ERR_UNSUPPORTED when one row's groups do not fit the on-chip
  * sort (n <= 32768 for one group per row; for groups of g columns,
  * ceil(n/g)·(4·P + 16) <= 150 KiB with P = g rounded up to a power of two).
- * Synchronises `stream` once at the end to return GPTQ_ERR_NONFINITE if W
- * holds a NaN or Inf.  m == 0 or n == 0 is a no-op.
+ * With clip_ratio = 1 (no order statistics), 16-byte aligned rows
+ * (n % 8 == 0), n <= 32768 and a group of 8·d columns with d dividing 64 (or
+ * one group per row), the rows are streamed in one pass; the outputs are the
+ * same.  Stream-ordered, no synchronisation.  m == 0 or n == 0 is a no-op.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t bits;
@@ -206,8 +221,8 @@ typedef struct {
 size_t gptq_rtn_workspace_bytes(int64_t m, int64_t n, const gptq_rtn_config* cfg);
 gptq_status gptq_rtn_quantize(const void* W, int32_t w_dtype, int64_t m, int64_t n,
                               const gptq_rtn_config* cfg, uint32_t* qweight, float* scales,
-                              int32_t* zeros, double* err, void* workspace, size_t ws_bytes,
-                              void* stream);
+                              int32_t* zeros, double* err, int32_t* status_out, void* workspace,
+                              size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Activation-aware channel scaling (AWQ) in front of the linear quantizer
@@ -232,9 +247,10 @@ gptq_status gptq_rtn_quantize(const void* W, int32_t w_dtype, int64_t m, int64_t
  * gptq_rtn_quantize (same cfg, same qweight / scales / zeros layout).  err[0],
  * err[1] are the MSE and cosine between W and the dequantized weight divided
  * by the channel factor.  protect > 0 and finite.  workspace: at least
- * gptq_awq_workspace_bytes(m, n, cfg) bytes.  Synchronises `stream` once and
- * returns GPTQ_ERR_NONFINITE if W or abs_sum holds a NaN or Inf.  The same
- * limits as gptq_rtn_quantize apply (GPTQ_ERR_UNSUPPORTED).
+ * gptq_awq_workspace_bytes(m, n, cfg) bytes.  status_out (device int32,
+ * may be NULL) receives GPTQ_ERR_NONFINITE if W or abs_sum holds a NaN or
+ * Inf, else GPTQ_OK, in stream order; the call does not synchronise.  The
+ * same limits as gptq_rtn_quantize apply (GPTQ_ERR_UNSUPPORTED).
  * ---------------------------------------------------------------------- */
 size_t gptq_awq_stats_workspace_bytes(int64_t n, int64_t tokens);
 gptq_status gptq_awq_channel_stats(const void* X, int32_t x_dtype, int64_t tokens, int64_t ldx,
@@ -244,8 +260,8 @@ size_t gptq_awq_workspace_bytes(int64_t m, int64_t n, const gptq_rtn_config* cfg
 gptq_status gptq_awq_quantize(const void* W, int32_t w_dtype, int64_t m, int64_t n,
                               const double* abs_sum, int64_t tokens, float protect,
                               const gptq_rtn_config* cfg, uint32_t* qweight, float* scales,
-                              int32_t* zeros, float* channel_scale, double* err, void* workspace,
-                              size_t ws_bytes, void* stream);
+                              int32_t* zeros, float* channel_scale, double* err, int32_t* status_out,
+                              void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Product of bf16 activations with the quantized weights (W4A16)

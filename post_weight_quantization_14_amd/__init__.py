@@ -9,6 +9,7 @@ from .gptq import (  # noqa: F401
     RtnConfig,
     alloc_outputs,
     awq_quantize,
+    check_status,
     gptq_awq_channel_stats,
     gptq_awq_quantize,
     gptq_awq_stats_workspace_bytes,

@@ -51,15 +51,15 @@ SIGNATURES = {
                                 ctypes.POINTER(ctypes.c_double), _P]),
     "gptq_quantize_workspace_bytes": (_SZ, [_I64, _I64, ctypes.POINTER(GptqConfig)]),
     "gptq_quantize_layer": (_ST, [_P, _I32, _I64, _I64, _P, _P, ctypes.POINTER(GptqConfig), _P, _P,
-                                  _P, _P, _P, _P, _SZ, _P]),
+                                  _P, _P, _P, _P, _P, _SZ, _P]),
     "gptq_rtn_workspace_bytes": (_SZ, [_I64, _I64, ctypes.POINTER(GptqRtnConfig)]),
     "gptq_rtn_quantize": (_ST, [_P, _I32, _I64, _I64, ctypes.POINTER(GptqRtnConfig), _P, _P, _P, _P,
-                                _P, _SZ, _P]),
+                                _P, _P, _SZ, _P]),
     "gptq_awq_stats_workspace_bytes": (_SZ, [_I64, _I64]),
     "gptq_awq_channel_stats": (_ST, [_P, _I32, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "gptq_awq_workspace_bytes": (_SZ, [_I64, _I64, ctypes.POINTER(GptqRtnConfig)]),
     "gptq_awq_quantize": (_ST, [_P, _I32, _I64, _I64, _P, _I64, ctypes.c_float, ctypes.POINTER(GptqRtnConfig),
-                                _P, _P, _P, _P, _P, _P, _SZ, _P]),
+                                _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "gptq_w4a16_packed_bytes": (_SZ, [_I64, _I64, _I32]),
     "gptq_w4a16_pack": (_ST, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _SZ, _P]),
     "gptq_w4a16_workspace_bytes": (_SZ, [_I64, _I64, _I64]),

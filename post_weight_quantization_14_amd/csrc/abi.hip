@@ -171,7 +171,8 @@ size_t gptq_quantize_workspace_bytes(int64_t m, int64_t n, const gptq_config* cf
 gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t m, int64_t n,
                                 const float* U, const int32_t* perm, const gptq_config* cfg,
                                 uint32_t* qweight, float* scales, int32_t* zeros, int32_t* g_idx,
-                                double* loss, void* workspace, size_t ws_bytes, void* stream) {
+                                double* loss, int32_t* status_out, void* workspace, size_t ws_bytes,
+                                void* stream) {
   clear_error();
   if (m < 0 || n < 0) return fail(GPTQ_ERR_INVALID_ARG, "m=%lld n=%lld", (long long)m, (long long)n);
   gptq_status st = check_config(cfg);
@@ -188,12 +189,13 @@ gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t m, int64
   if (bad_ptr(qweight, 4) || bad_ptr(scales, 4) || bad_ptr(zeros, 4) || bad_ptr(g_idx, 4))
     return fail(GPTQ_ERR_INVALID_ARG, "an output pointer is NULL or misaligned");
   if (bad_ptr(loss, 8)) return fail(GPTQ_ERR_INVALID_ARG, "loss is NULL or misaligned");
+  if (status_out && bad_ptr(status_out, 4)) return fail(GPTQ_ERR_INVALID_ARG, "status_out misaligned");
   const QuantPlan plan = plan_quantize(m, n, *cfg);
   if (workspace == nullptr || ws_bytes < plan.total || bad_ptr(workspace, 256))
     return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu (256-byte aligned)", ws_bytes,
                 plan.total);
   return run_quantize(W, w_dtype, m, n, U, perm, *cfg, qweight, scales, zeros, g_idx, loss,
-                      workspace, plan, static_cast<hipStream_t>(stream));
+                      status_out, workspace, plan, static_cast<hipStream_t>(stream));
 }
 
 static gptq_status check_rtn_config(const gptq_rtn_config* cfg) {
@@ -215,8 +217,8 @@ size_t gptq_rtn_workspace_bytes(int64_t m, int64_t n, const gptq_rtn_config* cfg
 
 gptq_status gptq_rtn_quantize(const void* W, int32_t w_dtype, int64_t m, int64_t n,
                               const gptq_rtn_config* cfg, uint32_t* qweight, float* scales,
-                              int32_t* zeros, double* err, void* workspace, size_t ws_bytes,
-                              void* stream) {
+                              int32_t* zeros, double* err, int32_t* status_out, void* workspace,
+                              size_t ws_bytes, void* stream) {
   clear_error();
   if (m < 0 || n < 0) return fail(GPTQ_ERR_INVALID_ARG, "m=%lld n=%lld", (long long)m, (long long)n);
   gptq_status st = check_rtn_config(cfg);
@@ -233,11 +235,12 @@ gptq_status gptq_rtn_quantize(const void* W, int32_t w_dtype, int64_t m, int64_t
   if (bad_ptr(qweight, 4) || bad_ptr(scales, 4) || bad_ptr(zeros, 4))
     return fail(GPTQ_ERR_INVALID_ARG, "an output pointer is NULL or misaligned");
   if (bad_ptr(err, 8)) return fail(GPTQ_ERR_INVALID_ARG, "err is NULL or misaligned");
+  if (status_out && bad_ptr(status_out, 4)) return fail(GPTQ_ERR_INVALID_ARG, "status_out misaligned");
   if (workspace == nullptr || ws_bytes < plan.total || bad_ptr(workspace, 256))
     return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu (256-byte aligned)", ws_bytes,
                 plan.total);
   return run_rtn(W, w_dtype, m, n, cfg->bits, cfg->sym, cfg->clip_ratio, qweight, scales, zeros, err,
-                 workspace, plan, static_cast<hipStream_t>(stream));
+                 status_out, workspace, plan, static_cast<hipStream_t>(stream));
 }
 
 size_t gptq_awq_stats_workspace_bytes(int64_t n, int64_t tokens) {
@@ -269,8 +272,8 @@ size_t gptq_awq_workspace_bytes(int64_t m, int64_t n, const gptq_rtn_config* cfg
 gptq_status gptq_awq_quantize(const void* W, int32_t w_dtype, int64_t m, int64_t n,
                               const double* abs_sum, int64_t tokens, float protect,
                               const gptq_rtn_config* cfg, uint32_t* qweight, float* scales,
-                              int32_t* zeros, float* channel_scale, double* err, void* workspace,
-                              size_t ws_bytes, void* stream) {
+                              int32_t* zeros, float* channel_scale, double* err, int32_t* status_out,
+                              void* workspace, size_t ws_bytes, void* stream) {
   clear_error();
   if (m < 0 || n < 0) return fail(GPTQ_ERR_INVALID_ARG, "m=%lld n=%lld", (long long)m, (long long)n);
   gptq_status st = check_rtn_config(cfg);
@@ -290,11 +293,12 @@ gptq_status gptq_awq_quantize(const void* W, int32_t w_dtype, int64_t m, int64_t
   if (bad_ptr(qweight, 4) || bad_ptr(scales, 4) || bad_ptr(zeros, 4) || bad_ptr(channel_scale, 4))
     return fail(GPTQ_ERR_INVALID_ARG, "an output pointer is NULL or misaligned");
   if (bad_ptr(err, 8)) return fail(GPTQ_ERR_INVALID_ARG, "err is NULL or misaligned");
+  if (status_out && bad_ptr(status_out, 4)) return fail(GPTQ_ERR_INVALID_ARG, "status_out misaligned");
   const size_t need = awq_extra_bytes() + plan.total;
   if (workspace == nullptr || ws_bytes < need || bad_ptr(workspace, 256))
     return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu (256-byte aligned)", ws_bytes, need);
   return run_awq_quantize(W, w_dtype, m, n, abs_sum, tokens, protect, cfg->bits, cfg->sym, cfg->clip_ratio,
-                          qweight, scales, zeros, channel_scale, err, workspace, plan,
+                          qweight, scales, zeros, channel_scale, err, status_out, workspace, plan,
                           static_cast<hipStream_t>(stream));
 }
 

@@ -103,10 +103,10 @@ __global__ __launch_bounds__(1024) void awq_scale_kernel(const double* __restric
   const int tid = threadIdx.x;
   bool bad = false;
   for (int64_t j = tid; j < n; j += 1024) bad |= !isfinite(abs_sum[j]);
-  if (__syncthreads_or(bad)) {
-    if (tid == 0) atomicOr(flag, 1);
-    return;
-  }
+  // the call's flag word: this single workgroup is its only writer
+  const int any_bad = __syncthreads_or(bad);
+  if (tid == 0) *flag = any_bad;
+  if (any_bad) return;
   if (tid == 0) {
     sel[0] = 0;
     sel[1] = (uint64_t)((n - 1) / 2);   // rank of the lower median
@@ -188,13 +188,12 @@ size_t awq_extra_bytes() { return 256; }
 gptq_status run_awq_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const double* abs_sum,
                              int64_t tokens, float protect, int bits, int sym, float clip,
                              uint32_t* qweight, float* scales, int32_t* zeros, float* channel_scale,
-                             double* err, void* ws, const RtnPlan& plan, hipStream_t stream) {
+                             double* err, int32_t* status, void* ws, const RtnPlan& plan, hipStream_t stream) {
   int* flag = static_cast<int*>(ws);
-  GPTQ_HIP_CHECK(hipMemsetAsync(flag, 0, sizeof(int), stream));
   hipLaunchKernelGGL(awq_scale_kernel, dim3(1), dim3(1024), 0, stream, abs_sum, n, (double)tokens, protect,
                      channel_scale, flag);
   GPTQ_LAUNCH_CHECK();
-  return run_rtn(W, w_dtype, m, n, bits, sym, clip, qweight, scales, zeros, err,
+  return run_rtn(W, w_dtype, m, n, bits, sym, clip, qweight, scales, zeros, err, status,
                  static_cast<char*>(ws) + awq_extra_bytes(), plan, stream, channel_scale, flag);
 }
 

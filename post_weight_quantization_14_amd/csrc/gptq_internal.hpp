@@ -66,6 +66,33 @@ struct SideStream {
 constexpr int kSideStreams = 3;
 gptq_status get_side_stream(SideStream& out, int which = 0);   // 0 <= which < kSideStreams
 
+// Joins side streams back into the caller's stream when a launcher returns
+// early (a failed launch or runtime call after side work was issued): the
+// caller's stream, and so the caller's allocator, must not run ahead of
+// kernels still reading or writing its buffers.  The normal path joins
+// explicitly and then calls release().
+class SideJoin {
+ public:
+  explicit SideJoin(hipStream_t caller) : caller_(caller) {}
+  SideJoin(const SideJoin&) = delete;
+  SideJoin& operator=(const SideJoin&) = delete;
+  void add(const SideStream& s) {
+    if (count_ < kSideStreams) sides_[count_++] = s;
+  }
+  void release() { count_ = 0; }
+  ~SideJoin() {
+    for (int i = 0; i < count_; ++i) {
+      if (hipEventRecord(sides_[i].done, sides_[i].stream) == hipSuccess)
+        (void)hipStreamWaitEvent(caller_, sides_[i].done, 0);
+    }
+  }
+
+ private:
+  hipStream_t caller_;
+  SideStream sides_[kSideStreams];
+  int count_ = 0;
+};
+
 // ---------------------------------------------------------------- Hessian (stage 1)
 constexpr int kSyrkTile = 256;      // output tile edge of the bf16 SYRK
 constexpr int kSyrkStage = 32;      // tokens per LDS ring slot
@@ -111,8 +138,8 @@ struct QuantPlan {
 QuantPlan plan_quantize(int64_t m, int64_t n, const gptq_config& cfg);
 gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const float* U,
                          const int32_t* perm, const gptq_config& cfg, uint32_t* qweight,
-                         float* scales, int32_t* zeros, int32_t* g_idx, double* loss, void* ws,
-                         const QuantPlan& plan, hipStream_t stream);
+                         float* scales, int32_t* zeros, int32_t* g_idx, double* loss,
+                         int32_t* status, void* ws, const QuantPlan& plan, hipStream_t stream);
 
 // ---------------------------------------------------------------- linear (RTN) quantizer
 // One workgroup per output row sorts each group's keys in LDS: G·P floats plus
@@ -127,8 +154,10 @@ RtnPlan plan_rtn(int64_t m, int64_t n, int32_t group_size);
 // colscale (optional, per input column): quantize fl(w·colscale) and take the
 // errors against w with ŵ = (q - z)·s / colscale.  extra_flag (optional):
 // a device flag set by an earlier kernel of the same call, read at the end.
+// status (device, optional): receives GPTQ_OK or GPTQ_ERR_NONFINITE in stream
+// order; nothing synchronises.
 gptq_status run_rtn(const void* W, int w_dtype, int64_t m, int64_t n, int bits, int sym, float clip,
-                    uint32_t* qweight, float* scales, int32_t* zeros, double* err, void* ws,
+                    uint32_t* qweight, float* scales, int32_t* zeros, double* err, int32_t* status, void* ws,
                     const RtnPlan& plan, hipStream_t stream, const float* colscale = nullptr,
                     const int* extra_flag = nullptr);
 
@@ -144,7 +173,7 @@ size_t awq_extra_bytes();   // workspace of the scale step, before the quantizer
 gptq_status run_awq_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const double* abs_sum,
                              int64_t tokens, float protect, int bits, int sym, float clip,
                              uint32_t* qweight, float* scales, int32_t* zeros, float* channel_scale,
-                             double* err, void* ws, const RtnPlan& plan, hipStream_t stream);
+                             double* err, int32_t* status, void* ws, const RtnPlan& plan, hipStream_t stream);
 
 // ---------------------------------------------------------------- W4A16 product
 struct W4Layout {

@@ -60,7 +60,8 @@ __global__ __launch_bounds__(1024) void stats_kernel(const double* key, const fl
   if (threadIdx.x == 0) {
     const double mean = red[0] / (double)n;
     *lam_out = damp * mean;
-    if (bad || !isfinite(mean)) atomicOr(flag, kFlagNonFinite);
+    // the first kernel of the call: it sets the flag word (later kernels OR into it)
+    *flag = (bad || !isfinite(mean)) ? kFlagNonFinite : 0;
   }
 }
 
@@ -447,7 +448,6 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
   int* flag = reinterpret_cast<int*>(w + p.flag_off);
   const int64_t lda = p.n_pad;
 
-  GPTQ_HIP_CHECK(hipMemsetAsync(flag, 0, sizeof(int), stream));
   hipLaunchKernelGGL(stats_kernel, dim3(1), dim3(1024), 0, stream, key, (const float*)H, n, damp,
                      lam, flag);
   GPTQ_LAUNCH_CHECK();
@@ -484,6 +484,10 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
   GPTQ_TRY(get_side_stream(side, 0));
   GPTQ_TRY(get_side_stream(tri, 1));
   GPTQ_TRY(get_side_stream(inr, 2));
+  SideJoin join(stream);
+  join.add(side);
+  join.add(tri);
+  join.add(inr);
   bool side_pending = false, tri_pending = false, inr_pending = false;
   // Triangular inverse, overlapped with the factorisation.  A node of the
   // bottom-up doubling joins blocks [l0, r0) and [r0, r1): its step 1
@@ -613,6 +617,7 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
     GPTQ_HIP_CHECK(hipEventRecord(tri.done, tri.stream));
     GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, tri.done, 0));
   }
+  join.release();
   hipLaunchKernelGGL(flip_kernel, dim3((unsigned)ceil_div(n, 256), (unsigned)n), dim3(256), 0,
                      stream, (const float*)Mm, lda, n, H);
   GPTQ_LAUNCH_CHECK();

@@ -31,6 +31,13 @@ struct QArgs {
 // asym -> range [min(w,0), max(w,0)] in 2^b - 1 steps, zero point = rounded
 // position of 0; sym -> scale max|w| / (2^(b-1) - 1), zero = storage offset
 // 2^(b-1).  Scales are floored at 1e-8.
+// The zero point is the round-half-to-even of -lo / step on the exact step
+// (hi - lo)/(2^b - 1), not on the rounded scale: in fp64, -lo·(2^b - 1) and
+// hi - lo of fp32 operands are exact (hi >= 0 >= lo), so the quotient is
+// correctly rounded and a range with max = -min lands exactly on the
+// half-integer (2^b - 1)/2 and goes to the even neighbour.  (When hi - lo
+// needs more than 53 bits, -lo is below 2^-29 of the range and the zero
+// point is 0 either way.)  It is taken once per group.
 __device__ __forceinline__ void grid_params(float lo, float hi, float amax, int bits, int sym,
                                             float& s, float& z) {
   if (sym) {
@@ -39,8 +46,11 @@ __device__ __forceinline__ void grid_params(float lo, float hi, float amax, int 
   } else {
     lo = fminf(lo, 0.f);
     hi = fmaxf(hi, 0.f);
-    s = fmaxf((hi - lo) / (float)((1 << bits) - 1), 1e-8f);
-    z = rintf(-lo / s);
+    const int qmax = (1 << bits) - 1;
+    s = fmaxf((hi - lo) / (float)qmax, 1e-8f);
+    const double span = (double)hi - (double)lo;
+    const double pos = span >= (double)qmax * 1e-8 ? -(double)lo * (double)qmax / span : -(double)lo / 1e-8;
+    z = (float)rint(pos);
   }
 }
 

@@ -181,10 +181,18 @@ __global__ __launch_bounds__(1024) void loss_reduce_kernel(const double* loss_ro
   }
 }
 
-__global__ void zero_f64_kernel(double* p, int64_t count) {
+// Clears the per-row loss accumulators and the call's flag word (a kernel,
+// not a memset, so the call can be captured in a graph).
+__global__ void zero_f64_kernel(double* p, int64_t count, int* flag) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *flag = 0;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
        i += (int64_t)gridDim.x * blockDim.x)
     p[i] = 0.0;
+}
+
+// The call's status word for the caller: 0, or GPTQ_ERR_NONFINITE.
+__global__ void status_kernel(const int* flag, int32_t* status) {
+  *status = (*flag & kFlagNonFinite) ? (int32_t)GPTQ_ERR_NONFINITE : (int32_t)GPTQ_OK;
 }
 
 
@@ -222,8 +230,8 @@ QuantPlan plan_quantize(int64_t m, int64_t n, const gptq_config& cfg) {
 
 gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const float* U,
                          const int32_t* perm, const gptq_config& cfg, uint32_t* qweight,
-                         float* scales, int32_t* zeros, int32_t* g_idx, double* loss, void* ws,
-                         const QuantPlan& p, hipStream_t stream) {
+                         float* scales, int32_t* zeros, int32_t* g_idx, double* loss,
+                         int32_t* status, void* ws, const QuantPlan& p, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
   float* Wp = reinterpret_cast<float*>(w + p.wp_off);
   double* part = reinterpret_cast<double*>(w + p.part_off);
@@ -233,9 +241,8 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
   int32_t* invperm = reinterpret_cast<int32_t*>(w + p.inv_off);
   int* flag = reinterpret_cast<int*>(w + p.flag_off);
 
-  GPTQ_HIP_CHECK(hipMemsetAsync(flag, 0, sizeof(int), stream));
   hipLaunchKernelGGL(zero_f64_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(m, 256), 1024)),
-                     dim3(256), 0, stream, loss_rows, m);
+                     dim3(256), 0, stream, loss_rows, m, flag);
   GPTQ_LAUNCH_CHECK();
 
   const size_t row_bytes = (size_t)n * sizeof(float);
@@ -279,6 +286,8 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
   // one superblock's errors never meet the next superblock's writes.
   SideStream side;
   GPTQ_TRY(get_side_stream(side));
+  SideJoin join(stream);
+  join.add(side);
   bool side_pending = false;
   for (int64_t s1 = 0; s1 < n; s1 += kQSuper) {
     const int64_t s2 = std::min<int64_t>(s1 + kQSuper, n);
@@ -335,6 +344,7 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
     }
   }
   if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
+  join.release();
 
   hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, perm, n,
                      (int64_t)(gw > 0 ? gw : 0), g_idx, invperm);
@@ -356,12 +366,9 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
                      (const double*)part, (int64_t)(m * bpr), loss);
   GPTQ_LAUNCH_CHECK();
 
-  int hflag = 0;
-  GPTQ_HIP_CHECK(hipMemcpyAsync(&hflag, flag, sizeof(int), hipMemcpyDeviceToHost, stream));
-  GPTQ_HIP_CHECK(hipStreamSynchronize(stream));
-  if (hflag & kFlagNonFinite) {
-    set_error("gptq_quantize_layer: W holds a NaN or Inf");
-    return GPTQ_ERR_NONFINITE;
+  if (status) {
+    hipLaunchKernelGGL(status_kernel, dim3(1), dim3(1), 0, stream, (const int*)flag, status);
+    GPTQ_LAUNCH_CHECK();
   }
   return GPTQ_OK;
 }

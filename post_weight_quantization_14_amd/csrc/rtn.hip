@@ -33,7 +33,6 @@ namespace gptq {
 namespace {
 
 constexpr int kRtnThreads = 512;
-constexpr int kFlagNonFinite = 1;
 
 template <typename T>
 __device__ __forceinline__ float rtn_f32(T x);
@@ -53,7 +52,7 @@ struct RtnArgs {
   float* scales;
   int32_t* zeros;
   double* part;      // [m][4]: Σ(w-ŵ)², Σwŵ, Σw², Σŵ²
-  int* flag;
+  int* badrow;       // [m]: 1 if the row holds a NaN or Inf (every row writes its own)
   const float* colscale;   // per input column, or null: quantize fl(w·colscale), errors against w
 };
 
@@ -441,7 +440,8 @@ __global__ __launch_bounds__(kRtnThreads) void rtn_row_kernel(RtnArgs a) {
     a.scales[r * a.G + j] = (float)gsc[j];
     a.zeros[r * a.G + j] = (int32_t)gzp[j] + off;
   }
-  if (bad) atomicOr(a.flag, kFlagNonFinite);
+  const int row_bad = __syncthreads_or(bad);
+  if (tid == 0) a.badrow[r] = row_bad;
 
   // row sums: wave butterflies, then the 8 waves in order
   __shared__ double red[4][kRtnThreads / 64];
@@ -462,16 +462,218 @@ __global__ __launch_bounds__(kRtnThreads) void rtn_row_kernel(RtnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming path for clip_ratio = 1, where every grid comes from its group's
+// extremes and no order statistic is needed: one workgroup of 256 threads
+// per output row, thread t owning the 8-column chunks t, t + 256, ... of the
+// row (one 16-byte load of bf16, two of fp32, per chunk), all of them loaded
+// before any arithmetic.  A group of g = 8·GL columns is GL consecutive lanes
+// of one wave (GL divides 64, and chunk t + 256k of lane l of wave w is
+// 64w + l + 256k); its extremes are xor-butterflies over those lanes.  GL = 0:
+// one group per row, extremes by a block reduction.  The grid, the codes and
+// the error sums are those of rtn_row_kernel (the same fp64 grid, the same
+// code rule), so the two paths give identical outputs.
+// ---------------------------------------------------------------------------
+constexpr int kStreamThreads = 256;
+constexpr int kStreamMaxChunks = 16;   // n <= 8·256·16 = 32768
+
+template <typename T> struct Chunk;
+template <> struct Chunk<uint16_t> {
+  uint4 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void get(float (&x)[8]) const {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(u[i] << 16);
+      x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Chunk<float> {
+  f32x4_t a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4_t*>(p);
+    b = *reinterpret_cast<const f32x4_t*>(p + 4);
+  }
+  __device__ __forceinline__ void get(float (&x)[8]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = a[i];
+      x[i + 4] = b[i];
+    }
+  }
+};
+
+template <typename T, int GL>
+__global__ __launch_bounds__(kStreamThreads) void rtn_stream_kernel(RtnArgs a) {
+  __shared__ float red_lo[kStreamThreads / 64], red_hi[kStreamThreads / 64];
+  __shared__ double red[4][kStreamThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t r = blockIdx.x;
+  const int nc = (int)(a.n >> 3);
+  const T* wrow = static_cast<const T*>(a.W) + r * a.n;
+  Chunk<T> raw[kStreamMaxChunks];
+  // unconditional loads at clamped chunk indices: all in flight at once (a
+  // conditional load compiles to a branch and a wait of its own)
+#pragma unroll
+  for (int k = 0; k < kStreamMaxChunks; ++k) {
+    const int c8 = min(tid + kStreamThreads * k, nc - 1);
+    raw[k].load(wrow + 8 * c8);
+  }
+  bool bad = false;
+  float glo[kStreamMaxChunks], ghi[kStreamMaxChunks];
+#pragma unroll
+  for (int k = 0; k < kStreamMaxChunks; ++k) {
+    const int c8 = tid + kStreamThreads * k;
+    float lo = INFINITY, hi = -INFINITY;
+    if (c8 < nc) {
+      float x[8];
+      raw[k].get(x);
+      float cs[8];
+      if (a.colscale) {
+        const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(a.colscale + 8 * c8);
+        const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(a.colscale + 8 * c8 + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { cs[i] = c0[i]; cs[i + 4] = c1[i]; }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = a.colscale ? x[e] * cs[e] : x[e];
+        bad |= !isfinite(v);
+        const float key = a.sym ? fabsf(v) : v;
+        lo = fminf(lo, key);
+        hi = fmaxf(hi, key);
+      }
+    }
+    if constexpr (GL > 0) {
+#pragma unroll
+      for (int d = 1; d < GL; d <<= 1) {
+        lo = fminf(lo, __shfl_xor(lo, d, 64));
+        hi = fmaxf(hi, __shfl_xor(hi, d, 64));
+      }
+    }
+    glo[k] = lo;
+    ghi[k] = hi;
+  }
+  if constexpr (GL == 0) {
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kStreamMaxChunks; ++k) { lo = fminf(lo, glo[k]); hi = fmaxf(hi, ghi[k]); }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      lo = fminf(lo, __shfl_xor(lo, d, 64));
+      hi = fmaxf(hi, __shfl_xor(hi, d, 64));
+    }
+    if (lane == 0) { red_lo[wave] = lo; red_hi[wave] = hi; }
+    __syncthreads();
+    lo = red_lo[0];
+    hi = red_hi[0];
+#pragma unroll
+    for (int wv = 1; wv < kStreamThreads / 64; ++wv) { lo = fminf(lo, red_lo[wv]); hi = fmaxf(hi, red_hi[wv]); }
+#pragma unroll
+    for (int k = 0; k < kStreamMaxChunks; ++k) { glo[k] = lo; ghi[k] = hi; }
+  }
+
+  const int off = a.sym ? (1 << (a.bits - 1)) : 0;
+  const float qminf = a.sym ? -(float)(1 << (a.bits - 1)) : 0.f;
+  const float qmaxf = a.sym ? (float)((1 << (a.bits - 1)) - 1) : (float)((1 << a.bits) - 1);
+  double se = 0.0, xd = 0.0, ww = 0.0;
+  uint32_t* qrow = a.qweight + r * a.words;
+#pragma unroll
+  for (int k = 0; k < kStreamMaxChunks; ++k) {
+    const int c8 = tid + kStreamThreads * k;
+    if (c8 >= nc) continue;
+    double s, z;
+    rtn_grid((double)glo[k], (double)ghi[k], a.bits, a.sym, s, z);
+    const float sf = (float)s, zf = (float)z;
+    float x[8];
+    raw[k].get(x);
+    float cs[8];
+    if (a.colscale) {
+      const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(a.colscale + 8 * c8);
+      const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(a.colscale + 8 * c8 + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { cs[i] = c0[i]; cs[i + 4] = c1[i]; }
+    }
+    uint32_t word0 = 0u, word1 = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x0 = x[e];
+      const float xf = a.colscale ? x0 * cs[e] : x0;
+      const float qf = xf / sf;
+      const float y = a.sym ? qf : qf + zf;
+      const float half = floorf(y) + 0.5f;
+      const float tol = 2e-7f * (fabsf(qf) + fabsf(y)) + 1e-30f;
+      float q;
+      if (fabsf(y - half) > tol) {
+        q = rintf(y);
+      } else {
+        const double xq = (double)xf / s;
+        q = (float)(a.sym ? rint(xq) : rint(xq + z));
+      }
+      q = fminf(fmaxf(q, qminf), qmaxf);
+      const uint32_t code = (uint32_t)((int)q + off);
+      const double xv = (double)x0;
+      const double d = a.colscale ? xv - ((double)q - z) * s / (double)cs[e] : xv - ((double)q - z) * s;
+      se += d * d;
+      xd += xv * d;
+      ww += xv * xv;
+      if (a.bits <= 4) word0 |= code << (4 * e);
+      else if (e < 4) word0 |= code << (8 * e);
+      else word1 |= code << (8 * (e - 4));
+    }
+    if (a.bits <= 4) {
+      qrow[c8] = word0;
+    } else {
+      qrow[2 * c8] = word0;
+      qrow[2 * c8 + 1] = word1;
+    }
+    const bool owner = GL == 0 ? c8 == 0 : (lane % (GL > 0 ? GL : 1)) == 0;
+    if (owner) {
+      const int64_t j = GL == 0 ? 0 : c8 / (GL > 0 ? GL : 1);
+      a.scales[r * a.G + j] = sf;
+      a.zeros[r * a.G + j] = (int32_t)z + off;
+    }
+  }
+  const int row_bad = __syncthreads_or(bad);
+  if (tid == 0) a.badrow[r] = row_bad;
+  double v4[4] = {se, ww - xd, ww, ww - 2.0 * xd + se};
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v4[q] += __shfl_xor(v4[q], d, 64);
+  if (lane == 0)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) red[q][wave] = v4[q];
+  __syncthreads();
+  if (tid < 4) {
+    double sum = 0.0;
+    for (int wv = 0; wv < kStreamThreads / 64; ++wv) sum += red[tid][wv];
+    a.part[r * 4 + tid] = sum;
+  }
+}
+
 // err[0] = Σse / (m·n), err[1] = Σdot / (sqrt(Σww)·sqrt(Σdd) + 1e-8); rows in a
-// fixed order (thread t sums rows t, t+1024, ...; then a fixed tree).
+// fixed order (thread t sums rows t, t+1024, ...; then a fixed tree).  The
+// status word: GPTQ_ERR_NONFINITE if a row (or, for AWQ, the channel
+// statistics: extra_flag) held a NaN or Inf, else GPTQ_OK.
 __global__ __launch_bounds__(1024) void rtn_reduce_kernel(const double* __restrict__ part, int64_t m,
-                                                          int64_t count, double* __restrict__ err) {
+                                                          int64_t count, double* __restrict__ err,
+                                                          const int* __restrict__ badrow,
+                                                          const int* extra_flag, int32_t* status) {
   __shared__ double sh[4][1024];
   const int tid = threadIdx.x;
   double v[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int64_t r = tid; r < m; r += 1024)
+  int bad = 0;
+  for (int64_t r = tid; r < m; r += 1024) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) v[q] += part[r * 4 + q];
+    bad |= badrow[r];
+  }
+  bad = __syncthreads_or(bad);
+  if (tid == 0 && status)
+    *status = (bad || (extra_flag && *extra_flag)) ? (int32_t)GPTQ_ERR_NONFINITE : (int32_t)GPTQ_OK;
 #pragma unroll
   for (int q = 0; q < 4; ++q) sh[q][tid] = v[q];
   __syncthreads();
@@ -498,13 +700,43 @@ RtnPlan plan_rtn(int64_t m, int64_t n, int32_t group_size) {
   p.lds_bytes = (size_t)((p.G * p.P + 3) & ~int64_t(3)) * sizeof(float) + (size_t)p.G * 2 * sizeof(double);
   if (p.G == 1) p.lds_bytes += 8 * 256 * sizeof(uint32_t);   // radix-select histograms
   p.part_off = 0;
-  p.flag_off = align256((size_t)std::max<int64_t>(m, 1) * 4 * sizeof(double));
-  p.total = p.flag_off + 256;
+  p.flag_off = align256((size_t)std::max<int64_t>(m, 1) * 4 * sizeof(double));   // per-row flags
+  p.total = p.flag_off + align256((size_t)std::max<int64_t>(m, 1) * sizeof(int));
   return p;
 }
 
+namespace {
+// Lanes per group of the streaming kernel (0: one group per row), or -1 when
+// the layer needs the general kernel (clipping, unaligned rows, an n beyond
+// what the registers hold, or a group width that is not 8 times a divisor of 64).
+int rtn_stream_lanes(const void* W, int w_dtype, int64_t n, float clip, const RtnPlan& p) {
+  if (!(clip >= 1.f) || n % 8 != 0 || n > 8 * kStreamThreads * kStreamMaxChunks) return -1;
+  if ((reinterpret_cast<uintptr_t>(W) & 15) != 0) return -1;
+  (void)w_dtype;
+  if (p.G == 1) return 0;
+  if (p.g % 8 != 0) return -1;
+  const int64_t gl = p.g / 8;
+  return (gl <= 64 && (64 % gl) == 0) ? (int)gl : -1;
+}
+
+template <typename T>
+void launch_stream(int gl, const RtnArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.m), block(kStreamThreads);
+  switch (gl) {
+    case 0: hipLaunchKernelGGL((rtn_stream_kernel<T, 0>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((rtn_stream_kernel<T, 1>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((rtn_stream_kernel<T, 2>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((rtn_stream_kernel<T, 4>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((rtn_stream_kernel<T, 8>), grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((rtn_stream_kernel<T, 16>), grid, block, 0, stream, a); break;
+    case 32: hipLaunchKernelGGL((rtn_stream_kernel<T, 32>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((rtn_stream_kernel<T, 64>), grid, block, 0, stream, a); break;
+  }
+}
+}  // namespace
+
 gptq_status run_rtn(const void* W, int w_dtype, int64_t m, int64_t n, int bits, int sym, float clip,
-                    uint32_t* qweight, float* scales, int32_t* zeros, double* err, void* ws,
+                    uint32_t* qweight, float* scales, int32_t* zeros, double* err, int32_t* status, void* ws,
                     const RtnPlan& p, hipStream_t stream, const float* colscale, const int* extra_flag) {
   char* w = static_cast<char*>(ws);
   RtnArgs a;
@@ -513,38 +745,30 @@ gptq_status run_rtn(const void* W, int w_dtype, int64_t m, int64_t n, int bits, 
   a.qweight = qweight; a.words = gptq_qweight_words(n, bits);
   a.scales = scales; a.zeros = zeros;
   a.part = reinterpret_cast<double*>(w + p.part_off);
-  a.flag = reinterpret_cast<int*>(w + p.flag_off);
+  a.badrow = reinterpret_cast<int*>(w + p.flag_off);
   a.colscale = colscale;
-  GPTQ_HIP_CHECK(hipMemsetAsync(a.flag, 0, sizeof(int), stream));
-  const int lds = (int)p.lds_bytes;
-  if (w_dtype == GPTQ_BF16) {
-    if (lds > 65536)
-      GPTQ_HIP_CHECK(hipFuncSetAttribute((const void*)rtn_row_kernel<uint16_t>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds));
-    hipLaunchKernelGGL(rtn_row_kernel<uint16_t>, dim3((unsigned)m), dim3(kRtnThreads), lds, stream, a);
+  const int gl = rtn_stream_lanes(W, w_dtype, n, clip, p);
+  if (gl >= 0) {
+    if (w_dtype == GPTQ_BF16) launch_stream<uint16_t>(gl, a, stream);
+    else launch_stream<float>(gl, a, stream);
   } else {
-    if (lds > 65536)
-      GPTQ_HIP_CHECK(hipFuncSetAttribute((const void*)rtn_row_kernel<float>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds));
-    hipLaunchKernelGGL(rtn_row_kernel<float>, dim3((unsigned)m), dim3(kRtnThreads), lds, stream, a);
+    const int lds = (int)p.lds_bytes;
+    if (w_dtype == GPTQ_BF16) {
+      if (lds > 65536)
+        GPTQ_HIP_CHECK(hipFuncSetAttribute((const void*)rtn_row_kernel<uint16_t>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+      hipLaunchKernelGGL(rtn_row_kernel<uint16_t>, dim3((unsigned)m), dim3(kRtnThreads), lds, stream, a);
+    } else {
+      if (lds > 65536)
+        GPTQ_HIP_CHECK(hipFuncSetAttribute((const void*)rtn_row_kernel<float>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds));
+      hipLaunchKernelGGL(rtn_row_kernel<float>, dim3((unsigned)m), dim3(kRtnThreads), lds, stream, a);
+    }
   }
   GPTQ_LAUNCH_CHECK();
   hipLaunchKernelGGL(rtn_reduce_kernel, dim3(1), dim3(1024), 0, stream, (const double*)a.part, m, m * n,
-                     err);
+                     err, (const int*)a.badrow, extra_flag, status);
   GPTQ_LAUNCH_CHECK();
-  int hflag = 0, xflag = 0;
-  GPTQ_HIP_CHECK(hipMemcpyAsync(&hflag, a.flag, sizeof(int), hipMemcpyDeviceToHost, stream));
-  if (extra_flag)
-    GPTQ_HIP_CHECK(hipMemcpyAsync(&xflag, extra_flag, sizeof(int), hipMemcpyDeviceToHost, stream));
-  GPTQ_HIP_CHECK(hipStreamSynchronize(stream));
-  if (xflag) {
-    set_error("channel statistics hold a NaN or Inf");
-    return GPTQ_ERR_NONFINITE;
-  }
-  if (hflag & kFlagNonFinite) {
-    set_error("%s: W holds a NaN or Inf", colscale ? "gptq_awq_quantize" : "gptq_rtn_quantize");
-    return GPTQ_ERR_NONFINITE;
-  }
   return GPTQ_OK;
 }
 

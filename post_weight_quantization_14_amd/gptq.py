@@ -129,8 +129,11 @@ def gptq_prepare_hinv(H: torch.Tensor, diag_key: Optional[torch.Tensor], damp_pe
 
 def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, cfg: QuantConfig,
                         qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
-                        g_idx: torch.Tensor, loss: torch.Tensor,
+                        g_idx: torch.Tensor, loss: torch.Tensor, status: Optional[torch.Tensor] = None,
                         workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue the quantization; never synchronises.  `status` (int32 [1] on
+    the device, optional) receives 0 or GPTQ_ERR_NONFINITE in stream order:
+    read it with check_status()."""
     if not W.is_contiguous():
         raise ValueError("W must be contiguous [m, n]")
     m, n = W.shape
@@ -139,8 +142,29 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, cf
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     st = lib().gptq_quantize_layer(_ptr(W), _dtype_code(W), m, n, _ptr(U), _ptr(perm), ctypes.byref(c),
                                    _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(g_idx), _ptr(loss),
-                                   _ptr(ws), nbytes, _stream(stream))
+                                   _ptr(status), _ptr(ws), nbytes, _stream(stream))
     _check(st, "gptq_quantize_layer")
+
+
+def check_status(*outs) -> None:
+    """Read the device status words of earlier quantizations (one host
+    synchronisation for all of them) and raise GptqError for the first that
+    is not GPTQ_OK.  Each argument is an output dict of quantize_layer /
+    quantize_shared_input, or a list of them."""
+    flat = []
+    for o in outs:
+        if isinstance(o, dict):
+            flat.append(o)
+        else:
+            for x in o:
+                flat.extend(x if isinstance(x, list) else [x])
+    if not flat:
+        return
+    words = torch.cat([o["status"] for o in flat]).cpu().tolist()
+    for w in words:
+        if w != _lib.GPTQ_OK:
+            lib().gptq_last_error()   # keeps the message API uniform
+            raise GptqError(int(w), "gptq_quantize_layer (status word)")
 
 
 # ---------------------------------------------------------------- linear (RTN) quantizer
@@ -162,18 +186,38 @@ def gptq_rtn_workspace_bytes(m: int, n: int, cfg: RtnConfig) -> int:
     return int(lib().gptq_rtn_workspace_bytes(m, n, ctypes.byref(c)))
 
 
+def _status_word(status: Optional[torch.Tensor], check: bool, device) -> Optional[torch.Tensor]:
+    if status is None and check:
+        status = torch.zeros(1, dtype=torch.int32, device=device)
+    return status
+
+
+def _read_status(status: torch.Tensor, where: str) -> None:
+    """Synchronise on the device status word and raise on a non-OK status."""
+    w = int(status.item())
+    if w != _lib.GPTQ_OK:
+        raise GptqError(w, f"{where} (status word: the input holds a NaN or Inf)")
+
+
 def gptq_rtn_quantize(W: torch.Tensor, cfg: RtnConfig, qweight: torch.Tensor, scales: torch.Tensor,
                       zeros: torch.Tensor, err: torch.Tensor, workspace: Optional[torch.Tensor] = None,
-                      stream=None) -> None:
+                      stream=None, status: Optional[torch.Tensor] = None, check: bool = True) -> None:
+    """Enqueue the quantizer (the call itself never synchronises).  check=True
+    reads the device status word afterwards and raises on a NaN/Inf in W;
+    check=False leaves it in `status` (int32 [1]) for the caller."""
     if not W.is_contiguous():
         raise ValueError("W must be contiguous [m, n]")
     m, n = W.shape
     c = cfg.c()
     ws = _workspace(gptq_rtn_workspace_bytes(m, n, cfg), W.device, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    status = _status_word(status, check, W.device)
     st = lib().gptq_rtn_quantize(_ptr(W), _dtype_code(W), m, n, ctypes.byref(c), _ptr(qweight),
-                                 _ptr(scales), _ptr(zeros), _ptr(err), _ptr(ws), nbytes, _stream(stream))
+                                 _ptr(scales), _ptr(zeros), _ptr(err), _ptr(status), _ptr(ws), nbytes,
+                                 _stream(stream))
     _check(st, "gptq_rtn_quantize")
+    if check and m > 0 and n > 0:
+        _read_status(status, "gptq_rtn_quantize")
 
 
 def rtn_quantize(W: torch.Tensor, cfg: RtnConfig) -> dict:
@@ -220,17 +264,22 @@ def gptq_awq_workspace_bytes(m: int, n: int, cfg: RtnConfig) -> int:
 def gptq_awq_quantize(W: torch.Tensor, abs_sum: torch.Tensor, tokens: int, protect: float, cfg: RtnConfig,
                       qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
                       channel_scale: torch.Tensor, err: torch.Tensor, workspace: Optional[torch.Tensor] = None,
-                      stream=None) -> None:
+                      stream=None, status: Optional[torch.Tensor] = None, check: bool = True) -> None:
+    """Enqueue the AWQ-scaled quantizer (never synchronises by itself);
+    check as in gptq_rtn_quantize (NaN/Inf in W or in abs_sum)."""
     if not W.is_contiguous():
         raise ValueError("W must be contiguous [m, n]")
     m, n = W.shape
     c = cfg.c()
     ws = _workspace(gptq_awq_workspace_bytes(m, n, cfg), W.device, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    status = _status_word(status, check, W.device)
     st = lib().gptq_awq_quantize(_ptr(W), _dtype_code(W), m, n, _ptr(abs_sum), tokens, float(protect),
                                  ctypes.byref(c), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(channel_scale),
-                                 _ptr(err), _ptr(ws), nbytes, _stream(stream))
+                                 _ptr(err), _ptr(status), _ptr(ws), nbytes, _stream(stream))
     _check(st, "gptq_awq_quantize")
+    if check and m > 0 and n > 0:
+        _read_status(status, "gptq_awq_quantize")
 
 
 def awq_quantize(W: torch.Tensor, x_tiles, cfg: RtnConfig, protect: float = 2.0) -> dict:
@@ -311,13 +360,16 @@ def alloc_outputs(m: int, n: int, cfg: QuantConfig, device) -> dict:
         g_idx=torch.empty(n, dtype=torch.int32, device=device),
         loss=torch.zeros(2, dtype=torch.float64, device=device),
         perm=torch.empty(n, dtype=torch.int32, device=device),
+        status=torch.zeros(1, dtype=torch.int32, device=device),
     )
 
 
 def quantize_layer(W: torch.Tensor, x_tiles, cfg: QuantConfig, alpha: float = 2.0,
-                   keep_hessian: bool = False) -> dict:
+                   keep_hessian: bool = False, check: bool = True) -> dict:
     """The three calls in order on one layer: accumulate every X tile into H,
-    prepare U, quantize W.  Returns the outputs (and H/key if keep_hessian)."""
+    prepare U, quantize W.  Returns the outputs (and H/key if keep_hessian).
+    check=False leaves the quantizer's status word unread (check_status()
+    reads many at once), so the quantization adds no host synchronisation."""
     m, n = W.shape
     dev = W.device
     H = torch.zeros(n, n, dtype=torch.float32, device=dev)
@@ -332,16 +384,20 @@ def quantize_layer(W: torch.Tensor, x_tiles, cfg: QuantConfig, alpha: float = 2.
     out["U"] = H
     out["lam"] = lam
     gptq_quantize_layer(W, H, out["perm"], cfg, out["qweight"], out["scales"], out["zeros"],
-                        out["g_idx"], out["loss"])
+                        out["g_idx"], out["loss"], out["status"])
+    if check:
+        check_status(out)
     return out
 
 
-def quantize_shared_input(Ws, x_tiles, cfgs, alpha: float = 2.0) -> list:
+def quantize_shared_input(Ws, x_tiles, cfgs, alpha: float = 2.0, check: bool = True) -> list:
     """Linears that read the same input (q/k/v of one attention block, gate/up
     of one MLP) have one Hessian H = 2·XᵀX, and the inverse factor U and the
     column order depend only on H, the damping and act-order: accumulate H and
     prepare U once, then quantize every W under every config (for instance
     two bit widths).  All configs must share damp_percent and desc_act.
+    The quantizations issue no host synchronisation; with check=True their
+    status words are read once, after the last of them.
 
     Returns out[i][j] for W i under config j (the alloc_outputs dict), each
     identical to what quantize_layer gives for that W, X and config."""
@@ -369,8 +425,10 @@ def quantize_shared_input(Ws, x_tiles, cfgs, alpha: float = 2.0) -> list:
             o = alloc_outputs(W.shape[0], n, cfg, dev)
             o["perm"].copy_(perm)
             gptq_quantize_layer(W, H, perm, cfg, o["qweight"], o["scales"], o["zeros"], o["g_idx"],
-                                o["loss"])
+                                o["loss"], o["status"])
             o["lam"] = lam
             row.append(o)
         res.append(row)
+    if check:
+        check_status(res)
     return res

@@ -127,11 +127,11 @@ def test_quantize_argument_errors(L):
     from post_weight_quantization_14_amd import _lib
     q = L.gptq_quantize_layer
 
-    def call(cfg, ws_bytes=None, m=64, n=256, W=FAKE, dtype=_lib.GPTQ_BF16, loss=FAKE):
+    def call(cfg, ws_bytes=None, m=64, n=256, W=FAKE, dtype=_lib.GPTQ_BF16, loss=FAKE, status=None):
         if ws_bytes is None:
             ws_bytes = L.gptq_quantize_workspace_bytes(m, n, ctypes.byref(_cfg()))
         return q(W, dtype, m, n, FAKE, FAKE, ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, loss,
-                 FAKE, ws_bytes, None)
+                 status, FAKE, ws_bytes, None)
 
     assert call(_cfg(bits=5)) == _lib.GPTQ_ERR_UNSUPPORTED
     assert call(_cfg(bits=1)) == _lib.GPTQ_ERR_UNSUPPORTED
@@ -142,10 +142,11 @@ def test_quantize_argument_errors(L):
     assert call(_cfg(), dtype=9) == _lib.GPTQ_ERR_UNSUPPORTED
     assert call(_cfg(), W=None) == _lib.GPTQ_ERR_INVALID_ARG
     assert call(_cfg(), loss=FAKE + 4) == _lib.GPTQ_ERR_INVALID_ARG     # misaligned fp64
+    assert call(_cfg(), status=FAKE + 2) == _lib.GPTQ_ERR_INVALID_ARG   # misaligned int32
     assert call(_cfg(), ws_bytes=16) == _lib.GPTQ_ERR_WORKSPACE
     assert "workspace" in _last(L)
     assert call(_cfg(), m=0) == _lib.GPTQ_OK
-    assert q(FAKE, 0, 4, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == _lib.GPTQ_ERR_INVALID_ARG
+    assert q(FAKE, 0, 4, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == _lib.GPTQ_ERR_INVALID_ARG
 
 
 def test_rtn_argument_errors(L):
@@ -158,7 +159,7 @@ def test_rtn_argument_errors(L):
     def call(cfg, ws_bytes=None, m=64, n=256, W=FAKE, dtype=_lib.GPTQ_BF16, err=FAKE):
         if ws_bytes is None:
             ws_bytes = L.gptq_rtn_workspace_bytes(m, n, ctypes.byref(rcfg()))
-        return q(W, dtype, m, n, ctypes.byref(cfg), FAKE, FAKE, FAKE, err, FAKE, ws_bytes, None)
+        return q(W, dtype, m, n, ctypes.byref(cfg), FAKE, FAKE, FAKE, err, None, FAKE, ws_bytes, None)
 
     assert L.gptq_rtn_workspace_bytes(64, 256, ctypes.byref(rcfg())) > 0
     assert call(rcfg(bits=5)) == _lib.GPTQ_ERR_UNSUPPORTED
@@ -175,7 +176,7 @@ def test_rtn_argument_errors(L):
     assert call(rcfg(), n=40000, ws_bytes=1 << 30) == _lib.GPTQ_ERR_UNSUPPORTED
     assert "LDS" in _last(L)
     assert call(rcfg(), m=0) == _lib.GPTQ_OK
-    assert q(FAKE, 0, 4, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == _lib.GPTQ_ERR_INVALID_ARG
+    assert q(FAKE, 0, 4, 4, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == _lib.GPTQ_ERR_INVALID_ARG
 
 
 def test_w4a16_argument_errors(L):
@@ -242,7 +243,7 @@ def test_awq_argument_errors(L):
     def call(cfg=None, tokens=T, protect=2.0, W=FAKE, cs=FAKE, nbytes=None, mm=m):
         cfg = cfg or rcfg()
         return q(W, _lib.GPTQ_BF16, mm, n, FAKE, tokens, protect, ctypes.byref(cfg), FAKE, FAKE, FAKE, cs,
-                 FAKE, FAKE, wsq if nbytes is None else nbytes, None)
+                 FAKE, None, FAKE, wsq if nbytes is None else nbytes, None)
 
     assert call(rcfg(bits=5)) == _lib.GPTQ_ERR_UNSUPPORTED
     assert call(tokens=0) == _lib.GPTQ_ERR_INVALID_ARG

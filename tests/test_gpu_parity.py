@@ -7,8 +7,8 @@ import torch
 
 import oracle
 import workloads
-from gpu_helpers import (CODE_AGREE, H_REL_FROB, LOSS_REL, SCALE_REL, assert_codes, compare_codes,
-                         f64, rel_frob, spec, unpack_u32)
+from gpu_helpers import (H_REL_FROB, LOSS_REL, check_hessian, check_quantizer, f64, rel_frob, spec,
+                         unpack_u32)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +44,11 @@ HESSIAN_CASES = [
     dict(m=16, n=64, tokens=5),
     dict(m=16, n=136, tokens=300, x_dtype="fp32"),
     dict(m=16, n=2600, tokens=70000),
+    # n % 8 != 0: rows are not 16-byte chunks of whole channels, so these run
+    # the element-load kernel (syrk_bf16_any_kernel)
+    dict(m=16, n=130, tokens=3000),
+    dict(m=16, n=301, tokens=9000),
+    dict(m=16, n=1037, tokens=40000),
 ]
 
 
@@ -60,10 +65,28 @@ def test_hessian_matches_oracle(pq, case):
     X = np.concatenate([f64(t) for t in tiles])
     H_ref, key_ref = oracle.hessian([X], n)
     Hg = f64(H)
-    err = rel_frob(Hg, H_ref)
-    print(f"H rel frob {err:.3e}")
-    assert err <= H_REL_FROB
+    check_hessian(Hg, H_ref)
     assert np.array_equal(Hg, Hg.T), "H must come back exactly symmetric"
+    np.testing.assert_allclose(f64(key), key_ref, rtol=1e-12)
+
+
+@pytest.mark.parametrize("n,ld,off", [(256, 259, 1), (640, 650, 3), (1037, 1040, 2)])
+def test_hessian_strided_unaligned_view(pq, n, ld, off):
+    """X as a column window of a wider bf16 buffer: row stride ld > n and a
+    base address 2·off bytes past a 16-byte boundary, which the direct-to-LDS
+    kernel cannot take (syrk_bf16_any_kernel runs)."""
+    sp = spec(16, ld, 30000)
+    full = workloads.gen_x(sp, "cuda")
+    X = full[:, off:off + n]
+    assert X.stride() == (ld, 1) and (X.data_ptr() % 16) != 0
+    H = torch.zeros(n, n, dtype=torch.float32, device="cuda")
+    key = torch.zeros(n, dtype=torch.float64, device="cuda")
+    pq.gptq_hessian_accumulate(H, key, X, 2.0)
+    torch.cuda.synchronize()
+    H_ref, key_ref = oracle.hessian([f64(X)], n)
+    Hg = f64(H)
+    check_hessian(Hg, H_ref, f"view n={n} ld={ld} +{off}")
+    assert np.array_equal(Hg, Hg.T)
     np.testing.assert_allclose(f64(key), key_ref, rtol=1e-12)
 
 
@@ -85,7 +108,7 @@ def test_hessian_accumulates_over_calls_and_is_deterministic(pq):
     assert torch.equal(H1, H2) and torch.equal(k1, k2), "not bitwise deterministic"
     H3, k3 = run([X[:12345], X[12345:30000], X[30000:]])
     H_ref, key_ref = oracle.hessian([f64(X)], n)
-    assert rel_frob(f64(H3), H_ref) <= H_REL_FROB
+    check_hessian(f64(H3), H_ref, "three calls")
     np.testing.assert_allclose(f64(k3), key_ref, rtol=1e-12)
     # zero tokens leave H and key untouched
     H4, k4 = H1.clone(), k1.clone()
@@ -95,6 +118,12 @@ def test_hessian_accumulates_over_calls_and_is_deterministic(pq):
 
 
 # ---------------------------------------------------------------- stages 2-3
+# The inverse factor from fp32 arithmetic: relative Frobenius error against
+# the oracle's float64 factor of the same H, and the residual of U·H_p·Uᵀ = I.
+# Observed 1.6e-7 to 3.6e-7 (about 3·2^-24) and up to 1.2e-6 on every prepare
+# and full-size case; the bounds are about ten times that.
+U_REL_FROB = 2e-6
+UHU_MAX = 1e-5
 PREPARE_CASES = [(128, True), (200, True), (256, False), (384, True), (1000, True), (1, True),
                  (1500, True)]
 
@@ -121,8 +150,8 @@ def test_prepare_matches_oracle(pq, n, desc):
     Hp = (Hin + lam_ref * np.eye(n))[np.ix_(perm_ref, perm_ref)]
     resid = float(np.abs(U @ Hp @ U.T - np.eye(n)).max())
     print(f"U rel frob {err:.3e}, max|U Hp Uᵀ - I| {resid:.3e}")
-    assert err <= 2e-4
-    assert resid <= 2e-3
+    assert err <= U_REL_FROB
+    assert resid <= UHU_MAX
 
 
 def test_not_positive_definite_and_nonfinite(pq):
@@ -189,33 +218,28 @@ def test_quantize_stage_matches_oracle(pq, case):
     Wf = f64(W)
     U = f64(out["U"])
     perm = out["perm"].cpu().numpy().astype(np.int64)
-    # oracle fed the GPU's own factor and order
-    ref = oracle.gptq_quantize(Wf[:, perm], U, sp.bits, sp.group_size, sp.sym)
-    Q_ref = oracle.unpermute_codes(ref["codes"], perm)
+    # the oracle fed the GPU's own factor and order
     Q = unpack_u32(out["qweight"], n, sp.bits)
-    agree, mx = assert_codes(Q, Q_ref)
-    gidx = out["g_idx"].cpu().numpy()
-    assert gidx.tolist() == oracle.g_index(perm, sp.group_size).tolist()
     sc = out["scales"].cpu().numpy().astype(np.float64)
     zr = out["zeros"].cpu().numpy()
-    clean = np.all(Q == Q_ref, axis=1)
-    np.testing.assert_allclose(sc[clean], ref["scales"][clean], rtol=SCALE_REL)
-    assert np.array_equal(zr[clean], ref["zeros"][clean])
     loss = out["loss"].cpu().numpy()
+    check_quantizer(_ids(case), Wf[:, perm], U, Q[:, perm], sc, zr, sp.bits, sp.group_size, sp.sym,
+                    loss0=loss[0])
+    gidx = out["g_idx"].cpu().numpy()
+    assert gidx.tolist() == oracle.g_index(perm, sp.group_size).tolist()
     Qhat = oracle.dequantize_layer(Q, sc, zr, gidx)
     loss1_ref = float(np.sum((Wf - Qhat) ** 2))
-    print(f"codes agree {agree:.6f} max {mx}; loss0 {loss[0]:.6e} ref {ref['loss0']:.6e}; loss1 {loss[1]:.6e} ref {loss1_ref:.6e}")
-    assert loss[0] == pytest.approx(ref["loss0"], rel=LOSS_REL)
     assert loss[1] == pytest.approx(loss1_ref, rel=1e-6)
     assert Q.min() >= (1 if sp.sym else 0) and Q.max() <= 2 ** sp.bits - 1
 
 
 @pytest.mark.parametrize("bits,group", [(2, -1), (3, -1), (4, -1), (8, -1), (4, 128), (8, 64)])
 def test_symmetric_range_zero_point_ties(pq, bits, group):
-    """Rows whose first group has max = -min put the zero point at exactly
-    (2^b - 1)/2 in exact arithmetic; the float32 quotient that decides it then
-    falls on either side of the tie.  Both sides decide in float32, so zeros
-    (and, given them, codes) must agree on every row."""
+    """Every row's first group has max = -min, which puts the grid position of
+    0 exactly at (2^b - 1)/2: the exact round half to even gives 2^(b-1),
+    and the kernel's zero point (an fp64 quotient of exact operands) must be
+    that on every row, as the oracle's is; the rest of the layer by the
+    tie-aware check."""
     m, n = 96, 384
     sp = spec(m=m, n=n, tokens=3000, bits=bits, group_size=group, desc_act=False, w_seed=4242)
     cfg = _cfg(pq, sp)
@@ -234,34 +258,37 @@ def test_symmetric_range_zero_point_ties(pq, bits, group):
     out = pq.quantize_layer(W, tiles, cfg, keep_hessian=True)
     torch.cuda.synchronize()
     perm = out["perm"].cpu().numpy().astype(np.int64)
-    ref = oracle.gptq_quantize(f64(W)[:, perm], f64(out["U"]), bits, group, False)
     zr = out["zeros"].cpu().numpy()
-    assert np.array_equal(zr[:, 0], ref["zeros"][:, 0])
+    assert zr[:, 0].tolist() == [2 ** (bits - 1)] * m
     Q = unpack_u32(out["qweight"], n, bits)
-    agree, mx = assert_codes(Q, oracle.unpermute_codes(ref["codes"], perm))
-    half = (2 ** bits - 1) / 2
-    print(f"{bits}-bit g{group}: zero points {sorted(set(zr[:, 0].tolist()))} around {half}; codes agree {agree:.6f}")
-    assert set(zr[:, 0].tolist()) <= {int(np.floor(half)), int(np.ceil(half))}
+    st = check_quantizer(f"{bits}-bit g{group} symmetric first groups", f64(W)[:, perm], f64(out["U"]),
+                         Q[:, perm], out["scales"].cpu().numpy().astype(np.float64), zr, bits, group,
+                         False, loss0=out["loss"].cpu().numpy()[0])
+    assert st["zero_flips"] == 0
 
 
 def test_end_to_end_tiny_layer_config(pq):
     """The 256 x 256 fp32 layer, 512 tokens, 4-bit asym g128, no act-order:
-    both sides free-running from W and X."""
+    both sides free-running from W and X (the oracle forms its own H, λ, order
+    and U)."""
     sp = workloads.CONFIGS["c1_tiny_256"]
     cfg = _cfg(pq, sp)
     W, tiles, out = _gpu_layer(pq, sp, cfg)
     X = np.concatenate([f64(t) for t in tiles])
     H_ref, key_ref = oracle.hessian([X], sp.n)
-    assert rel_frob(f64(out["H"]), H_ref) <= H_REL_FROB
+    check_hessian(f64(out["H"]), H_ref, "C1 H")
+    U_ref, perm_ref, lam_ref = oracle.prepare(H_ref, key_ref, sp.damp_percent, sp.desc_act)
+    assert out["perm"].cpu().numpy().tolist() == perm_ref.tolist()
+    assert out["lam"] == pytest.approx(lam_ref, rel=1e-9)
     ref = oracle.gptq_layer(f64(W), H_ref, key_ref, sp.bits, sp.group_size, sp.sym, sp.desc_act,
                             sp.damp_percent)
-    assert out["perm"].cpu().numpy().tolist() == ref["perm"].tolist()
     Q = unpack_u32(out["qweight"], sp.n, sp.bits)
-    agree, mx = assert_codes(Q, ref["codes"])
-    clean = np.all(Q == ref["codes"], axis=1)
-    np.testing.assert_allclose(out["scales"].cpu().numpy()[clean], ref["scales"][clean], rtol=SCALE_REL)
+    sc = out["scales"].cpu().numpy().astype(np.float64)
+    zr = out["zeros"].cpu().numpy()
     loss = out["loss"].cpu().numpy()
-    print(f"C1 codes agree {agree:.6f}; loss0 {loss[0]:.6e} vs {ref['loss0']:.6e}")
+    check_quantizer("C1 end to end", f64(W)[:, perm_ref], U_ref, Q[:, perm_ref], sc, zr, sp.bits,
+                    sp.group_size, sp.sym, loss0=loss[0])
+    print(f"C1: loss0 {loss[0]:.6e} vs {ref['loss0']:.6e}; loss1 {loss[1]:.6e} vs {ref['loss1']:.6e}")
     assert loss[0] == pytest.approx(ref["loss0"], rel=LOSS_REL)
     assert loss[1] == pytest.approx(ref["loss1"], rel=LOSS_REL)
-    assert out["lam"] == pytest.approx(ref["lam"], rel=1e-9)
+    assert out["g_idx"].cpu().numpy().tolist() == ref["g_idx"].tolist()

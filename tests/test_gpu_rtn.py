@@ -81,6 +81,41 @@ def test_rtn_matches_oracle(pq, case):
     _check(pq, W, bits, group, sym, clip)
 
 
+# clip_ratio 1: the streaming kernel (16-byte aligned rows, n % 8 == 0,
+# n <= 32768, groups of 8·d columns with d dividing 64, or one per row)
+STREAM_CASES = [
+    (16, 512, torch.bfloat16, 4, 8, False),
+    (16, 1024, torch.bfloat16, 2, 16, True),
+    (16, 1000, torch.bfloat16, 3, 32, False),     # ragged last group (8 columns)
+    (16, 4096, torch.float32, 8, 64, True),
+    (16, 11008, torch.bfloat16, 4, 128, False),
+    (16, 2048, torch.bfloat16, 4, 256, True),
+    (16, 4000, torch.float32, 3, 512, False),     # ragged last group (416 columns)
+    (4, 32768, torch.bfloat16, 8, -1, False),     # the longest row it takes
+    (16, 4096, torch.bfloat16, 4, -1, True),
+    (16, 8, torch.float32, 4, -1, False),
+    (16, 64, torch.bfloat16, 4, 128, False),      # one group wider than the row
+]
+
+
+@pytest.mark.parametrize("case", STREAM_CASES, ids=lambda c: f"m{c[0]}_n{c[1]}_{str(c[2])[6:]}_b{c[3]}_g{c[4]}_{'sym' if c[5] else 'asym'}")
+def test_rtn_streaming_path_matches_oracle_and_general_kernel(pq, case):
+    """Against the oracle, and bit for bit against the general (sorting)
+    kernel, which runs on the same weights copied to a row base 2 or 4 bytes
+    past a 16-byte boundary."""
+    m, n, dtype, bits, group, sym = case
+    W = _weights(m, n, dtype, seed=7 * m + n)
+    out, err = _check(pq, W, bits, group, sym, 1.0)
+    buf = torch.empty(m * n + 8, dtype=dtype, device="cuda")
+    Wm = buf[1:1 + m * n].view(m, n)
+    Wm.copy_(W)
+    assert Wm.is_contiguous() and Wm.data_ptr() % 16 != 0
+    gen = pq.rtn_quantize(Wm, pq.RtnConfig(bits=bits, group_size=group, sym=sym, clip_ratio=1.0))
+    for k in ("qweight", "scales", "zeros"):
+        assert torch.equal(out[k], gen[k]), k
+    np.testing.assert_allclose(gen["err"].cpu().numpy(), err, rtol=1e-12)
+
+
 def test_rtn_all_zero_rows_and_ties(pq):
     # zero rows use the 1e-8 floor; values on exact half steps round to even
     W = torch.zeros(4, 64, dtype=torch.float32, device="cuda")
@@ -134,11 +169,23 @@ def test_rtn_errors(pq):
     with pytest.raises(pq.GptqError) as ei:
         pq.rtn_quantize(W, pq.RtnConfig(clip_ratio=0.0))
     assert ei.value.status == -1
-    W2 = W.clone()
-    W2[2, 7] = float("nan")
-    with pytest.raises(pq.GptqError) as ei:
-        pq.rtn_quantize(W2, pq.RtnConfig())
-    assert ei.value.status == -5
+    for clip in (1.0, 0.99):   # the streaming kernel and the general one
+        for bad in (float("nan"), float("inf")):
+            W2 = W.clone()
+            W2[2, 7] = bad
+            with pytest.raises(pq.GptqError) as ei:
+                pq.rtn_quantize(W2, pq.RtnConfig(clip_ratio=clip))
+            assert ei.value.status == -5
+    # the call itself never synchronises: its status word is the caller's to read
+    cfg = pq.RtnConfig(bits=4, group_size=32, sym=False, clip_ratio=1.0)
+    out = pq.rtn_quantize(W, cfg)
+    status = torch.full((1,), 99, dtype=torch.int32, device="cuda")
+    pq.gptq_rtn_quantize(W2, cfg, out["qweight"], out["scales"], out["zeros"], out["err"],
+                         status=status, check=False)
+    assert int(status.item()) == -5
+    pq.gptq_rtn_quantize(W, cfg, out["qweight"], out["scales"], out["zeros"], out["err"],
+                         status=status, check=False)
+    assert int(status.item()) == 0
     big = torch.zeros(1, 40000, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(pq.GptqError) as ei:
         pq.rtn_quantize(big, pq.RtnConfig(group_size=-1))   # one 40000-column group: too large to sort on chip

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_helpers import LOSS_REL, SCALE_REL, assert_codes, f64, spec, unpack_u32
+from gpu_helpers import LOSS_REL, check_quantizer, f64, spec, unpack_u32
 
 pytestmark = pytest.mark.gpu
 
@@ -76,16 +76,12 @@ def test_shared_input_matches_oracle_and_per_linear_path(pq, case):
             ref = oracle.gptq_layer(f64(W), None, None, cfg.bits, cfg.group_size, sym, desc_act, 0.01,
                                     U=U, perm=perm_ref)
             Q = unpack_u32(out["qweight"], n, cfg.bits)
-            agree, mx = assert_codes(Q, ref["codes"], f"W{i} setting {j}")
-            clean = np.all(Q == ref["codes"], axis=1)
-            np.testing.assert_allclose(out["scales"].cpu().numpy()[clean], ref["scales"][clean],
-                                       rtol=SCALE_REL)
-            assert np.array_equal(out["zeros"].cpu().numpy()[clean], ref["zeros"][clean])
-            assert out["g_idx"].cpu().numpy().tolist() == ref["g_idx"].tolist()
             loss = out["loss"].cpu().numpy()
-            print(f"W{i} ({W.shape[0]}x{n}) {cfg.bits}-bit g{cfg.group_size}: codes agree {agree:.6f}; "
-                  f"loss0 {loss[0]:.6e} vs {ref['loss0']:.6e}")
-            assert loss[0] == pytest.approx(ref["loss0"], rel=LOSS_REL)
+            check_quantizer(f"W{i} ({W.shape[0]}x{n}) {cfg.bits}-bit g{cfg.group_size}",
+                            f64(W)[:, perm_ref], U, Q[:, perm_ref],
+                            out["scales"].cpu().numpy().astype(np.float64), out["zeros"].cpu().numpy(),
+                            cfg.bits, cfg.group_size, sym, loss0=loss[0])
+            assert out["g_idx"].cpu().numpy().tolist() == ref["g_idx"].tolist()
             assert loss[1] == pytest.approx(ref["loss1"], rel=LOSS_REL)
 
 
