@@ -300,6 +300,24 @@ gptq_status gptq_w4a16_matmul(const void* X, int64_t tokens, int64_t ldx, const 
                               int64_t m, int64_t n, int32_t group_size, float* Y, int64_t ldy,
                               void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * gptq_w4a16_matmul without a workspace: for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, result and rules as
+ * gptq_w4a16_matmul minus the workspace: the gather, partial sums and
+ * position sums live in a static device array the library holds on every GPU
+ * it runs on until the process ends (gptq_w4a16_noalloc_scratch_bytes()
+ * bytes, 32 MiB).  The call allocates nothing; when 64 tokens per launch
+ * sequence would not fit it takes fewer, and it returns GPTQ_ERR_UNSUPPORTED
+ * (before launching anything) when even 16 tokens per launch do not fit the
+ * array.  Calls that overlap on one GPU race on the array: serialise them
+ * (one stream, or events).  The result is bit-identical to gptq_w4a16_matmul.
+ * ---------------------------------------------------------------------- */
+size_t gptq_w4a16_noalloc_scratch_bytes(void);
+gptq_status gptq_w4a16_matmul_noalloc(const void* X, int64_t tokens, int64_t ldx, const void* packed,
+                                      int64_t m, int64_t n, int32_t group_size, float* Y, int64_t ldy,
+                                      void* stream);
+
 /* Sizes of the outputs above (host-only helpers, no GPU work). */
 int64_t gptq_qweight_words(int64_t n, int32_t bits);
 int64_t gptq_num_groups(int64_t n, int32_t group_size);

@@ -26,6 +26,7 @@ from .gptq import (  # noqa: F401
     gptq_rtn_quantize,
     gptq_rtn_workspace_bytes,
     gptq_w4a16_matmul,
+    gptq_w4a16_matmul_noalloc,
     gptq_w4a16_pack,
     gptq_w4a16_packed_bytes,
     gptq_w4a16_workspace_bytes,

@@ -360,4 +360,26 @@ gptq_status gptq_w4a16_matmul(const void* X, int64_t tokens, int64_t ldx, const 
                           static_cast<hipStream_t>(stream));
 }
 
+size_t gptq_w4a16_noalloc_scratch_bytes(void) { return w4a16_noalloc_scratch_bytes(); }
+
+gptq_status gptq_w4a16_matmul_noalloc(const void* X, int64_t tokens, int64_t ldx, const void* packed,
+                                      int64_t m, int64_t n, int32_t group_size, float* Y, int64_t ldy,
+                                      void* stream) {
+  clear_error();
+  if (tokens < 0 || m < 0 || n < 0)
+    return fail(GPTQ_ERR_INVALID_ARG, "tokens=%lld m=%lld n=%lld", (long long)tokens, (long long)m,
+                (long long)n);
+  if (!w4_group_ok(group_size))
+    return fail(GPTQ_ERR_UNSUPPORTED, "group_size=%d (32, 64, 128 or -1)", group_size);
+  if (tokens == 0 || m == 0 || n == 0) return GPTQ_OK;
+  if (m > ((int64_t)1 << 30) || n > ((int64_t)1 << 30))
+    return fail(GPTQ_ERR_UNSUPPORTED, "m=%lld n=%lld too large", (long long)m, (long long)n);
+  if (ldx < n || ldy < m)
+    return fail(GPTQ_ERR_INVALID_ARG, "ldx=%lld < n or ldy=%lld < m", (long long)ldx, (long long)ldy);
+  if (bad_ptr(X, 2) || bad_ptr(Y, 4)) return fail(GPTQ_ERR_INVALID_ARG, "X or Y is NULL or misaligned");
+  if (bad_ptr(packed, 256)) return fail(GPTQ_ERR_INVALID_ARG, "packed is NULL or not 256-byte aligned");
+  return run_w4a16_matmul_noalloc(static_cast<const uint16_t*>(X), tokens, ldx, packed,
+                                  plan_w4a16(m, n, group_size), Y, ldy, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

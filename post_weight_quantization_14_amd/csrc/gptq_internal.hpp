@@ -185,13 +185,21 @@ struct W4GemmPlan {
   int64_t chunk_tokens = 0, mp = 0, chunks = 0, splits = 0;
   size_t xp_off = 0, xs_off = 0, part_off = 0, total = 0;
 };
-W4GemmPlan plan_w4a16_gemm(int64_t tokens, int64_t m, int64_t n);
+// max_chunk_tokens: tokens per gather / product / reduce sequence, at most 64
+W4GemmPlan plan_w4a16_gemm(int64_t tokens, int64_t m, int64_t n, int64_t max_chunk_tokens = 64);
 gptq_status run_w4a16_pack(const uint32_t* qweight, const float* scales, const int32_t* zeros,
                            const int32_t* g_idx, int bits, const W4Layout& L, void* packed,
                            hipStream_t stream);
 gptq_status run_w4a16_matmul(const uint16_t* X, int64_t tokens, int64_t ldx, const void* packed,
                              const W4Layout& L, float* Y, int64_t ldy, void* ws,
                              const W4GemmPlan& p, hipStream_t stream);
+// The same product on the library's own per-device scratch array (no workspace
+// argument, no allocation); GPTQ_ERR_UNSUPPORTED when even 16 tokens per launch
+// need more than it holds.
+size_t w4a16_noalloc_scratch_bytes();
+W4GemmPlan plan_w4a16_noalloc(int64_t tokens, int64_t m, int64_t n);
+gptq_status run_w4a16_matmul_noalloc(const uint16_t* X, int64_t tokens, int64_t ldx, const void* packed,
+                                     const W4Layout& L, float* Y, int64_t ldy, hipStream_t stream);
 
 // ---------------------------------------------------------------- fp32-accurate GEMM on bf16 MFMA
 // Operands as three exact bf16 planes [3][rows][kp] (plane q at p + q·pstride,

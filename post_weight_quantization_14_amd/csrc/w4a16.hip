@@ -32,6 +32,8 @@
 //            scaled and folded into the result
 //   reduce : Y = Σ over slices in slice order (deterministic)
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "gptq_internal.hpp"
 
@@ -504,9 +506,10 @@ W4Layout plan_w4a16(int64_t m, int64_t n, int32_t group_size) {
   return L;
 }
 
-W4GemmPlan plan_w4a16_gemm(int64_t tokens, int64_t m, int64_t n) {
+W4GemmPlan plan_w4a16_gemm(int64_t tokens, int64_t m, int64_t n, int64_t max_chunk_tokens) {
   W4GemmPlan p;
-  p.chunk_tokens = std::min<int64_t>(std::max<int64_t>(tokens, 1), (int64_t)kW4TokTile * kW4MaxTokTiles);
+  p.chunk_tokens = std::min<int64_t>(std::max<int64_t>(tokens, 1),
+                                     std::min<int64_t>(max_chunk_tokens, (int64_t)kW4TokTile * kW4MaxTokTiles));
   p.mp = p.chunk_tokens;
   const int64_t mt = ceil_div(m, kW4Rows), kc = ceil_div(n, kW4Chunk);
   const int64_t wgs_rows = ceil_div(mt, kW4TilesPerWg);
@@ -630,6 +633,62 @@ gptq_status run_w4a16_matmul(const uint16_t* X, int64_t tokens, int64_t ldx, con
     GPTQ_LAUNCH_CHECK();
   }
   return GPTQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The product without caller workspace (gptq_w4a16_matmul_noalloc), for
+// callers that cannot allocate device memory: its gather, partial sums and
+// per-32-position sums live in this file-scope array, one copy per GPU, held
+// until the process ends.  Host code never passes the array's name to a
+// kernel (in host code it is only a stand-in for the symbol): each device's
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current, and every launch gets that address.  Nothing in the array
+// needs to start at zero (every byte a call reads it wrote first), and calls
+// that overlap on one GPU race on it.
+// ---------------------------------------------------------------------------
+constexpr size_t kW4NoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kW4NoAllocScratchBytes];
+
+namespace {
+gptq_status noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static std::vector<void*> per_device;
+  int dev = 0;
+  GPTQ_HIP_CHECK(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)per_device.size() <= dev) per_device.resize(dev + 1, nullptr);
+  if (per_device[dev] == nullptr) {
+    void* ptr = nullptr;
+    GPTQ_HIP_CHECK(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    per_device[dev] = ptr;
+  }
+  *out = per_device[dev];
+  return GPTQ_OK;
+}
+}  // namespace
+
+size_t w4a16_noalloc_scratch_bytes() { return kW4NoAllocScratchBytes; }
+
+W4GemmPlan plan_w4a16_noalloc(int64_t tokens, int64_t m, int64_t n) {
+  // fewer tokens per launch sequence when 64 would not fit the array
+  W4GemmPlan p = plan_w4a16_gemm(tokens, m, n);
+  for (int64_t chunk = p.chunk_tokens / 2; p.total > kW4NoAllocScratchBytes && chunk >= kW4TokTile; chunk /= 2)
+    p = plan_w4a16_gemm(tokens, m, n, chunk);
+  return p;
+}
+
+gptq_status run_w4a16_matmul_noalloc(const uint16_t* X, int64_t tokens, int64_t ldx, const void* packed,
+                                     const W4Layout& L, float* Y, int64_t ldy, hipStream_t stream) {
+  const W4GemmPlan p = plan_w4a16_noalloc(tokens, L.m, L.n);
+  if (p.total > kW4NoAllocScratchBytes) {
+    set_error("gptq_w4a16_matmul_noalloc: a %lld x %lld weight needs %zu bytes of scratch at 16 tokens "
+              "per launch; the library holds %zu (use gptq_w4a16_matmul with a workspace)",
+              (long long)L.m, (long long)L.n, p.total, kW4NoAllocScratchBytes);
+    return GPTQ_ERR_UNSUPPORTED;
+  }
+  void* ws = nullptr;
+  GPTQ_TRY(noalloc_scratch(&ws));
+  return run_w4a16_matmul(X, tokens, ldx, packed, L, Y, ldy, ws, p, stream);
 }
 
 }  // namespace gptq

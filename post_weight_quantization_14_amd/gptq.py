@@ -349,6 +349,19 @@ def gptq_w4a16_matmul(X: torch.Tensor, packed: torch.Tensor, m: int, n: int, gro
     return Y
 
 
+def gptq_w4a16_matmul_noalloc(X: torch.Tensor, packed: torch.Tensor, m: int, n: int, group_size: int,
+                              Y: torch.Tensor, stream=None) -> torch.Tensor:
+    """gptq_w4a16_matmul on the library's own device scratch (no workspace;
+    the C call allocates nothing).  Y [tokens, m] fp32 must be given."""
+    if X.dim() != 2 or X.shape[1] != n or (X.shape[0] > 0 and X.stride(1) != 1):
+        raise ValueError("X must be [tokens, n] with contiguous rows")
+    tokens = X.shape[0]
+    st = lib().gptq_w4a16_matmul_noalloc(_ptr(X), tokens, X.stride(0) if tokens > 0 else n, _ptr(packed), m, n,
+                                         group_size, _ptr(Y), Y.stride(0) if tokens > 0 else m, _stream(stream))
+    _check(st, "gptq_w4a16_matmul_noalloc")
+    return Y
+
+
 # ---------------------------------------------------------------- whole layer
 def alloc_outputs(m: int, n: int, cfg: QuantConfig, device) -> dict:
     words = gptq_qweight_words(n, cfg.bits)

@@ -217,6 +217,32 @@ def test_w4a16_argument_errors(L):
     assert mm_(tokens=0) == _lib.GPTQ_OK
 
 
+def test_w4a16_noalloc_argument_errors(L):
+    """The no-workspace product rejects bad arguments, and a weight whose
+    scratch would not fit the library's array even at 16 tokens per launch,
+    on the host before any launch."""
+    from post_weight_quantization_14_amd import _lib
+    assert L.gptq_w4a16_noalloc_scratch_bytes() == 32 << 20
+    m, n = 64, 256
+
+    def call(tokens=16, ldx=n, g=128, X=FAKE, Y=FAKE, ldy=m, packed=FAKE, mm=m, nn=n):
+        return L.gptq_w4a16_matmul_noalloc(X, tokens, ldx, packed, mm, nn, g, Y, ldy, None)
+
+    assert call(g=48) == _lib.GPTQ_ERR_UNSUPPORTED
+    assert call(ldx=n - 1) == _lib.GPTQ_ERR_INVALID_ARG
+    assert call(ldy=m - 1) == _lib.GPTQ_ERR_INVALID_ARG
+    assert call(X=None) == _lib.GPTQ_ERR_INVALID_ARG
+    assert call(Y=FAKE + 2) == _lib.GPTQ_ERR_INVALID_ARG
+    assert call(packed=FAKE + 16) == _lib.GPTQ_ERR_INVALID_ARG
+    assert call(tokens=-1) == _lib.GPTQ_ERR_INVALID_ARG
+    assert call(tokens=0) == _lib.GPTQ_OK
+    # 65536 x 65536: 128 slices x 16 tokens x 65536 rows of fp32 partials
+    # alone are 512 MiB
+    big = 65536
+    assert call(mm=big, nn=big, ldx=big, ldy=big) == _lib.GPTQ_ERR_UNSUPPORTED
+    assert "scratch" in _last(L)
+
+
 def test_awq_argument_errors(L):
     from post_weight_quantization_14_amd import _lib
     n, T = 256, 1000
