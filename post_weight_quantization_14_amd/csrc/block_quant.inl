@@ -43,12 +43,15 @@ struct BqCtx {
   float w[8];      // columns 8j .. 8j+7 of this lane's row
   float e8[8];     // errors of the owned columns (lane j owns columns 8j..8j+7)
   uint32_t c8[2];  // codes of the owned columns, one per byte
-  f32x4_t u0, u1;  // U[c][8j .. 8j+7] of the current column c (prefetched one step ahead)
-  float ud;        // U[c][c]
-  float s, z, lacc;
-  // branch-free code: clamp(rint(fl(w/s) + zpre), qlo, qhi) + post, with
-  // zpre = z, post = 0 (asym) or zpre = 0, post = z (sym): the same roundings
-  // as quant_code, no branch on sym in the column chain
+  // U[c][8j .. 8j+7] and 1/U[c][c] of column c in slot c % 3: each row is
+  // read two columns ahead into its own slot (no register moves, so no wait
+  // on the read until the column that uses it)
+  f32x4_t ua[3], ub[3];
+  float rd[3];
+  float s, rs, z, lacc;   // the group's scale, its reciprocal and zero point
+  // branch-free code: clamp(rint(w·(1/s) + zpre), qlo, qhi) + post, with
+  // zpre = z, post = 0 (asym) or zpre = 0, post = z (sym): no branch on sym
+  // and no division in the column chain
   float zpre, post, qlo, qhi;
   int bits, sym, bw, j;
   bool act;
@@ -56,11 +59,16 @@ struct BqCtx {
   int32_t* zrow;
   int64_t g_base;
   const float* us;   // LDS U block [128][128]
+  const float* rdg;  // LDS reciprocals of U's diagonal [128]
 };
 
-template <int GW, int C>
+// FULL: a whole 128-column block (no per-column bound check, so the column
+// chain is one straight basic block)
+template <int GW, bool FULL, int C>
 __device__ __forceinline__ void bq_col(BqCtx& x) {
-  if (C >= x.bw) return;   // uniform: ragged last block
+  if constexpr (!FULL) {
+    if (C >= x.bw) return;   // uniform: ragged last block
+  }
   constexpr int J = C >> 3, P = C & 7;
   if constexpr (GW > 0 && C % GW == 0) {
     // group = columns [C, C + GW) ∩ [0, bw), spread over lanes C/8 ..
@@ -81,6 +89,7 @@ __device__ __forceinline__ void bq_col(BqCtx& x) {
       am = fmaxf(am, __shfl_xor(am, d, 16));
     }
     grid_params(lo, hi, am, x.bits, x.sym, x.s, x.z);
+    x.rs = 1.f / x.s;
     x.zpre = x.sym ? 0.f : x.z;
     x.post = x.sym ? x.z : 0.f;
     if (x.act && x.j == 0) {
@@ -89,14 +98,23 @@ __device__ __forceinline__ void bq_col(BqCtx& x) {
       x.zrow[g] = (int32_t)x.z;
     }
   }
-  // U of the next column, in flight while this one is quantized
-  constexpr int CN = (C + 1 < QB) ? C + 1 : C;
-  const f32x4_t n0 = *reinterpret_cast<const f32x4_t*>(x.us + CN * QB + 8 * x.j);
-  const f32x4_t n1 = *reinterpret_cast<const f32x4_t*>(x.us + CN * QB + 8 * x.j + 4);
-  const float nd = x.us[CN * QB + CN];
+  // U of the column after next, in flight while this one and the next are
+  // quantized.  The scheduling barrier keeps these reads here: left to
+  // itself the scheduler sinks them to their use, two columns on, and the
+  // chain then waits for them.
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (C + 2 < QB) {
+    constexpr int CN = C + 2, SN = CN % 3;
+    x.ua[SN] = *reinterpret_cast<const f32x4_t*>(x.us + CN * QB + 8 * x.j);
+    x.ub[SN] = *reinterpret_cast<const f32x4_t*>(x.us + CN * QB + 8 * x.j + 4);
+    x.rd[SN] = x.rdg[CN];
+  }
+  constexpr int SC = C % 3;
   const float v = row_bcast<J>(x.w[P]);
-  const float code = fminf(fmaxf(rintf(v / x.s + x.zpre), x.qlo), x.qhi) + x.post;
-  const float e = (v - (code - x.z) * x.s) / x.ud;
+  // the code from w·(1/s) (within one ulp of w/s: only a grid position that
+  // close to a half-integer can round the other way) and e·(1/U[c][c])
+  const float code = fminf(fmaxf(rintf(v * x.rs + x.zpre), x.qlo), x.qhi) + x.post;
+  const float e = (v - (code - x.z) * x.s) * x.rd[SC];
   if (x.j == J) {
     x.e8[P] = e;
     x.c8[P >> 2] |= ((uint32_t)code) << (8 * (P & 3));
@@ -104,17 +122,14 @@ __device__ __forceinline__ void bq_col(BqCtx& x) {
   }
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    x.w[p] -= e * x.u0[p];
-    x.w[p + 4] -= e * x.u1[p];
+    x.w[p] -= e * x.ua[SC][p];
+    x.w[p + 4] -= e * x.ub[SC][p];
   }
-  x.u0 = n0;
-  x.u1 = n1;
-  x.ud = nd;
 }
 
-template <int GW, int... Cs>
+template <int GW, bool FULL, int... Cs>
 __device__ __forceinline__ void bq_cols(std::integer_sequence<int, Cs...>, BqCtx& x) {
-  (bq_col<GW, Cs>(x), ...);
+  (bq_col<GW, FULL, Cs>(x), ...);
 }
 
 // The lazy update of the rest of the superblock from this block's errors,
@@ -160,12 +175,13 @@ __device__ __forceinline__ void push_load(PushBlk& t, const float* __restrict__ 
 }
 
 // GW > 0: group width (a power of two dividing 128); GW == 0: one group per
-// row, its grid already in scales/zeros.
-template <int GW>
+// row, its grid already in scales/zeros.  FULL: bw == 128.
+template <int GW, bool FULL>
 __global__ __launch_bounds__(256) void block_quant_kernel(QArgs q, const float* __restrict__ ublk,
                                                          int64_t ldu, int64_t i1, int bw,
                                                          const float* __restrict__ upush, int ncols) {
   __shared__ __attribute__((aligned(16))) float us[QB * QB];
+  __shared__ float rdg[QB];
   __shared__ __attribute__((aligned(16))) float es[kBqRows * kEsPitch];
   const int tid = threadIdx.x;
   // the push's operands: its first block's loads go out now
@@ -182,6 +198,7 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs q, const float* 
     const int r = idx >> 7, c = idx & (QB - 1);
     us[idx] = (r < bw && c < bw && c >= r) ? ublk[r * ldu + c] : 0.f;
   }
+  if (tid < QB) rdg[tid] = tid < bw ? 1.f / ublk[tid * ldu + tid] : 1.f;
 
   const int lane = tid & 63, wave = tid >> 6;
   BqCtx x;
@@ -208,6 +225,7 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs q, const float* 
     x.s = q.scales[rr * q.G];
     x.z = (float)q.zeros[rr * q.G];
   }
+  x.rs = 1.f / x.s;
   x.qlo = q.sym ? -(float)((1 << (q.bits - 1)) - 1) : 0.f;
   x.qhi = q.sym ? (float)((1 << (q.bits - 1)) - 1) : (float)((1 << q.bits) - 1);
   x.zpre = q.sym ? 0.f : x.z;
@@ -217,11 +235,15 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs q, const float* 
   x.zrow = q.zeros + rr * q.G;
   x.g_base = i1;
   x.us = us;
+  x.rdg = rdg;
   __syncthreads();
-  x.u0 = *reinterpret_cast<const f32x4_t*>(us + 8 * x.j);
-  x.u1 = *reinterpret_cast<const f32x4_t*>(us + 8 * x.j + 4);
-  x.ud = us[0];
-  bq_cols<GW>(std::make_integer_sequence<int, QB>{}, x);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    x.ua[c] = *reinterpret_cast<const f32x4_t*>(us + c * QB + 8 * x.j);
+    x.ub[c] = *reinterpret_cast<const f32x4_t*>(us + c * QB + 8 * x.j + 4);
+    x.rd[c] = rdg[c];
+  }
+  bq_cols<GW, FULL>(std::make_integer_sequence<int, QB>{}, x);
 
   float lacc = x.lacc;
 #pragma unroll
@@ -288,8 +310,12 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs q, const float* 
 template <>
 void launch_block_quant<GPTQ_BQ_GW>(const QArgs& a, const float* ublk, int64_t ldu, int64_t i1,
                                     int bw, int ncols, hipStream_t stream) {
-  hipLaunchKernelGGL(block_quant_kernel<GPTQ_BQ_GW>, dim3((unsigned)ceil_div(a.m, kBqRows)), dim3(256), 0,
-                     stream, a, ublk, ldu, i1, bw, ublk + bw, ncols);
+  if (bw == QB)
+    hipLaunchKernelGGL((block_quant_kernel<GPTQ_BQ_GW, true>), dim3((unsigned)ceil_div(a.m, kBqRows)), dim3(256),
+                       0, stream, a, ublk, ldu, i1, bw, ublk + bw, ncols);
+  else
+    hipLaunchKernelGGL((block_quant_kernel<GPTQ_BQ_GW, false>), dim3((unsigned)ceil_div(a.m, kBqRows)), dim3(256),
+                       0, stream, a, ublk, ldu, i1, bw, ublk + bw, ncols);
 }
 
 }  // namespace gptq
