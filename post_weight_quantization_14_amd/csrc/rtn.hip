@@ -464,23 +464,21 @@ __global__ __launch_bounds__(kRtnThreads) void rtn_row_kernel(RtnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Streaming path for clip_ratio = 1, where every grid comes from its group's
-// extremes and no order statistic is needed: one workgroup of 256 threads
-// per output row, thread t owning the 8-column chunks t, t + 256, ... of the
-// row (one 16-byte load of bf16, two of fp32, per chunk), all of them loaded
-// before any arithmetic.  A group of g = 8·GL columns is GL consecutive lanes
-// of one wave (GL divides 64, and chunk t + 256k of lane l of wave w is
-// 64w + l + 256k); its extremes are xor-butterflies over those lanes.  GL = 0:
-// one group per row, extremes by a block reduction.  The grid, the codes and
-// the error sums are those of rtn_row_kernel (the same fp64 grid, the same
-// code rule), so the two paths give identical outputs.
+// extremes and no order statistic is needed: one workgroup per output row,
+// thread t holding the 8-column chunks t, t + NT, ... of the row in registers
+// (one 16-byte load of bf16, two of fp32, per chunk); groups are whole chunks
+// (g a multiple of 8, g/8 a power of two) or the whole row.  The grid is
+// rtn_row_kernel's fp64 grid and every code the same rounding decision, so
+// the two paths give identical codes, scales and zeros.
 // ---------------------------------------------------------------------------
-constexpr int kStreamThreads = 256;
-constexpr int kStreamMaxChunks = 16;   // n <= 8·256·16 = 32768
-
 template <typename T> struct Chunk;
+// hide() makes the held words opaque to the compiler (no instruction), so a
+// second pass unpacks them again instead of keeping the first pass's floats
+// alive in twice the registers.
 template <> struct Chunk<uint16_t> {
   uint4 v;
   __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void hide() { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
   __device__ __forceinline__ void get(float (&x)[8]) const {
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -496,6 +494,7 @@ template <> struct Chunk<float> {
     a = *reinterpret_cast<const f32x4_t*>(p);
     b = *reinterpret_cast<const f32x4_t*>(p + 4);
   }
+  __device__ __forceinline__ void hide() { asm volatile("" : "+v"(a), "+v"(b)); }
   __device__ __forceinline__ void get(float (&x)[8]) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -505,139 +504,233 @@ template <> struct Chunk<float> {
   }
 };
 
-template <typename T, int GL>
-__global__ __launch_bounds__(kStreamThreads) void rtn_stream_kernel(RtnArgs a) {
-  __shared__ float red_lo[kStreamThreads / 64], red_hi[kStreamThreads / 64];
-  __shared__ double red[4][kStreamThreads / 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t r = blockIdx.x;
-  const int nc = (int)(a.n >> 3);
-  const T* wrow = static_cast<const T*>(a.W) + r * a.n;
-  Chunk<T> raw[kStreamMaxChunks];
-  // unconditional loads at clamped chunk indices: all in flight at once (a
-  // conditional load compiles to a branch and a wait of its own)
-#pragma unroll
-  for (int k = 0; k < kStreamMaxChunks; ++k) {
-    const int c8 = min(tid + kStreamThreads * k, nc - 1);
-    raw[k].load(wrow + 8 * c8);
-  }
-  bool bad = false;
-  float glo[kStreamMaxChunks], ghi[kStreamMaxChunks];
-#pragma unroll
-  for (int k = 0; k < kStreamMaxChunks; ++k) {
-    const int c8 = tid + kStreamThreads * k;
-    float lo = INFINITY, hi = -INFINITY;
-    if (c8 < nc) {
-      float x[8];
-      raw[k].get(x);
-      float cs[8];
-      if (a.colscale) {
-        const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(a.colscale + 8 * c8);
-        const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(a.colscale + 8 * c8 + 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { cs[i] = c0[i]; cs[i + 4] = c1[i]; }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = a.colscale ? x[e] * cs[e] : x[e];
-        bad |= !isfinite(v);
-        const float key = a.sym ? fabsf(v) : v;
-        lo = fminf(lo, key);
-        hi = fmaxf(hi, key);
-      }
-    }
-    if constexpr (GL > 0) {
-#pragma unroll
-      for (int d = 1; d < GL; d <<= 1) {
-        lo = fminf(lo, __shfl_xor(lo, d, 64));
-        hi = fmaxf(hi, __shfl_xor(hi, d, 64));
-      }
-    }
-    glo[k] = lo;
-    ghi[k] = hi;
-  }
-  if constexpr (GL == 0) {
-    float lo = INFINITY, hi = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < kStreamMaxChunks; ++k) { lo = fminf(lo, glo[k]); hi = fmaxf(hi, ghi[k]); }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      lo = fminf(lo, __shfl_xor(lo, d, 64));
-      hi = fmaxf(hi, __shfl_xor(hi, d, 64));
-    }
-    if (lane == 0) { red_lo[wave] = lo; red_hi[wave] = hi; }
-    __syncthreads();
-    lo = red_lo[0];
-    hi = red_hi[0];
-#pragma unroll
-    for (int wv = 1; wv < kStreamThreads / 64; ++wv) { lo = fminf(lo, red_lo[wv]); hi = fmaxf(hi, red_hi[wv]); }
-#pragma unroll
-    for (int k = 0; k < kStreamMaxChunks; ++k) { glo[k] = lo; ghi[k] = hi; }
-  }
+// The grid of one group (rtn_grid's fp64 values, so the scale and zero are
+// those of the general kernel), plus what the code step needs in fp32.  The
+// stored code is c = q + off (off = 2^(bits-1) for sym, else 0, so c lies in
+// [0, 2^bits - 1] either way) and the fast path takes it as rint(y) with
+// y = fl(x·fl(1/fl(s)) + fl(z + off)) (one fma).  Against the fp64
+// x/s + z + off of the definition y errs by at most
+// 2^-23·|x/s| + 2^-24·(|y| + |z + off|) (the scale's, the reciprocal's and
+// the fma's roundings, z + off's own), below
+// tol = 4e-7·(2·max|x|/s + |z + off|) for every x of the group; where
+// |y - rint(y)| < half = fl(1/2 - tol) both round the same way, and the rest
+// is recomputed as rint(x/s + z) + off in fp64, as the general kernel does.
+// (fl(1/2 - tol) is within 2^-25 of 1/2 - tol; that slack only matters when
+// max|x|/s < 0.05 and z + off = 0, where every |y| < 0.06 is far from a
+// half-integer.)  A reciprocal below 2^-100 (scales near the fp32 limit)
+// sends every code of the group to the fp64 route.
+struct StreamGrid {
+  double s, zo;    // scale, z + off
+  float rf, zof;   // fl(1/fl(s)), fl(z + off)
+  float half;      // fl(1/2 - tol)
+  float pad;
+};
+static_assert(sizeof(StreamGrid) == 32, "StreamGrid is two 16-byte LDS words");
 
-  const int off = a.sym ? (1 << (a.bits - 1)) : 0;
-  const float qminf = a.sym ? -(float)(1 << (a.bits - 1)) : 0.f;
-  const float qmaxf = a.sym ? (float)((1 << (a.bits - 1)) - 1) : (float)((1 << a.bits) - 1);
-  double se = 0.0, xd = 0.0, ww = 0.0;
-  uint32_t* qrow = a.qweight + r * a.words;
+__device__ __forceinline__ StreamGrid stream_grid(float lo, float hi, int bits, int sym, float* scale_out,
+                                                  int32_t* zero_out) {
+  // sym: the grid is set by max|x| = max(-min x, max x)
+  const float amax = fmaxf(-lo, hi);
+  double s, z;
+  rtn_grid((double)(sym ? 0.f : lo), (double)(sym ? amax : hi), bits, sym, s, z);
+  const double off = sym ? (double)(1 << (bits - 1)) : 0.0;
+  StreamGrid g;
+  g.s = s;
+  g.zo = z + off;
+  g.pad = 0.f;
+  const float sf = (float)s;
+  g.rf = 1.f / sf;
+  g.zof = (float)g.zo;
+  const float tol = g.rf >= 0x1p-100f ? 4e-7f * (2.f * amax * g.rf + fabsf(g.zof)) : 1.f;
+  g.half = 0.5f - tol;
+  *scale_out = sf;
+  *zero_out = (int32_t)g.zo;
+  return g;
+}
+template <bool CS>
+__device__ __forceinline__ void chunk_colscale(const float* colscale, int c8, float (&cs)[8]) {
+  if constexpr (CS) {
+    const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(colscale + 8 * c8);
+    const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(colscale + 8 * c8 + 4);
 #pragma unroll
-  for (int k = 0; k < kStreamMaxChunks; ++k) {
-    const int c8 = tid + kStreamThreads * k;
-    if (c8 >= nc) continue;
-    double s, z;
-    rtn_grid((double)glo[k], (double)ghi[k], a.bits, a.sym, s, z);
-    const float sf = (float)s, zf = (float)z;
-    float x[8];
-    raw[k].get(x);
-    float cs[8];
-    if (a.colscale) {
-      const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(a.colscale + 8 * c8);
-      const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(a.colscale + 8 * c8 + 4);
+    for (int i = 0; i < 4; ++i) { cs[i] = c0[i]; cs[i + 4] = c1[i]; }
+  } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { cs[i] = c0[i]; cs[i + 4] = c1[i]; }
-    }
-    uint32_t word0 = 0u, word1 = 0u;
+    for (int i = 0; i < 8; ++i) cs[i] = 1.f;
+  }
+}
+
+// min and max of one chunk's x·colscale, and a non-finite detector: nf stays
+// 0 unless some value is NaN or ±Inf (then value·0 is NaN).
+template <typename T, bool CS>
+__device__ __forceinline__ void chunk_extremes(const float* colscale, const Chunk<T>& raw, int c8, float& lo,
+                                               float& hi, float& nf) {
+  float x[8], cs[8];
+  raw.get(x);
+  chunk_colscale<CS>(colscale, c8, cs);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float v = CS ? x[e] * cs[e] : x[e];
+    nf = fmaf(v, 0.f, nf);
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+}
+
+// Codes, packing and the error sums of one 8-column chunk on grid g.  The
+// error is taken in the original domain: d = x - (q - z)·s / colscale, with
+// q - z = c - (z + off) exact in fp64.
+template <typename T, bool CS>
+__device__ __forceinline__ void stream_chunk(const RtnArgs& a, const Chunk<T>& raw, int c8, const StreamGrid& g,
+                                             float cmax, float offf, uint32_t* qrow, double& se, double& xd,
+                                             double& ww) {
+  float x[8], cs[8];
+  raw.get(x);
+  chunk_colscale<CS>(a.colscale, c8, cs);
+  float c[8];
+  float dist = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float xf = CS ? x[e] * cs[e] : x[e];
+    const float y = fmaf(xf, g.rf, g.zof);
+    c[e] = rintf(y);
+    dist = fmaxf(dist, fabsf(y - c[e]));
+  }
+  if (dist >= g.half) {   // some code near a half-integer: decide those in fp64
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float x0 = x[e];
-      const float xf = a.colscale ? x0 * cs[e] : x0;
-      const float qf = xf / sf;
-      const float y = a.sym ? qf : qf + zf;
-      const float half = floorf(y) + 0.5f;
-      const float tol = 2e-7f * (fabsf(qf) + fabsf(y)) + 1e-30f;
-      float q;
-      if (fabsf(y - half) > tol) {
-        q = rintf(y);
-      } else {
-        const double xq = (double)xf / s;
-        q = (float)(a.sym ? rint(xq) : rint(xq + z));
-      }
-      q = fminf(fmaxf(q, qminf), qmaxf);
-      const uint32_t code = (uint32_t)((int)q + off);
-      const double xv = (double)x0;
-      const double d = a.colscale ? xv - ((double)q - z) * s / (double)cs[e] : xv - ((double)q - z) * s;
-      se += d * d;
-      xd += xv * d;
-      ww += xv * xv;
-      if (a.bits <= 4) word0 |= code << (4 * e);
-      else if (e < 4) word0 |= code << (8 * e);
-      else word1 |= code << (8 * (e - 4));
-    }
-    if (a.bits <= 4) {
-      qrow[c8] = word0;
-    } else {
-      qrow[2 * c8] = word0;
-      qrow[2 * c8 + 1] = word1;
-    }
-    const bool owner = GL == 0 ? c8 == 0 : (lane % (GL > 0 ? GL : 1)) == 0;
-    if (owner) {
-      const int64_t j = GL == 0 ? 0 : c8 / (GL > 0 ? GL : 1);
-      a.scales[r * a.G + j] = sf;
-      a.zeros[r * a.G + j] = (int32_t)z + off;
+      const float xf = CS ? x[e] * cs[e] : x[e];
+      const float y = fmaf(xf, g.rf, g.zof);
+      if (fabsf(y - c[e]) >= g.half) c[e] = (float)(rint((double)xf / g.s + (g.zo - (double)offf)) + (double)offf);
     }
   }
-  const int row_bad = __syncthreads_or(bad);
-  if (tid == 0) a.badrow[r] = row_bad;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    c[e] = __builtin_amdgcn_fmed3f(c[e], 0.f, cmax);
+    const double xv = (double)x[e];
+    const double qz = (double)c[e] - g.zo;
+    const double d = CS ? xv - qz * g.s / (double)cs[e] : fma(-qz, g.s, xv);
+    se = fma(d, d, se);
+    xd = fma(xv, d, xd);
+    ww = fma(xv, xv, ww);
+  }
+  // codes are exact integers in [0, 255]: convert and place them a byte at a
+  // time (4-bit: two codes per byte, c0 + 16·c1)
+  if (a.bits <= 4) {
+    uint32_t w = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(c[2 * i + 1], 16.f, c[2 * i]), i, w);
+    qrow[c8] = w;
+  } else {
+    uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w0 = __builtin_amdgcn_cvt_pk_u8_f32(c[i], i, w0);
+      w1 = __builtin_amdgcn_cvt_pk_u8_f32(c[i + 4], i, w1);
+    }
+    qrow[2 * c8] = w0;
+    qrow[2 * c8 + 1] = w1;
+  }
+}
+
+// LDS of the streaming kernel: the row's grids, then (groups of chunks) every
+// chunk's extremes, and the cross-wave reduction slots.
+template <int NT>
+struct StreamLds {
+  StreamGrid* grid;   // [G]
+  float2* ext;        // [nc] chunk (min, max)
+  float* red_lo;      // [NT/64]
+  float* red_hi;      // [NT/64]
+  double* red;        // [4][NT/64]
+};
+
+// The row's KR chunks of this thread (chunk t + NT·k), every load issued
+// (chunks past the row's end re-read its last chunk), so that the number of
+// loads in flight is the same on every path.
+template <typename T, int NT, int KR>
+__device__ __forceinline__ void stream_load(Chunk<T> (&buf)[KR], const T* wrow, int nc) {
+#pragma unroll
+  for (int k = 0; k < KR; ++k) buf[k].load(wrow + 8 * min((int)threadIdx.x + NT * k, nc - 1));
+}
+
+// One row: pass 1 writes every chunk's extremes to LDS, the first G threads
+// reduce them to their group's (one group per row, lgl < 0: a block
+// reduction instead) and turn them into grids (writing the scales and
+// zeros), and pass 2 takes the codes and the error sums from the same
+// registers.  Ends with the row's four sums in part[4r..4r+3] and its
+// non-finite flag.
+template <typename T, int NT, int KR, bool CS>
+__device__ __forceinline__ void stream_row(const RtnArgs& a, int lgl, int64_t r, Chunk<T> (&raw)[KR],
+                                           const StreamLds<NT>& L) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nc = (int)(a.n >> 3);
+  const int kc = (nc + NT - 1) / NT;   // chunks of the row per thread (uniform, <= KR)
+  uint32_t* qrow = a.qweight + r * a.words;
+  const int G = (int)a.G;
+  const bool rowgroup = lgl < 0;
+
+  // pass 1: extremes
+  float nf = 0.f, rlo = INFINITY, rhi = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < KR; ++k) {
+    const int c8 = tid + NT * k;
+    if (k < kc && c8 < nc) {
+      float lo = INFINITY, hi = -INFINITY;
+      chunk_extremes<T, CS>(a.colscale, raw[k], c8, lo, hi, nf);
+      if (rowgroup) {
+        rlo = fminf(rlo, lo);
+        rhi = fmaxf(rhi, hi);
+      } else {
+        L.ext[c8] = make_float2(lo, hi);
+      }
+    }
+  }
+  if (rowgroup) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      rlo = fminf(rlo, __shfl_xor(rlo, d, 64));
+      rhi = fmaxf(rhi, __shfl_xor(rhi, d, 64));
+    }
+    if (lane == 0) { L.red_lo[wave] = rlo; L.red_hi[wave] = rhi; }
+  }
+  if constexpr (CS) {
+    // x·colscale can overflow where x cannot: flag it here (nf != 0, NaN
+    // compares unequal); without a column scale the row's Σx² flags it
+    const int row_bad = __syncthreads_or(nf != 0.f);
+    if (tid == 0) a.badrow[r] = row_bad;
+  } else {
+    __syncthreads();
+  }
+  for (int j = tid; j < G; j += NT) {
+    float lo = INFINITY, hi = -INFINITY;
+    if (rowgroup) {
+#pragma unroll
+      for (int wv = 0; wv < NW; ++wv) { lo = fminf(lo, L.red_lo[wv]); hi = fmaxf(hi, L.red_hi[wv]); }
+    } else {
+      const int c0 = j << lgl, c1 = min(c0 + (1 << lgl), nc);
+      for (int c = c0; c < c1; ++c) {
+        const float2 e = L.ext[c];
+        lo = fminf(lo, e.x);
+        hi = fmaxf(hi, e.y);
+      }
+    }
+    L.grid[j] = stream_grid(lo, hi, a.bits, a.sym, a.scales + r * G + j, a.zeros + r * G + j);
+  }
+  __syncthreads();
+
+  // pass 2: codes and error sums
+#pragma unroll
+  for (int k = 0; k < KR; ++k) raw[k].hide();
+  const float cmax = (float)((1 << a.bits) - 1);
+  const float offf = a.sym ? (float)(1 << (a.bits - 1)) : 0.f;
+  const int gsh = rowgroup ? 31 : lgl;   // chunk -> group: c8 >> gsh (0 for one group per row)
+  double se = 0.0, xd = 0.0, ww = 0.0;
+#pragma unroll
+  for (int k = 0; k < KR; ++k) {
+    const int c8 = tid + NT * k;
+    if (k < kc && c8 < nc) stream_chunk<T, CS>(a, raw[k], c8, L.grid[c8 >> gsh], cmax, offf, qrow, se, xd, ww);
+  }
   double v4[4] = {se, ww - xd, ww, ww - 2.0 * xd + se};
 #pragma unroll
   for (int q = 0; q < 4; ++q)
@@ -645,13 +738,34 @@ __global__ __launch_bounds__(kStreamThreads) void rtn_stream_kernel(RtnArgs a) {
     for (int d = 32; d >= 1; d >>= 1) v4[q] += __shfl_xor(v4[q], d, 64);
   if (lane == 0)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) red[q][wave] = v4[q];
+    for (int q = 0; q < 4; ++q) L.red[q * NW + wave] = v4[q];
   __syncthreads();
   if (tid < 4) {
     double sum = 0.0;
-    for (int wv = 0; wv < kStreamThreads / 64; ++wv) sum += red[tid][wv];
+    for (int wv = 0; wv < NW; ++wv) sum += L.red[tid * NW + wv];
     a.part[r * 4 + tid] = sum;
+    // Σx² is finite exactly when every x is (x² <= 2^256 in fp64)
+    if (!CS && tid == 2) a.badrow[r] = !isfinite(sum);
   }
+}
+
+// One workgroup per row.
+template <typename T, int NT, int KR, bool CS>
+__global__ __launch_bounds__(NT) void rtn_stream_kernel(RtnArgs a, int lgl) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char stream_smem[];
+  constexpr int NW = NT / 64;
+  __shared__ float red_lo[NW], red_hi[NW];
+  __shared__ double red[4 * NW];
+  StreamLds<NT> L;
+  L.grid = reinterpret_cast<StreamGrid*>(stream_smem);
+  L.ext = reinterpret_cast<float2*>(L.grid + a.G);
+  L.red_lo = red_lo;
+  L.red_hi = red_hi;
+  L.red = red;
+  const int64_t r = blockIdx.x;
+  Chunk<T> raw[KR];
+  stream_load<T, NT, KR>(raw, static_cast<const T*>(a.W) + r * a.n, (int)(a.n >> 3));
+  stream_row<T, NT, KR, CS>(a, lgl, r, raw, L);
 }
 
 // err[0] = Σse / (m·n), err[1] = Σdot / (sqrt(Σww)·sqrt(Σdd) + 1e-8); rows in a
@@ -706,31 +820,68 @@ RtnPlan plan_rtn(int64_t m, int64_t n, int32_t group_size) {
 }
 
 namespace {
-// Lanes per group of the streaming kernel (0: one group per row), or -1 when
-// the layer needs the general kernel (clipping, unaligned rows, an n beyond
-// what the registers hold, or a group width that is not 8 times a divisor of 64).
-int rtn_stream_lanes(const void* W, int w_dtype, int64_t n, float clip, const RtnPlan& p) {
-  if (!(clip >= 1.f) || n % 8 != 0 || n > 8 * kStreamThreads * kStreamMaxChunks) return -1;
-  if ((reinterpret_cast<uintptr_t>(W) & 15) != 0) return -1;
-  (void)w_dtype;
-  if (p.G == 1) return 0;
-  if (p.g % 8 != 0) return -1;
+// log2(chunks per group) for the streaming kernel (-1: one group per row), or
+// -2 when the layer needs the general kernel: clipping, unaligned rows, a
+// group width that is not 8 times a power of two, a row longer than the
+// registers of one workgroup hold, or more LDS than a workgroup has.
+constexpr size_t kStreamMaxLds = 160 * 1024;
+
+// Workgroup shapes (threads, chunks per thread) by the row's chunk count.
+struct StreamShape { int nt, kr; };
+StreamShape stream_shape(int64_t nc, int w_dtype) {
+  if (nc <= 256 * 2) return {256, 2};
+  if (nc <= 256 * 4) return {256, 4};
+  if (nc <= 256 * 8) return {256, 8};
+  if (w_dtype == GPTQ_BF16) {
+    if (nc <= 256 * 16) return {256, 16};
+    if (nc <= 512 * 16) return {512, 16};
+  } else if (nc <= 512 * 8) {
+    return {512, 8};
+  }
+  return {0, 0};
+}
+
+size_t stream_lds_bytes(int64_t nc, const RtnPlan& p) {
+  return (size_t)p.G * sizeof(StreamGrid) + (p.G > 1 ? (size_t)nc * sizeof(float2) : 0);
+}
+
+int rtn_stream_lgl(const void* W, int w_dtype, const float* colscale, int64_t n, float clip, const RtnPlan& p) {
+  if (!(clip >= 1.f) || n % 8 != 0 || stream_shape(n / 8, w_dtype).nt == 0) return -2;
+  if (stream_lds_bytes(n / 8, p) > kStreamMaxLds) return -2;
+  if ((reinterpret_cast<uintptr_t>(W) & 15) != 0 || (reinterpret_cast<uintptr_t>(colscale) & 15) != 0) return -2;
+  if (p.G == 1) return -1;
+  if (p.g % 8 != 0) return -2;
   const int64_t gl = p.g / 8;
-  return (gl <= 64 && (64 % gl) == 0) ? (int)gl : -1;
+  if ((gl & (gl - 1)) != 0) return -2;
+  return __builtin_ctzll((unsigned long long)gl);
+}
+
+template <typename T, int NT, int KR, bool CS>
+gptq_status launch_stream_kernel(int lgl, const RtnArgs& a, size_t lds, hipStream_t stream) {
+  const void* fn = reinterpret_cast<const void*>(&rtn_stream_kernel<T, NT, KR, CS>);
+  if (lds > 65536) GPTQ_HIP_CHECK(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+  hipLaunchKernelGGL((rtn_stream_kernel<T, NT, KR, CS>), dim3((unsigned)a.m), dim3(NT), lds, stream, a, lgl);
+  return GPTQ_OK;
+}
+
+template <typename T, int NT, int KR>
+gptq_status launch_stream_shape(int lgl, const RtnArgs& a, size_t lds, hipStream_t stream) {
+  if (a.colscale) return launch_stream_kernel<T, NT, KR, true>(lgl, a, lds, stream);
+  return launch_stream_kernel<T, NT, KR, false>(lgl, a, lds, stream);
 }
 
 template <typename T>
-void launch_stream(int gl, const RtnArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.m), block(kStreamThreads);
-  switch (gl) {
-    case 0: hipLaunchKernelGGL((rtn_stream_kernel<T, 0>), grid, block, 0, stream, a); break;
-    case 1: hipLaunchKernelGGL((rtn_stream_kernel<T, 1>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((rtn_stream_kernel<T, 2>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((rtn_stream_kernel<T, 4>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((rtn_stream_kernel<T, 8>), grid, block, 0, stream, a); break;
-    case 16: hipLaunchKernelGGL((rtn_stream_kernel<T, 16>), grid, block, 0, stream, a); break;
-    case 32: hipLaunchKernelGGL((rtn_stream_kernel<T, 32>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((rtn_stream_kernel<T, 64>), grid, block, 0, stream, a); break;
+gptq_status launch_stream(int lgl, int w_dtype, const RtnArgs& a, const RtnPlan& p, hipStream_t stream) {
+  const StreamShape sh = stream_shape(a.n / 8, w_dtype);
+  const size_t lds = stream_lds_bytes(a.n / 8, p);
+  if (sh.nt == 256 && sh.kr == 2) return launch_stream_shape<T, 256, 2>(lgl, a, lds, stream);
+  if (sh.nt == 256 && sh.kr == 4) return launch_stream_shape<T, 256, 4>(lgl, a, lds, stream);
+  if (sh.nt == 256 && sh.kr == 8) return launch_stream_shape<T, 256, 8>(lgl, a, lds, stream);
+  if constexpr (sizeof(T) == 2) {   // bf16: up to 16 chunks (64 registers) per thread
+    if (sh.nt == 256) return launch_stream_shape<T, 256, 16>(lgl, a, lds, stream);
+    return launch_stream_shape<T, 512, 16>(lgl, a, lds, stream);
+  } else {                          // fp32: up to 8 chunks per thread
+    return launch_stream_shape<T, 512, 8>(lgl, a, lds, stream);
   }
 }
 }  // namespace
@@ -747,10 +898,11 @@ gptq_status run_rtn(const void* W, int w_dtype, int64_t m, int64_t n, int bits, 
   a.part = reinterpret_cast<double*>(w + p.part_off);
   a.badrow = reinterpret_cast<int*>(w + p.flag_off);
   a.colscale = colscale;
-  const int gl = rtn_stream_lanes(W, w_dtype, n, clip, p);
-  if (gl >= 0) {
-    if (w_dtype == GPTQ_BF16) launch_stream<uint16_t>(gl, a, stream);
-    else launch_stream<float>(gl, a, stream);
+  const int lgl = rtn_stream_lgl(W, w_dtype, colscale, n, clip, p);
+  if (lgl >= -1) {
+    const gptq_status st = w_dtype == GPTQ_BF16 ? launch_stream<uint16_t>(lgl, w_dtype, a, p, stream)
+                                                : launch_stream<float>(lgl, w_dtype, a, p, stream);
+    if (st != GPTQ_OK) return st;
   } else {
     const int lds = (int)p.lds_bytes;
     if (w_dtype == GPTQ_BF16) {
