@@ -26,10 +26,9 @@
 // Product (gptq_w4a16_matmul), per call of up to 64 tokens:
 //   gather : X' [Mp][n128] bf16 in processing order and its 32-position sums
 //   gemm   : split-K over 128-chunks; a workgroup of 4 waves holds 8 row tiles
-//            (128 rows) x one slice; each wave streams its codes straight from
-//            HBM into registers (16 B per lane per chunk), the slice of X' and
-//            the slice's scales sit in LDS; per group the accumulator is
-//            scaled and folded into the result
+//            (128 rows) x one slice x every token; X', its sums, the codes and
+//            the scales of each chunk are copied straight into an LDS ring;
+//            per group the accumulator is scaled and folded into the result
 //   reduce : Y = Σ over slices in slice order (deterministic)
 #include <algorithm>
 #include <mutex>
@@ -41,17 +40,19 @@ namespace gptq {
 namespace {
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kW4Rows = 16;          // rows per tile (MFMA N)
 constexpr int kW4Chunk = 128;        // positions per chunk (4 MFMA k-steps of 32)
-constexpr int kW4TilesPerWave = 2;
 constexpr int kW4Waves = 4;
-constexpr int kW4TilesPerWg = kW4TilesPerWave * kW4Waves;
-constexpr int kW4MaxChunks = 4;      // chunks per slice
-constexpr int kW4MaxGroups = kW4MaxChunks * 4 + 1;   // groups one slice can touch (g >= 32)
+constexpr int kW4TilesPerWave = 2;
+constexpr int kW4TilesPerWg = kW4Waves * kW4TilesPerWave;   // 128 rows per workgroup
+constexpr int kW4Ring = 4;           // LDS ring slots of the split-K product (chunks in flight + 1)
+constexpr int kW4TargetWgs = 256;    // split-K: slices so that about this many workgroups run
 constexpr int kW4TokTile = 16;
 constexpr int kW4MaxTokTiles = 4;    // tokens per launch <= 64
 constexpr int kW4Pad = 8;            // bf16 padding per LDS row of X'
+constexpr int kW4XRow = kW4Chunk + kW4Pad;   // bf16 per LDS row of one X' chunk
 constexpr int kW4GemvMaxTokens = 16; // the whole-K path: X' of every position in LDS
 
 // ---------------------------------------------------------------- pack
@@ -170,146 +171,264 @@ struct W4GemmArgs {
   const u32x4_t* codes;    // [mt][kc][64]
   float* part;             // [splits][tokens][m16]
   int64_t tokens, m16, mt, kc, n128, Gp;
-  int chunks;              // 128-chunks per slice (<= kW4MaxChunks)
+  int chunks;              // 128-chunks per slice
 };
 
 // The empty asm keeps the unpacking at its use: hoisted out of the token-tile
 // loop, the unpacked operands of every chunk would stay live (4x the VGPRs).
+// Each word is (shifted codes & 0x000F000F) | 0x43004300.  The two constants
+// are hidden from constant folding (an empty asm that claims to change them,
+// no instruction), so both sit in registers and the compiler selects one
+// v_and_or_b32 per word: gfx9 VOP3 takes no literal, and with the constants
+// folded it emits an AND and an OR.
 __device__ __forceinline__ bf16x8_t w4_unpack(uint32_t w) {
   asm volatile("" : "+v"(w));
+  uint32_t m = 0x000F000Fu, c = 0x43004300u;
+  asm volatile("" : "+v"(m), "+v"(c));
   u32x4_t r;
-  r[0] = (w & 0x000F000Fu) | 0x43004300u;
-  r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  r[0] = (w & m) | c;
+  r[1] = ((w >> 4) & m) | c;
+  r[2] = ((w >> 8) & m) | c;
+  r[3] = ((w >> 12) & m) | c;
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
+// s_waitcnt vmcnt(n) with the other counters left free
+__device__ __forceinline__ constexpr int w4_vmcnt(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
+// One ring slot of the split-K product: the chunk's X' (TT·16 token rows of
+// 16 pieces of 16 B; row t's piece p sits in slot p ^ (t mod 16), so the
+// A-operand reads of 16 consecutive rows hit distinct banks), its 32-sums
+// (64 tokens x 4), the codes of every row tile (1 KB each) and the group
+// parameters of every row tile (4 groups x 16 rows x (s, 128 + z), 512 B).
+template <int TT>
+struct W4Slot {
+  static constexpr int kX = TT * 16 * 256;
+  static constexpr int kS = kX;
+  static constexpr int kC = kS + 64 * 4 * 4;
+  static constexpr int kP = kC + kW4TilesPerWg * 1024;
+  static constexpr int kBytes = kP + kW4TilesPerWg * 512;
+  // copies per wave per chunk: X', sums, codes and params (x 2) per row tile
+  static constexpr int kCopies = TT + 1 + 3 * kW4TilesPerWave;
+};
+
+// Split-K product for up to 64 tokens.  Workgroup (rb, s): rows 128·rb ..
+// 128·rb + 127 (wave w: row tiles 8·rb + 2w, + 1) x slice s (chunks
+// [s·chunks, ...)),
+// every token of the launch at once (TT tiles of 16).  Every operand a chunk
+// needs -- X', its 32-position sums, the codes and the group parameters --
+// is copied from memory straight into LDS (buffer loads with an LDS
+// destination) through a ring of kW4Ring slots, kW4Ring - 1 chunks in flight
+// while one is multiplied; no register waits for a load, so nothing but the
+// explicit vmcnt below orders them.  Tokens past the last read as zero (the
+// X' and sum descriptors end at the last token).  Every code is
+// read once and every X' byte once per 128 rows; each A fragment feeds both
+// of a wave's row tiles.
 // GS = 32-position steps per group (1, 2, 4 for groups of 32, 64, 128), or 0
-// for one group per row.  Slices are whole 128-chunks, so with GS > 0 every
-// slice starts on a group boundary and holds steps / GS whole groups.
-template <int GS>
-__global__ __launch_bounds__(256) void w4_gemm_kernel(W4GemmArgs a) {
-  constexpr int RS = kW4MaxChunks * kW4Chunk + kW4Pad;   // LDS row of X' (bf16)
-  constexpr int SS = kW4MaxChunks * 4;                   // 32-sums per LDS row
-  constexpr int NG = GS > 0 ? SS / GS : 1;               // groups per slice (max)
-  constexpr int PI = (kW4TilesPerWg * NG * kW4Rows + 255) / 256;   // param items per thread
-  __shared__ __attribute__((aligned(16))) uint16_t xsh[kW4TokTile * RS];
-  __shared__ float ssh[kW4TokTile * SS];
-  __shared__ float2 psh[kW4TilesPerWg * NG * kW4Rows];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t s = blockIdx.y;
-  const int64_t C0 = s * a.chunks;
+// for one group per row.  A group of GS > 0 lies inside one chunk (chunks are
+// 128 positions, group starts are multiples of g), so a chunk closes 4/GS
+// groups; GS = 0 closes its one group at the end of the slice (the per-group
+// formula is linear, so each slice applies s and 128 + z to its own part).
+template <int GS, int TT>
+__device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, f32x4_t (&y)[kW4TilesPerWave][TT],
+                                               uint8_t* __restrict__ s0, uint8_t* __restrict__ s1,
+                                               uint8_t* __restrict__ s2, uint8_t* __restrict__ s3) {
+  using Sl = W4Slot<TT>;
+  constexpr int K = Sl::kCopies;
+  constexpr int RT = kW4TilesPerWave;
+  constexpr int NP = GS > 0 ? 4 / GS : 1;   // groups closed per chunk
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (a scalar register): the buffer descriptors below are then
+  // uniform and each copy is one instruction
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int row = lane & 15, quad = lane >> 4;
+  const int64_t C0 = (int64_t)blockIdx.y * a.chunks;
   const int nch = (int)std::min<int64_t>(a.chunks, a.kc - C0);
-  const int steps = 4 * nch;
-  const int ng = GS > 0 ? steps / GS : 1;
-  const int64_t T0 = (int64_t)blockIdx.x * kW4TilesPerWg;
-  const int64_t g0 = GS > 0 ? C0 * 4 / GS : 0;
+  const int64_t spr = a.n128 / 32;   // 32-sums per token
+  auto clamp32 = [](int64_t b) { return (int32_t)std::min<int64_t>(b, 0x7fffffff); };
+  // descriptors, once: tokens past the last read as zero (descriptor bounds)
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.Xp + C0 * kW4Chunk), 0, clamp32(a.tokens * a.n128 * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.xs + C0 * 4), 0, clamp32(a.tokens * spr * 4), 0x00020000);
+  __amdgpu_buffer_rsrc_t rc[RT], rp[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    // row tiles past the last compute on it and store nothing
+    const int64_t T = std::min<int64_t>((int64_t)blockIdx.x * kW4TilesPerWg + wave * RT + r, a.mt - 1);
+    rc[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4_t*>(a.codes + (T * a.kc + C0) * 64), 0,
+                                              nch * 1024, 0x00020000);
+    rp[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<float2*>(a.params + T * a.Gp * kW4Rows), 0,
+                                              clamp32(a.Gp * kW4Rows * 8), 0x00020000);
+  }
+  // this lane's pieces of the X' copies: piece q = (w·TT + u)·64 + lane is row
+  // q / 16, LDS slot q % 16, which holds X' piece (q % 16) ^ (row % 16)
+  int32_t xoff[TT];
+#pragma unroll
+  for (int u = 0; u < TT; ++u) {
+    const int q = (wave * TT + u) * 64 + lane, t = q >> 4, pc = (q & 15) ^ (t & 15);
+    xoff[u] = clamp32((int64_t)t * a.n128 * 2 + pc * 16);
+  }
+  const int sf = wave * 64 + lane;   // this lane's sum: token sf / 4, step sf % 4
+  const int32_t soff = clamp32(((int64_t)(sf >> 2) * spr + (sf & 3)) * 4);
 
-  // Every global load of the prologue is issued before the first store.  All
-  // loads and LDS stores are unconditional, at indices clamped into range (a
-  // load under a condition compiles to a branch and a wait of its own):
-  // clamped items reload and rewrite an in-range item with its own value, and
-  // tiles past the last row tile (never computed) hold the last tile's data.
-  u32x4_t cw[kW4TilesPerWave][kW4MaxChunks];
+  // chunk c of the slice -> slot; steps past the slice re-read its last
+  // chunk (nobody uses it).  Always K copies, so the vmcnt bookkeeping is the
+  // same on every step.
+  auto issue = [&](int c, uint8_t* slot) {
+    const int cl = std::min(c, nch - 1);
+#pragma unroll
+    for (int u = 0; u < TT; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(slot + (wave * TT + u) * 1024), 16,
+                                              xoff[u] + cl * kW4Chunk * 2, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(slot + Sl::kS + wave * 256), 4, soff + cl * 16, 0,
+                                            0, 0);
+    const int64_t g0 = GS > 0 ? (C0 + cl) * 4 / GS : 0;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int tl = wave * RT + r;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rc[r], (lds_void_t*)(slot + Sl::kC + tl * 1024), 16,
+                                              (cl * 64 + lane) * 16, 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rp[r], (lds_void_t*)(slot + Sl::kP + tl * 512 + k * 256), 4,
+                                                clamp32(g0 * kW4Rows * 8 + (k * 64 + lane) * 4), 0, 0, 0);
+    }
+  };
+
+  f32x4_t acc[RT][TT], sxa[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    sxa[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[r][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  float2 p0[RT];   // GS = 0: each row tile's (s, 128 + z)
+#pragma unroll
+  for (int r = 0; r < RT; ++r) p0[r] = make_float2(0.f, 0.f);
+  auto compute = [&](const uint8_t* cur) {
+    // every operand of the chunk from LDS first (one wait), then the MFMAs
+    u32x4_t cw[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+      cw[r] = *reinterpret_cast<const u32x4_t*>(cur + Sl::kC + (wave * RT + r) * 1024 + lane * 16);
+    uint4 av[4][TT];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+        av[j][tt] = *reinterpret_cast<const uint4*>(cur + ((16 * tt + row) * 16 + ((4 * j + quad) ^ row)) * 16);
+    f32x4_t sm[TT][4];   // the 4 step sums of token 16·tt + 4·quad + v
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        sm[tt][v] = *reinterpret_cast<const f32x4_t*>(cur + Sl::kS + (16 * tt + 4 * quad + v) * 16);
+    float2 pp[RT][NP];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int q = 0; q < NP; ++q)
+        pp[r][q] = reinterpret_cast<const float2*>(cur + Sl::kP + (wave * RT + r) * 512)[q * kW4Rows + row];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const bf16x8_t bw = w4_unpack(cw[r][j]);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+          acc[r][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[j][tt]), bw,
+                                                               acc[r][tt], 0, 0, 0);
+      }
+      if (GS > 0 && (j + 1) % (GS > 0 ? GS : 1) == 0) {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float sx = sm[tt][v][j + 1 - (GS > 0 ? GS : 1)];
+#pragma unroll
+            for (int q = 1; q < (GS > 0 ? GS : 1); ++q) sx += sm[tt][v][j + 1 - GS + q];
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+              const float2 p = pp[r][GS > 0 ? j / GS : 0];
+              y[r][tt][v] = fmaf(p.x, fmaf(-p.y, sx, acc[r][tt][v]), y[r][tt][v]);
+            }
+          }
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) acc[r][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    if (GS == 0) {   // one group per row: the slice's running 32-sums
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sxa[tt][v] += ((sm[tt][v][0] + sm[tt][v][1]) + sm[tt][v][2]) + sm[tt][v][3];
+#pragma unroll
+      for (int r = 0; r < RT; ++r) p0[r] = pp[r][0];
+    }
+  };
+  // One step: this wave's copies of chunk c are the oldest K of the 3K in
+  // flight; after the barrier every wave's are in LDS and every wave has
+  // finished reading the slot of chunk c - 1, which chunk c + 3 now refills.
+  auto step = [&](int c, const uint8_t* cur, uint8_t* refill) {
+    __builtin_amdgcn_s_waitcnt(w4_vmcnt(K * (kW4Ring - 2)));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    issue(c + kW4Ring - 1, refill);
+    if (c < nch) compute(cur);
+  };
+  issue(0, s0);
+  issue(1, s1);
+  issue(2, s2);
+  // the chunk count is rounded up to whole turns of the ring: steps past the
+  // slice only wait, meet and refill
+  for (int c = 0; c < nch; c += kW4Ring) {
+    step(c, s0, s3);
+    step(c + 1, s1, s0);
+    step(c + 2, s2, s1);
+    step(c + 3, s3, s2);
+  }
+  __builtin_amdgcn_s_waitcnt(w4_vmcnt(0));   // no copy may land after the workgroup ends
+  if (GS == 0) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) y[r][tt][v] = p0[r].x * fmaf(-p0[r].y, sxa[tt][v], acc[r][tt][v]);
+  }
+}
+
+template <int GS, int TT>
+__global__ __launch_bounds__(256) void w4_gemm_kernel(W4GemmArgs a) {
+  using Sl = W4Slot<TT>;
+  __shared__ __attribute__((aligned(16))) uint8_t s0[Sl::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s1[Sl::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s2[Sl::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s3[Sl::kBytes];
+  f32x4_t y[kW4TilesPerWave][TT];
+#pragma unroll
+  for (int r = 0; r < kW4TilesPerWave; ++r)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) y[r][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  w4_ring_stream<GS, TT>(a, y, s0, s1, s2, s3);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, quad = lane >> 4;
+  // D[4·quad + v][row] of token tile tt: token 16·tt + 4·quad + v, weight row 16T + row
 #pragma unroll
   for (int r = 0; r < kW4TilesPerWave; ++r) {
-    const int64_t T = std::min<int64_t>(T0 + wave * kW4TilesPerWave + r, a.mt - 1);
+    const int64_t T = (int64_t)blockIdx.x * kW4TilesPerWg + wave * kW4TilesPerWave + r;
+    if (T < a.mt) {
 #pragma unroll
-    for (int c = 0; c < kW4MaxChunks; ++c)
-      cw[r][c] = a.codes[(T * a.kc + C0 + std::min(c, nch - 1)) * 64 + lane];
-  }
-  const int npar = kW4TilesPerWg * ng * kW4Rows;
-  float2 pv[PI];
+      for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-  for (int u = 0; u < PI; ++u) {
-    const int i = std::min(tid + 256 * u, npar - 1);
-    const int tl = i / (ng * kW4Rows), gi = (i / kW4Rows) % ng, rr = i % kW4Rows;
-    const int64_t T = std::min<int64_t>(T0 + tl, a.mt - 1);
-    pv[u] = a.params[(T * a.Gp + g0 + gi) * kW4Rows + rr];
-  }
-  // (their LDS stores go with the first X' tile's, so the code loads are not
-  // held back behind a wait for these)
-
-  const int row = lane & 15, quad = lane >> 4;
-  const int vec_per_row = nch * (kW4Chunk / 8);   // 16-byte pieces of a row of the slice
-  const int ntt = (int)((a.tokens + kW4TokTile - 1) / kW4TokTile);
-  for (int tt = 0; tt < ntt; ++tt) {
-    const int64_t t0 = (int64_t)tt * kW4TokTile;
-    // X' tile: 16 rows x the slice.  Rows past the last token repeat the last
-    // token (their outputs are never written); loads and stores at clamped
-    // indices, unconditional, as above.
-    const int nxv = kW4TokTile * vec_per_row, nsv = kW4TokTile * steps;
-    // four named loads (an array here stays in scratch memory)
-    auto xidx = [&](int u) { return std::min(tid + 256 * u, nxv - 1); };
-    auto xload = [&](int u) {
-      const int i = xidx(u);
-      const int64_t t = std::min<int64_t>(t0 + i / vec_per_row, a.tokens - 1);
-      return *reinterpret_cast<const uint4*>(a.Xp + t * a.n128 + C0 * kW4Chunk + 8 * (i % vec_per_row));
-    };
-    auto xstore = [&](int u, const uint4& v) {
-      const int i = xidx(u);
-      *reinterpret_cast<uint4*>(xsh + (i / vec_per_row) * RS + 8 * (i % vec_per_row)) = v;
-    };
-    const uint4 x0 = xload(0), x1 = xload(1), x2 = xload(2), x3 = xload(3);
-    const int si = std::min(tid, nsv - 1);
-    const float sv = a.xs[std::min<int64_t>(t0 + si / steps, a.tokens - 1) * (a.n128 / 32) + C0 * 4 + si % steps];
-    if (tt > 0) __syncthreads();   // the previous tile is consumed
-    if (tt == 0) {
-#pragma unroll
-      for (int u = 0; u < PI; ++u) psh[std::min(tid + 256 * u, npar - 1)] = pv[u];
-    }
-    xstore(0, x0);
-    xstore(1, x1);
-    xstore(2, x2);
-    xstore(3, x3);
-    ssh[(si / steps) * SS + si % steps] = sv;
-    __syncthreads();
-
-#pragma unroll
-    for (int r = 0; r < kW4TilesPerWave; ++r) {
-      const int tl = wave * kW4TilesPerWave + r;
-      const int64_t T = T0 + tl;
-      if (T >= a.mt) break;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < kW4MaxChunks; ++c) {
-        if (c >= nch) break;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int ls = 4 * c + j;
-          const uint4 av = *reinterpret_cast<const uint4*>(
-              xsh + row * RS + c * kW4Chunk + 32 * j + 8 * quad);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                        w4_unpack(cw[r][c][j]), acc, 0, 0, 0);
-          const bool close = GS > 0 ? (ls + 1) % GS == 0 : (c == nch - 1 && j == 3);
-          if (close) {
-            const int gi = GS > 0 ? ls / GS : 0;
-            const int fs = GS > 0 ? ls + 1 - GS : 0;
-            const float2 p = psh[(tl * ng + gi) * kW4Rows + row];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const float* sp = ssh + (4 * quad + v) * SS;
-              float sx = 0.f;
-              if (GS > 0) {
-#pragma unroll
-                for (int q = 0; q < (GS > 0 ? GS : 1); ++q) sx += sp[fs + q];
-              } else {
-                for (int q = 0; q < steps; ++q) sx += sp[q];
-              }
-              y[v] = fmaf(p.x, fmaf(-p.y, sx, acc[v]), y[v]);
-            }
-            acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          }
+        for (int v = 0; v < 4; ++v) {
+          const int64_t t = 16 * tt + 4 * quad + v;
+          if (t < a.tokens) a.part[(blockIdx.y * a.tokens + t) * a.m16 + T * kW4Rows + row] = y[r][tt][v];
         }
-      }
-      // D[4·quad + v][row]: token t0 + 4·quad + v, weight row 16T + row
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t t = t0 + 4 * quad + v;
-        if (t < a.tokens) a.part[(s * a.tokens + t) * a.m16 + T * kW4Rows + row] = y[v];
-      }
     }
   }
 }
@@ -513,9 +632,9 @@ W4GemmPlan plan_w4a16_gemm(int64_t tokens, int64_t m, int64_t n, int64_t max_chu
   p.mp = p.chunk_tokens;
   const int64_t mt = ceil_div(m, kW4Rows), kc = ceil_div(n, kW4Chunk);
   const int64_t wgs_rows = ceil_div(mt, kW4TilesPerWg);
-  // chunks per slice: the largest (<= 4) that still gives >= 512 workgroups
-  p.chunks = kW4MaxChunks;
-  while (p.chunks > 1 && wgs_rows * ceil_div(kc, p.chunks) < 512) p.chunks /= 2;
+  // slices: about kW4TargetWgs workgroups in all, whole chunks per slice
+  const int64_t want = std::max<int64_t>(1, std::min<int64_t>(kc, ceil_div(kW4TargetWgs, wgs_rows)));
+  p.chunks = ceil_div(kc, want);
   p.splits = ceil_div(kc, p.chunks);
   const int64_t n128 = kc * kW4Chunk, m16 = mt * kW4Rows;
   p.xp_off = 0;
@@ -555,6 +674,30 @@ gptq_status run_w4a16_pack(const uint32_t* qweight, const float* scales, const i
     return GPTQ_ERR_INVALID_ARG;
   }
   return GPTQ_OK;
+}
+
+template <int GS>
+gptq_status launch_w4_gemm_gs(int tt, dim3 grid, const W4GemmArgs& a, hipStream_t stream) {
+  switch (tt) {
+    case 1: hipLaunchKernelGGL((w4_gemm_kernel<GS, 1>), grid, dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((w4_gemm_kernel<GS, 2>), grid, dim3(256), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((w4_gemm_kernel<GS, 3>), grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((w4_gemm_kernel<GS, 4>), grid, dim3(256), 0, stream, a); break;
+  }
+  GPTQ_LAUNCH_CHECK();
+  return GPTQ_OK;
+}
+
+gptq_status launch_w4_gemm(int gsteps, int tt, dim3 grid, const W4GemmArgs& a, hipStream_t stream) {
+  switch (gsteps) {
+    case 1: return launch_w4_gemm_gs<1>(tt, grid, a, stream);
+    case 2: return launch_w4_gemm_gs<2>(tt, grid, a, stream);
+    case 4: return launch_w4_gemm_gs<4>(tt, grid, a, stream);
+    case 0: return launch_w4_gemm_gs<0>(tt, grid, a, stream);
+    default:
+      set_error("group width not built (32, 64, 128 or one group per row)");
+      return GPTQ_ERR_UNSUPPORTED;
+  }
 }
 
 gptq_status run_w4a16_matmul(const uint16_t* X, int64_t tokens, int64_t ldx, const void* packed,
@@ -618,16 +761,8 @@ gptq_status run_w4a16_matmul(const uint16_t* X, int64_t tokens, int64_t ldx, con
     GPTQ_LAUNCH_CHECK();
     a.tokens = tk;
     const dim3 grid((unsigned)ceil_div(L.mt, kW4TilesPerWg), (unsigned)p.splits);
-    switch (gsteps) {
-      case 1: hipLaunchKernelGGL(w4_gemm_kernel<1>, grid, dim3(256), 0, stream, a); break;
-      case 2: hipLaunchKernelGGL(w4_gemm_kernel<2>, grid, dim3(256), 0, stream, a); break;
-      case 4: hipLaunchKernelGGL(w4_gemm_kernel<4>, grid, dim3(256), 0, stream, a); break;
-      case 0: hipLaunchKernelGGL(w4_gemm_kernel<0>, grid, dim3(256), 0, stream, a); break;
-      default:
-        set_error("group width %lld not built", (long long)L.g);
-        return GPTQ_ERR_UNSUPPORTED;
-    }
-    GPTQ_LAUNCH_CHECK();
+    const int tt = (int)ceil_div(tk, kW4TokTile);
+    GPTQ_TRY(launch_w4_gemm(gsteps, tt, grid, a, stream));
     hipLaunchKernelGGL(w4_reduce_kernel, dim3((unsigned)ceil_div(L.m, 256), (unsigned)tk), dim3(256),
                        0, stream, (const float*)part, p.splits, tk, a.m16, L.m, Y + t0 * ldy, ldy);
     GPTQ_LAUNCH_CHECK();
