@@ -52,15 +52,17 @@ NEXT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "next_rows_traffic.json")
 
 def next_rows_traffic(row: str, key: str):
     """HBM bytes per call of a next-row kernel from the committed counter runs,
-    if they were taken on the current source of that row; else None."""
+    if they were taken on the current source of that row (every file it
+    lists); else None."""
     try:
         with open(NEXT_TRAFFIC_FILE) as f:
             rec = json.load(f)
         src = rec["sources"][row]
-        if src["sha"] != source_hash(os.path.join(ROOT, src["file"])):
-            return None
+        for name, sha in src.items():
+            if sha != source_hash(os.path.join(ROOT, name)):
+                return None
         return rec["hbm_bytes_per_call"].get(key)
-    except (OSError, ValueError, KeyError):
+    except (OSError, ValueError, KeyError, AttributeError):
         return None
 
 
@@ -318,10 +320,14 @@ def measure_rtn(pq, torch, W, reps=20):
         nbytes = m * n * W.element_size() + m * words * 4 + m * groups * 8
         gbs = nbytes / (ms * 1e-3) / 1e9
         err = outs["err"].cpu().tolist()
+        # clip ratio 1 streams (extremes only); a clipped grid needs order statistics
+        kernel = ("rtn_stream_kernel + rtn_reduce_kernel" if cfg.clip_ratio >= 1.0 else
+                  "rtn_row_kernel + rtn_reduce_kernel")
         res[name] = {"ms": ms, "mse": err[0], "cos": err[1],
-                     "roofline": {"bound": "hbm", "kernel": "rtn_row_kernel + rtn_reduce_kernel",
+                     "roofline": {"bound": "hbm", "kernel": kernel,
                                   "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                  "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                                  "frac": gbs / PEAK_HBM_GBS,
+                                  "traffic": next_rows_traffic("rtn", name) if (m, n) == (4096, 11008) else None,
                                   "algorithmic_bytes_per_call": nbytes}}
         log(f"bench: rtn {name}: {ms:.3f} ms, {gbs:.0f} GB/s, mse {err[0]:.4e}, cos {err[1]:.6f}")
     return res
@@ -447,9 +453,11 @@ def measure_awq(pq, torch, W, X, gptq_out, reps=10, eval_tokens=4096):
             "traffic": next_rows_traffic("awq", "awq_channel_stats") if (m, n, T) == (4096, 11008, 262144) else None,
             "algorithmic_bytes_per_call": xbytes}},
         "quantize": {"ms": quant_ms, "weight_mse": err[0], "weight_cos": err[1], "roofline": {
-            "bound": "hbm", "kernel": "awq_scale_kernel + rtn_row_kernel + rtn_reduce_kernel",
+            "bound": "hbm", "kernel": ("awq_scale_kernel + rtn_stream_kernel + rtn_reduce_kernel" if cfg.clip_ratio >= 1.0
+                                       else "awq_scale_kernel + rtn_row_kernel + rtn_reduce_kernel"),
             "achieved": qbytes / (quant_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": qbytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
+            "frac": qbytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "traffic": next_rows_traffic("awq", "awq_quantize") if (m, n, T) == (4096, 11008, 262144) else None,
             "algorithmic_bytes_per_call": qbytes}},
         "output_rel_error_first_%d_tokens" % eval_tokens: rel,
     }

@@ -134,12 +134,20 @@ __global__ __launch_bounds__(256) void w4_codes_kernel(const uint32_t* __restric
 // ---------------------------------------------------------------- product
 // X' = X[:, order] and the sum of every 32 positions, for the real tokens.
 // Thread: 4 consecutive positions; 8 threads make one 32-position sum.
+// Workgroup L covers positions 1024·part ... of token t, with the
+// workgroups of one token on one XCD (dispatch goes round-robin over the 8
+// XCDs, L % 8): its row of X (read in scattered 2-byte pieces) then comes
+// from memory once, into that XCD's L2, instead of once per XCD.
+// wpt = workgroups per token; the grid is 8·ceil(tokens/8)·wpt.
 __global__ __launch_bounds__(256) void w4_gather_kernel(const uint16_t* __restrict__ X, int64_t ldx,
                                                         const int32_t* __restrict__ order,
                                                         int64_t n128, uint16_t* __restrict__ Xp,
-                                                        float* __restrict__ xs) {
-  const int64_t t = blockIdx.y;
-  const int64_t p0 = (int64_t)blockIdx.x * 1024 + 4 * threadIdx.x;
+                                                        float* __restrict__ xs, float* __restrict__ xs4,
+                                                        int64_t tokens, int wpt) {
+  const int64_t L = blockIdx.x, q = L >> 3;
+  const int64_t t = (L & 7) + 8 * (q / wpt);
+  if (t >= tokens) return;
+  const int64_t p0 = (q % wpt) * 1024 + 4 * threadIdx.x;
   if (p0 >= n128) return;   // n128 is a multiple of 128: whole 8-thread groups leave together
   uint16_t v[4];
   float s = 0.f;
@@ -162,11 +170,17 @@ __global__ __launch_bounds__(256) void w4_gather_kernel(const uint16_t* __restri
   s += __shfl_xor(s, 2);
   s += __shfl_xor(s, 4);
   if ((threadIdx.x & 7) == 0) xs[t * (n128 / 32) + (p0 >> 5)] = s;
+  // the 128-position sum ((s0 + s1) + s2) + s3 of the four 32-sums, for
+  // groups of 128 (32 threads; n128 is a multiple of 128, so whole 32-thread
+  // blocks leave together above)
+  const float s1 = __shfl_down(s, 8), s2 = __shfl_down(s, 16), s3 = __shfl_down(s, 24);
+  if ((threadIdx.x & 31) == 0) xs4[t * (n128 / 128) + (p0 >> 7)] = ((s + s1) + s2) + s3;
 }
 
 struct W4GemmArgs {
   const uint16_t* Xp;      // [tokens][n128], processing order
   const float* xs;         // [tokens][n128 / 32]
+  const float* xs4;        // [tokens][n128 / 128]
   const float2* params;    // [mt][Gp][16]
   const u32x4_t* codes;    // [mt][kc][64]
   float* part;             // [splits][tokens][m16]
@@ -203,15 +217,18 @@ __device__ __forceinline__ constexpr int w4_vmcnt(int n) {
 // A-operand reads of 16 consecutive rows hit distinct banks), its 32-sums
 // (64 tokens x 4), the codes of every row tile (1 KB each) and the group
 // parameters of every row tile (4 groups x 16 rows x (s, 128 + z), 512 B).
-template <int TT>
+template <int GS, int TT>
 struct W4Slot {
   static constexpr int kX = TT * 16 * 256;
   static constexpr int kS = kX;
   static constexpr int kC = kS + 64 * 4 * 4;
   static constexpr int kP = kC + kW4TilesPerWg * 1024;
   static constexpr int kBytes = kP + kW4TilesPerWg * 512;
-  // copies per wave per chunk: X', sums, codes and params (x 2) per row tile
-  static constexpr int kCopies = TT + 1 + 3 * kW4TilesPerWave;
+  // 256-byte copies of one row tile's parameters per chunk: the chunk's
+  // groups (4 for g = 32, else 1 or 2) are 128 bytes each
+  static constexpr int kPCopies = GS == 1 ? 2 : 1;
+  // copies per wave per chunk: X', sums, and codes and params per row tile
+  static constexpr int kCopies = TT + 1 + (1 + kPCopies) * kW4TilesPerWave;
 };
 
 // Split-K product for up to 64 tokens.  Workgroup (rb, s): rows 128·rb ..
@@ -235,7 +252,7 @@ template <int GS, int TT>
 __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, f32x4_t (&y)[kW4TilesPerWave][TT],
                                                uint8_t* __restrict__ s0, uint8_t* __restrict__ s1,
                                                uint8_t* __restrict__ s2, uint8_t* __restrict__ s3) {
-  using Sl = W4Slot<TT>;
+  using Sl = W4Slot<GS, TT>;
   constexpr int K = Sl::kCopies;
   constexpr int RT = kW4TilesPerWave;
   constexpr int NP = GS > 0 ? 4 / GS : 1;   // groups closed per chunk
@@ -251,8 +268,11 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, f32x4_t (&y)
   // descriptors, once: tokens past the last read as zero (descriptor bounds)
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.Xp + C0 * kW4Chunk), 0, clamp32(a.tokens * a.n128 * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(a.xs + C0 * 4), 0, clamp32(a.tokens * spr * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs =
+      GS == 4 ? __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.xs4 + C0), 0,
+                                                  clamp32(a.tokens * (a.n128 / 128) * 4), 0x00020000)
+              : __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.xs + C0 * 4), 0,
+                                                  clamp32(a.tokens * spr * 4), 0x00020000);
   __amdgpu_buffer_rsrc_t rc[RT], rp[RT];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
@@ -271,8 +291,11 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, f32x4_t (&y)
     const int q = (wave * TT + u) * 64 + lane, t = q >> 4, pc = (q & 15) ^ (t & 15);
     xoff[u] = clamp32((int64_t)t * a.n128 * 2 + pc * 16);
   }
-  const int sf = wave * 64 + lane;   // this lane's sum: token sf / 4, step sf % 4
-  const int32_t soff = clamp32(((int64_t)(sf >> 2) * spr + (sf & 3)) * 4);
+  // this lane's sum: GS = 4, the 128-sum of token `lane` (every wave keeps
+  // its own copy of the chunk's 64); else the 32-sum of token sf / 4, step sf % 4
+  const int sf = wave * 64 + lane;
+  const int32_t soff = GS == 4 ? clamp32((int64_t)lane * (a.n128 / 128) * 4)
+                               : clamp32(((int64_t)(sf >> 2) * spr + (sf & 3)) * 4);
 
   // chunk c of the slice -> slot; steps past the slice re-read its last
   // chunk (nobody uses it).  Always K copies, so the vmcnt bookkeeping is the
@@ -283,8 +306,8 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, f32x4_t (&y)
     for (int u = 0; u < TT; ++u)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(slot + (wave * TT + u) * 1024), 16,
                                               xoff[u] + cl * kW4Chunk * 2, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(slot + Sl::kS + wave * 256), 4, soff + cl * 16, 0,
-                                            0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(slot + Sl::kS + wave * 256), 4,
+                                            soff + cl * (GS == 4 ? 4 : 16), 0, 0, 0);
     const int64_t g0 = GS > 0 ? (C0 + cl) * 4 / GS : 0;
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
@@ -292,7 +315,7 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, f32x4_t (&y)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rc[r], (lds_void_t*)(slot + Sl::kC + tl * 1024), 16,
                                               (cl * 64 + lane) * 16, 0, 0, 0);
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
+      for (int k = 0; k < Sl::kPCopies; ++k)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rp[r], (lds_void_t*)(slot + Sl::kP + tl * 512 + k * 256), 4,
                                                 clamp32(g0 * kW4Rows * 8 + (k * 64 + lane) * 4), 0, 0, 0);
     }
@@ -320,12 +343,19 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, f32x4_t (&y)
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt)
         av[j][tt] = *reinterpret_cast<const uint4*>(cur + ((16 * tt + row) * 16 + ((4 * j + quad) ^ row)) * 16);
-    f32x4_t sm[TT][4];   // the 4 step sums of token 16·tt + 4·quad + v
+    // GS = 4: s4[tt][v] = the 128-sum of token 16·tt + 4·quad + v (this
+    // wave's copy); else sm[tt][v] = its 4 step sums
+    f32x4_t sm[TT][4], s4[TT];
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
+    for (int tt = 0; tt < TT; ++tt) {
+      if (GS == 4) {
+        s4[tt] = *reinterpret_cast<const f32x4_t*>(cur + Sl::kS + wave * 256 + (16 * tt + 4 * quad) * 4);
+      } else {
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        sm[tt][v] = *reinterpret_cast<const f32x4_t*>(cur + Sl::kS + (16 * tt + 4 * quad + v) * 16);
+        for (int v = 0; v < 4; ++v)
+          sm[tt][v] = *reinterpret_cast<const f32x4_t*>(cur + Sl::kS + (16 * tt + 4 * quad + v) * 16);
+      }
+    }
     float2 pp[RT][NP];
 #pragma unroll
     for (int r = 0; r < RT; ++r)
@@ -347,9 +377,14 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, f32x4_t (&y)
         for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            float sx = sm[tt][v][j + 1 - (GS > 0 ? GS : 1)];
+            float sx;
+            if (GS == 4) {
+              sx = s4[tt][v];
+            } else {
+              sx = sm[tt][v][j + 1 - (GS > 0 ? GS : 1)];
 #pragma unroll
-            for (int q = 1; q < (GS > 0 ? GS : 1); ++q) sx += sm[tt][v][j + 1 - GS + q];
+              for (int q = 1; q < (GS > 0 ? GS : 1); ++q) sx += sm[tt][v][j + 1 - GS + q];
+            }
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
               const float2 p = pp[r][GS > 0 ? j / GS : 0];
@@ -404,7 +439,7 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, f32x4_t (&y)
 
 template <int GS, int TT>
 __global__ __launch_bounds__(256) void w4_gemm_kernel(W4GemmArgs a) {
-  using Sl = W4Slot<TT>;
+  using Sl = W4Slot<GS, TT>;
   __shared__ __attribute__((aligned(16))) uint8_t s0[Sl::kBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s1[Sl::kBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s2[Sl::kBytes];
@@ -639,7 +674,8 @@ W4GemmPlan plan_w4a16_gemm(int64_t tokens, int64_t m, int64_t n, int64_t max_chu
   const int64_t n128 = kc * kW4Chunk, m16 = mt * kW4Rows;
   p.xp_off = 0;
   p.xs_off = align256((size_t)(p.mp * n128) * sizeof(uint16_t));
-  p.part_off = p.xs_off + align256((size_t)(p.mp * (n128 / 32)) * sizeof(float));
+  // 32-position sums, then 128-position sums
+  p.part_off = p.xs_off + align256((size_t)(p.mp * (n128 / 32 + n128 / 128)) * sizeof(float));
   p.total = p.part_off + (size_t)(p.splits * p.chunk_tokens * m16) * sizeof(float);
   return p;
 }
@@ -676,6 +712,16 @@ gptq_status run_w4a16_pack(const uint32_t* qweight, const float* scales, const i
   return GPTQ_OK;
 }
 
+gptq_status launch_w4_gather(const uint16_t* X, int64_t ldx, const int32_t* order, int64_t n128, uint16_t* Xp,
+                             float* xs, float* xs4, int64_t tokens, hipStream_t stream) {
+  const int64_t wpt = ceil_div(n128, 1024);
+  const int64_t grid = 8 * ceil_div(tokens, 8) * wpt;
+  hipLaunchKernelGGL(w4_gather_kernel, dim3((unsigned)grid), dim3(256), 0, stream, X, ldx, order, n128, Xp, xs,
+                     xs4, tokens, (int)wpt);
+  GPTQ_LAUNCH_CHECK();
+  return GPTQ_OK;
+}
+
 template <int GS>
 gptq_status launch_w4_gemm_gs(int tt, dim3 grid, const W4GemmArgs& a, hipStream_t stream) {
   switch (tt) {
@@ -707,10 +753,12 @@ gptq_status run_w4a16_matmul(const uint16_t* X, int64_t tokens, int64_t ldx, con
   char* w = static_cast<char*>(ws);
   uint16_t* Xp = reinterpret_cast<uint16_t*>(w + p.xp_off);
   float* xs = reinterpret_cast<float*>(w + p.xs_off);
+  float* xs4 = xs + p.mp * (L.n128 / 32);
   float* part = reinterpret_cast<float*>(w + p.part_off);
   W4GemmArgs a;
   a.Xp = Xp;
   a.xs = xs;
+  a.xs4 = xs4;
   a.params = reinterpret_cast<const float2*>(base + L.param_off);
   a.codes = reinterpret_cast<const u32x4_t*>(base + L.code_off);
   a.part = part;
@@ -727,8 +775,7 @@ gptq_status run_w4a16_matmul(const uint16_t* X, int64_t tokens, int64_t ldx, con
   // while its X' fits in LDS and every workgroup is resident at once
   const int64_t resident = 256 * std::max<int64_t>(1, (int64_t)(160 * 1024 / std::max<size_t>(gemv_lds, 1)));
   if (tokens <= kW4GemvMaxTokens && gemv_lds <= kW4GemvMaxLds && L.mt <= resident) {
-    hipLaunchKernelGGL(w4_gather_kernel, dim3((unsigned)ceil_div(L.n128, 1024), (unsigned)tokens),
-                       dim3(256), 0, stream, X, ldx, order, L.n128, Xp, xs);
+    GPTQ_TRY(launch_w4_gather(X, ldx, order, L.n128, Xp, xs, xs4, tokens, stream));
     GPTQ_LAUNCH_CHECK();
     W4GemvArgs g;
     g.Xp = Xp; g.xs = xs; g.params = a.params; g.codes = a.codes; g.Y = Y; g.ldy = ldy;
@@ -756,9 +803,7 @@ gptq_status run_w4a16_matmul(const uint16_t* X, int64_t tokens, int64_t ldx, con
   }
   for (int64_t t0 = 0; t0 < tokens; t0 += p.chunk_tokens) {
     const int64_t tk = std::min<int64_t>(p.chunk_tokens, tokens - t0);
-    hipLaunchKernelGGL(w4_gather_kernel, dim3((unsigned)ceil_div(L.n128, 1024), (unsigned)tk),
-                       dim3(256), 0, stream, X + t0 * ldx, ldx, order, L.n128, Xp, xs);
-    GPTQ_LAUNCH_CHECK();
+    GPTQ_TRY(launch_w4_gather(X + t0 * ldx, ldx, order, L.n128, Xp, xs, xs4, tk, stream));
     a.tokens = tk;
     const dim3 grid((unsigned)ceil_div(L.mt, kW4TilesPerWg), (unsigned)p.splits);
     const int tt = (int)ceil_div(tk, kW4TokTile);
