@@ -31,11 +31,15 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", SRC,
 ]
+# per-source additions: the W4A16 product keeps its MFMA accumulators in
+# ordinary VGPRs (they are read by VALU code after every group; in AGPRs each
+# read is a v_accvgpr_read first)
+EXTRA = {"w4a16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(SRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), "-c", os.path.join(SRC, src), "-o", obj]
     t0 = time.time()
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"

@@ -28,7 +28,8 @@
 //   gemm   : split-K over 128-chunks; a workgroup of 4 waves holds 8 row tiles
 //            (128 rows) x one slice x every token; X', its sums, the codes and
 //            the scales of each chunk are copied straight into an LDS ring;
-//            per group the accumulator is scaled and folded into the result
+//            per group the accumulator is scaled and folded into the result;
+//            partial results leave in the MFMA's own lane layout
 //   reduce : Y = Σ over slices in slice order (deterministic)
 #include <algorithm>
 #include <mutex>
@@ -183,22 +184,49 @@ struct W4GemmArgs {
   const float* xs4;        // [tokens][n128 / 128]
   const float2* params;    // [mt][Gp][16]
   const u32x4_t* codes;    // [mt][kc][64]
-  float* part;             // [splits][tokens][m16]
-  int64_t tokens, m16, mt, kc, n128, Gp;
+  float* part;             // [splits][mt][TT][64 lanes][4]: the D fragments of every 16 x 16 tile
+  int64_t tokens, mt, kc, n128, Gp;
+  int64_t nrb, splits;     // 128-row blocks, K-slices (nrb·splits workgroups)
   int chunks;              // 128-chunks per slice
 };
 
+// Workgroup -> (row block, slice).  Dispatch deals workgroups round-robin
+// to the 8 XCDs (workgroup i runs on XCD i mod 8); when the slice count is a
+// multiple of 8, every workgroup of slice s runs on XCD s mod 8, so each
+// XCD's L2 holds the X' columns of its own slices only (one miss per line
+// per XCD instead of one per line on every XCD).  Both are wave-uniform
+// (scalar registers), so the buffer descriptors built from them are too.
+__device__ __forceinline__ void w4_block_coords(const W4GemmArgs& a, int64_t& rb, int64_t& s) {
+  const uint32_t i = blockIdx.x, nrb = (uint32_t)a.nrb;
+  uint32_t r, t;
+  if ((a.splits & 7) == 0) {
+    const uint32_t q = i >> 3;
+    t = (i & 7) + 8 * (q / nrb);
+    r = q % nrb;
+  } else {
+    r = i % nrb;
+    t = i / nrb;
+  }
+  rb = __builtin_amdgcn_readfirstlane(r);
+  s = __builtin_amdgcn_readfirstlane(t);
+}
+
 // The empty asm keeps the unpacking at its use: hoisted out of the token-tile
 // loop, the unpacked operands of every chunk would stay live (4x the VGPRs).
-// Each word is (shifted codes & 0x000F000F) | 0x43004300.  The two constants
-// are hidden from constant folding (an empty asm that claims to change them,
-// no instruction), so both sit in registers and the compiler selects one
-// v_and_or_b32 per word: gfx9 VOP3 takes no literal, and with the constants
-// folded it emits an AND and an OR.
-__device__ __forceinline__ bf16x8_t w4_unpack(uint32_t w) {
+// Each word is (shifted codes & 0x000F000F) | 0x43004300, one v_and_or_b32:
+// gfx9 VOP3 takes no literal, so both constants must sit in registers, and
+// with them visible as constants the compiler folds them and emits an AND and
+// an OR.  W4Consts hides them (an empty asm that claims to change them, no
+// instruction) once per kernel, outside every loop.
+struct W4Consts {
+  uint32_t m, c;
+  __device__ __forceinline__ W4Consts() : m(0x000F000Fu), c(0x43004300u) {
+    asm volatile("" : "+v"(m), "+v"(c));
+  }
+};
+__device__ __forceinline__ bf16x8_t w4_unpack(uint32_t w, const W4Consts& k) {
   asm volatile("" : "+v"(w));
-  uint32_t m = 0x000F000Fu, c = 0x43004300u;
-  asm volatile("" : "+v"(m), "+v"(c));
+  const uint32_t m = k.m, c = k.c;
   u32x4_t r;
   r[0] = (w & m) | c;
   r[1] = ((w >> 4) & m) | c;
@@ -249,7 +277,8 @@ struct W4Slot {
 // groups; GS = 0 closes its one group at the end of the slice (the per-group
 // formula is linear, so each slice applies s and 128 + z to its own part).
 template <int GS, int TT>
-__device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, f32x4_t (&y)[kW4TilesPerWave][TT],
+__device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, int64_t rb, int64_t sl,
+                                               f32x4_t (&y)[kW4TilesPerWave][TT],
                                                uint8_t* __restrict__ s0, uint8_t* __restrict__ s1,
                                                uint8_t* __restrict__ s2, uint8_t* __restrict__ s3) {
   using Sl = W4Slot<GS, TT>;
@@ -261,7 +290,7 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, f32x4_t (&y)
   // uniform and each copy is one instruction
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int row = lane & 15, quad = lane >> 4;
-  const int64_t C0 = (int64_t)blockIdx.y * a.chunks;
+  const int64_t C0 = sl * a.chunks;
   const int nch = (int)std::min<int64_t>(a.chunks, a.kc - C0);
   const int64_t spr = a.n128 / 32;   // 32-sums per token
   auto clamp32 = [](int64_t b) { return (int32_t)std::min<int64_t>(b, 0x7fffffff); };
@@ -277,7 +306,7 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, f32x4_t (&y)
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     // row tiles past the last compute on it and store nothing
-    const int64_t T = std::min<int64_t>((int64_t)blockIdx.x * kW4TilesPerWg + wave * RT + r, a.mt - 1);
+    const int64_t T = std::min<int64_t>(rb * kW4TilesPerWg + wave * RT + r, a.mt - 1);
     rc[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4_t*>(a.codes + (T * a.kc + C0) * 64), 0,
                                               nch * 1024, 0x00020000);
     rp[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<float2*>(a.params + T * a.Gp * kW4Rows), 0,
@@ -321,6 +350,7 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, f32x4_t (&y)
     }
   };
 
+  const W4Consts kc;
   f32x4_t acc[RT][TT], sxa[TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
@@ -366,7 +396,7 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, f32x4_t (&y)
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
-        const bf16x8_t bw = w4_unpack(cw[r][j]);
+        const bf16x8_t bw = w4_unpack(cw[r][j], kc);
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
           acc[r][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[j][tt]), bw,
@@ -449,21 +479,20 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(W4GemmArgs a) {
   for (int r = 0; r < kW4TilesPerWave; ++r)
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) y[r][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  w4_ring_stream<GS, TT>(a, y, s0, s1, s2, s3);
+  int64_t rb, sl;
+  w4_block_coords(a, rb, sl);
+  w4_ring_stream<GS, TT>(a, rb, sl, y, s0, s1, s2, s3);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = lane & 15, quad = lane >> 4;
-  // D[4·quad + v][row] of token tile tt: token 16·tt + 4·quad + v, weight row 16T + row
+  // lane l's D fragment of tile (T, tt): tokens 16·tt + 4·(l/16) + v, v = 0..3,
+  // of weight row 16T + l % 16; one 16-byte store each (tokens past the last
+  // hold zeros and are never read)
 #pragma unroll
   for (int r = 0; r < kW4TilesPerWave; ++r) {
-    const int64_t T = (int64_t)blockIdx.x * kW4TilesPerWg + wave * kW4TilesPerWave + r;
+    const int64_t T = rb * kW4TilesPerWg + wave * kW4TilesPerWave + r;
     if (T < a.mt) {
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int64_t t = 16 * tt + 4 * quad + v;
-          if (t < a.tokens) a.part[(blockIdx.y * a.tokens + t) * a.m16 + T * kW4Rows + row] = y[r][tt][v];
-        }
+        *reinterpret_cast<f32x4_t*>(a.part + (((sl * a.mt + T) * TT + tt) * 64 + lane) * 4) = y[r][tt];
     }
   }
 }
@@ -545,6 +574,7 @@ __global__ __launch_bounds__(512) void w4_gemv_kernel(W4GemvArgs a) {
 
   const int row = lane & 15, quad = lane >> 4;
   const bool arow = row < a.tokens;           // A-operand rows past the last token are zero
+  const W4Consts kc;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
   int fs = 4 * c0;                            // first global 32-step of the open group
   for (int cb = c0; cb < c1; cb += B) {
@@ -561,7 +591,7 @@ __global__ __launch_bounds__(512) void w4_gemv_kernel(W4GemvArgs a) {
         uint4 av = make_uint4(0u, 0u, 0u, 0u);
         if (arow) av = *reinterpret_cast<const uint4*>(xsh + row * xrow + 32 * st + 8 * quad);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                      w4_unpack(cw[b][j]), acc, 0, 0, 0);
+                                                      w4_unpack(cw[b][j], kc), acc, 0, 0, 0);
         const bool close = GS > 0 ? (st + 1) % GS == 0 : (c == c1 - 1 && j == 3);
         if (close) {
           const int grp = GS > 0 ? st / GS : 0;
@@ -610,26 +640,31 @@ __global__ __launch_bounds__(512) void w4_gemv_kernel(W4GemvArgs a) {
   }
 }
 
-// Y = Σ over slices in slice order; eight loads in flight per thread.
+// Y = Σ over slices in slice order.  Thread (r, q): weight row r, tokens
+// 4q .. 4q + 3, one 16-byte fragment per slice (lane 16·(q % 4) + r % 16 of
+// tile (r / 16, q / 4)); eight loads in flight.
 __global__ __launch_bounds__(256) void w4_reduce_kernel(const float* __restrict__ part, int64_t splits,
-                                                        int64_t tokens, int64_t m16, int64_t m,
+                                                        int64_t mt, int tt_count, int64_t tokens, int64_t m,
                                                         float* __restrict__ Y, int64_t ldy) {
   const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t t = blockIdx.y;
+  const int64_t q = blockIdx.y;
   if (r >= m) return;
-  const int64_t stride = tokens * m16;
-  const float* p = part + t * m16 + r;
-  float acc = 0.f;
+  const int64_t stride = mt * tt_count * 64;   // fragments per slice
+  const f32x4_t* p = reinterpret_cast<const f32x4_t*>(part) +
+                     ((r >> 4) * tt_count + (q >> 2)) * 64 + (q & 3) * 16 + (r & 15);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   int64_t s = 0;
   for (; s + 8 <= splits; s += 8) {
-    float v[8];
+    f32x4_t v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = p[(s + u) * stride];
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc += v[u];
   }
   for (; s < splits; ++s) acc += p[s * stride];
-  Y[t * ldy + r] = acc;
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+    if (4 * q + v < tokens) Y[(4 * q + v) * ldy + r] = acc[v];
 }
 
 }  // namespace
@@ -676,7 +711,8 @@ W4GemmPlan plan_w4a16_gemm(int64_t tokens, int64_t m, int64_t n, int64_t max_chu
   p.xs_off = align256((size_t)(p.mp * n128) * sizeof(uint16_t));
   // 32-position sums, then 128-position sums
   p.part_off = p.xs_off + align256((size_t)(p.mp * (n128 / 32 + n128 / 128)) * sizeof(float));
-  p.total = p.part_off + (size_t)(p.splits * p.chunk_tokens * m16) * sizeof(float);
+  // partial results: whole 16-token tiles
+  p.total = p.part_off + (size_t)(p.splits * kW4TokTile * ceil_div(p.chunk_tokens, kW4TokTile) * m16) * sizeof(float);
   return p;
 }
 
@@ -762,8 +798,9 @@ gptq_status run_w4a16_matmul(const uint16_t* X, int64_t tokens, int64_t ldx, con
   a.params = reinterpret_cast<const float2*>(base + L.param_off);
   a.codes = reinterpret_cast<const u32x4_t*>(base + L.code_off);
   a.part = part;
-  a.m16 = L.mt * kW4Rows;
   a.mt = L.mt;
+  a.nrb = ceil_div(L.mt, kW4TilesPerWg);
+  a.splits = p.splits;
   a.kc = L.kc;
   a.n128 = L.n128;
   a.Gp = L.Gp;
@@ -805,11 +842,12 @@ gptq_status run_w4a16_matmul(const uint16_t* X, int64_t tokens, int64_t ldx, con
     const int64_t tk = std::min<int64_t>(p.chunk_tokens, tokens - t0);
     GPTQ_TRY(launch_w4_gather(X + t0 * ldx, ldx, order, L.n128, Xp, xs, xs4, tk, stream));
     a.tokens = tk;
-    const dim3 grid((unsigned)ceil_div(L.mt, kW4TilesPerWg), (unsigned)p.splits);
+    const dim3 grid((unsigned)(a.nrb * p.splits));
     const int tt = (int)ceil_div(tk, kW4TokTile);
     GPTQ_TRY(launch_w4_gemm(gsteps, tt, grid, a, stream));
-    hipLaunchKernelGGL(w4_reduce_kernel, dim3((unsigned)ceil_div(L.m, 256), (unsigned)tk), dim3(256),
-                       0, stream, (const float*)part, p.splits, tk, a.m16, L.m, Y + t0 * ldy, ldy);
+    hipLaunchKernelGGL(w4_reduce_kernel, dim3((unsigned)ceil_div(L.m, 256), (unsigned)ceil_div(tk, 4)),
+                       dim3(256), 0, stream, (const float*)part, p.splits, L.mt, tt, tk, L.m, Y + t0 * ldy,
+                       ldy);
     GPTQ_LAUNCH_CHECK();
   }
   return GPTQ_OK;
