@@ -94,15 +94,39 @@ __device__ __forceinline__ uint64_t d2u(double x) {
   return b ^ ((b >> 63) ? ~0ull : 0x8000000000000000ull);
 }
 
-// One workgroup of 1024.
+// One workgroup of 1024.  Each radix pass counts the keys that match the
+// selected prefix into 256 bins; threads 0..255 (one bin each) take an
+// inclusive scan of the bins (a 64-lane shuffle scan per wave, then the wave
+// totals), and the one thread whose bin holds the remaining rank extends the
+// prefix.  REG: the keys (n <= 1024·kAwqKeys) are computed once and held in
+// registers, kAwqKeys per thread, for all eight passes; otherwise every
+// pass recomputes them from abs_sum.
+constexpr int kAwqKeys = 16;
+template <bool REG>
 __global__ __launch_bounds__(1024) void awq_scale_kernel(const double* __restrict__ abs_sum, int64_t n,
                                                          double tokens, float protect,
                                                          float* __restrict__ channel_scale, int* flag) {
   __shared__ uint32_t hist[256];
+  __shared__ uint32_t wtot[4];
   __shared__ uint64_t sel[2];   // prefix, remaining rank
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // this thread's keys j = tid + 1024·i (REG); past n they are ~0, which no
+  // prefix of a finite key's matches before the last pass and which the
+  // count skips by index
+  uint64_t key[REG ? kAwqKeys : 1];
   bool bad = false;
-  for (int64_t j = tid; j < n; j += 1024) bad |= !isfinite(abs_sum[j]);
+  if constexpr (REG) {
+    double v[kAwqKeys];
+#pragma unroll
+    for (int i = 0; i < kAwqKeys; ++i) v[i] = abs_sum[std::min<int64_t>(tid + 1024 * i, n - 1)];
+#pragma unroll
+    for (int i = 0; i < kAwqKeys; ++i) {
+      bad |= !isfinite(v[i]);
+      key[i] = d2u(v[i] / tokens);
+    }
+  } else {
+    for (int64_t j = tid; j < n; j += 1024) bad |= !isfinite(abs_sum[j]);
+  }
   // the call's flag word: this single workgroup is its only writer
   const int any_bad = __syncthreads_or(bad);
   if (tid == 0) *flag = any_bad;
@@ -113,30 +137,53 @@ __global__ __launch_bounds__(1024) void awq_scale_kernel(const double* __restric
   }
   uint64_t mask = 0;
   for (int shift = 56; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += 1024) hist[i] = 0;
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    const uint64_t prefix = sel[0];
-    for (int64_t j = tid; j < n; j += 1024) {
-      const uint64_t k = d2u(abs_sum[j] / tokens);
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    const uint64_t prefix = sel[0], rem = sel[1];
+    if constexpr (REG) {
+#pragma unroll
+      for (int i = 0; i < kAwqKeys; ++i)
+        if (tid + 1024 * i < n && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> shift) & 255u], 1u);
+    } else {
+      for (int64_t j = tid; j < n; j += 1024) {
+        const uint64_t k = d2u(abs_sum[j] / tokens);
+        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+      }
     }
     __syncthreads();
-    if (tid == 0) {
-      uint64_t rem = sel[1];
-      int b = 0;
-      while (rem >= hist[b]) {
-        rem -= hist[b];
-        ++b;
+    uint32_t v = 0, x = 0;
+    if (tid < 256) {
+      v = hist[tid];
+      x = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
       }
-      sel[0] = prefix | ((uint64_t)b << shift);
-      sel[1] = rem;
+      if (lane == 63) wtot[wave] = x;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t off = 0;
+      for (int w = 0; w < wave; ++w) off += wtot[w];
+      const uint64_t incl = (uint64_t)(x + off), excl = incl - v;
+      if (excl <= rem && rem < incl) {   // exactly one bin (empty bins have excl == incl)
+        sel[0] = prefix | ((uint64_t)tid << shift);
+        sel[1] = rem - excl;
+      }
     }
     mask |= 255ull << shift;
     __syncthreads();
   }
   const uint64_t med = sel[0];
-  for (int64_t j = tid; j < n; j += 1024)
-    channel_scale[j] = d2u(abs_sum[j] / tokens) > med ? protect : 1.f;
+  if constexpr (REG) {
+#pragma unroll
+    for (int i = 0; i < kAwqKeys; ++i)
+      if (tid + 1024 * i < n) channel_scale[tid + 1024 * i] = key[i] > med ? protect : 1.f;
+  } else {
+    for (int64_t j = tid; j < n; j += 1024)
+      channel_scale[j] = d2u(abs_sum[j] / tokens) > med ? protect : 1.f;
+  }
 }
 
 }  // namespace
@@ -190,8 +237,12 @@ gptq_status run_awq_quantize(const void* W, int w_dtype, int64_t m, int64_t n, c
                              uint32_t* qweight, float* scales, int32_t* zeros, float* channel_scale,
                              double* err, int32_t* status, void* ws, const RtnPlan& plan, hipStream_t stream) {
   int* flag = static_cast<int*>(ws);
-  hipLaunchKernelGGL(awq_scale_kernel, dim3(1), dim3(1024), 0, stream, abs_sum, n, (double)tokens, protect,
-                     channel_scale, flag);
+  if (n <= 1024 * kAwqKeys)
+    hipLaunchKernelGGL(awq_scale_kernel<true>, dim3(1), dim3(1024), 0, stream, abs_sum, n, (double)tokens,
+                       protect, channel_scale, flag);
+  else
+    hipLaunchKernelGGL(awq_scale_kernel<false>, dim3(1), dim3(1024), 0, stream, abs_sum, n, (double)tokens,
+                       protect, channel_scale, flag);
   GPTQ_LAUNCH_CHECK();
   return run_rtn(W, w_dtype, m, n, bits, sym, clip, qweight, scales, zeros, err, status,
                  static_cast<char*>(ws) + awq_extra_bytes(), plan, stream, channel_scale, flag);

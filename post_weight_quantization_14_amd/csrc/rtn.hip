@@ -579,7 +579,9 @@ __device__ __forceinline__ void chunk_extremes(const float* colscale, const Chun
 
 // Codes, packing and the error sums of one 8-column chunk on grid g.  The
 // error is taken in the original domain: d = x - (q - z)·s / colscale, with
-// q - z = c - (z + off) exact in fp64.
+// q - z = c - (z + off) exact in fp64; the division is a multiplication by
+// 1/colscale from v_rcp_f64 and one Newton step (within an ulp or two of the
+// quotient, far below the sums' tolerance of relative 1e-12).
 template <typename T, bool CS>
 __device__ __forceinline__ void stream_chunk(const RtnArgs& a, const Chunk<T>& raw, int c8, const StreamGrid& g,
                                              float cmax, float offf, uint32_t* qrow, double& se, double& xd,
@@ -609,7 +611,15 @@ __device__ __forceinline__ void stream_chunk(const RtnArgs& a, const Chunk<T>& r
     c[e] = __builtin_amdgcn_fmed3f(c[e], 0.f, cmax);
     const double xv = (double)x[e];
     const double qz = (double)c[e] - g.zo;
-    const double d = CS ? xv - qz * g.s / (double)cs[e] : fma(-qz, g.s, xv);
+    double d;
+    if constexpr (CS) {
+      const double c = (double)cs[e];
+      double r = __builtin_amdgcn_rcp(c);
+      r = fma(r, fma(-c, r, 1.0), r);
+      d = xv - (qz * g.s) * r;
+    } else {
+      d = fma(-qz, g.s, xv);
+    }
     se = fma(d, d, se);
     xd = fma(xv, d, xd);
     ww = fma(xv, xv, ww);
