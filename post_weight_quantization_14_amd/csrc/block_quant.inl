@@ -184,22 +184,31 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs q, const float* 
   __shared__ float rdg[QB];
   __shared__ __attribute__((aligned(16))) float es[kBqRows * kEsPitch];
   const int tid = threadIdx.x;
-  // the push's operands: its first block's loads go out now
+  // the push's operands (its first block's loads go out below)
   const int64_t prow0 = (int64_t)blockIdx.x * kBqRows;
   const int64_t rows_left = q.m - prow0;
   float* wpush = q.Wp + prow0 * q.ldw + i1 + bw;   // processed column i2 = i1 + bw
   const bool pvec = ((ldu | q.ldw | (i1 + bw)) & 1) == 0 &&
                     ((reinterpret_cast<uintptr_t>(upush) | reinterpret_cast<uintptr_t>(q.Wp)) & 7) == 0;
   PushBlk pb[2];
-  if ((tid >> 6) * kPushCols < ncols)
-    push_load(pb[0], upush, ldu, wpush, q.ldw, rows_left, tid >> 6, ncols, pvec, tid & 63);
-  // U block: rows and columns < bw, upper triangle only (the rest zero)
-  for (int idx = tid; idx < QB * QB; idx += 256) {
-    const int r = idx >> 7, c = idx & (QB - 1);
-    us[idx] = (r < bw && c < bw && c >= r) ? ublk[r * ldu + c] : 0.f;
+  // U block: rows and columns < bw, upper triangle only (the rest zero), and
+  // the reciprocals of its diagonal.  Every load is unconditional (indices
+  // clamped into the block) and a thread's loads are in flight together
+  // before its first LDS store: under a condition each load compiles to a
+  // branch and a wait of its own, 64 round trips to L2 per thread.  Loads
+  // complete in issue order, so the block's loads go out first, then the
+  // row's weights, then the push's first operands: each wait then covers
+  // only what its use needs.
+  const bool uvec = FULL && (ldu & 3) == 0 && (reinterpret_cast<uintptr_t>(ublk) & 15) == 0;
+  constexpr int kV = QB * QB / 4 / 256;   // 16-byte pieces per thread
+  f32x4_t uv[kV];
+  if (uvec) {
+#pragma unroll
+    for (int k = 0; k < kV; ++k) {
+      const int i4 = tid + 256 * k, ur = i4 >> 5, uc = (i4 & 31) << 2;
+      uv[k] = *reinterpret_cast<const f32x4_t*>(ublk + (int64_t)ur * ldu + uc);
+    }
   }
-  if (tid < QB) rdg[tid] = tid < bw ? 1.f / ublk[tid * ldu + tid] : 1.f;
-
   const int lane = tid & 63, wave = tid >> 6;
   BqCtx x;
   x.j = lane & 15;
@@ -216,6 +225,36 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs q, const float* 
       x.w[p + 4] = b[p];
     }
   }
+  if ((tid >> 6) * kPushCols < ncols)
+    push_load(pb[0], upush, ldu, wpush, q.ldw, rows_left, tid >> 6, ncols, pvec, tid & 63);
+  if (uvec) {
+#pragma unroll
+    for (int k = 0; k < kV; ++k) {
+      const int i4 = tid + 256 * k, ur = i4 >> 5, uc = (i4 & 31) << 2;
+      f32x4_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = uc + e >= ur ? uv[k][e] : 0.f;
+      *reinterpret_cast<f32x4_t*>(us + ur * QB + uc) = o;
+      if (uc <= ur && ur < uc + 4) rdg[ur] = 1.f / uv[k][ur - uc];
+    }
+  } else {
+    constexpr int kS = 16;   // loads in flight per round
+    for (int k0 = 0; k0 < QB * QB / 256; k0 += kS) {
+      float v[kS];
+#pragma unroll
+      for (int u = 0; u < kS; ++u) {
+        const int idx = tid + 256 * (k0 + u), ur = idx >> 7, uc = idx & (QB - 1);
+        v[u] = ublk[(int64_t)std::min(ur, bw - 1) * ldu + std::min(uc, bw - 1)];
+      }
+#pragma unroll
+      for (int u = 0; u < kS; ++u) {
+        const int idx = tid + 256 * (k0 + u), ur = idx >> 7, uc = idx & (QB - 1);
+        us[idx] = (ur < bw && uc < bw && uc >= ur) ? v[u] : 0.f;
+        if (ur == uc) rdg[ur] = ur < bw ? 1.f / v[u] : 1.f;
+      }
+    }
+  }
+
 #pragma unroll
   for (int p = 0; p < 8; ++p) x.e8[p] = 0.f;
   x.c8[0] = x.c8[1] = 0u;
