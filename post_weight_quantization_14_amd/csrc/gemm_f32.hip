@@ -31,20 +31,29 @@ struct GemmSmem {
   float b[2][SB];
 };
 
+// Sixteen zero bytes: the source of every out-of-range 16-byte piece.
+__device__ __attribute__((aligned(16))) float gemm_zero4[4];
+
 // base[row * ld + col + e] for e < 4, zero outside row < row_lim, col + e < col_lim.
+// Every load is unconditional and its value is used as loaded: a load under
+// a condition, or a select on its value, makes the compiler wait for it at
+// once, so the loads of a stage would go out one memory latency apart
+// instead of together.  VEC (16-byte aligned rows, col and col_lim multiples
+// of 4, so a piece is wholly in range or wholly out): one 16-byte load, of
+// gemm_zero4 for a piece out of range.  Otherwise every element is loaded
+// from a clamped address inside the operand and selected.
 template <bool VEC>
 __device__ __forceinline__ f32x4_t load4(const float* __restrict__ base, int64_t row, int64_t ld,
                                          int64_t col, int64_t row_lim, int64_t col_lim) {
-  f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-  if (row < row_lim && col < col_lim) {
-    const float* p = base + row * ld + col;
-    if (VEC && col + 4 <= col_lim) {
-      v = *reinterpret_cast<const f32x4_t*>(p);
-    } else {
+  const bool rok = row < row_lim;
+  const float* prow = base + (rok ? row : 0) * ld;
+  if (VEC) return *reinterpret_cast<const f32x4_t*>(rok && col < col_lim ? prow + col : gemm_zero4);
+  f32x4_t v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (col + e < col_lim) v[e] = p[e];
-    }
+  for (int e = 0; e < 4; ++e) {
+    const bool ok = rok && col + e < col_lim;
+    const float y = prow[ok ? col + e : 0];
+    v[e] = ok ? y : 0.f;
   }
   return v;
 }
@@ -292,10 +301,12 @@ __global__ __launch_bounds__(256) void trtri_step2_kernel(const float* Amat, flo
                          0.f, acc);
 }
 
+// The 16-byte loads: aligned operand rows, and every 4-element piece wholly
+// inside or wholly outside the k range and (row-major B) the columns.
 bool vec_ok(const GemmArgs& g, bool bcol) {
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   return al(g.A) && al(g.B) && (g.lda % 4 == 0) && (g.ldb % 4 == 0) && (g.k_begin % 4 == 0) &&
-         (bcol || true);
+         (g.k_end % 4 == 0) && (bcol || g.N % 4 == 0);
 }
 
 }  // namespace
