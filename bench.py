@@ -206,26 +206,38 @@ def cpu_baseline(spec, W, X, log_prefix="cpu_baseline", full=False):
     import workloads
 
     cores = len(os.sched_getaffinity(0))
-    t_tok = spec.tokens if full else min(2048, spec.tokens)
-    r_rows = spec.m if full else min(32, spec.m)
+    # the sample: one 8192-token tile (BLAS-sized, so the Hessian rate is the
+    # whole layer's) and 256 rows
+    t_tok = spec.tokens if full else min(8192, spec.tokens)
+    r_rows = spec.m if full else min(256, spec.m)
     if full:
         with threadpool_limits(limits=cores):
             t0 = time.perf_counter()
             H = np.zeros((spec.n, spec.n))
             key = np.zeros(spec.n)
+            last = t0
             for r0 in range(0, spec.tokens, workloads.TILE_TOKENS):
                 H, key = oracle.hessian_accumulate(H, key, workloads.to_numpy_f64(X[r0:r0 + workloads.TILE_TOKENS]))
+                if time.perf_counter() - last > 30:
+                    last = time.perf_counter()
+                    log(f"{log_prefix}: full hessian {r0 + workloads.TILE_TOKENS}/{spec.tokens} tokens, "
+                        f"{last - t0:.0f}s")
             t1 = time.perf_counter()
             log(f"{log_prefix}: full hessian {t1 - t0:.1f}s")
             U, perm, lam = oracle.prepare(H, key, spec.damp_percent, spec.desc_act)
             t2 = time.perf_counter()
+            log(f"{log_prefix}: full prepare {t2 - t1:.1f}s")
             Wf = workloads.to_numpy_f64(W)
-            oracle.gptq_quantize(Wf[:, perm], U, spec.bits, spec.group_size, spec.sym, block=128)
+            # rows are independent given U: 256 at a time, with progress lines
+            for r0 in range(0, spec.m, 256):
+                oracle.gptq_quantize(Wf[r0:r0 + 256, perm], U, spec.bits, spec.group_size, spec.sym, block=128)
+                log(f"{log_prefix}: full quantize {min(r0 + 256, spec.m)}/{spec.m} rows, "
+                    f"{time.perf_counter() - t2:.0f}s")
             t3 = time.perf_counter()
         th, tp, tq = t1 - t0, t2 - t1, t3 - t2
         log(f"{log_prefix}: full layer: hessian {th:.1f}s, prepare {tp:.1f}s, quantize {tq:.1f}s")
         return {"value": th + tp + tq, "unit": "s/layer", "cores": cores, "kind": "oracle",
-                "sample": "float64 NumPy oracle on the whole layer (every token and row), not scaled",
+                "sample": "float64 NumPy oracle on the whole layer (every token; every row, 256 rows per call), not scaled",
                 "stage_s": {"hessian": th, "prepare": tp, "quantize": tq}}
     Xs = workloads.to_numpy_f64(X[:t_tok])
     Ws = workloads.to_numpy_f64(W[:r_rows])
