@@ -45,7 +45,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kW4Rows = 16;          // rows per tile (MFMA N)
 constexpr int kW4Chunk = 128;        // positions per chunk (4 MFMA k-steps of 32)
-constexpr int kW4Waves = 4;
+constexpr int kW4Waves = 4;           // waves per workgroup that split the rows (x2 when the tokens split too)
 constexpr int kW4TilesPerWave = 2;
 constexpr int kW4TilesPerWg = kW4Waves * kW4TilesPerWave;   // 128 rows per workgroup
 constexpr int kW4Ring = 4;           // LDS ring slots of the split-K product (chunks in flight + 1)
@@ -245,7 +245,9 @@ __device__ __forceinline__ constexpr int w4_vmcnt(int n) {
 // A-operand reads of 16 consecutive rows hit distinct banks), its 32-sums
 // (64 tokens x 4), the codes of every row tile (1 KB each) and the group
 // parameters of every row tile (4 groups x 16 rows x (s, 128 + z), 512 B).
-template <int GS, int TT>
+// TS: the workgroup's waves split the tokens TS ways (4·TS waves, each with
+// TT/TS token tiles of its row pair); the copies are spread over all of them.
+template <int GS, int TT, int TS>
 struct W4Slot {
   static constexpr int kX = TT * 16 * 256;
   static constexpr int kS = kX;
@@ -255,8 +257,12 @@ struct W4Slot {
   // 256-byte copies of one row tile's parameters per chunk: the chunk's
   // groups (4 for g = 32, else 1 or 2) are 128 bytes each
   static constexpr int kPCopies = GS == 1 ? 2 : 1;
-  // copies per wave per chunk: X', sums, and codes and params per row tile
-  static constexpr int kCopies = TT + 1 + (1 + kPCopies) * kW4TilesPerWave;
+  static constexpr int kWaves = 4 * TS;
+  static constexpr int kTilesPerWave = TT / TS;                  // token tiles each wave multiplies
+  static constexpr int kCopyTiles = kW4TilesPerWg / kWaves;      // row tiles each wave copies
+  static_assert(TT % TS == 0, "token tiles split evenly");
+  // copies per wave per chunk: X', sums, and codes and params per copied row tile
+  static constexpr int kCopies = kTilesPerWave + 1 + (1 + kPCopies) * kCopyTiles;
 };
 
 // Split-K product for up to 64 tokens.  Workgroup (rb, s): rows 128·rb ..
@@ -276,19 +282,24 @@ struct W4Slot {
 // 128 positions, group starts are multiples of g), so a chunk closes 4/GS
 // groups; GS = 0 closes its one group at the end of the slice (the per-group
 // formula is linear, so each slice applies s and 128 + z to its own part).
-template <int GS, int TT>
+template <int GS, int TT, int TS>
 __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, int64_t rb, int64_t sl,
-                                               f32x4_t (&y)[kW4TilesPerWave][TT],
+                                               f32x4_t (&y)[kW4TilesPerWave][TT / TS],
                                                uint8_t* __restrict__ s0, uint8_t* __restrict__ s1,
                                                uint8_t* __restrict__ s2, uint8_t* __restrict__ s3) {
-  using Sl = W4Slot<GS, TT>;
+  using Sl = W4Slot<GS, TT, TS>;
   constexpr int K = Sl::kCopies;
   constexpr int RT = kW4TilesPerWave;
+  constexpr int TW = Sl::kTilesPerWave;
+  constexpr int CT = Sl::kCopyTiles;
   constexpr int NP = GS > 0 ? 4 / GS : 1;   // groups closed per chunk
   const int lane = threadIdx.x & 63;
   // wave-uniform (a scalar register): the buffer descriptors below are then
   // uniform and each copy is one instruction
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  // the wave multiplies row tiles RT·rg .. RT·rg + RT - 1 of the workgroup
+  // by token tiles TW·th .. TW·th + TW - 1
+  const int rg = wave & 3, th = wave >> 2;
   const int row = lane & 15, quad = lane >> 4;
   const int64_t C0 = sl * a.chunks;
   const int nch = (int)std::min<int64_t>(a.chunks, a.kc - C0);
@@ -302,27 +313,29 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, int64_t rb, 
                                                   clamp32(a.tokens * (a.n128 / 128) * 4), 0x00020000)
               : __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.xs + C0 * 4), 0,
                                                   clamp32(a.tokens * spr * 4), 0x00020000);
-  __amdgpu_buffer_rsrc_t rc[RT], rp[RT];
+  // the row tiles this wave copies: CT·wave .. CT·wave + CT - 1
+  __amdgpu_buffer_rsrc_t rc[CT], rp[CT];
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
+  for (int r = 0; r < CT; ++r) {
     // row tiles past the last compute on it and store nothing
-    const int64_t T = std::min<int64_t>(rb * kW4TilesPerWg + wave * RT + r, a.mt - 1);
+    const int64_t T = std::min<int64_t>(rb * kW4TilesPerWg + wave * CT + r, a.mt - 1);
     rc[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4_t*>(a.codes + (T * a.kc + C0) * 64), 0,
                                               nch * 1024, 0x00020000);
     rp[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<float2*>(a.params + T * a.Gp * kW4Rows), 0,
                                               clamp32(a.Gp * kW4Rows * 8), 0x00020000);
   }
-  // this lane's pieces of the X' copies: piece q = (w·TT + u)·64 + lane is row
+  // this lane's pieces of the X' copies: piece q = (w·TW + u)·64 + lane is row
   // q / 16, LDS slot q % 16, which holds X' piece (q % 16) ^ (row % 16)
-  int32_t xoff[TT];
+  int32_t xoff[TW];
 #pragma unroll
-  for (int u = 0; u < TT; ++u) {
-    const int q = (wave * TT + u) * 64 + lane, t = q >> 4, pc = (q & 15) ^ (t & 15);
+  for (int u = 0; u < TW; ++u) {
+    const int q = (wave * TW + u) * 64 + lane, t = q >> 4, pc = (q & 15) ^ (t & 15);
     xoff[u] = clamp32((int64_t)t * a.n128 * 2 + pc * 16);
   }
-  // this lane's sum: GS = 4, the 128-sum of token `lane` (every wave keeps
-  // its own copy of the chunk's 64); else the 32-sum of token sf / 4, step sf % 4
-  const int sf = wave * 64 + lane;
+  // this lane's sum: GS = 4, the 128-sum of token `lane` (every wave writes
+  // the same 64 to one place); else the 32-sum of token sf / 4, step sf % 4
+  // (waves 4.. write the same quarters as waves 0..3)
+  const int sf = (wave & 3) * 64 + lane;
   const int32_t soff = GS == 4 ? clamp32((int64_t)lane * (a.n128 / 128) * 4)
                                : clamp32(((int64_t)(sf >> 2) * spr + (sf & 3)) * 4);
 
@@ -332,15 +345,15 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, int64_t rb, 
   auto issue = [&](int c, uint8_t* slot) {
     const int cl = std::min(c, nch - 1);
 #pragma unroll
-    for (int u = 0; u < TT; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(slot + (wave * TT + u) * 1024), 16,
+    for (int u = 0; u < TW; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(slot + (wave * TW + u) * 1024), 16,
                                               xoff[u] + cl * kW4Chunk * 2, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(slot + Sl::kS + wave * 256), 4,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(slot + Sl::kS + (GS == 4 ? 0 : (wave & 3) * 256)), 4,
                                             soff + cl * (GS == 4 ? 4 : 16), 0, 0, 0);
     const int64_t g0 = GS > 0 ? (C0 + cl) * 4 / GS : 0;
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const int tl = wave * RT + r;
+    for (int r = 0; r < CT; ++r) {
+      const int tl = wave * CT + r;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rc[r], (lds_void_t*)(slot + Sl::kC + tl * 1024), 16,
                                               (cl * 64 + lane) * 16, 0, 0, 0);
 #pragma unroll
@@ -351,9 +364,9 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, int64_t rb, 
   };
 
   const W4Consts kc;
-  f32x4_t acc[RT][TT], sxa[TT];
+  f32x4_t acc[RT][TW], sxa[TW];
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
+  for (int tt = 0; tt < TW; ++tt) {
     sxa[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < RT; ++r) acc[r][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -366,24 +379,27 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, int64_t rb, 
     u32x4_t cw[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r)
-      cw[r] = *reinterpret_cast<const u32x4_t*>(cur + Sl::kC + (wave * RT + r) * 1024 + lane * 16);
-    uint4 av[4][TT];
+      cw[r] = *reinterpret_cast<const u32x4_t*>(cur + Sl::kC + (rg * RT + r) * 1024 + lane * 16);
+    // token tile tt of this wave is tile TW·th + tt of the chunk
+    uint4 av[4][TW];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
-        av[j][tt] = *reinterpret_cast<const uint4*>(cur + ((16 * tt + row) * 16 + ((4 * j + quad) ^ row)) * 16);
-    // GS = 4: s4[tt][v] = the 128-sum of token 16·tt + 4·quad + v (this
-    // wave's copy); else sm[tt][v] = its 4 step sums
-    f32x4_t sm[TT][4], s4[TT];
+      for (int tt = 0; tt < TW; ++tt)
+        av[j][tt] = *reinterpret_cast<const uint4*>(
+            cur + ((16 * (TW * th + tt) + row) * 16 + ((4 * j + quad) ^ row)) * 16);
+    // GS = 4: s4[tt][v] = the 128-sum of token 16·tt' + 4·quad + v; else
+    // sm[tt][v] = its 4 step sums
+    f32x4_t sm[TW][4], s4[TW];
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
+    for (int tt = 0; tt < TW; ++tt) {
+      const int tg = TW * th + tt;
       if (GS == 4) {
-        s4[tt] = *reinterpret_cast<const f32x4_t*>(cur + Sl::kS + wave * 256 + (16 * tt + 4 * quad) * 4);
+        s4[tt] = *reinterpret_cast<const f32x4_t*>(cur + Sl::kS + (16 * tg + 4 * quad) * 4);
       } else {
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          sm[tt][v] = *reinterpret_cast<const f32x4_t*>(cur + Sl::kS + (16 * tt + 4 * quad + v) * 16);
+          sm[tt][v] = *reinterpret_cast<const f32x4_t*>(cur + Sl::kS + (16 * tg + 4 * quad + v) * 16);
       }
     }
     float2 pp[RT][NP];
@@ -391,20 +407,20 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, int64_t rb, 
     for (int r = 0; r < RT; ++r)
 #pragma unroll
       for (int q = 0; q < NP; ++q)
-        pp[r][q] = reinterpret_cast<const float2*>(cur + Sl::kP + (wave * RT + r) * 512)[q * kW4Rows + row];
+        pp[r][q] = reinterpret_cast<const float2*>(cur + Sl::kP + (rg * RT + r) * 512)[q * kW4Rows + row];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
         const bf16x8_t bw = w4_unpack(cw[r][j], kc);
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
+        for (int tt = 0; tt < TW; ++tt)
           acc[r][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[j][tt]), bw,
                                                                acc[r][tt], 0, 0, 0);
       }
       if (GS > 0 && (j + 1) % (GS > 0 ? GS : 1) == 0) {
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
+        for (int tt = 0; tt < TW; ++tt)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             float sx;
@@ -424,12 +440,12 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, int64_t rb, 
 #pragma unroll
         for (int r = 0; r < RT; ++r)
 #pragma unroll
-          for (int tt = 0; tt < TT; ++tt) acc[r][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          for (int tt = 0; tt < TW; ++tt) acc[r][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
     }
     if (GS == 0) {   // one group per row: the slice's running 32-sums
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
+      for (int tt = 0; tt < TW; ++tt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) sxa[tt][v] += ((sm[tt][v][0] + sm[tt][v][1]) + sm[tt][v][2]) + sm[tt][v][3];
 #pragma unroll
@@ -461,38 +477,40 @@ __device__ __forceinline__ void w4_ring_stream(const W4GemmArgs& a, int64_t rb, 
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
+      for (int tt = 0; tt < TW; ++tt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) y[r][tt][v] = p0[r].x * fmaf(-p0[r].y, sxa[tt][v], acc[r][tt][v]);
   }
 }
 
-template <int GS, int TT>
-__global__ __launch_bounds__(256) void w4_gemm_kernel(W4GemmArgs a) {
-  using Sl = W4Slot<GS, TT>;
+template <int GS, int TT, int TS>
+__global__ __launch_bounds__(256 * TS) void w4_gemm_kernel(W4GemmArgs a) {
+  using Sl = W4Slot<GS, TT, TS>;
+  constexpr int TW = Sl::kTilesPerWave;
   __shared__ __attribute__((aligned(16))) uint8_t s0[Sl::kBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s1[Sl::kBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s2[Sl::kBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s3[Sl::kBytes];
-  f32x4_t y[kW4TilesPerWave][TT];
+  f32x4_t y[kW4TilesPerWave][TW];
 #pragma unroll
   for (int r = 0; r < kW4TilesPerWave; ++r)
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) y[r][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < TW; ++tt) y[r][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   int64_t rb, sl;
   w4_block_coords(a, rb, sl);
-  w4_ring_stream<GS, TT>(a, rb, sl, y, s0, s1, s2, s3);
+  w4_ring_stream<GS, TT, TS>(a, rb, sl, y, s0, s1, s2, s3);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rg = wave & 3, th = wave >> 2;
   // lane l's D fragment of tile (T, tt): tokens 16·tt + 4·(l/16) + v, v = 0..3,
   // of weight row 16T + l % 16; one 16-byte store each (tokens past the last
   // hold zeros and are never read)
 #pragma unroll
   for (int r = 0; r < kW4TilesPerWave; ++r) {
-    const int64_t T = rb * kW4TilesPerWg + wave * kW4TilesPerWave + r;
+    const int64_t T = rb * kW4TilesPerWg + rg * kW4TilesPerWave + r;
     if (T < a.mt) {
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
-        *reinterpret_cast<f32x4_t*>(a.part + (((sl * a.mt + T) * TT + tt) * 64 + lane) * 4) = y[r][tt];
+      for (int tt = 0; tt < TW; ++tt)
+        *reinterpret_cast<f32x4_t*>(a.part + (((sl * a.mt + T) * TT + TW * th + tt) * 64 + lane) * 4) = y[r][tt];
     }
   }
 }
@@ -758,13 +776,16 @@ gptq_status launch_w4_gather(const uint16_t* X, int64_t ldx, const int32_t* orde
   return GPTQ_OK;
 }
 
+// Two or four token tiles: eight waves, each pair sharing a row pair and
+// splitting the tokens (two waves per SIMD, so one's VALU work runs beside
+// the other's matrix and LDS work); one or three: four waves.
 template <int GS>
 gptq_status launch_w4_gemm_gs(int tt, dim3 grid, const W4GemmArgs& a, hipStream_t stream) {
   switch (tt) {
-    case 1: hipLaunchKernelGGL((w4_gemm_kernel<GS, 1>), grid, dim3(256), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((w4_gemm_kernel<GS, 2>), grid, dim3(256), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((w4_gemm_kernel<GS, 3>), grid, dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL((w4_gemm_kernel<GS, 4>), grid, dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((w4_gemm_kernel<GS, 1, 1>), grid, dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((w4_gemm_kernel<GS, 2, 2>), grid, dim3(512), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((w4_gemm_kernel<GS, 3, 1>), grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((w4_gemm_kernel<GS, 4, 2>), grid, dim3(512), 0, stream, a); break;
   }
   GPTQ_LAUNCH_CHECK();
   return GPTQ_OK;
