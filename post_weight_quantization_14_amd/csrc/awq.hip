@@ -95,10 +95,13 @@ __device__ __forceinline__ uint64_t d2u(double x) {
 }
 
 // One workgroup of 1024.  Each radix pass counts the keys that match the
-// selected prefix into 256 bins; threads 0..255 (one bin each) take an
-// inclusive scan of the bins (a 64-lane shuffle scan per wave, then the wave
-// totals), and the one thread whose bin holds the remaining rank extends the
-// prefix.  REG: the keys (n <= 1024·kAwqKeys) are computed once and held in
+// selected prefix into 256 bins, each wave into a histogram of its own (the
+// first passes see nearly every key in one bin: one shared histogram would
+// serialise 11008 atomics on one address), and a wave whose matching keys
+// all fall in one bin adds their count with one atomic; threads 0..255 (one
+// bin each) sum the 16 histograms and take an inclusive scan (a 64-lane
+// shuffle scan per wave, then the wave totals), and the one thread whose bin
+// holds the remaining rank extends the prefix.  REG: the keys (n <= 1024·kAwqKeys) are computed once and held in
 // registers, kAwqKeys per thread, for all eight passes; otherwise every
 // pass recomputes them from abs_sum.
 constexpr int kAwqKeys = 16;
@@ -106,7 +109,7 @@ template <bool REG>
 __global__ __launch_bounds__(1024) void awq_scale_kernel(const double* __restrict__ abs_sum, int64_t n,
                                                          double tokens, float protect,
                                                          float* __restrict__ channel_scale, int* flag) {
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[16][256];   // per wave
   __shared__ uint32_t wtot[4];
   __shared__ uint64_t sel[2];   // prefix, remaining rank
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -137,23 +140,40 @@ __global__ __launch_bounds__(1024) void awq_scale_kernel(const double* __restric
   }
   uint64_t mask = 0;
   for (int shift = 56; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hist[q * 4 + (tid >> 8)][tid & 255] = 0;
     __syncthreads();
     const uint64_t prefix = sel[0], rem = sel[1];
+    uint32_t* hw = hist[wave];
+    // count key k if it matches the prefix (act); a wave whose active keys
+    // share one bin adds their number at once
+    auto count = [&](bool act, uint64_t k) {
+      const uint32_t b = (uint32_t)(k >> shift) & 255u;
+      const uint64_t am = __ballot(act);
+      if (am == 0) return;
+      const int first = __builtin_ctzll(am);
+      const uint32_t bf = (uint32_t)__shfl((int)b, first, 64);
+      if (__ballot(act && b != bf) == 0) {
+        if (lane == first) atomicAdd(&hw[bf], (uint32_t)__popcll(am));
+      } else if (act) {
+        atomicAdd(&hw[b], 1u);
+      }
+    };
     if constexpr (REG) {
 #pragma unroll
-      for (int i = 0; i < kAwqKeys; ++i)
-        if (tid + 1024 * i < n && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> shift) & 255u], 1u);
+      for (int i = 0; i < kAwqKeys; ++i) count(tid + 1024 * i < n && (key[i] & mask) == prefix, key[i]);
     } else {
-      for (int64_t j = tid; j < n; j += 1024) {
-        const uint64_t k = d2u(abs_sum[j] / tokens);
-        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+      for (int64_t j0 = 0; j0 < n; j0 += 1024) {
+        const int64_t j = j0 + tid;
+        const uint64_t k = j < n ? d2u(abs_sum[j] / tokens) : 0;
+        count(j < n && (k & mask) == prefix, k);
       }
     }
     __syncthreads();
     uint32_t v = 0, x = 0;
     if (tid < 256) {
-      v = hist[tid];
+#pragma unroll
+      for (int w = 0; w < 16; ++w) v += hist[w][tid];
       x = v;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
