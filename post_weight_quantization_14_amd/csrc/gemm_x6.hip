@@ -157,7 +157,11 @@ __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B,
                                                         int64_t ldc, int64_t M, int64_t N, float alpha,
                                                         float beta) {
   __shared__ __attribute__((aligned(16))) uint8_t s0[X6SLOTB], s1[X6SLOTB], s2[X6SLOTB];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index in a scalar register: every buffer descriptor and LDS
+  // destination below derives from it, and only wave-uniform ones give one
+  // instruction per copy (from a vector register the compiler wraps each
+  // copy in a loop over the distinct values, a dozen instructions a copy)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
   int64_t ti, tj;
   static_assert(TM == X6T || (TM == 64 && !LOWER), "64-row tiles for the full product only");
