@@ -34,10 +34,11 @@ constexpr int X6OPB = 3 * X6PLANEB;  // 12 KB per operand
 constexpr int X6SLOTB = 2 * X6OPB;   // 24 KB per stage
 constexpr int X6RING = 3;
 constexpr int kX6Band = 16;         // tile rows per band of the tile order
-// 73728 B static + this > 80 KB (one workgroup per CU), and <= 160 KB - 75264 B
+// 73728 B static + this > 80 KB (one workgroup per CU), and <= 160 KB - 77312 B
+// (the Cholesky leaf's LDS, the largest workgroup meant to run beside it)
 constexpr size_t kX6PolitePad = 12288;
-static_assert(3 * X6SLOTB + kX6PolitePad > 81920 && 3 * X6SLOTB + kX6PolitePad + 75264 <= 163840,
-              "polite footprint: one per CU, a 74 KB workgroup beside it");
+static_assert(3 * X6SLOTB + kX6PolitePad > 81920 && 3 * X6SLOTB + kX6PolitePad + 77312 <= 163840,
+              "polite footprint: one per CU, a 75.5 KB workgroup beside it");
 
 __device__ __forceinline__ constexpr int x6_vmcnt(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);

@@ -164,9 +164,12 @@ __global__ __launch_bounds__(256) void permute_kernel(const float* __restrict__ 
 //     v_rsq_f32; the solves multiply by the kept 1/L[c][c]); owners of (bi, jb)
 //     solve X · L_jbᵀ = A_bi,jb along their row; owners of (bi, bj),
 //     jb < bj <= bi, subtract L_bi,jb · L_bj,jbᵀ.
-//   Inverse (R = I, row block kb per step): owners of (kb, bj) solve
-//     L_kb,kb · M_kb,bj = R_kb,bj down their column; owners of (bi, bj),
-//     bi > kb, bj <= kb, subtract L_bi,kb · M_kb,bj.
+//   Inverse by doubling: the owners of the eight diagonal sub-blocks invert
+//     them at once (forward substitution down their column); then three
+//     levels join neighbouring lower-triangular blocks of 1, 2 and 4
+//     sub-blocks, [M11 0; M21 M22] with M21 = -M22 · (L21 · M11), as
+//     v_mfma_f32_16x16x4f32 products of 16 x 16 sub-blocks spread over the
+//     nine waves (two barriers per level instead of two per 16-row step).
 // Writes L back into A (lower triangle of the block) and D = L⁻¹ into the same
 // block of Mmat (strict upper part of that block set to 0).
 // ---------------------------------------------------------------------------
@@ -228,13 +231,32 @@ __device__ __forceinline__ void diag_factor(float (&a)[LE], int r, bool& bad, fl
 // small enough to share a CU with a trailing-update GEMM workgroup.
 constexpr int kPk = 32;          // columns of P per staged pass
 constexpr int kPp = kPk + 4;     // row pitch of the staged pass
+// Ps holds a pass of P, or the 16 sub-blocks of T at the last inverse level
+constexpr int kPsFloats = (NB * kPp > 16 * LSZ) ? NB * kPp : 16 * LSZ;
+
+// C += A · B for 16 x 16 sub-blocks stored row-major in LDS (pitch LP), by
+// four v_mfma_f32_16x16x4f32: lane l supplies A[l % 16][4kk + l / 16] and
+// B[4kk + l / 16][l % 16]; C[4 (l / 16) + v][l % 16] is element v of the result.
+__device__ __forceinline__ f32x4_t sub_mma(const float* A, const float* B, f32x4_t c, int lane) {
+  const float* pa = A + (lane & 15) * LP + (lane >> 4);
+  const float* pb = B + (lane >> 4) * LP + (lane & 15);
+#pragma unroll
+  for (int kk = 0; kk < LE / 4; ++kk) c = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[4 * kk], pb[4 * kk * LP], c, 0, 0, 0);
+  return c;
+}
+__device__ __forceinline__ void sub_store(float* dst, f32x4_t c, float sign, int lane) {
+  float* p = dst + 4 * (lane >> 4) * LP + (lane & 15);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) p[v * LP] = sign * c[v];
+}
 
 __global__ __launch_bounds__(kLeafThreads) void chol_leaf_kernel(float* A, float* Mm, int64_t lda,
                                                                  int64_t k0, int pre, int* flag) {
   __shared__ __attribute__((aligned(16))) float Ls[LT * LSZ];   // L by lower sub-block
   __shared__ __attribute__((aligned(16))) float Ms[LN * LSZ];   // M row block of the step
   __shared__ float Ldi[NB];                                     // 1 / L[c][c]
-  __shared__ __attribute__((aligned(16))) float Ps[NB * kPp];   // one pass of P
+  // one pass of P (pre-update), later T = L21 · M11 of one inverse level
+  __shared__ __attribute__((aligned(16))) float Ps[kPsFloats];
   const int tid = threadIdx.x;
   const int t = tid >> 4, r = tid & (LE - 1);
   int bi, bj;
@@ -363,47 +385,67 @@ __global__ __launch_bounds__(kLeafThreads) void chol_leaf_kernel(float* A, float
   for (int c = 0; c < LE; ++c)
     if (bi != bj || c <= r) Ab[(int64_t)(LE * bi + r) * lda + LE * bj + c] = a[c];
 
-  // ---- inverse by 16-row block steps (R starts as I); thread = column r of (bi, bj)
-  float m[LE];
+  // ---- D = L⁻¹.  Diagonal sub-blocks of D go to Ms, an off-diagonal one
+  // replaces the sub-block of L at its place in Ls: every L sub-block below
+  // the diagonal belongs to exactly one join and is last read by that join's
+  // first product, before the barrier after which its D block is written.
+  // (The Cholesky's last reads of Ls ended at its final barrier.)
+  auto dblk = [&](int i, int j) -> float* { return i == j ? Ms + i * LSZ : Ls + lblk(i, j); };
+  if (bi == bj) {
+    // column r of L_ii⁻¹: m[i] = (δ_ir - Σ_{k<i} L[i][k] m[k]) / L[i][i]
+    const float* L = Ls + lblk(bi, bi);
+    float m[LE];
 #pragma unroll
-  for (int i = 0; i < LE; ++i) m[i] = (bi == bj && i == r) ? 1.f : 0.f;
+    for (int i = 0; i < LE; ++i) {
+      float v = (i == r) ? 1.f : 0.f;
+#pragma unroll
+      for (int k = 0; k < i; ++k) v -= L[i * LP + k] * m[k];
+      m[i] = v * Ldi[LE * bi + i];
+    }
+    float* dst = Ms + bi * LSZ + r;
+#pragma unroll
+    for (int i = 0; i < LE; ++i) dst[i * LP] = m[i];
+  }
+  __syncthreads();
+  {
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    constexpr int kWaves = kLeafThreads / 64;
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
-  for (int kb = 0; kb < LN; ++kb) {
-    if (bi == kb) {
-      // L · M = R down the column: m[i] = (m[i] - Σ_{k<i} L[i][k] m[k]) / L[i][i]
-      const float* L = Ls + lblk(kb, kb);
-#pragma unroll
-      for (int i = 0; i < LE; ++i) {
-        float v = m[i];
-#pragma unroll
-        for (int k = 0; k < i; ++k) v -= L[i * LP + k] * m[k];
-        m[i] = v * Ldi[LE * kb + i];
+    for (int h = 1; h < LN; h *= 2) {   // join pairs of lower-triangular blocks of h sub-blocks
+      const int jobs = (LN / (2 * h)) * h * h;   // 16 x 16 outputs per product phase
+      // T(i, j) = Σ_{k=j}^{h-1} L21(i, k) · M11(k, j)
+#pragma unroll 1
+      for (int job = wave; job < jobs; job += kWaves) {
+        const int q = job / (h * h), i = (job / h) % h, j = job % h;
+        const int c1 = 2 * q * h, r2 = c1 + h;
+        f32x4_t c = zero;
+#pragma unroll 1
+        for (int k = j; k < h; ++k) c = sub_mma(Ls + lblk(r2 + i, c1 + k), dblk(c1 + k, c1 + j), c, lane);
+        sub_store(Ps + job * LSZ, c, 1.f, lane);
       }
-      float* dst = Ms + bj * LSZ + r;
-#pragma unroll
-      for (int i = 0; i < LE; ++i) dst[i * LP] = m[i];
-    }
-    __syncthreads();
-    if (bi > kb && bj <= kb) {
-      const float* L = Ls + lblk(bi, kb);
-      const float* Mk = Ms + bj * LSZ + r;
-      float mk[LE];
-#pragma unroll
-      for (int k = 0; k < LE; ++k) mk[k] = Mk[k * LP];
-#pragma unroll
-      for (int i = 0; i < LE; ++i) {
-        float acc = m[i];
-#pragma unroll
-        for (int k = 0; k < LE; ++k) acc -= L[i * LP + k] * mk[k];
-        m[i] = acc;
+      __syncthreads();
+      // M21(i, j) = -Σ_{k=0}^{i} M22(i, k) · T(k, j), written over L21(i, j)
+#pragma unroll 1
+      for (int job = wave; job < jobs; job += kWaves) {
+        const int q = job / (h * h), i = (job / h) % h, j = job % h;
+        const int c1 = 2 * q * h, r2 = c1 + h;
+        f32x4_t c = zero;
+#pragma unroll 1
+        for (int k = 0; k <= i; ++k) c = sub_mma(dblk(r2 + i, r2 + k), Ps + (q * h * h + k * h + j) * LSZ, c, lane);
+        sub_store(Ls + lblk(r2 + i, c1 + j), c, -1.f, lane);
       }
+      __syncthreads();
     }
-    __syncthreads();   // Ms is rewritten by the next step
   }
 
-  // ---- D = L⁻¹ (lower) to Mmat; owners of (bi, bj), bi > bj, also zero (bj, bi)
+  // ---- D to Mmat: thread r of (bi, bj) writes column r; owners of (bi, bj),
+  // bi > bj, also zero (bj, bi)
+  {
+    const float* src = dblk(bi, bj) + r;
 #pragma unroll
-  for (int i = 0; i < LE; ++i) Mb[(int64_t)(LE * bi + i) * lda + LE * bj + r] = m[i];
+    for (int i = 0; i < LE; ++i) Mb[(int64_t)(LE * bi + i) * lda + LE * bj + r] = src[i * LP];
+  }
   if (bi > bj) {
 #pragma unroll
     for (int i = 0; i < LE; ++i) Mb[(int64_t)(LE * bj + i) * lda + LE * bi + r] = 0.f;
