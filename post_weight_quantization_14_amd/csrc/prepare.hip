@@ -608,7 +608,7 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
         r.B = Pc; r.ldb = lda;
         r.C = A + (k0 + 2 * NB) * lda + k0 + NB; r.ldc = lda;
         r.M = rows - NB; r.N = NB; r.k_begin = 0; r.k_end = NB; r.alpha = -1.f; r.beta = 1.f;
-        GPTQ_TRY(launch_gemm_rect(r, /*b_colmajor=*/true, inr.stream));
+        GPTQ_TRY(launch_gemm_rect(r, /*b_colmajor=*/true, inr.stream, ceil_div(r.M, NB) < 128 ? 64 : NB));
         if (cols > NB) {
           r.B = P;
           r.C = A + (k0 + 2 * NB) * lda + k0 + 2 * NB;
