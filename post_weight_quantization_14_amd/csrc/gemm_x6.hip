@@ -10,9 +10,13 @@
 // than v_mfma_f32_32x32x2f32 on the same GEMM, with a result within fp32
 // rounding of it (relative Frobenius difference ~5e-8).
 //
-// Planes are [3][rows][kp] bf16 (k contiguous, kp a multiple of 16, zero
-// padded); the split kernels write them from fp32 rows (A, or B stored with
-// k contiguous) or from fp32 columns (B stored k-major, transposed on the way).
+// Planes are three bf16 arrays stored k-step-major ([kp/16][rows][16], kp a
+// multiple of 16, zero padded), so that one k-step of a tile's rows is one
+// contiguous block and every direct-to-LDS copy reads 1 KB in one piece (with
+// rows of kp contiguous positions a copy gathered 32 bytes from each of 32
+// rows kp·2 bytes apart, and the copies took 70% of the GEMM's time); the split
+// kernels write them from fp32 rows (A, or B stored with k contiguous) or from
+// fp32 columns (B stored k-major, transposed on the way).
 //
 // GEMM: tiles of 128 x 128 per workgroup of 4 waves (64 x 64 each); per
 // 16-position k-step the six operand planes (2 x 3 x 4 KB) stream into a
@@ -28,6 +32,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int X6T = 128;             // tile edge
 constexpr int X6KS = 16;             // k per stage (one MFMA k-step)
+static_assert(X6KS == kX6Step, "a stage is one contiguous k-step piece of the planes");
 constexpr int X6ROWB = X6KS * 2;     // 32 bytes per row per plane
 constexpr int X6PLANEB = X6T * X6ROWB;
 constexpr int X6OPB = 3 * X6PLANEB;  // 12 KB per operand
@@ -55,27 +60,34 @@ __device__ __forceinline__ void x6_split(float x, uint16_t& h, uint16_t& m, uint
   l = (uint16_t)(lb >> 16);
 }
 
-// planes[q][r][k] from X[r][k] (k < K), zero for K <= k < kp
+// planes of X[r][k] (k < K), zero for K <= k < kp.  Element i of the sweep is
+// k-step i / (16 rows), row (i / 16) % rows, position i % 16: the writes are
+// contiguous, the reads 64-byte row pieces.
 __global__ __launch_bounds__(256) void x6_split_rows_kernel(const float* __restrict__ X, int64_t ldx,
                                                             int64_t rows, int64_t K, int64_t kp,
-                                                            uint16_t* __restrict__ out, int64_t pstride) {
+                                                            uint16_t* __restrict__ out, int64_t pstride,
+                                                            int64_t sst) {
   const int64_t total = rows * kp;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int64_t r = i / kp, k = i % kp;
+    const int64_t ks = i / (rows * kX6Step), r = (i / kX6Step) % rows, kk = i % kX6Step;
+    const int64_t k = ks * kX6Step + kk;
     const float x = k < K ? X[r * ldx + k] : 0.f;
     uint16_t h, m, l;
     x6_split(x, h, m, l);
-    out[r * kp + k] = h;
-    out[pstride + r * kp + k] = m;
-    out[2 * pstride + r * kp + k] = l;
+    const int64_t o = ks * sst + r * kX6Step + kk;
+    out[o] = h;
+    out[pstride + o] = m;
+    out[2 * pstride + o] = l;
   }
 }
 
-// planes[q][c][k] from X[k][c] (k < K, c < cols), zero for K <= k < kp:
-// 64 x 64 tiles through LDS, read along c and written along k
+// planes of row c = X[k][c] over k (k < K, c < cols), zero for K <= k < kp:
+// 64 x 64 tiles through LDS, read along c; written as 4 k-steps of 64 rows,
+// 256 contiguous elements per pass of the workgroup
 __global__ __launch_bounds__(256) void x6_split_cols_kernel(const float* __restrict__ X, int64_t ldx,
                                                             int64_t K, int64_t cols, int64_t kp,
-                                                            uint16_t* __restrict__ out, int64_t pstride) {
+                                                            uint16_t* __restrict__ out, int64_t pstride,
+                                                            int64_t sst) {
   __shared__ float t[64][65];
   const int64_t c0 = (int64_t)blockIdx.x * 64, k0 = (int64_t)blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -93,14 +105,18 @@ __global__ __launch_bounds__(256) void x6_split_cols_kernel(const float* __restr
     t[r][tx] = (k0 + r < K && c0 + tx < cols) ? v[u] : 0.f;
   }
   __syncthreads();
-  for (int r = ty; r < 64; r += 4) {
-    const int64_t c = c0 + r, k = k0 + tx;
+#pragma unroll 1
+  for (int j = 0; j < 16; ++j) {
+    const int e = 256 * j + (int)threadIdx.x;
+    const int ks = e >> 10, cl = (e >> 4) & 63, kk = e & 15;
+    const int64_t c = c0 + cl, k = k0 + 16 * ks + kk;
     if (c < cols && k < kp) {
       uint16_t h, m, l;
-      x6_split(t[tx][r], h, m, l);
-      out[c * kp + k] = h;
-      out[pstride + c * kp + k] = m;
-      out[2 * pstride + c * kp + k] = l;
+      x6_split(t[16 * ks + kk][cl], h, m, l);
+      const int64_t o = (k / kX6Step) * sst + c * kX6Step + kk;
+      out[o] = h;
+      out[pstride + o] = m;
+      out[2 * pstride + o] = l;
     }
   }
 }
@@ -173,11 +189,13 @@ __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B,
   const int64_t nst = kp / X6KS;
   // 24 copy instructions per stage = (operand, plane, row quarter); wave w
   // issues 6 of them.  Lane i of one covers row 32q + i/2, 16 bytes, into LDS
-  // chunk i%2 holding source chunk (i%2) ^ ((row >> 3) & 1) (bank spread).
+  // chunk i%2 holding source chunk (i%2) ^ ((row >> 3) & 1) (bank spread); the
+  // source of one instruction is the 1 KB k-step piece of its 32 rows.
   constexpr int32_t kOut = 0x7ffffff0;
   int32_t voff[6];
   const uint16_t* obase[6];
-  int64_t obytes[6];
+  int64_t ostep[6];
+  int32_t obytes[6];
   int ldso[6];
 #pragma unroll
   for (int u = 0; u < 6; ++u) {
@@ -188,9 +206,10 @@ __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B,
     const X6Planes& P = op == 0 ? A : B;
     const int64_t grow = (op == 0 ? i0 : j0) + row;
     obase[u] = P.p + (int64_t)plane * P.pstride;
-    obytes[u] = P.rows * kp * 2;
+    ostep[u] = P.sst;
+    obytes[u] = (int32_t)(P.rows * kX6Step * 2);
     // A rows past the tile (TM = 64) read as zero like rows past the operand
-    voff[u] = (grow < P.rows && (op != 0 || row < TM)) ? (int32_t)(grow * kp * 2 + cs * 16) : kOut;
+    voff[u] = (grow < P.rows && (op != 0 || row < TM)) ? (int32_t)(grow * kX6Step * 2 + cs * 16) : kOut;
     ldso[u] = op * X6OPB + plane * X6PLANEB + q * 1024;
   }
   auto issue = [&](int64_t st, uint8_t* slot) {
@@ -198,8 +217,7 @@ __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B,
     for (int u = 0; u < 6; ++u) {
       const bool live = st < nst;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(obase[u]) + (live ? st * X6KS : 0), 0,
-          live ? (int32_t)(obytes[u] - st * X6KS * 2) : 0, 0x00020000);
+          const_cast<uint16_t*>(obase[u]) + (live ? st * ostep[u] : 0), 0, live ? obytes[u] : 0, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(slot + ldso[u]), 16, voff[u], 0, 0, 0);
     }
   };
@@ -305,24 +323,34 @@ __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B,
 }  // namespace
 
 gptq_status launch_x6_split_rows(const float* X, int64_t ldx, int64_t rows, int64_t K, int64_t kp,
-                                 uint16_t* out, int64_t pstride, hipStream_t stream) {
+                                 uint16_t* out, int64_t pstride, int64_t sst, hipStream_t stream) {
   if (rows <= 0) return GPTQ_OK;
+  if (kp % kX6Step != 0 || sst < rows * kX6Step) {
+    set_error("launch_x6_split_rows: kp %lld, step stride %lld for %lld rows", (long long)kp, (long long)sst,
+              (long long)rows);
+    return GPTQ_ERR_INVALID_ARG;
+  }
   const int64_t total = rows * kp;
   hipLaunchKernelGGL(x6_split_rows_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(total, 256), 4096)),
-                     dim3(256), 0, stream, X, ldx, rows, K, kp, out, pstride);
+                     dim3(256), 0, stream, X, ldx, rows, K, kp, out, pstride, sst);
   GPTQ_LAUNCH_CHECK();
   return GPTQ_OK;
 }
 
 gptq_status launch_x6_split_cols(const float* X, int64_t ldx, int64_t K, int64_t cols, int64_t kp,
-                                 uint16_t* out, int64_t pstride, hipStream_t stream) {
+                                 uint16_t* out, int64_t pstride, int64_t sst, hipStream_t stream) {
   if (cols <= 0) return GPTQ_OK;
+  if (kp % 64 != 0 || sst < cols * kX6Step) {   // the kernel writes whole 64-position tiles of k
+    set_error("launch_x6_split_cols: kp %lld, step stride %lld for %lld columns", (long long)kp, (long long)sst,
+              (long long)cols);
+    return GPTQ_ERR_INVALID_ARG;
+  }
   if (K <= 0 || K > kp) {   // the kernel reads rows up to min(k, K - 1)
     set_error("launch_x6_split_cols: K = %lld (1 .. %lld)", (long long)K, (long long)kp);
     return GPTQ_ERR_INVALID_ARG;
   }
   hipLaunchKernelGGL(x6_split_cols_kernel, dim3((unsigned)ceil_div(cols, 64), (unsigned)ceil_div(kp, 64)),
-                     dim3(256), 0, stream, X, ldx, K, cols, kp, out, pstride);
+                     dim3(256), 0, stream, X, ldx, K, cols, kp, out, pstride, sst);
   GPTQ_LAUNCH_CHECK();
   return GPTQ_OK;
 }
@@ -331,7 +359,8 @@ gptq_status launch_x6_gemm(const X6Planes& A, const X6Planes& B, float* C, int64
                            int64_t N, float alpha, float beta, bool lower, hipStream_t stream, bool polite,
                            int tile_rows) {
   if (M <= 0 || N <= 0) return GPTQ_OK;
-  if (A.kp != B.kp || A.kp % X6KS != 0) {
+  if (A.kp != B.kp || A.kp % X6KS != 0 || A.sst < A.rows * kX6Step || B.sst < B.rows * kX6Step ||
+      A.rows * kX6Step * 2 > INT32_MAX || B.rows * kX6Step * 2 > INT32_MAX) {
     set_error("launch_x6_gemm: plane widths %lld / %lld", (long long)A.kp, (long long)B.kp);
     return GPTQ_ERR_INVALID_ARG;
   }

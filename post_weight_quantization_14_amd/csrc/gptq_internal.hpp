@@ -202,17 +202,24 @@ gptq_status run_w4a16_matmul_noalloc(const uint16_t* X, int64_t tokens, int64_t 
                                      const W4Layout& L, float* Y, int64_t ldy, hipStream_t stream);
 
 // ---------------------------------------------------------------- fp32-accurate GEMM on bf16 MFMA
-// Operands as three exact bf16 planes [3][rows][kp] (plane q at p + q·pstride,
-// k contiguous); C = alpha·A·Bᵀ + beta·C, or only its lower part (row >= column).
+// Operands as three exact bf16 planes, each stored k-step-major: element
+// (r, k) of plane q at p + q·pstride + (k / 16)·sst + 16·r + k % 16, so the 16
+// k positions of one MFMA step are 32 contiguous bytes per row and a step of
+// consecutive rows is one contiguous block (sst = 16 × the rows allocated; a
+// view of rows r0.. of a plane is p + 16·r0 with the same sst).
+// C = alpha·A·Bᵀ + beta·C, or only its lower part (row >= column).
 struct X6Planes {
   const uint16_t* p;
-  int64_t rows, kp, pstride;
+  int64_t rows, kp, pstride, sst;
 };
 constexpr int64_t kX6K = 512;   // k extent of the trailing updates that use it
+constexpr int64_t kX6Step = 16;  // k positions per contiguous row piece
+// planes of X[r][k] (r < rows, k < K; zero for K <= k < kp) at out, rows 0..rows-1
 gptq_status launch_x6_split_rows(const float* X, int64_t ldx, int64_t rows, int64_t K, int64_t kp,
-                                 uint16_t* out, int64_t pstride, hipStream_t stream);
+                                 uint16_t* out, int64_t pstride, int64_t sst, hipStream_t stream);
+// planes of the transpose of X[k][c] (k < K, c < cols): plane row c holds column c
 gptq_status launch_x6_split_cols(const float* X, int64_t ldx, int64_t K, int64_t cols, int64_t kp,
-                                 uint16_t* out, int64_t pstride, hipStream_t stream);
+                                 uint16_t* out, int64_t pstride, int64_t sst, hipStream_t stream);
 // polite: at most one workgroup per CU, leaving LDS for a latency-bound
 // kernel of another stream (the leaf or the block quantizer) beside it.
 // tile_rows: 128, or 64 (full product only) for products of few tiles.

@@ -633,14 +633,14 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
       // the panel rows L[K1:, K0:K1] as exact bf16 planes: A and B operand alike
       const int par = (int)((K0 / OB) & 1);
       uint16_t* pl = reinterpret_cast<uint16_t*>(w + p.x6_off) + (size_t)par * 3 * p.n_pad * kX6K;
-      const int64_t pst = p.n_pad * kX6K;
-      GPTQ_TRY(launch_x6_split_rows(A + K1 * lda + K0, lda, rest, K1 - K0, kX6K, pl, pst, stream));
+      const int64_t pst = p.n_pad * kX6K, sst = p.n_pad * kX6Step;
+      GPTQ_TRY(launch_x6_split_rows(A + K1 * lda + K0, lda, rest, K1 - K0, kX6K, pl, pst, sst, stream));
       if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
       side_pending = false;
       if (far > 0) {
         GPTQ_HIP_CHECK(hipEventRecord(side.ready, stream));
         GPTQ_HIP_CHECK(hipStreamWaitEvent(side.stream, side.ready, 0));
-        const X6Planes PF{pl + near * kX6K, far, kX6K, pst};
+        const X6Planes PF{pl + near * kX6Step, far, kX6K, pst, sst};
         // a small far update leaves CU room for the next outer block's
         // leaves; a large one is the bottleneck and takes the whole chip
         const bool polite = far < kPolitePrepFar;
@@ -649,7 +649,7 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
         GPTQ_HIP_CHECK(hipEventRecord(side.done, side.stream));
         side_pending = true;
       }
-      const X6Planes PR{pl, rest, kX6K, pst}, PN{pl, near, kX6K, pst};
+      const X6Planes PR{pl, rest, kX6K, pst, sst}, PN{pl, near, kX6K, pst, sst};
       GPTQ_TRY(launch_x6_gemm(PR, PN, A + K1 * lda + K1, lda, rest, near, -1.f, 1.f, true, stream));
     }
   }

@@ -321,15 +321,15 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
       uint16_t* pa = reinterpret_cast<uint16_t*>(w + p.x6a_off) + (size_t)par * 3 * m * kX6K;
       uint16_t* pb = reinterpret_cast<uint16_t*>(w + p.x6b_off) + (size_t)par * 3 * n * kX6K;
       const int64_t K = s2 - s1;
-      GPTQ_TRY(launch_x6_split_rows(errs, kQSuper, m, K, kX6K, pa, m * kX6K, stream));
-      GPTQ_TRY(launch_x6_split_cols(U + s1 * n + s2, n, K, n - s2, kX6K, pb, n * kX6K, stream));
-      const X6Planes PA{pa, m, kX6K, m * kX6K};
+      GPTQ_TRY(launch_x6_split_rows(errs, kQSuper, m, K, kX6K, pa, m * kX6K, m * kX6Step, stream));
+      GPTQ_TRY(launch_x6_split_cols(U + s1 * n + s2, n, K, n - s2, kX6K, pb, n * kX6K, n * kX6Step, stream));
+      const X6Planes PA{pa, m, kX6K, m * kX6K, m * kX6Step};
       if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
       side_pending = false;
       if (far > 0) {
         GPTQ_HIP_CHECK(hipEventRecord(side.ready, stream));
         GPTQ_HIP_CHECK(hipStreamWaitEvent(side.stream, side.ready, 0));
-        const X6Planes PF{pb + near * kX6K, far, kX6K, n * kX6K};
+        const X6Planes PF{pb + near * kX6Step, far, kX6K, n * kX6K, n * kX6Step};
         // a small far update leaves CU room for the next superblock's blocks;
         // a large one is the stage's bottleneck and takes the whole chip
         const bool polite = far < kQPoliteFar;
@@ -337,7 +337,7 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
         GPTQ_HIP_CHECK(hipEventRecord(side.done, side.stream));
         side_pending = true;
       }
-      const X6Planes PN{pb, near, kX6K, n * kX6K};
+      const X6Planes PN{pb, near, kX6K, n * kX6K, n * kX6Step};
       // on the chain: with fewer 128-row tiles than CUs, 64-row tiles
       const int near_rows = ceil_div(m, 128) * ceil_div(near, 128) < 256 ? 64 : 128;
       GPTQ_TRY(launch_x6_gemm(PA, PN, Wp + s2, p.ldw, m, near, -1.f, 1.f, false, stream, false, near_rows));
