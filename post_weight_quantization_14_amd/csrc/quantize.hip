@@ -107,7 +107,10 @@ __global__ __launch_bounds__(256) void row_params_kernel(const float* __restrict
 __global__ __launch_bounds__(256) void gidx_kernel(const int32_t* __restrict__ perm, int64_t n,
                                                    int64_t gw, int32_t* g_idx, int32_t* invperm) {
   const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (p >= n) return;
+  if (p >= n) {   // invperm is padded to whole 8-entry pieces: positions n.. read as 0
+    if (p < (n + 7) / 8 * 8) invperm[p] = 0;
+    return;
+  }
   const int32_t j = perm[p];
   invperm[j] = (int32_t)p;
   g_idx[j] = gw > 0 ? (int32_t)(p / gw) : 0;
@@ -116,45 +119,69 @@ __global__ __launch_bounds__(256) void gidx_kernel(const int32_t* __restrict__ p
 // qweight word (r, wd) in original column order, and this word's share of
 // ‖W − Ŵ‖² (Ŵ rebuilt from the stored code, scale and zero), reduced per
 // workgroup into part[].
-template <typename T>
+template <typename T, int PER>
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ codes, int64_t ldw,
-                                                   const int32_t* __restrict__ invperm,
-                                                   const int32_t* __restrict__ g_idx,
+                                                   const int32_t* __restrict__ invperm, int64_t gw,
                                                    const float* __restrict__ scales,
                                                    const int32_t* __restrict__ zeros, int64_t G,
-                                                   const T* __restrict__ W, int64_t m, int64_t n,
-                                                   int bits, int64_t words, int64_t bpr,
+                                                   const T* __restrict__ W, int64_t n, int64_t words,
                                                    uint32_t* __restrict__ qweight, double* part) {
+  constexpr int kWidth = 32 / PER;   // bits per code slot: 4 (2-4 bit codes) or 8
+  // the row's codes (in processing order) and group parameters go to LDS
+  // first: read in original order they are a gather, one cache line per
+  // byte, which bound the kernel on the address units
+  extern __shared__ __attribute__((aligned(16))) uint8_t psm[];
+  uint8_t* cs = psm;
+  float* ss = reinterpret_cast<float*>(psm + ldw);
+  float* zs = ss + G;
   __shared__ double red[256];
-  const int64_t r = blockIdx.x / bpr;
-  const int64_t wd = (blockIdx.x % bpr) * 256 + threadIdx.x;
-  const int per = bits <= 4 ? 8 : 4, width = bits <= 4 ? 4 : 8;
-  double acc = 0.0;
-  if (wd < words) {
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  for (int64_t o = 16 * tid; o < ldw; o += 16 * 256)   // ldw is a multiple of 128
+    *reinterpret_cast<uint4*>(cs + o) = *reinterpret_cast<const uint4*>(codes + r * ldw + o);
+  for (int64_t g = tid; g < G; g += 256) {
+    ss[g] = scales[r * G + g];
+    zs[g] = (float)zeros[r * G + g];
+  }
+  __syncthreads();
+  float dacc = 0.f;
+  for (int64_t wd = tid; wd < words; wd += 256) {
+    // unconditional loads at clamped positions, all in flight together (a
+    // conditional load compiles to a branch and a wait of its own)
+    // the word's processing positions: 16-byte loads (invperm is padded to
+    // whole pieces of 8); its group is the position's 128-column block of
+    // groups, position / gw (gw = 0: one group)
+    int32_t ip[PER];
+    float wv[PER];
+#pragma unroll
+    for (int h = 0; h < PER / 4; ++h) {
+      const int4 q = *reinterpret_cast<const int4*>(invperm + wd * PER + 4 * h);
+      ip[4 * h] = q.x; ip[4 * h + 1] = q.y; ip[4 * h + 2] = q.z; ip[4 * h + 3] = q.w;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) wv[i] = to_f32<T>(W[r * n + std::min<int64_t>(wd * PER + i, n - 1)]);
+    int32_t gi[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) gi[i] = gw > 0 ? ip[i] / (int32_t)gw : 0;
     uint32_t word = 0;
-    float dacc = 0.f;
-    for (int i = 0; i < per; ++i) {
-      const int64_t j = wd * per + i;
-      if (j < n) {
-        const uint32_t c = codes[r * ldw + invperm[j]];
-        word |= c << (width * i);
-        const int64_t g = g_idx[j];
-        const float s = scales[r * G + g];
-        const float zz = (float)zeros[r * G + g];
-        const float d = to_f32<T>(W[r * n + j]) - ((float)c - zz) * s;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (wd * PER + i < n) {
+        const uint32_t c = cs[ip[i]];
+        word |= c << (kWidth * i);
+        const float d = wv[i] - ((float)c - zs[gi[i]]) * ss[gi[i]];
         dacc += d * d;
       }
     }
     qweight[r * words + wd] = word;
-    acc = dacc;
   }
-  red[threadIdx.x] = acc;
+  red[tid] = dacc;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    if (tid < w) red[tid] += red[tid + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+  if (tid == 0) part[r] = red[0];
 }
 
 // loss[0] = Σ_rows ½Σe², loss[1] = Σ parts; one workgroup, fixed order.
@@ -210,15 +237,14 @@ QuantPlan plan_quantize(int64_t m, int64_t n, const gptq_config& cfg) {
   p.ldw = round_up(std::max<int64_t>(n, 1), QB);
   p.groups = gptq_num_groups(n, cfg.group_size);
   p.words = gptq_qweight_words(n, cfg.bits);
-  const int64_t bpr = ceil_div(std::max<int64_t>(p.words, 1), 256);
   size_t off = 0;
   p.wp_off = off; off += align256((size_t)m * p.ldw * sizeof(float));
-  p.part_off = off;  // pack partials: one double per (row, word-block)
-  off += align256((size_t)m * bpr * sizeof(double));
+  p.part_off = off;  // pack partials: one double per row
+  off += align256((size_t)m * sizeof(double));
   p.codes_off = off; off += align256((size_t)m * p.ldw);
   p.err_off = off; off += align256((size_t)2 * m * kQSuper * sizeof(float));   // two superblocks
   p.loss_off = off; off += align256((size_t)m * sizeof(double));
-  p.inv_off = off; off += align256((size_t)n * sizeof(int32_t));
+  p.inv_off = off; off += align256((size_t)round_up(n, int64_t(8)) * sizeof(int32_t));   // padded to 8
   p.flag_off = off; off += 256;
   // bf16 planes of the superblock errors and of U's rows for the trailing
   // updates, double-buffered like the errors
@@ -346,24 +372,33 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
   if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
   join.release();
 
-  hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, perm, n,
+  hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)ceil_div(round_up(n, int64_t(8)), 256)), dim3(256), 0, stream, perm, n,
                      (int64_t)(gw > 0 ? gw : 0), g_idx, invperm);
   GPTQ_LAUNCH_CHECK();
-  const int64_t bpr = ceil_div(std::max<int64_t>(p.words, 1), 256);
-  const unsigned pgrid = (unsigned)(m * bpr);
-  if (w_dtype == GPTQ_BF16)
-    hipLaunchKernelGGL(pack_kernel<uint16_t>, dim3(pgrid), dim3(256), 0, stream, (const uint8_t*)codes,
-                       p.ldw, (const int32_t*)invperm, (const int32_t*)g_idx, (const float*)scales,
-                       (const int32_t*)zeros, p.groups, static_cast<const uint16_t*>(W), m, n,
-                       cfg.bits, p.words, bpr, qweight, part);
-  else
-    hipLaunchKernelGGL(pack_kernel<float>, dim3(pgrid), dim3(256), 0, stream, (const uint8_t*)codes,
-                       p.ldw, (const int32_t*)invperm, (const int32_t*)g_idx, (const float*)scales,
-                       (const int32_t*)zeros, p.groups, static_cast<const float*>(W), m, n,
-                       cfg.bits, p.words, bpr, qweight, part);
+  // one workgroup per row; its codes and group parameters staged in LDS
+  const unsigned pgrid = (unsigned)m;
+  const size_t pack_lds = (size_t)p.ldw + 8 * (size_t)p.groups;
+  const bool bf = w_dtype == GPTQ_BF16, nib = cfg.bits <= 4;   // 8 codes per word, else 4
+  const int32_t* ip = (const int32_t*)invperm;
+  const float* sc = (const float*)scales;
+  const int32_t* zp = (const int32_t*)zeros;
+  const uint8_t* cd = (const uint8_t*)codes;
+  auto pack = [&](auto kern, const auto* Wt) -> gptq_status {
+    if (pack_lds > 64 * 1024)
+      GPTQ_HIP_CHECK(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pack_lds));
+    hipLaunchKernelGGL(kern, dim3(pgrid), dim3(256), pack_lds, stream, cd, p.ldw, ip, (int64_t)(gw > 0 ? gw : 0), sc, zp, p.groups, Wt, n,
+                       p.words, qweight, part);
+    return GPTQ_OK;
+  };
+  const uint16_t* Wb = static_cast<const uint16_t*>(W);
+  const float* Wf = static_cast<const float*>(W);
+  if (bf && nib) GPTQ_TRY(pack(pack_kernel<uint16_t, 8>, Wb));
+  else if (bf) GPTQ_TRY(pack(pack_kernel<uint16_t, 4>, Wb));
+  else if (nib) GPTQ_TRY(pack(pack_kernel<float, 8>, Wf));
+  else GPTQ_TRY(pack(pack_kernel<float, 4>, Wf));
   GPTQ_LAUNCH_CHECK();
   hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(1024), 0, stream, (const double*)loss_rows, m,
-                     (const double*)part, (int64_t)(m * bpr), loss);
+                     (const double*)part, m, loss);
   GPTQ_LAUNCH_CHECK();
 
   if (status) {
