@@ -36,37 +36,75 @@ __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
-template <typename T>
+// VEC: rows of 16-byte pieces (n a multiple of 16 / sizeof(T), W 16-byte
+// aligned), staged with one 16-byte load per piece.  Loads are unconditional
+// at clamped indices, eight (staging) and sixteen (gather) in flight per
+// thread: a conditional load compiles to a branch and a wait of its own.
+template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void qprep_kernel(const T* __restrict__ W, int64_t n,
                                                     const int32_t* __restrict__ perm,
                                                     float* __restrict__ Wp, int64_t ldw, int* flag) {
-  extern __shared__ float row[];
+  extern __shared__ __attribute__((aligned(16))) float row[];
   __shared__ int bad;
   const int64_t r = blockIdx.x;
-  if (threadIdx.x == 0) bad = 0;
+  const int tid = threadIdx.x;
+  if (tid == 0) bad = 0;
   __syncthreads();
-  // four loads per thread in flight (unconditional, at clamped indices; a
-  // conditional load compiles to a branch and a wait of its own)
   int b = 0;
-  for (int64_t j0 = threadIdx.x; j0 < n; j0 += 4 * 256) {
-    float x[4];
+  if constexpr (VEC) {
+    constexpr int E = 16 / sizeof(T);   // elements per piece
+    const int64_t nq = n / E;
+    const uint4* src = reinterpret_cast<const uint4*>(W + r * n);
+    for (int64_t q0 = tid; q0 < nq; q0 += 8 * 256) {
+      uint4 v[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) x[u] = to_f32<T>(W[r * n + std::min<int64_t>(j0 + 256 * u, n - 1)]);
+      for (int u = 0; u < 8; ++u) v[u] = src[std::min<int64_t>(q0 + 256 * u, nq - 1)];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (!isfinite(x[u])) b = 1;
-      row[std::min<int64_t>(j0 + 256 * u, n - 1)] = x[u];
+      for (int u = 0; u < 8; ++u) {
+        const int64_t q = q0 + 256 * u;
+        if (q < nq) {
+          const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+          float x[E];
+          if constexpr (E == 8) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[2 * e] = __uint_as_float(wd[e] << 16);
+              x[2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(wd[e]);
+          }
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if (!isfinite(x[e])) b = 1;
+#pragma unroll
+          for (int e = 0; e < E; e += 4)
+            *reinterpret_cast<f32x4_t*>(row + q * E + e) = f32x4_t{x[e], x[e + 1], x[e + 2], x[e + 3]};
+        }
+      }
+    }
+  } else {
+    for (int64_t j0 = tid; j0 < n; j0 += 8 * 256) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = to_f32<T>(W[r * n + std::min<int64_t>(j0 + 256 * u, n - 1)]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (!isfinite(x[u])) b = 1;
+        row[std::min<int64_t>(j0 + 256 * u, n - 1)] = x[u];
+      }
     }
   }
   if (b) atomicOr(&bad, 1);
   __syncthreads();
-  if (threadIdx.x == 0 && bad) atomicOr(flag, kFlagNonFinite);
-  for (int64_t p0 = threadIdx.x; p0 < ldw; p0 += 4 * 256) {
-    int32_t pi[4];
+  if (tid == 0 && bad) atomicOr(flag, kFlagNonFinite);
+  for (int64_t p0 = tid; p0 < ldw; p0 += 16 * 256) {
+    int32_t pi[16];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) pi[u] = perm[std::min<int64_t>(p0 + 256 * u, n - 1)];
+    for (int u = 0; u < 16; ++u) pi[u] = perm[std::min<int64_t>(p0 + 256 * u, n - 1)];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 16; ++u) {
       const int64_t p = p0 + 256 * u;
       if (p < ldw) Wp[r * ldw + p] = (p < n) ? row[pi[u]] : 0.f;
     }
@@ -272,18 +310,21 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
   GPTQ_LAUNCH_CHECK();
 
   const size_t row_bytes = (size_t)n * sizeof(float);
+  auto qprep = [&](auto kern, const auto* Wt) -> gptq_status {
+    if (row_bytes > 65536)
+      GPTQ_HIP_CHECK(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)row_bytes));
+    hipLaunchKernelGGL(kern, dim3((unsigned)m), dim3(256), row_bytes, stream, Wt, n, perm, Wp, p.ldw, flag);
+    return GPTQ_OK;
+  };
+  const bool w16 = (reinterpret_cast<uintptr_t>(W) & 15) == 0;
   if (w_dtype == GPTQ_BF16) {
-    if (row_bytes > 65536)
-      GPTQ_HIP_CHECK(hipFuncSetAttribute((const void*)qprep_kernel<uint16_t>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)row_bytes));
-    hipLaunchKernelGGL(qprep_kernel<uint16_t>, dim3((unsigned)m), dim3(256), row_bytes, stream,
-                       static_cast<const uint16_t*>(W), n, perm, Wp, p.ldw, flag);
+    const uint16_t* Wb = static_cast<const uint16_t*>(W);
+    if (w16 && n % 8 == 0) GPTQ_TRY(qprep(qprep_kernel<uint16_t, true>, Wb));
+    else GPTQ_TRY(qprep(qprep_kernel<uint16_t, false>, Wb));
   } else {
-    if (row_bytes > 65536)
-      GPTQ_HIP_CHECK(hipFuncSetAttribute((const void*)qprep_kernel<float>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)row_bytes));
-    hipLaunchKernelGGL(qprep_kernel<float>, dim3((unsigned)m), dim3(256), row_bytes, stream,
-                       static_cast<const float*>(W), n, perm, Wp, p.ldw, flag);
+    const float* Wf = static_cast<const float*>(W);
+    if (w16 && n % 4 == 0) GPTQ_TRY(qprep(qprep_kernel<float, true>, Wf));
+    else GPTQ_TRY(qprep(qprep_kernel<float, false>, Wf));
   }
   GPTQ_LAUNCH_CHECK();
 
