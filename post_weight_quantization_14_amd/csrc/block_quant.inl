@@ -290,9 +290,19 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs q, const float* 
   if (x.act) {
     // columns >= bw carry code 0 and error 0
     *reinterpret_cast<uint2*>(q.codes + r * q.ldw + i1 + 8 * x.j) = make_uint2(x.c8[0], x.c8[1]);
-    float* erow = q.err + r * q.lde + 8 * x.j;
-    *reinterpret_cast<f32x4_t*>(erow) = f32x4_t{x.e8[0], x.e8[1], x.e8[2], x.e8[3]};
-    *reinterpret_cast<f32x4_t*>(erow + 4) = f32x4_t{x.e8[4], x.e8[5], x.e8[6], x.e8[7]};
+    // the errors straight into the superblock's x6 planes: columns 8j..8j+7
+    // are 16 contiguous bytes of k-step j/2 in each plane
+    uint16_t hv[8], mv[8], lv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x6_split(x.e8[e], hv[e], mv[e], lv[e]);
+    uint16_t* ep = q.eplane + (x.j >> 1) * q.esst + 16 * r + 8 * (x.j & 1);
+    auto pack8 = [](const uint16_t (&v)[8]) {
+      return make_uint4(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16), v[4] | ((uint32_t)v[5] << 16),
+                        v[6] | ((uint32_t)v[7] << 16));
+    };
+    *reinterpret_cast<uint4*>(ep) = pack8(hv);
+    *reinterpret_cast<uint4*>(ep + q.epstride) = pack8(mv);
+    *reinterpret_cast<uint4*>(ep + 2 * q.epstride) = pack8(lv);
     if (x.j == 0) q.loss_rows[r] += 0.5 * (double)lacc;
   }
   if (ncols <= 0) return;   // uniform: last block of its superblock

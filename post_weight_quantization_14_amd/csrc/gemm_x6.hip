@@ -49,16 +49,6 @@ __device__ __forceinline__ constexpr int x6_vmcnt(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
-__device__ __forceinline__ void x6_split(float x, uint16_t& h, uint16_t& m, uint16_t& l) {
-  const uint32_t hb = __float_as_uint(x) & 0xffff0000u;
-  const float r1 = x - __uint_as_float(hb);
-  const uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
-  const float r2 = r1 - __uint_as_float(mb);
-  const uint32_t lb = __float_as_uint(r2) & 0xffff0000u;
-  h = (uint16_t)(hb >> 16);
-  m = (uint16_t)(mb >> 16);
-  l = (uint16_t)(lb >> 16);
-}
 
 // planes of X[r][k] (k < K), zero for K <= k < kp.  Element i of the sweep is
 // k-step i / (16 rows), row (i / 16) % rows, position i % 16: the writes are

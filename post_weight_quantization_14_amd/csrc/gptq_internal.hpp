@@ -132,7 +132,7 @@ constexpr int kQBlock = 128;
 
 struct QuantPlan {
   int64_t m = 0, n = 0, ldw = 0, groups = 0, words = 0;
-  size_t wp_off = 0, part_off = 0, codes_off = 0, err_off = 0, loss_off = 0, inv_off = 0,
+  size_t wp_off = 0, part_off = 0, codes_off = 0, loss_off = 0, inv_off = 0,
          flag_off = 0, x6a_off = 0, x6b_off = 0, total = 0;
 };
 QuantPlan plan_quantize(int64_t m, int64_t n, const gptq_config& cfg);
@@ -213,6 +213,18 @@ struct X6Planes {
   int64_t rows, kp, pstride, sst;
 };
 constexpr int64_t kX6K = 512;   // k extent of the trailing updates that use it
+// x = h + m + l exactly, each a bf16 (bit pattern): h = x truncated to bf16,
+// m = (x - h) truncated, l = the rest (24 significand bits in three pieces)
+__device__ __forceinline__ void x6_split(float x, uint16_t& h, uint16_t& m, uint16_t& l) {
+  const uint32_t hb = __float_as_uint(x) & 0xffff0000u;
+  const float r1 = x - __uint_as_float(hb);
+  const uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
+  const float r2 = r1 - __uint_as_float(mb);
+  const uint32_t lb = __float_as_uint(r2) & 0xffff0000u;
+  h = (uint16_t)(hb >> 16);
+  m = (uint16_t)(mb >> 16);
+  l = (uint16_t)(lb >> 16);
+}
 constexpr int64_t kX6Step = 16;  // k positions per contiguous row piece
 // planes of X[r][k] (r < rows, k < K; zero for K <= k < kp) at out, rows 0..rows-1
 gptq_status launch_x6_split_rows(const float* X, int64_t ldx, int64_t rows, int64_t K, int64_t kp,

@@ -21,8 +21,11 @@ struct QArgs {
   float* scales;      // [m][G]
   int32_t* zeros;     // [m][G]
   int64_t G;
-  float* err;         // [m][lde]: errors of the current block start here
-  int64_t lde;
+  // the superblock's errors as x6 planes (k-step-major, see X6Planes): this
+  // block's first k-step of plane 0 at eplane, planes epstride apart, k-steps
+  // esst apart
+  uint16_t* eplane;
+  int64_t epstride, esst;
   uint8_t* codes;     // [m][ldw], processing order
   double* loss_rows;  // [m]
 };

@@ -280,7 +280,6 @@ QuantPlan plan_quantize(int64_t m, int64_t n, const gptq_config& cfg) {
   p.part_off = off;  // pack partials: one double per row
   off += align256((size_t)m * sizeof(double));
   p.codes_off = off; off += align256((size_t)m * p.ldw);
-  p.err_off = off; off += align256((size_t)2 * m * kQSuper * sizeof(float));   // two superblocks
   p.loss_off = off; off += align256((size_t)m * sizeof(double));
   p.inv_off = off; off += align256((size_t)round_up(n, int64_t(8)) * sizeof(int32_t));   // padded to 8
   p.flag_off = off; off += 256;
@@ -300,7 +299,6 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
   float* Wp = reinterpret_cast<float*>(w + p.wp_off);
   double* part = reinterpret_cast<double*>(w + p.part_off);
   uint8_t* codes = reinterpret_cast<uint8_t*>(w + p.codes_off);
-  float* err = reinterpret_cast<float*>(w + p.err_off);
   double* loss_rows = reinterpret_cast<double*>(w + p.loss_off);
   int32_t* invperm = reinterpret_cast<int32_t*>(w + p.inv_off);
   int* flag = reinterpret_cast<int*>(w + p.flag_off);
@@ -338,7 +336,7 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
   QArgs a;
   a.Wp = Wp; a.ldw = p.ldw; a.m = m; a.n = n; a.U = U; a.ldu = n;
   a.bits = cfg.bits; a.sym = cfg.sym; a.scales = scales; a.zeros = zeros; a.G = p.groups;
-  a.err = err; a.lde = kQSuper; a.codes = codes; a.loss_rows = loss_rows;
+  a.eplane = nullptr; a.epstride = m * kX6K; a.esst = m * kX6Step; a.codes = codes; a.loss_rows = loss_rows;
 
   // Two-level lazy update (exact: the same rank-1 corrections, grouped).  A
   // block's errors update the rest of its 512-column superblock at once
@@ -358,13 +356,17 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
   bool side_pending = false;
   for (int64_t s1 = 0; s1 < n; s1 += kQSuper) {
     const int64_t s2 = std::min<int64_t>(s1 + kQSuper, n);
-    float* errs = err + ((s1 / kQSuper) & 1) * m * kQSuper;
+    // the superblock's errors go straight into its x6 planes (double-buffered
+    // by parity: the far update of superblock s reads them while the blocks
+    // of s + 1 write the other buffer, and s + 2 starts after that update)
+    const int par = (int)((s1 / kQSuper) & 1);
+    uint16_t* pa = reinterpret_cast<uint16_t*>(w + p.x6a_off) + (size_t)par * 3 * m * kX6K;
     for (int64_t i1 = s1; i1 < s2; i1 += QB) {
       const int bw = (int)std::min<int64_t>(QB, s2 - i1);
       // the quantizer reads only rows and columns < bw of U's diagonal block
       const float* ublk = U + i1 * n + i1;
       const int64_t ldub = n;
-      a.err = errs + (i1 - s1);
+      a.eplane = pa + ((i1 - s1) / kX6Step) * a.esst;
       // W_p[rows, i1+bw : s2] -= Err_block · U[i1:i1+bw, i1+bw:s2], in the kernel
       const int ncols = (int)(s2 - i1 - bw);
       switch (gw) {
@@ -384,11 +386,8 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
       const int64_t near = std::min<int64_t>(kQSuper, n - s2), far = n - s2 - near;
       // both operands as exact bf16 planes (fp32-accurate on bf16 MFMA): the
       // errors [m][512] as rows, U[s1:s2, s2:] transposed to [n - s2][512]
-      const int par = (int)((s1 / kQSuper) & 1);
-      uint16_t* pa = reinterpret_cast<uint16_t*>(w + p.x6a_off) + (size_t)par * 3 * m * kX6K;
       uint16_t* pb = reinterpret_cast<uint16_t*>(w + p.x6b_off) + (size_t)par * 3 * n * kX6K;
       const int64_t K = s2 - s1;
-      GPTQ_TRY(launch_x6_split_rows(errs, kQSuper, m, K, kX6K, pa, m * kX6K, m * kX6Step, stream));
       GPTQ_TRY(launch_x6_split_cols(U + s1 * n + s2, n, K, n - s2, kX6K, pb, n * kX6K, n * kX6Step, stream));
       const X6Planes PA{pa, m, kX6K, m * kX6K, m * kX6Step};
       if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
