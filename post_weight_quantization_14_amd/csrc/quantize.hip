@@ -268,6 +268,15 @@ static_assert(kQSuper <= kX6K, "a superblock's errors must fit the plane width")
 // between the block quantizer's chain and the far GEMM as the bottleneck)
 constexpr int64_t kQPoliteFar = 6500;
 
+// Plane rows of U's trailing-update operands for the superblocks before s1
+// (all of them for s1 = n): superblock [t, t + 512) contributes n - t - 512
+// rows when t + 512 < n.
+int64_t uplane_rows(int64_t n, int64_t s1) {
+  int64_t rows = 0;
+  for (int64_t t = 0; t < s1 && t + kQSuper < n; t += kQSuper) rows += n - t - kQSuper;
+  return rows;
+}
+
 QuantPlan plan_quantize(int64_t m, int64_t n, const gptq_config& cfg) {
   QuantPlan p;
   p.m = m;
@@ -283,10 +292,11 @@ QuantPlan plan_quantize(int64_t m, int64_t n, const gptq_config& cfg) {
   p.loss_off = off; off += align256((size_t)m * sizeof(double));
   p.inv_off = off; off += align256((size_t)round_up(n, int64_t(8)) * sizeof(int32_t));   // padded to 8
   p.flag_off = off; off += 256;
-  // bf16 planes of the superblock errors and of U's rows for the trailing
-  // updates, double-buffered like the errors
+  // bf16 planes of the superblock errors (double-buffered by superblock
+  // parity) and of U[s1:s2, s2:] for every superblock with a trailing update,
+  // back to back (superblock s: n - s2 plane rows)
   p.x6a_off = off; off += align256((size_t)2 * 3 * m * kX6K * sizeof(uint16_t));
-  p.x6b_off = off; off += align256((size_t)2 * 3 * n * kX6K * sizeof(uint16_t));
+  p.x6b_off = off; off += align256((size_t)3 * kX6K * sizeof(uint16_t) * (size_t)uplane_rows(n, n));
   p.total = off;
   return p;
 }
@@ -351,9 +361,38 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
   // one superblock's errors never meet the next superblock's writes.
   SideStream side;
   GPTQ_TRY(get_side_stream(side));
+  SideStream usplit;
+  GPTQ_TRY(get_side_stream(usplit, 2));
   SideJoin join(stream);
   join.add(side);
+  join.add(usplit);
   bool side_pending = false;
+  // U is fixed for the whole call: the planes of U[s1:s2, s2:] for every
+  // superblock after the first are split up front on side stream 2, beside
+  // the first superblock's blocks; the first superblock's own split stays on
+  // this stream, and the second's update waits for the rest once
+  uint16_t* const ub = reinterpret_cast<uint16_t*>(w + p.x6b_off);
+  auto uplanes = [&](int64_t s1) {
+    const int64_t s2 = s1 + kQSuper, rows = n - s2;
+    return X6Planes{ub + 3 * kX6K * uplane_rows(n, s1), rows, kX6K, rows * kX6K, rows * kX6Step};
+  };
+  auto split_u = [&](int64_t s1, hipStream_t st) -> gptq_status {
+    const X6Planes P = uplanes(s1);
+    const int64_t s2 = s1 + kQSuper;
+    return launch_x6_split_cols(U + s1 * n + s2, n, kQSuper, n - s2, kX6K, const_cast<uint16_t*>(P.p), P.pstride,
+                                P.sst, st);
+  };
+  bool usplit_pending = false;
+  if (kQSuper < n) {
+    GPTQ_TRY(split_u(0, stream));
+    if (2 * kQSuper < n) {
+      GPTQ_HIP_CHECK(hipEventRecord(usplit.ready, stream));
+      GPTQ_HIP_CHECK(hipStreamWaitEvent(usplit.stream, usplit.ready, 0));
+      for (int64_t s1 = kQSuper; s1 + kQSuper < n; s1 += kQSuper) GPTQ_TRY(split_u(s1, usplit.stream));
+      GPTQ_HIP_CHECK(hipEventRecord(usplit.done, usplit.stream));
+      usplit_pending = true;
+    }
+  }
   for (int64_t s1 = 0; s1 < n; s1 += kQSuper) {
     const int64_t s2 = std::min<int64_t>(s1 + kQSuper, n);
     // the superblock's errors go straight into its x6 planes (double-buffered
@@ -386,16 +425,18 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
       const int64_t near = std::min<int64_t>(kQSuper, n - s2), far = n - s2 - near;
       // both operands as exact bf16 planes (fp32-accurate on bf16 MFMA): the
       // errors [m][512] as rows, U[s1:s2, s2:] transposed to [n - s2][512]
-      uint16_t* pb = reinterpret_cast<uint16_t*>(w + p.x6b_off) + (size_t)par * 3 * n * kX6K;
-      const int64_t K = s2 - s1;
-      GPTQ_TRY(launch_x6_split_cols(U + s1 * n + s2, n, K, n - s2, kX6K, pb, n * kX6K, n * kX6Step, stream));
+      const X6Planes PU = uplanes(s1);
+      if (usplit_pending && s1 > 0) {   // superblock 0's planes were split on this stream
+        GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, usplit.done, 0));
+        usplit_pending = false;
+      }
       const X6Planes PA{pa, m, kX6K, m * kX6K, m * kX6Step};
       if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
       side_pending = false;
       if (far > 0) {
         GPTQ_HIP_CHECK(hipEventRecord(side.ready, stream));
         GPTQ_HIP_CHECK(hipStreamWaitEvent(side.stream, side.ready, 0));
-        const X6Planes PF{pb + near * kX6Step, far, kX6K, n * kX6K, n * kX6Step};
+        const X6Planes PF{PU.p + near * kX6Step, far, kX6K, PU.pstride, PU.sst};
         // a small far update leaves CU room for the next superblock's blocks;
         // a large one is the stage's bottleneck and takes the whole chip
         const bool polite = far < kQPoliteFar;
@@ -403,13 +444,14 @@ gptq_status run_quantize(const void* W, int w_dtype, int64_t m, int64_t n, const
         GPTQ_HIP_CHECK(hipEventRecord(side.done, side.stream));
         side_pending = true;
       }
-      const X6Planes PN{pb, near, kX6K, n * kX6K, n * kX6Step};
+      const X6Planes PN{PU.p, near, kX6K, PU.pstride, PU.sst};
       // on the chain: with fewer 128-row tiles than CUs, 64-row tiles
       const int near_rows = ceil_div(m, 128) * ceil_div(near, 128) < 256 ? 64 : 128;
       GPTQ_TRY(launch_x6_gemm(PA, PN, Wp + s2, p.ldw, m, near, -1.f, 1.f, false, stream, false, near_rows));
     }
   }
   if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
+  if (usplit_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, usplit.done, 0));
   join.release();
 
   hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)ceil_div(round_up(n, int64_t(8)), 256)), dim3(256), 0, stream, perm, n,
