@@ -207,6 +207,32 @@ __global__ __launch_bounds__(256) void gemm_rect_kernel(GemmArgs g) {
   const int64_t cols = g.N - j0 < GT ? g.N - j0 : GT;
   gemm_tile_acc<BCOL, VEC, TM>(A, g.lda, rows, B, g.ldb, cols, g.k_begin, g.k_end, sm, acc);
   gemm_tile_store<false, TM>(g.C + i0 * g.ldc + j0, g.ldc, rows, cols, 0, g.alpha, g.beta, acc);
+  if (g.pl != nullptr && i0 + TM > g.pl_row0) {   // uniform: the tile reaches the plane rows
+    constexpr int BI = TM / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 1, wc = wave & 1, li = lane & 31, lk = lane >> 5;
+#pragma unroll
+    for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj) {
+        const int j = wc * 64 + bj * 32 + li;
+        const int ib = wr * (TM / 2) + bi * 32 + 4 * lk;
+        const int64_t kc = g.pl_col0 + j0 + j;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int i = ib + 8 * (v >> 2) + (v & 3);
+          const int64_t pr = i0 + i - g.pl_row0;
+          if (i < rows && j < cols && pr >= 0) {
+            uint16_t h, m, l;
+            x6_split(g.alpha * acc[bi][bj][v], h, m, l);
+            uint16_t* o = g.pl + (kc / kX6Step) * g.pl_sst + pr * kX6Step + kc % kX6Step;
+            o[0] = h;
+            o[g.pl_pstride] = m;
+            o[2 * g.pl_pstride] = l;
+          }
+        }
+      }
+  }
 }
 
 __device__ __forceinline__ void tri_decode(int64_t t, int64_t& ti, int64_t& tj) {
@@ -313,6 +339,10 @@ bool vec_ok(const GemmArgs& g, bool bcol) {
 
 gptq_status launch_gemm_rect(const GemmArgs& g, bool b_colmajor, hipStream_t stream, int tile_rows) {
   if (g.M <= 0 || g.N <= 0) return GPTQ_OK;
+  if (g.pl != nullptr && g.beta != 0.f) {
+    set_error("launch_gemm_rect: plane output needs beta = 0");
+    return GPTQ_ERR_INVALID_ARG;
+  }
   if (tile_rows != GT && (tile_rows != 64 || !b_colmajor)) {
     set_error("launch_gemm_rect: tile_rows %d (128, or 64 with a column-major B)", tile_rows);
     return GPTQ_ERR_INVALID_ARG;

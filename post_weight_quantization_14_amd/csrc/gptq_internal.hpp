@@ -249,6 +249,11 @@ struct GemmArgs {
   int64_t M, N;
   int64_t k_begin, k_end;
   float alpha, beta;
+  // optional (launch_gemm_rect, beta = 0): rows >= pl_row0 of the result also
+  // go to x6 planes, result (i, j) as plane row i - pl_row0, position
+  // pl_col0 + j (layout of X6Planes: planes pl_pstride apart, k-steps pl_sst)
+  uint16_t* pl = nullptr;
+  int64_t pl_pstride = 0, pl_sst = 0, pl_row0 = 0, pl_col0 = 0;
 };
 // tile_rows: 128, or 64 (column-major B only) for products of few row tiles.
 gptq_status launch_gemm_rect(const GemmArgs& g, bool b_colmajor, hipStream_t stream, int tile_rows = 128);

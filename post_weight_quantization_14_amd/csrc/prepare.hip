@@ -569,6 +569,13 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
   // one event for the two.  Concurrent kernels always touch disjoint parts of A.
   for (int64_t K0 = 0; K0 < p.n_pad; K0 += OB) {
     const int64_t K1 = std::min<int64_t>(K0 + OB, p.n_pad);
+    // the panel rows L[K1:, K0:K1] as exact bf16 planes for the outer update,
+    // written by the panel solves (double-buffered by block parity: the far
+    // update of the previous block reads the other buffer, and the one of the
+    // block before that was awaited before that previous far update began)
+    const int par = (int)((K0 / OB) & 1);
+    uint16_t* const pl = reinterpret_cast<uint16_t*>(w + p.x6_off) + (size_t)par * 3 * p.n_pad * kX6K;
+    const int64_t pst = p.n_pad * kX6K, sst = p.n_pad * kX6Step;
     for (int64_t k0 = K0; k0 < K1; k0 += NB) {
       // inside an outer block, the leaf applies the previous panel's update to
       // its own diagonal block (the rows below get it on the inner stream)
@@ -589,6 +596,10 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
       g.B = Mm + k0 * lda + k0; g.ldb = lda;
       g.C = A + (k0 + NB) * lda + k0; g.ldc = lda;
       g.M = rows; g.N = NB; g.k_begin = 0; g.k_end = NB; g.alpha = 1.f; g.beta = 0.f;
+      if (K1 < p.n_pad) {   // rows K1.. of this panel also go to the outer update's planes
+        g.pl = pl; g.pl_pstride = pst; g.pl_sst = sst;
+        g.pl_row0 = K1 - (k0 + NB); g.pl_col0 = k0 - K0;
+      }
       // on the chain: with fewer than 128 row tiles of 128, tiles of 64 rows
       GPTQ_TRY(launch_gemm_rect(g, /*b_colmajor=*/true, stream, ceil_div(rows, NB) < 128 ? 64 : NB));
       GPTQ_HIP_CHECK(hipEventRecord(inr.ready, stream));
@@ -630,11 +641,8 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
     const int64_t rest = p.n_pad - K1;
     if (rest > 0) {
       const int64_t near = std::min<int64_t>(OB, rest), far = rest - near;
-      // the panel rows L[K1:, K0:K1] as exact bf16 planes: A and B operand alike
-      const int par = (int)((K0 / OB) & 1);
-      uint16_t* pl = reinterpret_cast<uint16_t*>(w + p.x6_off) + (size_t)par * 3 * p.n_pad * kX6K;
-      const int64_t pst = p.n_pad * kX6K, sst = p.n_pad * kX6Step;
-      GPTQ_TRY(launch_x6_split_rows(A + K1 * lda + K0, lda, rest, K1 - K0, kX6K, pl, pst, sst, stream));
+      // the panel rows L[K1:, K0:K1] (A and B operand alike) are in the
+      // planes: the block's panel solves wrote them
       if (side_pending) GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, side.done, 0));
       side_pending = false;
       if (far > 0) {
