@@ -208,7 +208,13 @@ __global__ __launch_bounds__(256) void gemm_rect_kernel(GemmArgs g) {
   gemm_tile_acc<BCOL, VEC, TM>(A, g.lda, rows, B, g.ldb, cols, g.k_begin, g.k_end, sm, acc);
   gemm_tile_store<false, TM>(g.C + i0 * g.ldc + j0, g.ldc, rows, cols, 0, g.alpha, g.beta, acc);
   if (g.pl != nullptr && i0 + TM > g.pl_row0) {   // uniform: the tile reaches the plane rows
+    // the tile through LDS (free after the main loop's last barrier), then
+    // eight consecutive columns of one row per thread: 16 contiguous bytes of
+    // one k-step in each plane
     constexpr int BI = TM / 64;
+    constexpr int TP = GT + 4;   // row pitch of the staged tile (floats)
+    static_assert(TM * TP * sizeof(float) <= sizeof(GemmSmem), "the staged tile fits the GEMM's LDS");
+    float* st = reinterpret_cast<float*>(&sm);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1, li = lane & 31, lk = lane >> 5;
 #pragma unroll
@@ -217,21 +223,35 @@ __global__ __launch_bounds__(256) void gemm_rect_kernel(GemmArgs g) {
       for (int bj = 0; bj < 2; ++bj) {
         const int j = wc * 64 + bj * 32 + li;
         const int ib = wr * (TM / 2) + bi * 32 + 4 * lk;
-        const int64_t kc = g.pl_col0 + j0 + j;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int i = ib + 8 * (v >> 2) + (v & 3);
-          const int64_t pr = i0 + i - g.pl_row0;
-          if (i < rows && j < cols && pr >= 0) {
-            uint16_t h, m, l;
-            x6_split(g.alpha * acc[bi][bj][v], h, m, l);
-            uint16_t* o = g.pl + (kc / kX6Step) * g.pl_sst + pr * kX6Step + kc % kX6Step;
-            o[0] = h;
-            o[g.pl_pstride] = m;
-            o[2 * g.pl_pstride] = l;
-          }
-        }
+        for (int v = 0; v < 16; ++v) st[(ib + 8 * (v >> 2) + (v & 3)) * TP + j] = g.alpha * acc[bi][bj][v];
       }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < TM * GT / 8 / 256; ++u) {
+      const int e = tid + 256 * u;
+      const int i = e / (GT / 8), j = 8 * (e % (GT / 8));
+      const int64_t pr = i0 + i - g.pl_row0;
+      if (i < rows && j < cols && pr >= 0) {
+        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(st + i * TP + j);
+        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(st + i * TP + j + 4);
+        uint32_t hw[4], mw[4], lw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint16_t h0, m0, l0, h1, m1, l1;
+          x6_split(q < 2 ? x0[2 * q] : x1[2 * q - 4], h0, m0, l0);
+          x6_split(q < 2 ? x0[2 * q + 1] : x1[2 * q - 3], h1, m1, l1);
+          hw[q] = h0 | ((uint32_t)h1 << 16);
+          mw[q] = m0 | ((uint32_t)m1 << 16);
+          lw[q] = l0 | ((uint32_t)l1 << 16);
+        }
+        const int64_t kc = g.pl_col0 + j0 + j;   // a multiple of 8
+        uint16_t* o = g.pl + (kc / kX6Step) * g.pl_sst + pr * kX6Step + kc % kX6Step;
+        *reinterpret_cast<uint4*>(o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4*>(o + g.pl_pstride) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+        *reinterpret_cast<uint4*>(o + 2 * g.pl_pstride) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      }
+    }
   }
 }
 
@@ -339,8 +359,9 @@ bool vec_ok(const GemmArgs& g, bool bcol) {
 
 gptq_status launch_gemm_rect(const GemmArgs& g, bool b_colmajor, hipStream_t stream, int tile_rows) {
   if (g.M <= 0 || g.N <= 0) return GPTQ_OK;
-  if (g.pl != nullptr && g.beta != 0.f) {
-    set_error("launch_gemm_rect: plane output needs beta = 0");
+  if (g.pl != nullptr && (g.beta != 0.f || g.N % 8 != 0 || g.pl_col0 % 8 != 0 ||
+                          (reinterpret_cast<uintptr_t>(g.pl) & 15) != 0 || g.pl_sst % 8 != 0 || g.pl_pstride % 8 != 0)) {
+    set_error("launch_gemm_rect: plane output needs beta = 0 and 16-byte pieces of 8 columns");
     return GPTQ_ERR_INVALID_ARG;
   }
   if (tile_rows != GT && (tile_rows != 64 || !b_colmajor)) {
