@@ -109,11 +109,12 @@ __global__ __launch_bounds__(256) void rank_perm_kernel(const int32_t* __restric
 }
 
 // One output row a of A = J P (H + λI) Pᵀ J, padded with the identity.
+template <bool VEC>
 __global__ __launch_bounds__(256) void permute_kernel(const float* __restrict__ H, int64_t n,
                                                       const int32_t* __restrict__ perm,
                                                       const double* lam, float* __restrict__ A,
                                                       int64_t lda) {
-  extern __shared__ float row[];
+  extern __shared__ __attribute__((aligned(16))) float row[];
   const int64_t a = blockIdx.x;
   float* out = A + a * lda;
   if (a >= n) {
@@ -122,23 +123,37 @@ __global__ __launch_bounds__(256) void permute_kernel(const float* __restrict__ 
   }
   const int64_t src = perm[n - 1 - a];
   const float* h = H + src * n;
-  // four loads per thread in flight (unconditional, at clamped indices; a
-  // conditional load compiles to a branch and a wait of its own)
-  for (int64_t b0 = threadIdx.x; b0 < n; b0 += 4 * 256) {
-    float v[4];
+  // loads unconditional at clamped indices, eight (row) and sixteen (gather)
+  // in flight per thread: a conditional load compiles to a branch and a wait
+  // of its own.  VEC (n a multiple of 4, H 16-byte aligned): 16-byte pieces.
+  if constexpr (VEC) {
+    const int64_t nq = n / 4;
+    const f32x4_t* hq = reinterpret_cast<const f32x4_t*>(h);
+    for (int64_t q0 = threadIdx.x; q0 < nq; q0 += 8 * 256) {
+      f32x4_t v[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = h[std::min<int64_t>(b0 + 256 * u, n - 1)];
+      for (int u = 0; u < 8; ++u) v[u] = hq[std::min<int64_t>(q0 + 256 * u, nq - 1)];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) row[std::min<int64_t>(b0 + 256 * u, n - 1)] = v[u];
+      for (int u = 0; u < 8; ++u)
+        reinterpret_cast<f32x4_t*>(row)[std::min<int64_t>(q0 + 256 * u, nq - 1)] = v[u];
+    }
+  } else {
+    for (int64_t b0 = threadIdx.x; b0 < n; b0 += 8 * 256) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = h[std::min<int64_t>(b0 + 256 * u, n - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) row[std::min<int64_t>(b0 + 256 * u, n - 1)] = v[u];
+    }
   }
   __syncthreads();
   const float l = (float)*lam;
-  for (int64_t b0 = threadIdx.x; b0 < lda; b0 += 4 * 256) {
-    int32_t pi[4];
+  for (int64_t b0 = threadIdx.x; b0 < lda; b0 += 16 * 256) {
+    int32_t pi[16];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) pi[u] = perm[n - 1 - std::min<int64_t>(b0 + 256 * u, n - 1)];
+    for (int u = 0; u < 16; ++u) pi[u] = perm[n - 1 - std::min<int64_t>(b0 + 256 * u, n - 1)];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 16; ++u) {
       const int64_t b = b0 + 256 * u;
       if (b >= lda) break;
       float v = 0.f;
@@ -504,11 +519,16 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
                      (const int32_t*)reinterpret_cast<int32_t*>(Mm), chunks, n, desc_act, perm);
   GPTQ_LAUNCH_CHECK();
   const size_t row_bytes = (size_t)n * sizeof(float);
+  const bool vec = n % 4 == 0 && (reinterpret_cast<uintptr_t>(H) & 15) == 0;
+  const void* pk = vec ? (const void*)permute_kernel<true> : (const void*)permute_kernel<false>;
   if (row_bytes > 65536)
-    GPTQ_HIP_CHECK(hipFuncSetAttribute((const void*)permute_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)row_bytes));
-  hipLaunchKernelGGL(permute_kernel, dim3((unsigned)p.n_pad), dim3(256), row_bytes, stream,
-                     (const float*)H, n, (const int32_t*)perm, (const double*)lam, A, lda);
+    GPTQ_HIP_CHECK(hipFuncSetAttribute(pk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)row_bytes));
+  if (vec)
+    hipLaunchKernelGGL(permute_kernel<true>, dim3((unsigned)p.n_pad), dim3(256), row_bytes, stream,
+                       (const float*)H, n, (const int32_t*)perm, (const double*)lam, A, lda);
+  else
+    hipLaunchKernelGGL(permute_kernel<false>, dim3((unsigned)p.n_pad), dim3(256), row_bytes, stream,
+                       (const float*)H, n, (const int32_t*)perm, (const double*)lam, A, lda);
   GPTQ_LAUNCH_CHECK();
 
   // Blocked right-looking Cholesky of A (lower), leaf inverses into Mm, with
