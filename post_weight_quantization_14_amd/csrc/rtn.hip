@@ -836,11 +836,14 @@ namespace {
 // registers of one workgroup hold, or more LDS than a workgroup has.
 constexpr size_t kStreamMaxLds = 160 * 1024;
 
-// Workgroup shapes (threads, chunks per thread) by the row's chunk count.
+// Workgroup shapes (threads, chunks per thread) by the row's chunk count: the
+// fewest chunks per thread that hold the row, since registers a row does not
+// need only lower the number of rows in flight per CU.
 struct StreamShape { int nt, kr; };
 StreamShape stream_shape(int64_t nc, int w_dtype) {
   if (nc <= 256 * 2) return {256, 2};
   if (nc <= 256 * 4) return {256, 4};
+  if (nc <= 256 * 6) return {256, 6};
   if (nc <= 256 * 8) return {256, 8};
   if (w_dtype == GPTQ_BF16) {
     if (nc <= 256 * 16) return {256, 16};
@@ -886,6 +889,7 @@ gptq_status launch_stream(int lgl, int w_dtype, const RtnArgs& a, const RtnPlan&
   const size_t lds = stream_lds_bytes(a.n / 8, p);
   if (sh.nt == 256 && sh.kr == 2) return launch_stream_shape<T, 256, 2>(lgl, a, lds, stream);
   if (sh.nt == 256 && sh.kr == 4) return launch_stream_shape<T, 256, 4>(lgl, a, lds, stream);
+  if (sh.nt == 256 && sh.kr == 6) return launch_stream_shape<T, 256, 6>(lgl, a, lds, stream);
   if (sh.nt == 256 && sh.kr == 8) return launch_stream_shape<T, 256, 8>(lgl, a, lds, stream);
   if constexpr (sizeof(T) == 2) {   // bf16: up to 16 chunks (64 registers) per thread
     if (sh.nt == 256) return launch_stream_shape<T, 256, 16>(lgl, a, lds, stream);

@@ -89,6 +89,7 @@ STREAM_CASES = [
     (16, 1000, torch.bfloat16, 3, 32, False),     # ragged last group (8 columns)
     (16, 4096, torch.float32, 8, 64, True),
     (16, 11008, torch.bfloat16, 4, 128, False),
+    (16, 9000, torch.float32, 4, 64, True),       # 6 chunks per thread, ragged last group
     (16, 2048, torch.bfloat16, 4, 256, True),
     (16, 4000, torch.float32, 3, 512, False),     # ragged last group (416 columns)
     (4, 32768, torch.bfloat16, 8, -1, False),     # the longest row it takes
