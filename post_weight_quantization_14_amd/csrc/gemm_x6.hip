@@ -50,18 +50,19 @@ __device__ __forceinline__ constexpr int x6_vmcnt(int n) {
 }
 
 
-// planes of X[r][k] (k < K), zero for K <= k < kp.  Element i of the sweep is
-// k-step i / (16 rows), row (i / 16) % rows, position i % 16: the writes are
-// contiguous, the reads 64-byte row pieces.
+// planes of X[r][k] (k < K), zero for K <= k < kp, and with `lower` zero for
+// k > r as well (X's strictly upper part is not read).  Element i of the sweep
+// is k-step i / (16 rows), row (i / 16) % rows, position i % 16: the writes
+// are contiguous, the reads 64-byte row pieces.
 __global__ __launch_bounds__(256) void x6_split_rows_kernel(const float* __restrict__ X, int64_t ldx,
                                                             int64_t rows, int64_t K, int64_t kp,
                                                             uint16_t* __restrict__ out, int64_t pstride,
-                                                            int64_t sst) {
+                                                            int64_t sst, int lower) {
   const int64_t total = rows * kp;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
     const int64_t ks = i / (rows * kX6Step), r = (i / kX6Step) % rows, kk = i % kX6Step;
     const int64_t k = ks * kX6Step + kk;
-    const float x = k < K ? X[r * ldx + k] : 0.f;
+    const float x = (k < K && (!lower || k <= r)) ? X[r * ldx + k] : 0.f;
     uint16_t h, m, l;
     x6_split(x, h, m, l);
     const int64_t o = ks * sst + r * kX6Step + kk;
@@ -71,13 +72,14 @@ __global__ __launch_bounds__(256) void x6_split_rows_kernel(const float* __restr
   }
 }
 
-// planes of row c = X[k][c] over k (k < K, c < cols), zero for K <= k < kp:
-// 64 x 64 tiles through LDS, read along c; written as 4 k-steps of 64 rows,
-// 256 contiguous elements per pass of the workgroup
+// planes of row c = X[k][c] over k (k < K, c < cols), zero for K <= k < kp,
+// and with `lower` zero for k < c as well (X's strictly upper part is not
+// used): 64 x 64 tiles through LDS, read along c; written as 4 k-steps of 64
+// rows, 256 contiguous elements per pass of the workgroup
 __global__ __launch_bounds__(256) void x6_split_cols_kernel(const float* __restrict__ X, int64_t ldx,
                                                             int64_t K, int64_t cols, int64_t kp,
                                                             uint16_t* __restrict__ out, int64_t pstride,
-                                                            int64_t sst) {
+                                                            int64_t sst, int lower) {
   __shared__ float t[64][65];
   const int64_t c0 = (int64_t)blockIdx.x * 64, k0 = (int64_t)blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(256) void x6_split_cols_kernel(const float* __restr
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     const int r = ty + 4 * u;
-    t[r][tx] = (k0 + r < K && c0 + tx < cols) ? v[u] : 0.f;
+    t[r][tx] = (k0 + r < K && c0 + tx < cols && (!lower || k0 + r >= c0 + tx)) ? v[u] : 0.f;
   }
   __syncthreads();
 #pragma unroll 1
@@ -159,10 +161,12 @@ __host__ __device__ inline void x6_tile(int64_t b, int64_t T, int64_t M, int64_t
 
 // TM: rows of C per tile, 128 or (full product only) 64 for products of few
 // tiles; the waves then hold one 32-row block each instead of two.
+// krange: the k-steps a tile multiplies, for an A that is triangular
+// (X6KRange): all, from the tile's first row on, or up to its last row.
 template <bool LOWER, int GM, int TM>
 __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B, float* __restrict__ C,
                                                         int64_t ldc, int64_t M, int64_t N, float alpha,
-                                                        float beta) {
+                                                        float beta, int krange) {
   __shared__ __attribute__((aligned(16))) uint8_t s0[X6SLOTB], s1[X6SLOTB], s2[X6SLOTB];
   // the wave index in a scalar register: every buffer descriptor and LDS
   // destination below derives from it, and only wave-uniform ones give one
@@ -177,6 +181,9 @@ __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B,
   const int64_t i0 = ti * TM, j0 = tj * X6T;
   const int64_t kp = A.kp;
   const int64_t nst = kp / X6KS;
+  // stages [st0, st1) of the tile; the ring below runs from st0
+  const int64_t st0 = krange == kX6FromRow ? (i0 / X6KS < nst ? i0 / X6KS : nst) : 0;
+  const int64_t st1 = krange == kX6ToRow ? ((i0 + TM) / X6KS < nst ? (i0 + TM) / X6KS : nst) : nst;
   // 24 copy instructions per stage = (operand, plane, row quarter); wave w
   // issues 6 of them.  Lane i of one covers row 32q + i/2, 16 bytes, into LDS
   // chunk i%2 holding source chunk (i%2) ^ ((row >> 3) & 1) (bank spread); the
@@ -205,7 +212,7 @@ __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B,
   auto issue = [&](int64_t st, uint8_t* slot) {
 #pragma unroll
     for (int u = 0; u < 6; ++u) {
-      const bool live = st < nst;
+      const bool live = st < st1;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t*>(obase[u]) + (live ? st * ostep[u] : 0), 0, live ? obytes[u] : 0, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(slot + ldso[u]), 16, voff[u], 0, 0, 0);
@@ -246,17 +253,18 @@ __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B,
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][0], fb[j][0], acc[i][j], 0, 0, 0);
       }
   };
-  // stage st is in slot st % 3; before computing it, every wave's copies of
-  // it are done (its own by vmcnt, the others' by the barrier) and every wave
-  // has finished stage st - 1, whose slot the refill of stage st + 2 reuses
+  // stage st is in slot (st - st0) % 3; before computing it, every wave's
+  // copies of it are done (its own by vmcnt, the others' by the barrier) and
+  // every wave has finished stage st - 1, whose slot the refill of stage
+  // st + 2 reuses
   auto step = [&](int64_t st, const uint8_t* cur, uint8_t* refill) {
     __builtin_amdgcn_s_waitcnt(x6_vmcnt(6 * (X6RING - 2)));
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     compute(cur, st, refill);
   };
-  issue(0, s0);
-  issue(1, s1);
-  for (int64_t st = 0; st < nst; st += 3) {
+  issue(st0, s0);
+  issue(st0 + 1, s1);
+  for (int64_t st = st0; st < st1; st += 3) {
     step(st, s0, s2);
     step(st + 1, s1, s0);
     step(st + 2, s2, s1);
@@ -313,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void x6_gemm_kernel(X6Planes A, X6Planes B,
 }  // namespace
 
 gptq_status launch_x6_split_rows(const float* X, int64_t ldx, int64_t rows, int64_t K, int64_t kp,
-                                 uint16_t* out, int64_t pstride, int64_t sst, hipStream_t stream) {
+                                 uint16_t* out, int64_t pstride, int64_t sst, hipStream_t stream, bool lower) {
   if (rows <= 0) return GPTQ_OK;
   if (kp % kX6Step != 0 || sst < rows * kX6Step) {
     set_error("launch_x6_split_rows: kp %lld, step stride %lld for %lld rows", (long long)kp, (long long)sst,
@@ -322,13 +330,13 @@ gptq_status launch_x6_split_rows(const float* X, int64_t ldx, int64_t rows, int6
   }
   const int64_t total = rows * kp;
   hipLaunchKernelGGL(x6_split_rows_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(total, 256), 4096)),
-                     dim3(256), 0, stream, X, ldx, rows, K, kp, out, pstride, sst);
+                     dim3(256), 0, stream, X, ldx, rows, K, kp, out, pstride, sst, (int)lower);
   GPTQ_LAUNCH_CHECK();
   return GPTQ_OK;
 }
 
 gptq_status launch_x6_split_cols(const float* X, int64_t ldx, int64_t K, int64_t cols, int64_t kp,
-                                 uint16_t* out, int64_t pstride, int64_t sst, hipStream_t stream) {
+                                 uint16_t* out, int64_t pstride, int64_t sst, hipStream_t stream, bool lower) {
   if (cols <= 0) return GPTQ_OK;
   if (kp % 64 != 0 || sst < cols * kX6Step) {   // the kernel writes whole 64-position tiles of k
     set_error("launch_x6_split_cols: kp %lld, step stride %lld for %lld columns", (long long)kp, (long long)sst,
@@ -340,14 +348,14 @@ gptq_status launch_x6_split_cols(const float* X, int64_t ldx, int64_t K, int64_t
     return GPTQ_ERR_INVALID_ARG;
   }
   hipLaunchKernelGGL(x6_split_cols_kernel, dim3((unsigned)ceil_div(cols, 64), (unsigned)ceil_div(kp, 64)),
-                     dim3(256), 0, stream, X, ldx, K, cols, kp, out, pstride, sst);
+                     dim3(256), 0, stream, X, ldx, K, cols, kp, out, pstride, sst, (int)lower);
   GPTQ_LAUNCH_CHECK();
   return GPTQ_OK;
 }
 
 gptq_status launch_x6_gemm(const X6Planes& A, const X6Planes& B, float* C, int64_t ldc, int64_t M,
                            int64_t N, float alpha, float beta, bool lower, hipStream_t stream, bool polite,
-                           int tile_rows) {
+                           int tile_rows, int krange) {
   if (M <= 0 || N <= 0) return GPTQ_OK;
   if (A.kp != B.kp || A.kp % X6KS != 0 || A.sst < A.rows * kX6Step || B.sst < B.rows * kX6Step ||
       A.rows * kX6Step * 2 > INT32_MAX || B.rows * kX6Step * 2 > INT32_MAX) {
@@ -358,6 +366,10 @@ gptq_status launch_x6_gemm(const X6Planes& A, const X6Planes& B, float* C, int64
   // polite: dynamic LDS padding to more than half a CU's LDS, so one workgroup
   // per CU and room beside it for a 74 KB workgroup of another kernel
   const size_t pad = polite ? kX6PolitePad : 0;
+  if (krange != kX6All && (lower || tile_rows != X6T || krange < kX6All || krange > kX6ToRow)) {
+    set_error("launch_x6_gemm: k range %d (full products of 128-row tiles)", krange);
+    return GPTQ_ERR_INVALID_ARG;
+  }
   if (tile_rows != X6T && (tile_rows != 64 || lower)) {
     set_error("launch_x6_gemm: tile_rows %d (128, or 64 for a full product)", tile_rows);
     return GPTQ_ERR_INVALID_ARG;
@@ -368,13 +380,13 @@ gptq_status launch_x6_gemm(const X6Planes& A, const X6Planes& B, float* C, int64
       return GPTQ_ERR_INVALID_ARG;
     }
     hipLaunchKernelGGL((x6_gemm_kernel<true, kX6Band, X6T>), dim3((unsigned)(nt * (nt + 1) / 2 + (mt - nt) * nt)),
-                       dim3(256), pad, stream, A, B, C, ldc, M, N, alpha, beta);
+                       dim3(256), pad, stream, A, B, C, ldc, M, N, alpha, beta, krange);
   } else if (tile_rows == 64) {
     hipLaunchKernelGGL((x6_gemm_kernel<false, kX6Band, 64>), dim3((unsigned)(ceil_div(M, 64) * nt)), dim3(256), pad,
-                       stream, A, B, C, ldc, M, N, alpha, beta);
+                       stream, A, B, C, ldc, M, N, alpha, beta, krange);
   } else {
     hipLaunchKernelGGL((x6_gemm_kernel<false, kX6Band, X6T>), dim3((unsigned)(mt * nt)), dim3(256), pad, stream, A,
-                       B, C, ldc, M, N, alpha, beta);
+                       B, C, ldc, M, N, alpha, beta, krange);
   }
   GPTQ_LAUNCH_CHECK();
   return GPTQ_OK;

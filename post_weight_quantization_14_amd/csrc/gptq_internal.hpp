@@ -120,7 +120,7 @@ constexpr int64_t kPrepareMaxN = 40960;  // one row of H must fit in LDS (160 KB
 
 struct PreparePlan {
   int64_t n = 0, n_pad = 0, nblk = 0;
-  size_t a_off = 0, m_off = 0, lam_off = 0, flag_off = 0, x6_off = 0, total = 0;
+  size_t a_off = 0, m_off = 0, lam_off = 0, flag_off = 0, x6_off = 0, tx6_off = 0, total = 0;
 };
 PreparePlan plan_prepare(int64_t n);
 gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int desc_act,
@@ -226,18 +226,26 @@ __device__ __forceinline__ void x6_split(float x, uint16_t& h, uint16_t& m, uint
   l = (uint16_t)(lb >> 16);
 }
 constexpr int64_t kX6Step = 16;  // k positions per contiguous row piece
-// planes of X[r][k] (r < rows, k < K; zero for K <= k < kp) at out, rows 0..rows-1
+// planes of X[r][k] (r < rows, k < K; zero for K <= k < kp) at out, rows
+// 0..rows-1; lower: X is lower triangular, its entries k > r taken as zero
 gptq_status launch_x6_split_rows(const float* X, int64_t ldx, int64_t rows, int64_t K, int64_t kp,
-                                 uint16_t* out, int64_t pstride, int64_t sst, hipStream_t stream);
-// planes of the transpose of X[k][c] (k < K, c < cols): plane row c holds column c
+                                 uint16_t* out, int64_t pstride, int64_t sst, hipStream_t stream,
+                                 bool lower = false);
+// planes of the transpose of X[k][c] (k < K, c < cols): plane row c holds
+// column c; lower: X is lower triangular, its entries k < c taken as zero
 gptq_status launch_x6_split_cols(const float* X, int64_t ldx, int64_t K, int64_t cols, int64_t kp,
-                                 uint16_t* out, int64_t pstride, int64_t sst, hipStream_t stream);
+                                 uint16_t* out, int64_t pstride, int64_t sst, hipStream_t stream,
+                                 bool lower = false);
+// k range of a full product whose A is triangular (128-row tiles): every
+// k-step; from the tile's first row on (A upper triangular: A[i][k] = 0 for
+// k < i); up to the tile's last row (A lower triangular: A[i][k] = 0 for k > i)
+enum X6KRange { kX6All = 0, kX6FromRow = 1, kX6ToRow = 2 };
 // polite: at most one workgroup per CU, leaving LDS for a latency-bound
 // kernel of another stream (the leaf or the block quantizer) beside it.
 // tile_rows: 128, or 64 (full product only) for products of few tiles.
 gptq_status launch_x6_gemm(const X6Planes& A, const X6Planes& B, float* C, int64_t ldc, int64_t M,
                            int64_t N, float alpha, float beta, bool lower, hipStream_t stream,
-                           bool polite = false, int tile_rows = 128);
+                           bool polite = false, int tile_rows = 128, int krange = kX6All);
 
 // ---------------------------------------------------------------- fp32 MFMA GEMM (shared)
 // C[M,N] = alpha * A[M,K] * B[K,N] + beta * C, A row-major; B row-major or, with

@@ -478,6 +478,19 @@ __global__ __launch_bounds__(256) void flip_kernel(const float* __restrict__ Mm,
 
 }  // namespace
 
+// Triangular-inverse nodes whose halves span at least this many 128-blocks
+// run on bf16 MFMA from exact three-plane splits of their operands (the
+// fp32-accurate product of the trailing updates); smaller ones stay on fp32
+// MFMA, where the splits would cost more than they save.
+constexpr int64_t kTriX6Half = 16;
+
+// Bytes of the planes of one such node: step 1 splits M11ᵀ (h x h blocks) and
+// L21 (r x h), step 2 M22 (r x r) and Tᵀ (h x r), with r <= h.
+size_t tri_x6_bytes(int64_t h, int64_t r) {
+  const int64_t H = h * NB, R = r * NB;
+  return align256((size_t)3 * H * H * sizeof(uint16_t)) + align256((size_t)3 * R * H * sizeof(uint16_t));
+}
+
 PreparePlan plan_prepare(int64_t n) {
   PreparePlan p;
   p.n = n;
@@ -491,7 +504,14 @@ PreparePlan plan_prepare(int64_t n) {
   // bf16 planes of an outer block's panel rows for its trailing update,
   // double-buffered (the far part of one block runs beside the next block)
   p.x6_off = p.flag_off + 256;
-  p.total = p.x6_off + align256((size_t)2 * 3 * p.n_pad * kX6K * sizeof(uint16_t));
+  p.tx6_off = p.x6_off + align256((size_t)2 * 3 * p.n_pad * kX6K * sizeof(uint16_t));
+  // planes of the largest triangular-inverse node on the bf16 path (the
+  // nodes run one after another on one stream and reuse them)
+  size_t tx6 = 0;
+  for (int64_t half = kTriX6Half; half < p.nblk; half *= 2)
+    for (int64_t r0 = half; r0 < p.nblk; r0 += 2 * half)
+      tx6 = std::max(tx6, tri_x6_bytes(half, std::min<int64_t>(r0 + half, p.nblk) - r0));
+  p.total = p.tx6_off + tx6;
   return p;
 }
 
@@ -560,6 +580,34 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
   // parents).  Their writes (T parked in A's strict upper block triangle, M's
   // off-diagonal blocks) touch nothing the factorisation still uses.
   // `solved` is recorded on the caller's stream once panel kb is solved.
+  // A large node as two x6 products from planes split on the same stream:
+  //   step 1: Tᵀ = M11ᵀ · L21ᵀ; row j of M11ᵀ (column j of M11) is zero before
+  //           position j, so a tile of rows from j0 on starts at k = j0;
+  //   step 2: M21 = -M22 · (Tᵀ)ᵀ; row i of M22 ends at position i.
+  // The planes of a node are dead once its product has run, so every node
+  // reuses the same region.
+  uint16_t* const tx6 = reinterpret_cast<uint16_t*>(w + p.tx6_off);
+  auto trtri_x6 = [&](int64_t half, int64_t q, int step) -> gptq_status {
+    const int64_t l0 = q * 2 * half, r0 = l0 + half, r1 = std::min<int64_t>(r0 + half, p.nblk);
+    const int64_t H = half * NB, R = (r1 - r0) * NB;
+    float* const Tt = A + l0 * NB * lda + r0 * NB;   // Tᵀ, H x R, in A's strict upper block triangle
+    if (step == 1) {
+      uint16_t* const pb = tx6 + align256((size_t)3 * H * H * sizeof(uint16_t)) / sizeof(uint16_t);
+      GPTQ_TRY(launch_x6_split_cols(Mm + l0 * NB * lda + l0 * NB, lda, H, H, H, tx6, H * H, H * kX6Step,
+                                    tri.stream, /*lower=*/true));
+      GPTQ_TRY(launch_x6_split_rows(A + r0 * NB * lda + l0 * NB, lda, R, H, H, pb, R * H, R * kX6Step,
+                                    tri.stream));
+      const X6Planes PA{tx6, H, H, H * H, H * kX6Step}, PB{pb, R, H, R * H, R * kX6Step};
+      return launch_x6_gemm(PA, PB, Tt, lda, H, R, 1.f, 0.f, false, tri.stream, false, NB, kX6FromRow);
+    }
+    uint16_t* const pb = tx6 + align256((size_t)3 * R * R * sizeof(uint16_t)) / sizeof(uint16_t);
+    GPTQ_TRY(launch_x6_split_rows(Mm + r0 * NB * lda + r0 * NB, lda, R, R, R, tx6, R * R, R * kX6Step,
+                                  tri.stream, /*lower=*/true));
+    GPTQ_TRY(launch_x6_split_rows(Tt, lda, H, R, R, pb, H * R, H * kX6Step, tri.stream));
+    const X6Planes PA{tx6, R, R, R * R, R * kX6Step}, PB{pb, H, R, H * R, H * kX6Step};
+    return launch_x6_gemm(PA, PB, Mm + r0 * NB * lda + l0 * NB, lda, R, H, -1.f, 0.f, false, tri.stream, false,
+                          NB, kX6ToRow);
+  };
   auto issue_trtri = [&](int64_t kb, hipEvent_t solved) -> gptq_status {
     bool waited = false;
     for (int64_t half = 1; half < p.nblk; half *= 2) {
@@ -572,7 +620,11 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
             GPTQ_HIP_CHECK(hipStreamWaitEvent(tri.stream, solved, 0));
             waited = true;
           }
-          GPTQ_TRY(launch_trtri_nodes(A, Mm, lda, p.nblk, half, q, 1, step, tri.stream));
+          if (half >= kTriX6Half) {
+            GPTQ_TRY(trtri_x6(half, q, step));
+          } else {
+            GPTQ_TRY(launch_trtri_nodes(A, Mm, lda, p.nblk, half, q, 1, step, tri.stream));
+          }
           tri_pending = true;
         }
       }

@@ -124,10 +124,12 @@ def test_hessian_accumulates_over_calls_and_is_deterministic(pq):
 # and full-size case; the bounds are about ten times that.
 U_REL_FROB = 2e-6
 UHU_MAX = 1e-5
-# n_pad / 128 = 1, 2, 3, 4, 8, 12, 13 blocks (trees of the blocked inverse
-# with a top join of 1, 2, 2, 4, 4, 8 and 8 blocks over 1 .. 5 on its right)
+# n_pad / 128 = 1, 2, 3, 4, 8, 12, 13, 18, 33 blocks (trees of the blocked
+# inverse with a top join of 1, 2, 2, 4, 4, 8, 8, 16 and 32 blocks over 1 .. 5
+# on its right); the last two take joins of 16 and 32 blocks a side through
+# the bf16-plane products
 PREPARE_CASES = [(128, True), (200, True), (256, False), (384, True), (500, True), (1000, True), (1, True),
-                 (1500, True), (1600, False)]
+                 (1500, True), (1600, False), (2300, True), (4200, False)]
 
 
 @pytest.mark.parametrize("n,desc", PREPARE_CASES, ids=lambda v: str(v))
