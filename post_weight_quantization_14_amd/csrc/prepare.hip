@@ -480,9 +480,9 @@ __global__ __launch_bounds__(256) void flip_kernel(const float* __restrict__ Mm,
 
 // Triangular-inverse nodes whose halves span at least this many 128-blocks
 // run on bf16 MFMA from exact three-plane splits of their operands (the
-// fp32-accurate product of the trailing updates); smaller ones stay on fp32
-// MFMA, where the splits would cost more than they save.
-constexpr int64_t kTriX6Half = 16;
+// fp32-accurate product of the trailing updates); the joins of single and
+// paired blocks stay on fp32 MFMA (one launch each instead of three).
+constexpr int64_t kTriX6Half = 4;
 
 // Bytes of the planes of one such node: step 1 splits M11ᵀ (h x h blocks) and
 // L21 (r x h), step 2 M22 (r x r) and Tᵀ (h x r), with r <= h.

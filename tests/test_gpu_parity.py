@@ -126,8 +126,8 @@ U_REL_FROB = 2e-6
 UHU_MAX = 1e-5
 # n_pad / 128 = 1, 2, 3, 4, 8, 12, 13, 18, 33 blocks (trees of the blocked
 # inverse with a top join of 1, 2, 2, 4, 4, 8, 8, 16 and 32 blocks over 1 .. 5
-# on its right); the last two take joins of 16 and 32 blocks a side through
-# the bf16-plane products
+# on its right); from 8 blocks on, joins of 4 or more blocks a side run
+# through the bf16-plane products, below that on fp32 MFMA only
 PREPARE_CASES = [(128, True), (200, True), (256, False), (384, True), (500, True), (1000, True), (1, True),
                  (1500, True), (1600, False), (2300, True), (4200, False)]
 
