@@ -392,6 +392,28 @@ def measure_w4a16(pq, torch, out, m, n, bits, group_size, reps=200):
                          "algorithmic_bytes_per_call": nbytes}}
         log(f"bench: w4a16 {m}x{n} tokens {tokens}: {us:.2f} us ({gbs:.0f} GB/s), "
             f"bf16 matmul {us_bf16:.2f} us, speedup {us_bf16 / us:.2f}x")
+    # the same output exported to the GPTQ-checkpoint tensors (qweight
+    # [n·b/32, m], qzeros [G, m·b/32], fp16 scales [G, m]): read the
+    # quantizer's words, scales and zeros once, write the three tensors once
+    for _ in range(10):
+        pq.gptq_export_checkpoint(out["qweight"], out["scales"], out["zeros"], n, bits, group_size)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        pq.gptq_export_checkpoint(out["qweight"], out["scales"], out["zeros"], n, bits, group_size)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    words = pq.gptq_qweight_words(n, bits)
+    nbytes = (m * words * 4 + m * groups * 8 + pq.gptq_checkpoint_qweight_rows(n, bits) * m * 4
+              + groups * pq.gptq_checkpoint_qzeros_words(m, bits) * 4 + groups * m * 2)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    res["checkpoint_export"] = {
+        "us": us,
+        "roofline": {"bound": "hbm", "kernel": "ck_qweight_kernel + ck_params_kernel", "achieved": gbs,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                     "algorithmic_bytes_per_call": nbytes}}
+    log(f"bench: checkpoint export {m}x{n}: {us:.2f} us ({gbs:.0f} GB/s)")
     return res
 
 

@@ -318,6 +318,37 @@ gptq_status gptq_w4a16_matmul_noalloc(const void* X, int64_t tokens, int64_t ldx
                                       int64_t m, int64_t n, int32_t group_size, float* Y, int64_t ldy,
                                       void* stream);
 
+/* ------------------------------------------------------------------------
+ * Export of a quantized layer to the tensor layout of GPTQ checkpoints.
+ * Page "模型量化实战：从 INT8 PTQ 到 GPTQ…" §3.3 saves the quantized model as
+ * a GPTQ checkpoint (about 4.1 GB for 7B) but does not define its tensors;
+ * the layout here is the one such checkpoints commonly carry, defined as bit
+ * streams (b = bits; "the bit stream" of a list of codes puts code k in bits
+ * [k·b, k·b + b) of consecutive little-endian 32-bit words, padding bits 0):
+ *
+ *   qweight, scales, zeros  gptq_quantize_layer's (or gptq_rtn_quantize's)
+ *            outputs for an m x n weight with this bits and group_size;
+ *            only the low b bits of each code field are read.
+ *   zero_offset  0: zero points stored as they are; 1: stored as zero - 1
+ *            (the older checkpoints' convention).  Values are kept mod 2^b.
+ * Outputs (device, caller-owned, all fully written):
+ *   ck_qweight [gptq_checkpoint_qweight_rows(n, bits)][m] int32: column i is
+ *            the bit stream of output row i's n codes in input order.
+ *   ck_qzeros  [G][gptq_checkpoint_qzeros_words(m, bits)] int32: row g is the
+ *            bit stream of (zeros[i][g] - zero_offset) mod 2^b over i.
+ *   ck_scales  [G][m] IEEE fp16 (uint16 bits): scales[i][g] rounded to
+ *            nearest even (overflow to infinity, subnormals kept).
+ * g_idx is the quantizer's own, unchanged.  G = gptq_num_groups(n,
+ * group_size).  Stream-ordered, no synchronisation, no workspace.  m == 0 or
+ * n == 0 is a no-op.  Returns GPTQ_ERR_UNSUPPORTED for bits outside
+ * {2, 3, 4, 8} or more than 65535 groups or 4194240 rows.
+ * ---------------------------------------------------------------------- */
+int64_t gptq_checkpoint_qweight_rows(int64_t n, int32_t bits);
+int64_t gptq_checkpoint_qzeros_words(int64_t m, int32_t bits);
+gptq_status gptq_export_checkpoint(const uint32_t* qweight, const float* scales, const int32_t* zeros,
+                                   int64_t m, int64_t n, int32_t bits, int32_t group_size, int32_t zero_offset,
+                                   int32_t* ck_qweight, int32_t* ck_qzeros, uint16_t* ck_scales, void* stream);
+
 /* Sizes of the outputs above (host-only helpers, no GPU work). */
 int64_t gptq_qweight_words(int64_t n, int32_t bits);
 int64_t gptq_num_groups(int64_t n, int32_t group_size);

@@ -47,3 +47,14 @@ from .awq import (  # noqa: F401,E402
     channel_scale,
     lower_median,
 )
+from .checkpoint import (  # noqa: F401,E402
+    bit_stream_codes,
+    bit_stream_words,
+    checkpoint_qweight_rows,
+    checkpoint_qzeros_words,
+    export_checkpoint,
+    export_qweight_columns,
+    export_qzeros,
+    export_scales,
+    import_checkpoint,
+)

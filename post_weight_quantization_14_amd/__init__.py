@@ -14,6 +14,9 @@ from .gptq import (  # noqa: F401
     gptq_awq_quantize,
     gptq_awq_stats_workspace_bytes,
     gptq_awq_workspace_bytes,
+    gptq_checkpoint_qweight_rows,
+    gptq_checkpoint_qzeros_words,
+    gptq_export_checkpoint,
     gptq_hessian_accumulate,
     gptq_hessian_workspace_bytes,
     gptq_last_error,

@@ -66,6 +66,9 @@ SIGNATURES = {
     "gptq_w4a16_matmul": (_ST, [_P, _I64, _I64, _P, _I64, _I64, _I32, _P, _I64, _P, _SZ, _P]),
     "gptq_w4a16_noalloc_scratch_bytes": (_SZ, []),
     "gptq_w4a16_matmul_noalloc": (_ST, [_P, _I64, _I64, _P, _I64, _I64, _I32, _P, _I64, _P]),
+    "gptq_checkpoint_qweight_rows": (_I64, [_I64, _I32]),
+    "gptq_checkpoint_qzeros_words": (_I64, [_I64, _I32]),
+    "gptq_export_checkpoint": (_ST, [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P]),
     "gptq_qweight_words": (_I64, [_I64, _I32]),
     "gptq_num_groups": (_I64, [_I64, _I32]),
     "gptq_last_error": (ctypes.c_char_p, []),

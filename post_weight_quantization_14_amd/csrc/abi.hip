@@ -331,6 +331,38 @@ gptq_status gptq_w4a16_pack(const uint32_t* qweight, const float* scales, const 
                         static_cast<hipStream_t>(stream));
 }
 
+int64_t gptq_checkpoint_qweight_rows(int64_t n, int32_t bits) {
+  if (n < 0 || !(bits == 2 || bits == 3 || bits == 4 || bits == 8)) return -1;
+  return ceil_div(n * bits, 32);
+}
+
+int64_t gptq_checkpoint_qzeros_words(int64_t m, int32_t bits) {
+  if (m < 0 || !(bits == 2 || bits == 3 || bits == 4 || bits == 8)) return -1;
+  return ceil_div(m * bits, 32);
+}
+
+gptq_status gptq_export_checkpoint(const uint32_t* qweight, const float* scales, const int32_t* zeros,
+                                   int64_t m, int64_t n, int32_t bits, int32_t group_size, int32_t zero_offset,
+                                   int32_t* ck_qweight, int32_t* ck_qzeros, uint16_t* ck_scales, void* stream) {
+  clear_error();
+  if (m < 0 || n < 0) return fail(GPTQ_ERR_INVALID_ARG, "m=%lld n=%lld", (long long)m, (long long)n);
+  if (!(bits == 2 || bits == 3 || bits == 4 || bits == 8))
+    return fail(GPTQ_ERR_UNSUPPORTED, "bits=%d (2, 3, 4 or 8)", bits);
+  if (zero_offset != 0 && zero_offset != 1) return fail(GPTQ_ERR_INVALID_ARG, "zero_offset=%d (0 or 1)", zero_offset);
+  const int64_t G = gptq_num_groups(n, group_size);
+  if (G < 0) return fail(GPTQ_ERR_INVALID_ARG, "group_size=%d", group_size);
+  if (m == 0 || n == 0) return GPTQ_OK;
+  if (m > 65535LL * 64 || G > 65535 || n > ((int64_t)1 << 40))
+    return fail(GPTQ_ERR_UNSUPPORTED, "m=%lld n=%lld (%lld groups) too large", (long long)m, (long long)n,
+                (long long)G);
+  if (bad_ptr(qweight, 4) || bad_ptr(scales, 4) || bad_ptr(zeros, 4))
+    return fail(GPTQ_ERR_INVALID_ARG, "an input pointer is NULL or misaligned");
+  if (bad_ptr(ck_qweight, 4) || bad_ptr(ck_qzeros, 4) || bad_ptr(ck_scales, 2))
+    return fail(GPTQ_ERR_INVALID_ARG, "an output pointer is NULL or misaligned");
+  return run_checkpoint_export(qweight, scales, zeros, m, n, bits, G, zero_offset, ck_qweight, ck_qzeros,
+                               ck_scales, static_cast<hipStream_t>(stream));
+}
+
 size_t gptq_w4a16_workspace_bytes(int64_t tokens, int64_t m, int64_t n) {
   if (tokens < 0 || m < 0 || n < 0) return 0;
   return plan_w4a16_gemm(tokens, m, n).total;

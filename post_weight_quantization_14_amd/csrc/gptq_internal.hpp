@@ -275,4 +275,11 @@ gptq_status launch_gemm_lower(const GemmArgs& g, bool b_colmajor, hipStream_t st
 gptq_status launch_trtri_nodes(float* Amat, float* Mmat, int64_t lda, int64_t nblk, int64_t half,
                                int64_t p0, int64_t count, int step, hipStream_t stream);
 
+// Export to the checkpoint tensor layout (checkpoint.hip): qweight
+// [ceil(n·bits/32)][m], qzeros [G][ceil(m·bits/32)] int32 bit streams,
+// scales [G][m] fp16.  Arguments checked by the caller.
+gptq_status run_checkpoint_export(const uint32_t* qweight, const float* scales, const int32_t* zeros, int64_t m,
+                                  int64_t n, int bits, int64_t G, int zero_offset, int32_t* ck_qweight,
+                                  int32_t* ck_qzeros, uint16_t* ck_scales, hipStream_t stream);
+
 }  // namespace gptq

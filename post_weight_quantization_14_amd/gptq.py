@@ -327,6 +327,36 @@ def gptq_w4a16_pack(qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Te
     return packed
 
 
+def gptq_checkpoint_qweight_rows(n: int, bits: int) -> int:
+    return int(lib().gptq_checkpoint_qweight_rows(n, bits))
+
+
+def gptq_checkpoint_qzeros_words(m: int, bits: int) -> int:
+    return int(lib().gptq_checkpoint_qzeros_words(m, bits))
+
+
+def gptq_export_checkpoint(qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, n: int,
+                           bits: int, group_size: int, zero_offset: int = 0, stream=None) -> dict:
+    """The quantizer's output of an m x n weight -> the checkpoint tensors
+    {"qweight": int32 [ceil(n·bits/32), m], "qzeros": int32 [G, ceil(m·bits/32)],
+    "scales": float16 [G, m]} (g_idx is the quantizer's own)."""
+    m = qweight.shape[0]
+    G = gptq_num_groups(n, group_size)
+    rows = gptq_checkpoint_qweight_rows(n, bits)
+    zw = gptq_checkpoint_qzeros_words(m, bits)
+    if G < 0 or rows < 0 or zw < 0:
+        raise ValueError(f"bits={bits} group_size={group_size} n={n}")
+    dev = qweight.device
+    out = {"qweight": torch.empty(rows, m, dtype=torch.int32, device=dev),
+           "qzeros": torch.empty(G, zw, dtype=torch.int32, device=dev),
+           "scales": torch.empty(G, m, dtype=torch.float16, device=dev)}
+    st = lib().gptq_export_checkpoint(_ptr(qweight), _ptr(scales), _ptr(zeros), m, n, bits, group_size,
+                                      zero_offset, _ptr(out["qweight"]), _ptr(out["qzeros"]),
+                                      _ptr(out["scales"]), _stream(stream))
+    _check(st, "gptq_export_checkpoint")
+    return out
+
+
 def gptq_w4a16_workspace_bytes(tokens: int, m: int, n: int) -> int:
     return int(lib().gptq_w4a16_workspace_bytes(tokens, m, n))
 
