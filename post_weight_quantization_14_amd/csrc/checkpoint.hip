@@ -23,7 +23,7 @@
 // The tile starts at code 256·x (b <= 4) or 128·x (b = 8), a multiple of 32
 // codes, so it maps to whole output words; for 4- and 8-bit codes the input
 // words are the output words and the kernel is a transpose.  params kernel:
-// 32 rows x 128 groups per workgroup through LDS (coalesced reads of each
+// 32 rows x 32 groups per workgroup through LDS (coalesced reads of each
 // row's run of groups): fp16 scales, and the zeros' bit streams.
 #include "gptq_internal.hpp"
 
@@ -34,7 +34,7 @@ constexpr int kCkRows = 64;    // input rows (output columns) per qweight tile
 constexpr int kCkWords = 32;   // input words per qweight tile
 constexpr int kCkThreads = 256;
 constexpr int kPrRows = 32;    // rows per params tile (32·b bits: b whole qzeros words)
-constexpr int kPrGroups = 128; // groups per params tile
+constexpr int kPrGroups = 32;  // groups per params tile (m/32 x G/32 workgroups)
 
 // Bits [32·ow, 32·ow + 32) of a stream whose code c is field(c).
 template <int B, typename F>
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kCkThreads) void ck_qweight_kernel(const uint32_t* 
   }
 }
 
-// One workgroup per 32 rows x 128 groups: the rows' scales and zero points
+// One workgroup per 32 rows x 32 groups: the rows' scales and zero points
 // (contiguous runs of each row) through LDS, then fp16 scales [g][i] and the
 // zero points' b words per group.
 template <int B>
