@@ -467,13 +467,32 @@ __global__ __launch_bounds__(kLeafThreads) void chol_leaf_kernel(float* A, float
   }
 }
 
-// U[a][b] = M[n-1-a][n-1-b] for a <= b, 0 below the diagonal.
+// U[a][b] = M[n-1-a][n-1-b] for a <= b, 0 below the diagonal.  Four
+// consecutive b per thread: with vec (n % 4 == 0 and 16-byte aligned U and M;
+// M's rows are padded to 128) one 16-byte load of M's row n-1-a read back to
+// front and one 16-byte store; a piece wholly below the diagonal stores
+// zeros without reading M.
 __global__ __launch_bounds__(256) void flip_kernel(const float* __restrict__ Mm, int64_t lda,
-                                                   int64_t n, float* __restrict__ U) {
+                                                   int64_t n, float* __restrict__ U, int vec) {
   const int64_t a = blockIdx.y;
-  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (b >= n) return;
-  U[a * n + b] = (a <= b) ? Mm[(n - 1 - a) * lda + (n - 1 - b)] : 0.f;
+  const int64_t b0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (b0 >= n) return;
+  const float* mrow = Mm + (n - 1 - a) * lda;
+  if (vec) {
+    f32x4_t out = {0.f, 0.f, 0.f, 0.f};
+    if (b0 + 3 >= a) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(mrow + (n - 4 - b0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e] = (b0 + e >= a) ? v[3 - e] : 0.f;
+    }
+    *reinterpret_cast<f32x4_t*>(U + a * n + b0) = out;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t b = b0 + e;
+      if (b < n) U[a * n + b] = (a <= b) ? mrow[n - 1 - b] : 0.f;
+    }
+  }
 }
 
 }  // namespace
@@ -740,8 +759,10 @@ gptq_status run_prepare(float* H, const double* key, int64_t n, double damp, int
     GPTQ_HIP_CHECK(hipStreamWaitEvent(stream, tri.done, 0));
   }
   join.release();
-  hipLaunchKernelGGL(flip_kernel, dim3((unsigned)ceil_div(n, 256), (unsigned)n), dim3(256), 0,
-                     stream, (const float*)Mm, lda, n, H);
+  const int flip_vec = (n % 4 == 0) && (reinterpret_cast<uintptr_t>(H) % 16 == 0) &&
+                       (reinterpret_cast<uintptr_t>(Mm) % 16 == 0) && (lda % 4 == 0);
+  hipLaunchKernelGGL(flip_kernel, dim3((unsigned)ceil_div(n, 1024), (unsigned)n), dim3(256), 0,
+                     stream, (const float*)Mm, lda, n, H, flip_vec);
   GPTQ_LAUNCH_CHECK();
 
   int hflag = 0;
